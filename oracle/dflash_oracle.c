@@ -1,0 +1,489 @@
+/* DFlash 2 block drafter -- CPU oracle (TEST INFRASTRUCTURE ONLY; see dflash_oracle.h).
+ *
+ * Sources: the docs.rs source pages of the Rust crate cortiq-engine --
+ *   "dflash.rs" (0.8.71): the module header (the method in brief), fn rms, Drafter::new
+ *   (inv_freq), Drafter::rotate, Drafter::mlp, Drafter::queue_context / truncate / reset,
+ *   Drafter::settle_rows (context append), Drafter::block (the block forward);
+ *   "gpu_wgpu/dflash_dev.rs" (0.8.75): the module header (the device block keeps the host
+ *   block's f32 arithmetic), Dev::q4 (int8 activations per group of 32).
+ * Readings where those pages are silent (formats, the activation quantizer, which rows get
+ * logits, eps/theta) are this project's contract, restated at each function.
+ *
+ * Precision: f64 inside every step, f32 storage between steps (the pages keep f32 buffers),
+ * except where the pages fix the arithmetic: RMSNorm's scale and products (fn rms), the RoPE
+ * angle (Drafter::rotate), the attention scale (Drafter::block) and the activation quantizer's
+ * f32 decisions.  Built without fast-math and with fp-contract off, so every expression is
+ * rounded as written.
+ */
+#include "dflash_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int g_threads = 1;
+
+void og_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int og_get_threads(void) { return g_threads; }
+
+/* IEEE 754 binary16 -> value, from the format's definition (sign, 5-bit biased exponent,
+ * 10-bit fraction; exponent 0 subnormal, 31 inf/nan). */
+double og_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1, e = (h >> 10) & 31, f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
+/* dflash.rs, Drafter::new: inv_freq[i] = theta^(-2i/hd) evaluated in f64, stored f32. */
+void og_inv_freq(double theta, int head_dim, float* out) {
+  for (int i = 0; i < head_dim / 2; i++) out[i] = (float)pow(theta, -(2.0 * i) / (double)head_dim);
+}
+
+/* dflash.rs, fn rms: mean of squares accumulated in f64; s = 1/sqrt(f32(ms) + eps) in f32;
+ * each element (x * s) * w in f32. */
+void og_rmsnorm_row(const float* x, const float* w, int n, float eps, float* y) {
+  double ms = 0.0;
+  for (int i = 0; i < n; i++) ms += (double)x[i] * (double)x[i];
+  ms /= (double)n;
+  float s = 1.0f / sqrtf((float)ms + eps);
+  for (int i = 0; i < n; i++) {
+    float t = x[i] * s;
+    y[i] = t * w[i];
+  }
+}
+
+/* dflash.rs, Drafter::rotate: half-split pairs (i, i + hd/2); the angle is the f32 product
+ * f32(pos) * inv_freq[i]; lo' = a cos - b sin, hi' = b cos + a sin.  cos/sin and the rotation
+ * are evaluated in f64 on that f32 angle. */
+void og_rope_head(float* x, int head_dim, int64_t pos, const float* inv_freq) {
+  int half = head_dim / 2;
+  float p = (float)pos;
+  for (int i = 0; i < half; i++) {
+    float ang = p * inv_freq[i];
+    double c = cos((double)ang), s = sin((double)ang);
+    double a = x[i], b = x[i + half];
+    x[i] = (float)(a * c - b * s);
+    x[i + half] = (float)(b * c + a * s);
+  }
+}
+
+/* Activations before a quantized matrix: int8 per row and group of 32 consecutive columns
+ * (gpu_wgpu/dflash_dev.rs, Dev::q4: "int8 activations", 32 codes plus side data per group).
+ * The pages give no rounding rule, so this is the contract: amax = max |x| of the group;
+ * d = amax / 127 and inv = 127 / amax as f32 divisions; q = clamp(rint(x * inv), -127, 127)
+ * with the f32 product rounded to nearest even; a zero group has d = 0 and q = 0. */
+void og_quant_act_row(const float* x, int n, int8_t* q, float* d) {
+  for (int g = 0; g < n / 32; g++) {
+    const float* xs = x + 32 * g;
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++) {
+      float a = fabsf(xs[i]);
+      if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+      d[g] = 0.0f;
+      for (int i = 0; i < 32; i++) q[32 * g + i] = 0;
+      continue;
+    }
+    d[g] = amax / 127.0f;
+    float inv = 127.0f / amax;
+    for (int i = 0; i < 32; i++) {
+      float t = xs[i] * inv;
+      float r = nearbyintf(t); /* default rounding mode: to nearest, ties to even */
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
+      q[32 * g + i] = (int8_t)r;
+    }
+  }
+}
+
+/* the integer code of column k of row r */
+static int code_at(int fmt, og_matrix w, int cols, int r, int k) {
+  if (fmt == OG_Q8_32) return ((const int8_t*)w.codes)[(size_t)r * cols + k];
+  uint8_t b = ((const uint8_t*)w.codes)[(size_t)r * (cols / 2) + k / 2];
+  int nib = (k & 1) ? (b >> 4) : (b & 15);
+  return nib >= 8 ? nib - 16 : nib;
+}
+
+/* Quantized matrix times A8_32 activations: for each group, s = sum q_w * q_x exactly; then
+ * y = sum over groups of f16(d_w) * d_x * s, accumulated in f64 and rounded once. */
+void og_matmul_q(int fmt, og_matrix w, int rows, int cols, const int8_t* xq, const float* dx, int m, float* y) {
+  int groups = cols / 32;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int r = 0; r < rows; r++) {
+    int8_t* wr = (int8_t*)malloc((size_t)cols);
+    double* dw = (double*)malloc(sizeof(double) * (size_t)groups);
+    for (int k = 0; k < cols; k++) wr[k] = (int8_t)code_at(fmt, w, cols, r, k);
+    for (int g = 0; g < groups; g++) dw[g] = og_f16_to_f64(w.scales[(size_t)r * groups + g]);
+    for (int i = 0; i < m; i++) {
+      const int8_t* xr = xq + (size_t)i * cols;
+      double acc = 0.0;
+      for (int g = 0; g < groups; g++) {
+        int s = 0;
+        for (int k = 32 * g; k < 32 * g + 32; k++) s += (int)wr[k] * (int)xr[k];
+        acc += dw[g] * (double)dx[(size_t)i * groups + g] * (double)s;
+      }
+      y[(size_t)i * rows + r] = (float)acc;
+    }
+    free(dw);
+    free(wr);
+  }
+}
+
+void og_group_sums(int fmt, og_matrix w, int rows, int cols, const int8_t* xq, int m, int32_t* s) {
+  int groups = cols / 32;
+  for (int i = 0; i < m; i++)
+    for (int r = 0; r < rows; r++)
+      for (int g = 0; g < groups; g++) {
+        int acc = 0;
+        for (int k = 32 * g; k < 32 * g + 32; k++) acc += code_at(fmt, w, cols, r, k) * (int)xq[(size_t)i * cols + k];
+        s[((size_t)i * rows + r) * groups + g] = acc;
+      }
+}
+
+void og_matmul_f32(const float* w, int rows, int cols, const float* x, int m, float* y) {
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int r = 0; r < rows; r++) {
+    const float* wr = w + (size_t)r * cols;
+    for (int i = 0; i < m; i++) {
+      const float* xr = x + (size_t)i * cols;
+      double acc = 0.0;
+      for (int k = 0; k < cols; k++) acc += (double)wr[k] * (double)xr[k];
+      y[(size_t)i * rows + r] = (float)acc;
+    }
+  }
+}
+
+/* dflash.rs, Drafter::block (the per-head scores, softmax and values): s = (q . k) * scale,
+ * p = exp(s - max) / sum, y = sum p v; in f64. */
+void og_attend(const float* q, int nq, const float* k, const float* v, int nk, int head_dim, float scale,
+               float* y, double* p) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+  for (int i = 0; i < nq; i++) {
+    const float* qi = q + (size_t)i * head_dim;
+    double top = -INFINITY;
+    for (int j = 0; j < nk; j++) {
+      double dot = 0.0;
+      for (int d = 0; d < head_dim; d++) dot += (double)qi[d] * (double)k[(size_t)j * head_dim + d];
+      s[j] = dot * (double)scale;
+      if (s[j] > top) top = s[j];
+    }
+    double sum = 0.0;
+    for (int j = 0; j < nk; j++) {
+      s[j] = exp(s[j] - top);
+      sum += s[j];
+    }
+    for (int j = 0; j < nk; j++) {
+      s[j] /= sum;
+      if (p) p[(size_t)i * nk + j] = s[j];
+    }
+    for (int d = 0; d < head_dim; d++) {
+      double acc = 0.0;
+      for (int j = 0; j < nk; j++) acc += s[j] * (double)v[(size_t)j * head_dim + d];
+      y[(size_t)i * head_dim + d] = (float)acc;
+    }
+  }
+  free(s);
+}
+
+/* dflash.rs, Drafter::mlp: a = g / (1 + e^-g) * u, in f64, stored f32. */
+void og_silu_mul(const float* g, const float* u, int n, float* a) {
+  for (int i = 0; i < n; i++) {
+    double gv = g[i];
+    a[i] = (float)(gv / (1.0 + exp(-gv)) * (double)u[i]);
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t first, len;
+  float* k; /* [layers][max_ctx][kv_heads][head_dim] */
+  float* v;
+} og_seq;
+
+struct og_model {
+  og_geometry g;
+  og_weights w;
+  og_layer* layers;
+  float* inv_freq;
+  og_seq* seqs;
+};
+
+static size_t seq_floats(const og_geometry* g) {
+  return (size_t)g->layers * (size_t)g->max_ctx * (size_t)g->kv_heads * (size_t)g->head_dim;
+}
+
+og_model* og_create(const og_geometry* g, const og_weights* w) {
+  if (!g || !w || g->layers <= 0 || g->block < 1 || g->kv_heads <= 0 || g->heads % g->kv_heads ||
+      g->head_dim % 2 || g->max_seqs <= 0 || g->max_ctx < 0)
+    return NULL;
+  og_model* m = (og_model*)calloc(1, sizeof(og_model));
+  m->g = *g;
+  m->w = *w;
+  m->layers = (og_layer*)malloc(sizeof(og_layer) * (size_t)g->layers);
+  memcpy(m->layers, w->layer, sizeof(og_layer) * (size_t)g->layers);
+  m->w.layer = m->layers;
+  m->inv_freq = (float*)malloc(sizeof(float) * (size_t)(g->head_dim / 2));
+  og_inv_freq(g->rope_theta, g->head_dim, m->inv_freq);
+  m->seqs = (og_seq*)calloc((size_t)g->max_seqs, sizeof(og_seq));
+  for (int s = 0; s < g->max_seqs; s++) {
+    m->seqs[s].k = (float*)calloc(seq_floats(g) ? seq_floats(g) : 1, sizeof(float));
+    m->seqs[s].v = (float*)calloc(seq_floats(g) ? seq_floats(g) : 1, sizeof(float));
+  }
+  return m;
+}
+
+void og_destroy(og_model* m) {
+  if (!m) return;
+  for (int s = 0; s < m->g.max_seqs; s++) {
+    free(m->seqs[s].k);
+    free(m->seqs[s].v);
+  }
+  free(m->seqs);
+  free(m->inv_freq);
+  free(m->layers);
+  free(m);
+}
+
+/* y[n][rows] = W . x[n] with x f32: A8_32 first when W is quantized */
+static void mm(int fmt, og_matrix w, int rows, int cols, const float* x, int n, float* y) {
+  if (fmt == OG_F32) {
+    og_matmul_f32((const float*)w.codes, rows, cols, x, n, y);
+    return;
+  }
+  int8_t* xq = (int8_t*)malloc((size_t)n * cols);
+  float* dx = (float*)malloc(sizeof(float) * (size_t)n * (cols / 32));
+  for (int i = 0; i < n; i++) og_quant_act_row(x + (size_t)i * cols, cols, xq + (size_t)i * cols, dx + (size_t)i * (cols / 32));
+  og_matmul_q(fmt, w, rows, cols, xq, dx, n, y);
+  free(dx);
+  free(xq);
+}
+
+/* dflash.rs, Drafter::queue_context and Drafter::truncate: a position inside the held span
+ * replaces it and what follows; a gap, or a position before the first, starts over there. */
+int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
+  const og_geometry* g = &m->g;
+  if (seq < 0 || seq >= g->max_seqs || pos < 0 || n < 0 || (n > 0 && !taps)) return -1;
+  og_seq* s = &m->seqs[seq];
+  int64_t first = s->first, len = s->len;
+  if (pos > first + len || pos < first) {
+    first = pos;
+    len = 0;
+  } else {
+    len = pos - first;
+  }
+  if (len + n > g->max_ctx) return -2;
+  s->first = first;
+  s->len = len;
+  if (n == 0) return 0;
+  /* dflash.rs, Drafter::settle_rows: t = rms(FC . taps, hidden_norm); every layer's k, v of t;
+   * k = rotate(rms(k, k_norm), position); then the rows are kept. */
+  const int H = g->hidden, T = g->n_taps * g->hidden, kvh = g->kv_heads, hd = g->head_dim, kvd = kvh * hd;
+  float* t = (float*)malloc(sizeof(float) * (size_t)n * H);
+  float* tn = (float*)malloc(sizeof(float) * (size_t)n * H);
+  float* k = (float*)malloc(sizeof(float) * (size_t)n * kvd);
+  float* v = (float*)malloc(sizeof(float) * (size_t)n * kvd);
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)hd);
+  mm(g->fc_fmt, m->w.fc, H, T, taps, n, t);
+  for (int i = 0; i < n; i++) og_rmsnorm_row(t + (size_t)i * H, m->w.hidden_norm, H, (float)g->eps, tn + (size_t)i * H);
+  for (int l = 0; l < g->layers; l++) {
+    const og_layer* L = &m->layers[l];
+    mm(g->body_fmt, L->k, kvd, H, tn, n, k);
+    mm(g->body_fmt, L->v, kvd, H, tn, n, v);
+    for (int i = 0; i < n; i++) {
+      int64_t p = pos + i;
+      size_t row = (size_t)(p - s->first);
+      for (int h = 0; h < kvh; h++) {
+        float* kh = k + (size_t)i * kvd + (size_t)h * hd;
+        og_rmsnorm_row(kh, L->k_norm, hd, (float)g->eps, tmp);
+        og_rope_head(tmp, hd, p, m->inv_freq);
+        size_t off = (((size_t)l * g->max_ctx + row) * kvh + h) * hd;
+        memcpy(s->k + off, tmp, sizeof(float) * hd);
+        memcpy(s->v + off, v + (size_t)i * kvd + (size_t)h * hd, sizeof(float) * hd);
+      }
+    }
+  }
+  s->len = len + n;
+  free(tmp);
+  free(v);
+  free(k);
+  free(tn);
+  free(t);
+  return 0;
+}
+
+/* dflash.rs, Drafter::truncate: keep positions before pos (the first stays). */
+int og_ctx_truncate(og_model* m, int seq, int64_t pos) {
+  if (seq < 0 || seq >= m->g.max_seqs || pos < 0) return -1;
+  og_seq* s = &m->seqs[seq];
+  int64_t keep = pos - s->first;
+  if (keep < 0) keep = 0;
+  if (keep > s->len) keep = s->len;
+  s->len = keep;
+  return 0;
+}
+
+/* dflash.rs, Drafter::reset */
+int og_ctx_reset(og_model* m, int seq) {
+  if (seq < 0 || seq >= m->g.max_seqs) return -1;
+  m->seqs[seq].len = 0;
+  m->seqs[seq].first = 0;
+  return 0;
+}
+
+int og_ctx_span(const og_model* m, int seq, int64_t* first, int64_t* end) {
+  if (seq < 0 || seq >= m->g.max_seqs) return -1;
+  *first = m->seqs[seq].first;
+  *end = m->seqs[seq].first + m->seqs[seq].len;
+  return 0;
+}
+
+int og_read_kv(const og_model* m, int layer, int seq, int row0, int n, float* k, float* v) {
+  const og_geometry* g = &m->g;
+  if (layer < 0 || layer >= g->layers || seq < 0 || seq >= g->max_seqs || row0 < 0 || n < 0 || row0 + n > g->max_ctx)
+    return -1;
+  size_t per = (size_t)g->kv_heads * g->head_dim;
+  size_t off = ((size_t)layer * g->max_ctx + (size_t)row0) * per;
+  memcpy(k, m->seqs[seq].k + off, sizeof(float) * per * (size_t)n);
+  memcpy(v, m->seqs[seq].v + off, sizeof(float) * per * (size_t)n);
+  return 0;
+}
+
+/* dflash.rs, Drafter::block, for one sequence: rows [anchor, MASK...] at positions a, a+1, ...
+ * pass every layer; returns the rows after the last norm.  Window 0 and every layer rotary
+ * (the workloads declare no windows), and no row convolutions (the plain Qwen3 layer). */
+static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, float* out) {
+  const og_geometry* g = &m->g;
+  const int B = g->block, H = g->hidden, nh = g->heads, kvh = g->kv_heads, hd = g->head_dim;
+  const int qd = nh * hd, kvd = kvh * hd, I = g->intermediate, rep = nh / kvh;
+  const float eps = (float)g->eps;
+  const float scale = powf((float)hd, -0.5f); /* Drafter::block: (hd as f32).powf(-0.5) */
+  og_seq* s = &m->seqs[seq];
+  /* Drafter::block: the context rows before the anchor: lo = first, hi = clamp(min(anchor,
+   * first + len), >= lo) */
+  int64_t lo = s->first, hi = anchor < s->first + s->len ? anchor : s->first + s->len;
+  if (hi < lo) hi = lo;
+  const int nctx = (int)(hi - lo);
+  const int nk = nctx + B;
+
+  float* h = (float*)malloc(sizeof(float) * (size_t)B * H);
+  memcpy(h, h_in, sizeof(float) * (size_t)B * H);
+  float* x = (float*)malloc(sizeof(float) * (size_t)B * H);
+  float* q = (float*)malloc(sizeof(float) * (size_t)B * qd);
+  float* k = (float*)malloc(sizeof(float) * (size_t)B * kvd);
+  float* v = (float*)malloc(sizeof(float) * (size_t)B * kvd);
+  float* y = (float*)malloc(sizeof(float) * (size_t)B * qd);
+  float* o = (float*)malloc(sizeof(float) * (size_t)B * H);
+  float* gt = (float*)malloc(sizeof(float) * (size_t)B * I);
+  float* up = (float*)malloc(sizeof(float) * (size_t)B * I);
+  float* a = (float*)malloc(sizeof(float) * (size_t)B * I);
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)hd);
+
+  for (int l = 0; l < g->layers; l++) {
+    const og_layer* L = &m->layers[l];
+    for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, L->in_norm, H, eps, x + (size_t)r * H);
+    mm(g->body_fmt, L->q, qd, H, x, B, q);
+    mm(g->body_fmt, L->k, kvd, H, x, B, k);
+    mm(g->body_fmt, L->v, kvd, H, x, B, v);
+    for (int r = 0; r < B; r++) {
+      for (int j = 0; j < nh; j++) {
+        float* qh = q + (size_t)r * qd + (size_t)j * hd;
+        og_rmsnorm_row(qh, L->q_norm, hd, eps, tmp);
+        og_rope_head(tmp, hd, anchor + r, m->inv_freq);
+        memcpy(qh, tmp, sizeof(float) * hd);
+      }
+      for (int j = 0; j < kvh; j++) {
+        float* kh = k + (size_t)r * kvd + (size_t)j * hd;
+        og_rmsnorm_row(kh, L->k_norm, hd, eps, tmp);
+        og_rope_head(tmp, hd, anchor + r, m->inv_freq);
+        memcpy(kh, tmp, sizeof(float) * hd);
+      }
+    }
+    /* per kv head gi: its keys and values are the context rows then the block's rows (not
+     * causal); q head j reads kv head j / rep */
+#pragma omp parallel for schedule(dynamic) num_threads(g_threads)
+    for (int gi = 0; gi < kvh; gi++) {
+      float* kk = (float*)malloc(sizeof(float) * (size_t)nk * hd);
+      float* vv = (float*)malloc(sizeof(float) * (size_t)nk * hd);
+      float* qq = (float*)malloc(sizeof(float) * (size_t)hd);
+      for (int c = 0; c < nctx; c++) {
+        size_t off = (((size_t)l * g->max_ctx + (size_t)c) * kvh + gi) * hd;
+        memcpy(kk + (size_t)c * hd, s->k + off, sizeof(float) * hd);
+        memcpy(vv + (size_t)c * hd, s->v + off, sizeof(float) * hd);
+      }
+      for (int r = 0; r < B; r++) {
+        memcpy(kk + (size_t)(nctx + r) * hd, k + (size_t)r * kvd + (size_t)gi * hd, sizeof(float) * hd);
+        memcpy(vv + (size_t)(nctx + r) * hd, v + (size_t)r * kvd + (size_t)gi * hd, sizeof(float) * hd);
+      }
+      for (int j = gi * rep; j < (gi + 1) * rep; j++)
+        for (int r = 0; r < B; r++) {
+          memcpy(qq, q + (size_t)r * qd + (size_t)j * hd, sizeof(float) * hd);
+          og_attend(qq, 1, kk, vv, nk, hd, scale, y + (size_t)r * qd + (size_t)j * hd, NULL);
+        }
+      free(qq);
+      free(vv);
+      free(kk);
+    }
+    mm(g->body_fmt, L->o, H, qd, y, B, o);
+    for (size_t i = 0; i < (size_t)B * H; i++) h[i] = h[i] + o[i];
+    for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, L->post_norm, H, eps, x + (size_t)r * H);
+    mm(g->body_fmt, L->gate, I, H, x, B, gt);
+    mm(g->body_fmt, L->up, I, H, x, B, up);
+    og_silu_mul(gt, up, B * I, a);
+    mm(g->body_fmt, L->down, H, I, a, B, o);
+    for (size_t i = 0; i < (size_t)B * H; i++) h[i] = h[i] + o[i];
+  }
+  for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, m->w.norm, H, eps, out + (size_t)r * H);
+  free(tmp);
+  free(a);
+  free(up);
+  free(gt);
+  free(o);
+  free(y);
+  free(v);
+  free(k);
+  free(q);
+  free(x);
+  free(h);
+}
+
+static int check_block_args(const og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors) {
+  if (n_seqs < 0 || n_seqs > m->g.max_seqs || (n_seqs > 0 && (!seqs || !anchors))) return -1;
+  for (int i = 0; i < n_seqs; i++) {
+    if (seqs[i] < 0 || seqs[i] >= m->g.max_seqs || anchors[i] < 0) return -1;
+    for (int j = 0; j < i; j++)
+      if (seqs[j] == seqs[i]) return -1;
+  }
+  return 0;
+}
+
+int og_block_hidden(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
+                    float* hidden) {
+  if (check_block_args(m, n_seqs, seqs, anchors)) return -1;
+  size_t per = (size_t)m->g.block * m->g.hidden;
+  for (int i = 0; i < n_seqs; i++) block_one(m, seqs[i], anchors[i], h + per * i, hidden + per * i);
+  return 0;
+}
+
+/* dflash.rs, module header: logits = head . norm(h); every block row gets its logits. */
+int og_block_forward(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
+                     float* logits) {
+  if (check_block_args(m, n_seqs, seqs, anchors)) return -1;
+  const og_geometry* g = &m->g;
+  size_t per = (size_t)g->block * g->hidden;
+  float* x = (float*)malloc(sizeof(float) * per * (size_t)(n_seqs > 0 ? n_seqs : 1));
+  for (int i = 0; i < n_seqs; i++) block_one(m, seqs[i], anchors[i], h + per * i, x + per * i);
+  if (n_seqs > 0) mm(g->head_fmt, m->w.head, g->vocab, g->hidden, x, n_seqs * g->block, logits);
+  free(x);
+  return 0;
+}

@@ -1,0 +1,96 @@
+"""The pins bite: plant plausible mistakes in a copy of the oracle's source (a dropped term, a
+wrong sign, index or operand), build each copy, and require some pin to fail on every one.
+Everything here runs on the CPU; the real oracle is restored afterwards."""
+import os
+
+import pytest
+
+import dflash_inputs as di
+import oracle
+import test_oracle_model as TM
+import test_oracle_units as TU
+
+# (what the mistake is, text in dflash_oracle.c, its replacement)
+MUTANTS = [
+    ("mean of squares over n-1", "ms /= (double)n;", "ms /= (double)(n - 1);"),
+    ("eps dropped", "sqrtf((float)ms + eps)", "sqrtf((float)ms)"),
+    ("norm weight dropped", "y[i] = t * w[i];", "y[i] = t;"),
+    ("rotation sign", "x[i] = (float)(a * c - b * s);", "x[i] = (float)(a * c + b * s);"),
+    ("position off by one", "float p = (float)pos;", "float p = (float)(pos + 1);"),
+    ("interleaved pairs", "double a = x[i], b = x[i + half];", "double a = x[2 * i], b = x[2 * i + 1];"),
+    ("act scale over 128", "d[g] = amax / 127.0f;", "d[g] = amax / 128.0f;"),
+    ("truncating quantizer", "float r = nearbyintf(t);", "float r = truncf(t);"),
+    ("one scale per row", "dw[g] = og_f16_to_f64(w.scales[(size_t)r * groups + g]);",
+     "dw[g] = og_f16_to_f64(w.scales[(size_t)r * groups]);"),
+    ("nibble order swapped", "int nib = (k & 1) ? (b >> 4) : (b & 15);", "int nib = (k & 1) ? (b & 15) : (b >> 4);"),
+    ("unsigned nibbles", "return nib >= 8 ? nib - 16 : nib;", "return nib;"),
+    ("attention scale dropped", "s[j] = dot * (double)scale;", "s[j] = dot;"),
+    ("wrong kv head for the context", "(((size_t)l * g->max_ctx + (size_t)c) * kvh + gi) * hd;",
+     "(((size_t)l * g->max_ctx + (size_t)c) * kvh + (kvh - 1 - gi)) * hd;"),
+    ("causal block rows", "og_attend(qq, 1, kk, vv, nk, hd, scale,", "og_attend(qq, 1, kk, vv, nctx + r + 1, hd, scale,"),
+    ("context past the anchor read", "int64_t lo = s->first, hi = anchor < s->first + s->len ? anchor : s->first + s->len;",
+     "int64_t lo = s->first, hi = s->first + s->len;"),
+    ("silu sign", "a[i] = (float)(gv / (1.0 + exp(-gv)) * (double)u[i]);", "a[i] = (float)(gv / (1.0 + exp(gv)) * (double)u[i]);"),
+    ("gate and up swapped", "og_silu_mul(gt, up, B * I, a);", "og_silu_mul(up, gt, B * I, a);"),
+    ("attention residual dropped", "mm(g->body_fmt, L->o, H, qd, y, B, o);\n    for (size_t i = 0; i < (size_t)B * H; i++) h[i] = h[i] + o[i];",
+     "mm(g->body_fmt, L->o, H, qd, y, B, o);\n    for (size_t i = 0; i < (size_t)B * H; i++) h[i] = o[i];"),
+    ("post-norm weight is the in-norm's", "og_rmsnorm_row(h + (size_t)r * H, L->post_norm, H, eps,",
+     "og_rmsnorm_row(h + (size_t)r * H, L->in_norm, H, eps,"),
+    ("k-norm on the context is the q-norm", "og_rmsnorm_row(kh, L->k_norm, hd, (float)g->eps, tmp);",
+     "og_rmsnorm_row(kh, L->q_norm, hd, (float)g->eps, tmp);"),
+    ("context rotated at its index, not its position", "og_rope_head(tmp, hd, p, m->inv_freq);",
+     "og_rope_head(tmp, hd, (int64_t)row, m->inv_freq);"),
+    ("hidden norm skipped", "og_rmsnorm_row(t + (size_t)i * H, m->w.hidden_norm, H, (float)g->eps, tn + (size_t)i * H);",
+     "memcpy(tn + (size_t)i * H, t + (size_t)i * H, sizeof(float) * H);"),
+    ("a gap keeps the old first", "  if (pos > first + len || pos < first) {\n    first = pos;",
+     "  if (pos > first + len || pos < first) {\n    first = first;"),
+    ("softmax max not subtracted consistently", "s[j] = exp(s[j] - top);", "s[j] = exp(s[j] - top) * (j == 0 ? 2.0 : 1.0);"),
+]
+
+CHECKS = [
+    (TU.test_rmsnorm_against_torch, (4096,)),
+    (TU.test_rope_against_transformers_rotate_half, (4095,)),
+    (TU.test_rope_invariants, ()),
+    (TU.test_quant_act_nearest_code_brute_force, ()),
+    (TU.test_quant_act_zero_group_and_ties, ()),
+    (TU.test_canonical_formats_by_hand, ()),
+    (TU.test_quantized_matmul_against_dense, (di.Q4_32,)),
+    (TU.test_quantized_matmul_against_dense, (di.Q8_32,)),
+    (TU.test_attention_against_torch_sdpa, ()),
+    (TU.test_attention_special_cases, ()),
+    (TU.test_silu_against_torch, ()),
+    (TM.test_forward_matches_transformers_qwen3_layers, (TM.SHARP,)),
+    (TM.test_forward_matches_transformers_qwen3_layers, (TM.QTINY,)),
+    (TM.test_anchor_row_vs_draft_rows_non_causal, ()),
+    (TM.test_context_past_the_anchor_is_not_read, ()),
+    (TM.test_append_chunking_truncate_and_reset, ()),
+]
+
+
+@pytest.fixture(scope="module")
+def restore_oracle():
+    yield
+    oracle.use_library(None)
+
+
+def _caught(fn, args) -> bool:
+    try:
+        fn(*args)
+    except (AssertionError, ValueError):
+        return True
+    return False
+
+
+@pytest.mark.parametrize("what,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_every_planted_mistake_fails_a_pin(what, old, new, tmp_path, restore_oracle):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site for '{what}' not unique in the oracle source"
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    so = oracle.build(src=path, out=os.path.join(tmp_path, "libmutant.so"), opt="-O1")
+    oracle.use_library(so)
+    try:
+        assert any(_caught(fn, args) for fn, args in CHECKS), f"no pin caught: {what}"
+    finally:
+        oracle.use_library(None)
