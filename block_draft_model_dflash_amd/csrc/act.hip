@@ -1,0 +1,293 @@
+// Row-wise producers of the next matrix's activations: split-K reduction, residual add,
+// RMSNorm, SwiGLU, q/k-norm + RoPE (block rows and context append), and the A8_32 quantizer.
+//
+// Sources: cortiq-engine "dflash.rs" -- fn rms (mean of squares in f64, scale 1/sqrt(f32(ms)
+// + eps) in f32, (x*s)*w), Drafter::rotate (half-split pairs, angle = f32(pos)*inv_freq),
+// Drafter::mlp (g/(1+e^-g)*u), Drafter::block (h += o), Drafter::settle_rows (K and V of
+// context rows); "gpu_wgpu/dflash_dev.rs" -- dflash_qk (q/k rms then rotation, one workgroup
+// a head and row).  A8_32 (int8 per row and group of 32): amax, d = amax/127, inv = 127/amax,
+// q = clamp(rint(x*inv)), all f32 and correctly rounded (hipcc keeps IEEE division/sqrt).
+#include "common.h"
+
+namespace dfl {
+
+// A8_32 of one element whose 32-element group sits in 32 consecutive lanes of the wave.
+__device__ __forceinline__ void emit_q(float y, size_t qi, int8_t* __restrict__ xq, float* __restrict__ dx,
+                                       size_t di, int lane) {
+  float amax = fabsf(y);
+#pragma unroll
+  for (int o = 16; o; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+  int8_t q = 0;
+  float d = 0.f;
+  if (amax > 0.f) {
+    d = amax / 127.0f;
+    const float inv = 127.0f / amax;
+    float r = __builtin_rintf(y * inv);
+    r = fminf(fmaxf(r, -127.f), 127.f);
+    q = (int8_t)r;
+  }
+  xq[qi] = q;
+  if ((lane & 31) == 0) dx[di] = d;
+}
+
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int i = 0; i < nw; i++) t += red[i];
+  return t;
+}
+
+// v = resid + sum of S partial slices; optional write-back; optional RMSNorm; then A8_32 or f32.
+// dx element of (row m, group g) at g*dxg + m*dxm.
+template <bool NORM, bool QUANT>
+__global__ __launch_bounds__(256) void k_norm_act(const float* __restrict__ src, int S, int src_mstride,
+                                                 const float* __restrict__ resid, float* __restrict__ h_out,
+                                                 const float* __restrict__ w, float eps, int M, int N,
+                                                 int8_t* __restrict__ xq, float* __restrict__ dx, int dxg, int dxm,
+                                                 float* __restrict__ xf) {
+  extern __shared__ float row[];  // N floats when NORM
+  __shared__ double red[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  if (m >= M) {
+    for (int i = tid; i < N; i += 256) {
+      if (QUANT) {
+        xq[(size_t)m * N + i] = 0;
+        if ((lane & 31) == 0) dx[(size_t)(i >> 5) * dxg + (size_t)m * dxm] = 0.f;
+      } else {
+        xf[(size_t)m * N + i] = 0.f;
+      }
+    }
+    return;
+  }
+  double ss = 0.0;
+  for (int i = tid; i < N; i += 256) {
+    float o = src[(size_t)m * N + i];
+    for (int s = 1; s < S; s++) o += src[((size_t)s * src_mstride + m) * N + i];
+    const float v = resid ? resid[(size_t)m * N + i] + o : o;
+    if (h_out) h_out[(size_t)m * N + i] = v;
+    if (NORM) {
+      row[i] = v;
+      ss += (double)v * (double)v;
+    } else if (QUANT) {
+      emit_q(v, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
+    } else {
+      xf[(size_t)m * N + i] = v;
+    }
+  }
+  if (!NORM) return;
+  ss = block_sum_f64(ss, red);
+  const float sc = 1.0f / sqrtf((float)(ss / (double)N) + eps);
+  for (int i = tid; i < N; i += 256) {
+    const float t = row[i] * sc;
+    const float y = t * w[i];
+    if (QUANT)
+      emit_q(y, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
+    else
+      xf[(size_t)m * N + i] = y;
+  }
+}
+
+hipError_t launch_norm_act(const float* src, int S, int src_mstride, const float* resid, float* h_out,
+                           const float* w, float eps, int M, int Mpad, int N, bool quant, int8_t* xq, float* dxT,
+                           float* xf, hipStream_t st) {
+  const size_t lds = w ? (size_t)N * 4 : 0;
+  if (lds > 96 * 1024 || N % 32) return hipErrorInvalidValue;
+  dim3 g(Mpad), b(256);
+  if (w && quant) {
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_norm_act<true, true>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL((k_norm_act<true, true>), g, b, lds, st, src, S, src_mstride, resid, h_out, w, eps, M, N, xq,
+                       dxT, Mpad, 1, xf);
+  } else if (w) {
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_norm_act<true, false>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    hipLaunchKernelGGL((k_norm_act<true, false>), g, b, lds, st, src, S, src_mstride, resid, h_out, w, eps, M, N, xq,
+                       dxT, Mpad, 1, xf);
+  } else if (quant) {
+    hipLaunchKernelGGL((k_norm_act<false, true>), g, b, 0, st, src, S, src_mstride, resid, h_out, w, eps, M, N, xq,
+                       dxT, Mpad, 1, xf);
+  } else {
+    hipLaunchKernelGGL((k_norm_act<false, false>), g, b, 0, st, src, S, src_mstride, resid, h_out, w, eps, M, N, xq,
+                       dxT, Mpad, 1, xf);
+  }
+  return hipGetLastError();
+}
+
+// A8_32 of plain rows with scales in row order [rows][cols/32] (a unit entry point).
+hipError_t launch_quant_rows(const float* x, int rows, int cols, int8_t* q, float* d, hipStream_t st) {
+  if (cols % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_norm_act<false, true>), dim3(rows), dim3(256), 0, st, x, 1, rows, (const float*)nullptr,
+                     (float*)nullptr, (const float*)nullptr, 0.f, rows, cols, q, d, 1, cols / 32, (float*)nullptr);
+  return hipGetLastError();
+}
+
+__global__ void k_transpose_scales(const float* __restrict__ d, int rows, int groups, int Mpad,
+                                   float* __restrict__ dT) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= groups * Mpad) return;
+  const int g = i / Mpad, m = i % Mpad;
+  dT[i] = m < rows ? d[(size_t)m * groups + g] : 0.f;
+}
+
+hipError_t launch_transpose_scales(const float* d, int rows, int groups, int Mpad, float* dT, hipStream_t st) {
+  const int n = groups * Mpad;
+  hipLaunchKernelGGL(k_transpose_scales, dim3((n + 255) / 256), dim3(256), 0, st, d, rows, groups, Mpad, dT);
+  return hipGetLastError();
+}
+
+// a = silu(g) * u.  Gate and up share n-tiles pairwise: column (i/16)*32 + i%16 is gate row i,
+// 16 further the up row i.  Grid (ceil(I/1024), Mpad).
+template <bool QUANT>
+__global__ __launch_bounds__(256) void k_swiglu_act(const float* __restrict__ part, int S, int M, int Mpad, int I,
+                                                   int8_t* __restrict__ xq, float* __restrict__ dxT,
+                                                   float* __restrict__ xf) {
+  const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const size_t N2 = 2 * (size_t)I;
+  for (int it = 0; it < 4; it++) {
+    const int i = blockIdx.x * 1024 + it * 256 + tid;
+    if (i >= I) break;
+    float a = 0.f;
+    if (m < M) {
+      const size_t gc = (size_t)(i >> 4) * 32 + (i & 15);
+      float g = part[(size_t)m * N2 + gc], u = part[(size_t)m * N2 + gc + 16];
+      for (int s = 1; s < S; s++) {
+        g += part[((size_t)s * Mpad + m) * N2 + gc];
+        u += part[((size_t)s * Mpad + m) * N2 + gc + 16];
+      }
+      a = g / (1.0f + expf(-g)) * u;
+    }
+    if (QUANT)
+      emit_q(a, (size_t)m * I + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
+    else
+      xf[(size_t)m * I + i] = a;
+  }
+}
+
+hipError_t launch_swiglu_act(const float* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
+                             float* xf, hipStream_t st) {
+  if (I % 32) return hipErrorInvalidValue;
+  dim3 g((unsigned)((I + 1023) / 1024), (unsigned)Mpad);
+  if (quant)
+    hipLaunchKernelGGL(k_swiglu_act<true>, g, dim3(256), 0, st, part, S, M, Mpad, I, xq, dxT, xf);
+  else
+    hipLaunchKernelGGL(k_swiglu_act<false>, g, dim3(256), 0, st, part, S, M, Mpad, I, xq, dxT, xf);
+  return hipGetLastError();
+}
+
+// RMSNorm of one head (threads d < hd of a 128-thread block) then its rotation to `pos`.
+__device__ __forceinline__ float head_norm_rope(float x, int d, int hd, const float* __restrict__ w, float eps,
+                                                const float* __restrict__ inv_freq, long long pos, float* ybuf,
+                                                double* red) {
+  double ss = d < hd ? (double)x * (double)x : 0.0;
+  ss = block_sum_f64(ss, red);
+  const float sc = 1.0f / sqrtf((float)(ss / (double)hd) + eps);
+  float y = 0.f;
+  if (d < hd) {
+    const float t = x * sc;
+    y = t * w[d];
+  }
+  ybuf[d] = y;
+  __syncthreads();
+  if (d >= hd) return 0.f;
+  const int half = hd >> 1;
+  const int i = d < half ? d : d - half;
+  const float ang = (float)pos * inv_freq[i];
+  float sn, cs;
+  sincosf(ang, &sn, &cs);
+  return d < half ? y * cs - ybuf[d + half] * sn : y * cs + ybuf[d - half] * sn;
+}
+
+// Grid (nh + 2 kvh heads, M rows), block 128.  Columns of the fused projection: q heads, then
+// k heads, then v heads, hd each.
+__global__ __launch_bounds__(128) void k_qkv_epilogue(const float* __restrict__ part, int S, int Mpad, int B,
+                                                     SeqInfo si, int nh, int kvh, int hd,
+                                                     const float* __restrict__ q_norm,
+                                                     const float* __restrict__ k_norm,
+                                                     const float* __restrict__ inv_freq, float eps,
+                                                     float* __restrict__ q, float* __restrict__ k,
+                                                     float* __restrict__ v) {
+  __shared__ float ybuf[128];
+  __shared__ double red[2];
+  const int head = blockIdx.x, m = blockIdx.y, d = threadIdx.x;
+  const size_t N = (size_t)(nh + 2 * kvh) * hd;
+  const size_t col = (size_t)head * hd + d;
+  float x = 0.f;
+  if (d < hd) {
+    x = part[(size_t)m * N + col];
+    for (int s = 1; s < S; s++) x += part[((size_t)s * Mpad + m) * N + col];
+  }
+  if (head >= nh + kvh) {
+    if (d < hd) v[((size_t)m * kvh + (head - nh - kvh)) * hd + d] = x;
+    return;
+  }
+  const long long pos = si.pos0[m / B] + (m % B);
+  const bool isq = head < nh;
+  const float out = head_norm_rope(x, d, hd, isq ? q_norm : k_norm, eps, inv_freq, pos, ybuf, red);
+  if (d < hd) {
+    if (isq)
+      q[((size_t)m * nh + head) * hd + d] = out;
+    else
+      k[((size_t)m * kvh + (head - nh)) * hd + d] = out;
+  }
+}
+
+hipError_t launch_qkv_epilogue(const float* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
+                               int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
+                               float* q, float* k, float* v, hipStream_t st) {
+  if (hd > 128 || hd % 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_qkv_epilogue, dim3(nh + 2 * kvh, M), dim3(128), 0, st, part, S, Mpad, B, si, nh, kvh, hd,
+                     q_norm, k_norm, inv_freq, eps, q, k, v);
+  return hipGetLastError();
+}
+
+// Context append: grid (layers * 2 * kvh, n), block 128.  Columns of the all-layer K|V
+// projection: layer l's k heads then its v heads.  Cache layout [L][max_seqs][kvh][max_ctx][hd].
+__global__ __launch_bounds__(128) void k_kv_append(const float* __restrict__ part, int S, int Mpad, int layers,
+                                                  int kvh, int hd, const float* __restrict__ k_norms,
+                                                  const float* __restrict__ inv_freq, float eps, long long pos0,
+                                                  int row0, int slot, int max_seqs, int max_ctx,
+                                                  float* __restrict__ kc, float* __restrict__ vc) {
+  __shared__ float ybuf[128];
+  __shared__ double red[2];
+  const int unit = blockIdx.x, i = blockIdx.y, d = threadIdx.x;
+  const int l = unit / (2 * kvh), rem = unit % (2 * kvh), kind = rem / kvh, h = rem % kvh;
+  const size_t kvd = (size_t)kvh * hd, N = (size_t)layers * 2 * kvd;
+  const size_t col = ((size_t)l * 2 + kind) * kvd + (size_t)h * hd + d;
+  float x = 0.f;
+  if (d < hd) {
+    x = part[(size_t)i * N + col];
+    for (int s = 1; s < S; s++) x += part[((size_t)s * Mpad + i) * N + col];
+  }
+  const size_t dst = ((((size_t)l * max_seqs + slot) * kvh + h) * max_ctx + (size_t)(row0 + i)) * hd + d;
+  if (kind == 1) {
+    if (d < hd) vc[dst] = x;
+    return;
+  }
+  const float out = head_norm_rope(x, d, hd, k_norms + (size_t)l * hd, eps, inv_freq, pos0 + i, ybuf, red);
+  if (d < hd) kc[dst] = out;
+}
+
+hipError_t launch_kv_append(const float* part, int S, int Mpad, int n, int layers, int kvh, int hd,
+                            const float* k_norms, const float* inv_freq, float eps, long long pos0, int row0,
+                            int slot, int max_seqs, int max_ctx, float* kc, float* vc, hipStream_t st) {
+  if (hd > 128 || hd % 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_kv_append, dim3(layers * 2 * kvh, n), dim3(128), 0, st, part, S, Mpad, layers, kvh, hd,
+                     k_norms, inv_freq, eps, pos0, row0, slot, max_seqs, max_ctx, kc, vc);
+  return hipGetLastError();
+}
+
+}  // namespace dfl

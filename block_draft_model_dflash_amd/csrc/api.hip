@@ -1,0 +1,674 @@
+// The C ABI (include/dflash.h): argument checks, workspace carving, weight repacking, context
+// bookkeeping and the enqueue order of the append and block paths on the caller's stream.
+//
+// Bookkeeping follows cortiq-engine "dflash.rs" (Drafter::queue_context: a position inside the
+// held span replaces it and what follows, a gap or a position before the first starts over;
+// Drafter::truncate; Drafter::reset; Drafter::block: layer context = [first, clamp(min(anchor,
+// first+len), >= first))).  The stage order of a block follows gpu_wgpu/dflash_dev.rs,
+// Dev::block (norm, q k v, q/k norm + rotation, attention, o + residual, norm, gate/up + silu,
+// down + residual; final norm; head), without the row convolutions and the selector.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "common.h"
+
+using namespace dfl;
+
+namespace {
+
+constexpr int APPEND_CHUNK = 128;  // context rows per append pass (8 row tiles of 16)
+constexpr int MROWS = 128;         // activation rows the workspace holds
+constexpr int MAXCH = 65;          // attention chunks per (sequence, kv head), block chunk included
+
+thread_local std::string g_create_err;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int round16(int x) { return (x + 15) & ~15; }
+
+struct Layout {
+  size_t fc, head, kvall;
+  std::vector<size_t> qkv, o, gu, down;
+  size_t hidden_norm, norm, in_norm, post_norm, q_norm, k_norm, inv_freq;
+  size_t kc, vc;
+  size_t h, xq, dxT, xf, q, kb, vb, part, apart, aml;
+  size_t act_begin, total;
+  size_t part_floats;
+};
+
+bool is_fmt(int f) { return f == DFLASH_F32 || f == DFLASH_Q4_32 || f == DFLASH_Q8_32; }
+
+// Geometry checks (cortiq-engine dflash.rs, Geometry::of, plus this library's kernel limits).
+int check_geometry(const dflash_geometry* g, std::string* err) {
+  char buf[256];
+  auto fail = [&](int code, const char* msg) {
+    snprintf(buf, sizeof buf, "geometry: %s", msg);
+    *err = buf;
+    return code;
+  };
+  if (!g) return fail(DFLASH_EINVAL, "null");
+  if (g->layers < 1 || g->hidden < 1 || g->heads < 1 || g->kv_heads < 1 || g->head_dim < 2 || g->intermediate < 1 ||
+      g->vocab < 1 || g->n_taps < 1 || g->max_seqs < 1 || g->max_ctx < 0)
+    return fail(DFLASH_EINVAL, "a size is not positive");
+  if (g->block < 2) return fail(DFLASH_EINVAL, "block must hold the anchor and at least one draft row");
+  if (g->heads % g->kv_heads) return fail(DFLASH_EINVAL, "heads must be a multiple of kv_heads");
+  if (!(g->eps >= 0) || !(g->rope_theta > 0)) return fail(DFLASH_EINVAL, "eps / rope_theta out of range");
+  if (!is_fmt(g->body_fmt) || !is_fmt(g->fc_fmt) || !is_fmt(g->head_fmt)) return fail(DFLASH_EINVAL, "unknown format");
+  if (g->block > 16) return fail(DFLASH_ENOTSUP, "block > 16 rows");
+  if (g->heads / g->kv_heads > 16) return fail(DFLASH_ENOTSUP, "more than 16 q heads per kv head");
+  if (g->head_dim != 64 && g->head_dim != 128) return fail(DFLASH_ENOTSUP, "head_dim must be 64 or 128");
+  if ((long)g->max_seqs * g->block > MROWS) return fail(DFLASH_ENOTSUP, "max_seqs * block > 128 rows");
+  const long H = g->hidden, qd = (long)g->heads * g->head_dim, kvd = (long)g->kv_heads * g->head_dim;
+  const long I = g->intermediate, T = (long)g->n_taps * g->hidden, V = g->vocab;
+  auto mat_ok = [&](int fmt, long rows, long cols) {
+    if (rows % 16) return false;
+    return fmt == DFLASH_F32 ? cols % 4 == 0 : cols % 128 == 0;
+  };
+  if (!mat_ok(g->fc_fmt, H, T)) return fail(DFLASH_ENOTSUP, "fc shape outside the kernels' tiles");
+  if (!mat_ok(g->head_fmt, V, H)) return fail(DFLASH_ENOTSUP, "head shape outside the kernels' tiles");
+  if (!mat_ok(g->body_fmt, qd + 2 * kvd, H) || !mat_ok(g->body_fmt, H, qd) || !mat_ok(g->body_fmt, 2 * I, H) ||
+      !mat_ok(g->body_fmt, H, I) || !mat_ok(g->body_fmt, 2 * kvd, H))
+    return fail(DFLASH_ENOTSUP, "body shapes outside the kernels' tiles");
+  if (H % 32 || I % 32 || qd % 32 || T % 32) return fail(DFLASH_ENOTSUP, "activation widths must be multiples of 32");
+  if (H * 4 > 96 * 1024) return fail(DFLASH_ENOTSUP, "hidden too wide for one workgroup's row");
+  return DFLASH_OK;
+}
+
+int splits_for(int fmt, int N, int K) { return fmt == DFLASH_F32 ? 1 : choose_splits(N, K, MROWS); }
+
+void plan(const dflash_geometry* g, Layout* L) {
+  const long H = g->hidden, qd = (long)g->heads * g->head_dim, kvd = (long)g->kv_heads * g->head_dim;
+  const long I = g->intermediate, T = (long)g->n_taps * g->hidden, V = g->vocab, hd = g->head_dim;
+  const long NL = g->layers, kvh = g->kv_heads, rep = g->heads / g->kv_heads;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L->fc = take(packed_bytes(g->fc_fmt, H, T));
+  L->head = take(packed_bytes(g->head_fmt, V, H));
+  L->kvall = take(packed_bytes(g->body_fmt, NL * 2 * kvd, H));
+  L->qkv.resize(NL);
+  L->o.resize(NL);
+  L->gu.resize(NL);
+  L->down.resize(NL);
+  for (long l = 0; l < NL; l++) {
+    L->qkv[l] = take(packed_bytes(g->body_fmt, qd + 2 * kvd, H));
+    L->o[l] = take(packed_bytes(g->body_fmt, H, qd));
+    L->gu[l] = take(packed_bytes(g->body_fmt, 2 * I, H));
+    L->down[l] = take(packed_bytes(g->body_fmt, H, I));
+  }
+  L->hidden_norm = take(H * 4);
+  L->norm = take(H * 4);
+  L->in_norm = take(NL * H * 4);
+  L->post_norm = take(NL * H * 4);
+  L->q_norm = take(NL * hd * 4);
+  L->k_norm = take(NL * hd * 4);
+  L->inv_freq = take(hd / 2 * 4);
+  const size_t cache = (size_t)NL * g->max_seqs * kvh * (size_t)g->max_ctx * hd * 4;
+  L->kc = take(cache);
+  L->vc = take(cache);
+  L->act_begin = off;
+  long Kmax = H;
+  if (qd > Kmax) Kmax = qd;
+  if (I > Kmax) Kmax = I;
+  if (T > Kmax) Kmax = T;
+  L->h = take((size_t)MROWS * H * 4);
+  L->xq = take((size_t)MROWS * Kmax);
+  L->dxT = take((size_t)(Kmax / 32) * MROWS * 4);
+  L->xf = take((size_t)MROWS * Kmax * 4);
+  L->q = take((size_t)MROWS * qd * 4);
+  L->kb = take((size_t)MROWS * kvd * 4);
+  L->vb = take((size_t)MROWS * kvd * 4);
+  size_t pf = 0;
+  auto need = [&](int fmt, long N, long K) {
+    const size_t f = (size_t)splits_for(fmt, (int)N, (int)K) * MROWS * N;
+    if (f > pf) pf = f;
+  };
+  need(g->fc_fmt, H, T);
+  need(g->body_fmt, NL * 2 * kvd, H);
+  need(g->body_fmt, qd + 2 * kvd, H);
+  need(g->body_fmt, H, qd);
+  need(g->body_fmt, 2 * I, H);
+  need(g->body_fmt, H, I);
+  L->part_floats = pf;
+  L->part = take(pf * 4);
+  const size_t arows = (size_t)g->max_seqs * kvh * MAXCH * rep * 16;
+  L->apart = take(arows * hd * 4);
+  L->aml = take(arows * 2 * 4);
+  L->total = off;
+}
+
+}  // namespace
+
+struct dflash_ctx {
+  dflash_geometry g;
+  hipStream_t st = nullptr;
+  std::string err;
+  Layout lay;
+  uint8_t* ws = nullptr;
+  std::vector<int64_t> first, len;
+  // stage timing: event pairs recorded around one stage's launches
+  int timed_stage = -1;
+  std::vector<hipEvent_t> ev_pool;  // created on first use, reused
+  size_t ev_used = 0;
+
+  hipError_t mark() {  // record the next event of a pair
+    if (ev_used == ev_pool.size()) {
+      hipEvent_t e;
+      hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) return r;
+      ev_pool.push_back(e);
+    }
+    return hipEventRecord(ev_pool[ev_used++], st);
+  }
+  ~dflash_ctx() {
+    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+  }
+
+  template <class T>
+  T* at(size_t off) const {
+    return (T*)(ws + off);
+  }
+  int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    err = buf;
+    return code;
+  }
+  int hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return DFLASH_OK;
+    return fail(DFLASH_EHIP, "%s: %s", what, hipGetErrorString(e));
+  }
+};
+
+#define TRY_HIP(c, expr, what)                     \
+  do {                                             \
+    int _rc = (c)->hip((expr), (what));            \
+    if (_rc != DFLASH_OK) return _rc;              \
+  } while (0)
+
+// Brackets a stage with an event pair when that stage is being timed.
+struct StageTimer {
+  dflash_ctx* c;
+  bool on;
+  StageTimer(dflash_ctx* c_, int stage) : c(c_), on(c_->timed_stage == stage && c_->ev_used + 2 <= 65536) {
+    if (on && c->mark() != hipSuccess) on = false;
+  }
+  ~StageTimer() {
+    if (on) (void)c->mark();
+  }
+};
+
+namespace {
+
+bool bodyq(const dflash_ctx* c) { return c->g.body_fmt != DFLASH_F32; }
+
+// One matrix product over the activations prepared by the previous producer.  Returns the
+// number of K slices written to the partial buffer (1 when direct).
+int run_gemm(dflash_ctx* c, int fmt, size_t woff, int N, int K, int Mpad, int M, float* out, bool direct, int out_ld,
+             int m_store, int* slices) {
+  const void* W = c->ws + woff;
+  if (fmt == DFLASH_F32) {
+    *slices = 1;
+    return c->hip(launch_gemm_f32((const float*)W, N, K, c->at<float>(c->lay.xf), Mpad, M, out, direct, out_ld,
+                                  m_store, c->st),
+                  "f32 gemm");
+  }
+  const int s = direct ? 1 : choose_splits(N, K, Mpad);
+  *slices = s;
+  return c->hip(launch_gemm_q(fmt, W, N, K, c->at<int8_t>(c->lay.xq), c->at<float>(c->lay.dxT), Mpad, s, out, direct,
+                              out_ld, m_store, c->st),
+                "quantized gemm");
+}
+
+int check_weights(const dflash_geometry* g, const dflash_weights* w, std::string* err) {
+  auto bad = [&](const char* m) {
+    *err = std::string("weights: ") + m;
+    return DFLASH_EINVAL;
+  };
+  auto mat = [&](const dflash_matrix& m, int fmt) { return m.codes && (fmt == DFLASH_F32 || m.scales); };
+  if (!w || !w->layer) return bad("null");
+  if (!mat(w->fc, g->fc_fmt) || !mat(w->head, g->head_fmt) || !w->hidden_norm || !w->norm) return bad("fc/head/norms");
+  for (int l = 0; l < g->layers; l++) {
+    const dflash_layer_weights& L = w->layer[l];
+    const int f = g->body_fmt;
+    if (!L.in_norm || !L.post_norm || !L.q_norm || !L.k_norm || !mat(L.q, f) || !mat(L.k, f) || !mat(L.v, f) ||
+        !mat(L.o, f) || !mat(L.gate, f) || !mat(L.up, f) || !mat(L.down, f))
+      return bad("a layer matrix or norm is null");
+  }
+  return DFLASH_OK;
+}
+
+int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
+                 float* out, bool hidden_only) {
+  const dflash_geometry& g = c->g;
+  if (n_seqs < 1 || n_seqs > g.max_seqs) return c->fail(DFLASH_EINVAL, "n_seqs %d outside [1, %d]", n_seqs, g.max_seqs);
+  if (!seqs || !anchors || !h || !out) return c->fail(DFLASH_EINVAL, "null pointer");
+  SeqInfo si;
+  memset(&si, 0, sizeof si);
+  si.n = n_seqs;
+  for (int i = 0; i < n_seqs; i++) {
+    if (seqs[i] < 0 || seqs[i] >= g.max_seqs) return c->fail(DFLASH_EINVAL, "sequence %d out of range", seqs[i]);
+    for (int j = 0; j < i; j++)
+      if (seqs[j] == seqs[i]) return c->fail(DFLASH_EINVAL, "sequence %d given twice", seqs[i]);
+    if (anchors[i] < 0) return c->fail(DFLASH_EINVAL, "negative anchor");
+    const int64_t first = c->first[seqs[i]], end = first + c->len[seqs[i]];
+    int64_t hi = anchors[i] < end ? anchors[i] : end;
+    if (hi < first) hi = first;
+    si.slot[i] = seqs[i];
+    si.nctx[i] = (int)(hi - first);
+    si.pos0[i] = anchors[i];
+  }
+  const int B = g.block, H = g.hidden, nh = g.heads, kvh = g.kv_heads, hd = g.head_dim, NL = g.layers;
+  const int qd = nh * hd, kvd = kvh * hd, I = g.intermediate, V = g.vocab;
+  const int M = n_seqs * B, Mpad = round16(M);
+  const float eps = (float)g.eps;
+  const Layout& L = c->lay;
+  float* hbuf = c->at<float>(L.h);
+  float* part = c->at<float>(L.part);
+  int8_t* xq = c->at<int8_t>(L.xq);
+  float* dxT = c->at<float>(L.dxT);
+  float* xf = c->at<float>(L.xf);
+  const bool bq = bodyq(c);
+
+  AttnShape as;
+  as.nh = nh;
+  as.kvh = kvh;
+  as.hd = hd;
+  as.B = B;
+  as.max_ctx = g.max_ctx;
+  as.max_seqs = g.max_seqs;
+  as.maxch = MAXCH;
+  as.scale = powf((float)hd, -0.5f);  // dflash.rs, Drafter::block: (hd as f32).powf(-0.5)
+  int nmax = 0;
+  for (int i = 0; i < n_seqs; i++)
+    if (si.nctx[i] > nmax) nmax = si.nctx[i];
+  int nch_target = 512 / (n_seqs * kvh);
+  if (nch_target < 1) nch_target = 1;
+  if (nch_target > MAXCH - 1) nch_target = MAXCH - 1;
+  int ck = round16((nmax + nch_target - 1) / nch_target);
+  if (ck < 16) ck = 16;
+  as.ck = ck;
+
+  TRY_HIP(c, hipMemcpyAsync(hbuf, h, (size_t)M * H * 4, hipMemcpyDeviceToDevice, c->st), "copy block rows");
+  TRY_HIP(c,
+          launch_norm_act(hbuf, 1, Mpad, nullptr, nullptr, c->at<float>(L.in_norm), eps, M, Mpad, H, bq, xq, dxT, xf,
+                          c->st),
+          "in-norm");
+  const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd;
+  for (int l = 0; l < NL; l++) {
+    int S = 1, rc;
+    {
+      StageTimer t(c, DFLASH_STAGE_QKV);
+      if ((rc = run_gemm(c, g.body_fmt, L.qkv[l], qd + 2 * kvd, H, Mpad, M, part, false, 0, 0, &S))) return rc;
+    }
+    TRY_HIP(c,
+            launch_qkv_epilogue(part, S, Mpad, M, B, si, nh, kvh, hd, c->at<float>(L.q_norm) + (size_t)l * hd,
+                                c->at<float>(L.k_norm) + (size_t)l * hd, c->at<float>(L.inv_freq), eps,
+                                c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb), c->st),
+            "q/k norm + rope");
+    {
+      StageTimer t(c, DFLASH_STAGE_ATTENTION);
+      TRY_HIP(c,
+            launch_attention(as, si, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
+                             c->at<float>(L.kc) + (size_t)l * layer_cache, c->at<float>(L.vc) + (size_t)l * layer_cache,
+                             c->at<float>(L.apart), c->at<float>(L.aml), Mpad, bq, xq, dxT, xf, c->st),
+              "attention");
+    }
+    {
+      StageTimer t(c, DFLASH_STAGE_O);
+      if ((rc = run_gemm(c, g.body_fmt, L.o[l], H, qd, Mpad, M, part, false, 0, 0, &S))) return rc;
+    }
+    TRY_HIP(c,
+            launch_norm_act(part, S, Mpad, hbuf, hbuf, c->at<float>(L.post_norm) + (size_t)l * H, eps, M, Mpad, H, bq,
+                            xq, dxT, xf, c->st),
+            "o residual + post-norm");
+    {
+      StageTimer t(c, DFLASH_STAGE_GATE_UP);
+      if ((rc = run_gemm(c, g.body_fmt, L.gu[l], 2 * I, H, Mpad, M, part, false, 0, 0, &S))) return rc;
+    }
+    TRY_HIP(c, launch_swiglu_act(part, S, M, Mpad, I, bq, xq, dxT, xf, c->st), "swiglu");
+    {
+      StageTimer t(c, DFLASH_STAGE_DOWN);
+      if ((rc = run_gemm(c, g.body_fmt, L.down[l], H, I, Mpad, M, part, false, 0, 0, &S))) return rc;
+    }
+    const bool last = l + 1 == NL;
+    const float* nw = last ? c->at<float>(L.norm) : c->at<float>(L.in_norm) + (size_t)(l + 1) * H;
+    const bool nq = last ? (!hidden_only && g.head_fmt != DFLASH_F32) : bq;
+    TRY_HIP(c, launch_norm_act(part, S, Mpad, hbuf, hbuf, nw, eps, M, Mpad, H, nq, xq, dxT, xf, c->st),
+            "down residual + next norm");
+  }
+  if (hidden_only) {
+    TRY_HIP(c, hipMemcpyAsync(out, xf, (size_t)M * H * 4, hipMemcpyDeviceToDevice, c->st), "copy hidden");
+    return DFLASH_OK;
+  }
+  int S = 1;
+  StageTimer t(c, DFLASH_STAGE_HEAD);
+  return run_gemm(c, g.head_fmt, L.head, V, H, Mpad, M, out, true, V, M, &S);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dflash_workspace_bytes(const dflash_geometry* g, size_t* bytes) {
+  std::string err;
+  int rc = check_geometry(g, &err);
+  if (rc) {
+    g_create_err = err;
+    return rc;
+  }
+  if (!bytes) return DFLASH_EINVAL;
+  Layout L;
+  plan(g, &L);
+  *bytes = L.total;
+  return DFLASH_OK;
+}
+
+int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* workspace, size_t bytes, void* stream,
+                  dflash_ctx** out) {
+  std::string err;
+  int rc = check_geometry(g, &err);
+  if (!rc) rc = check_weights(g, w, &err);
+  if (!rc && (!workspace || !out)) {
+    err = "null workspace or out";
+    rc = DFLASH_EINVAL;
+  }
+  if (!rc && ((uintptr_t)workspace & 255)) {
+    err = "workspace must be 256-byte aligned";
+    rc = DFLASH_EINVAL;
+  }
+  Layout L;
+  if (!rc) {
+    plan(g, &L);
+    if (bytes < L.total) {
+      err = "workspace too small";
+      rc = DFLASH_EINVAL;
+    }
+  }
+  if (rc) {
+    g_create_err = err;
+    return rc;
+  }
+  dflash_ctx* c = new dflash_ctx();
+  c->g = *g;
+  c->lay = L;
+  c->ws = (uint8_t*)workspace;
+  c->st = (hipStream_t)stream;
+  c->first.assign(g->max_seqs, 0);
+  c->len.assign(g->max_seqs, 0);
+  const long H = g->hidden, qd = (long)g->heads * g->head_dim, kvd = (long)g->kv_heads * g->head_dim;
+  const long I = g->intermediate, T = (long)g->n_taps * g->hidden, V = g->vocab, hd = g->head_dim;
+  auto fin = [&](int code) -> int {
+    if (code) {
+      g_create_err = c->err;
+      delete c;
+      return code;
+    }
+    *out = c;
+    return DFLASH_OK;
+  };
+  auto pack = [&](int fmt, const dflash_matrix& m, long rows, long cols, size_t off, long tile_off, long stride) {
+    return c->hip(launch_pack(fmt, m.codes, m.scales, (int)rows, (int)cols, c->ws + off, tile_off, stride, c->st),
+                  "pack");
+  };
+  int e;
+  // activations start at zero (rows past a call's last row are read as zeros)
+  if ((e = c->hip(hipMemsetAsync(c->ws + L.act_begin, 0, L.total - L.act_begin, c->st), "clear activations")))
+    return fin(e);
+  if ((e = pack(g->fc_fmt, w->fc, H, T, L.fc, 0, 1))) return fin(e);
+  if ((e = pack(g->head_fmt, w->head, V, H, L.head, 0, 1))) return fin(e);
+  const int bf = g->body_fmt;
+  for (int l = 0; l < g->layers; l++) {
+    const dflash_layer_weights& W = w->layer[l];
+    if ((e = pack(bf, W.q, qd, H, L.qkv[l], 0, 1))) return fin(e);
+    if ((e = pack(bf, W.k, kvd, H, L.qkv[l], qd / 16, 1))) return fin(e);
+    if ((e = pack(bf, W.v, kvd, H, L.qkv[l], (qd + kvd) / 16, 1))) return fin(e);
+    if ((e = pack(bf, W.o, H, qd, L.o[l], 0, 1))) return fin(e);
+    if ((e = pack(bf, W.gate, I, H, L.gu[l], 0, 2))) return fin(e);
+    if ((e = pack(bf, W.up, I, H, L.gu[l], 1, 2))) return fin(e);
+    if ((e = pack(bf, W.down, H, I, L.down[l], 0, 1))) return fin(e);
+    if ((e = pack(bf, W.k, kvd, H, L.kvall, (2 * l) * kvd / 16, 1))) return fin(e);
+    if ((e = pack(bf, W.v, kvd, H, L.kvall, (2 * l + 1) * kvd / 16, 1))) return fin(e);
+    auto cp = [&](size_t off, const float* src, long n) {
+      return c->hip(hipMemcpyAsync(c->ws + off, src, n * 4, hipMemcpyDeviceToDevice, c->st), "copy norm");
+    };
+    if ((e = cp(L.in_norm + (size_t)l * H * 4, W.in_norm, H))) return fin(e);
+    if ((e = cp(L.post_norm + (size_t)l * H * 4, W.post_norm, H))) return fin(e);
+    if ((e = cp(L.q_norm + (size_t)l * hd * 4, W.q_norm, hd))) return fin(e);
+    if ((e = cp(L.k_norm + (size_t)l * hd * 4, W.k_norm, hd))) return fin(e);
+  }
+  if ((e = c->hip(hipMemcpyAsync(c->ws + L.hidden_norm, w->hidden_norm, H * 4, hipMemcpyDeviceToDevice, c->st),
+                  "copy norm")))
+    return fin(e);
+  if ((e = c->hip(hipMemcpyAsync(c->ws + L.norm, w->norm, H * 4, hipMemcpyDeviceToDevice, c->st), "copy norm")))
+    return fin(e);
+  if ((e = c->hip(launch_inv_freq(g->rope_theta, (int)hd, c->at<float>(L.inv_freq), c->st), "rope table")))
+    return fin(e);
+  if ((e = c->hip(hipStreamSynchronize(c->st), "create sync"))) return fin(e);
+  return fin(DFLASH_OK);
+}
+
+int dflash_set_stream(dflash_ctx* c, void* stream) {
+  if (!c) return DFLASH_EINVAL;
+  c->st = (hipStream_t)stream;
+  return DFLASH_OK;
+}
+
+int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps, int32_t n) {
+  if (!c) return DFLASH_EINVAL;
+  const dflash_geometry& g = c->g;
+  if (seq < 0 || seq >= g.max_seqs) return c->fail(DFLASH_EINVAL, "sequence %d out of range", seq);
+  if (pos < 0 || n < 0 || (n > 0 && !taps)) return c->fail(DFLASH_EINVAL, "bad position, count or taps");
+  int64_t first = c->first[seq], len = c->len[seq];
+  if (pos > first + len || pos < first) {
+    first = pos;
+    len = 0;
+  } else {
+    len = pos - first;
+  }
+  if (len + n > g.max_ctx)
+    return c->fail(DFLASH_ECAPACITY, "sequence %d: %lld + %d rows exceed max_ctx %d", seq, (long long)len, n,
+                   g.max_ctx);
+  c->first[seq] = first;
+  c->len[seq] = len;
+  StageTimer timer(c, DFLASH_STAGE_APPEND);
+  const int H = g.hidden, T = g.n_taps * g.hidden, kvd = g.kv_heads * g.head_dim, NL = g.layers;
+  const float eps = (float)g.eps;
+  const Layout& L = c->lay;
+  float* part = c->at<float>(L.part);
+  int8_t* xq = c->at<int8_t>(L.xq);
+  float* dxT = c->at<float>(L.dxT);
+  float* xf = c->at<float>(L.xf);
+  for (int c0 = 0; c0 < n; c0 += APPEND_CHUNK) {
+    const int nn = n - c0 < APPEND_CHUNK ? n - c0 : APPEND_CHUNK;
+    const int Mpad = round16(nn);
+    const float* rows = taps + (size_t)c0 * T;
+    int S = 1, rc;
+    if (g.fc_fmt != DFLASH_F32) {
+      TRY_HIP(c, launch_norm_act(rows, 1, Mpad, nullptr, nullptr, nullptr, eps, nn, Mpad, T, true, xq, dxT, xf, c->st),
+              "taps quant");
+      rc = run_gemm(c, g.fc_fmt, L.fc, H, T, Mpad, nn, part, false, 0, 0, &S);
+    } else {
+      S = 1;
+      rc = c->hip(launch_gemm_f32((const float*)(c->ws + L.fc), H, T, rows, Mpad, nn, part, false, 0, 0, c->st),
+                  "f32 gemm");
+    }
+    if (rc) return rc;
+    TRY_HIP(c,
+            launch_norm_act(part, S, Mpad, nullptr, nullptr, c->at<float>(L.hidden_norm), eps, nn, Mpad, H, bodyq(c),
+                            xq, dxT, xf, c->st),
+            "hidden norm");
+    if ((rc = run_gemm(c, g.body_fmt, L.kvall, NL * 2 * kvd, H, Mpad, nn, part, false, 0, 0, &S))) return rc;
+    TRY_HIP(c,
+            launch_kv_append(part, S, Mpad, nn, NL, g.kv_heads, g.head_dim, c->at<float>(L.k_norm),
+                             c->at<float>(L.inv_freq), eps, pos + c0, (int)(pos - first) + c0, seq, g.max_seqs,
+                             g.max_ctx, c->at<float>(L.kc), c->at<float>(L.vc), c->st),
+            "k/v into the cache");
+  }
+  c->len[seq] = len + n;
+  return DFLASH_OK;
+}
+
+int dflash_ctx_truncate(dflash_ctx* c, int32_t seq, int64_t pos) {
+  if (!c) return DFLASH_EINVAL;
+  if (seq < 0 || seq >= c->g.max_seqs || pos < 0) return c->fail(DFLASH_EINVAL, "bad sequence or position");
+  int64_t keep = pos - c->first[seq];
+  if (keep < 0) keep = 0;
+  if (keep > c->len[seq]) keep = c->len[seq];
+  c->len[seq] = keep;
+  return DFLASH_OK;
+}
+
+int dflash_ctx_reset(dflash_ctx* c, int32_t seq) {
+  if (!c) return DFLASH_EINVAL;
+  if (seq < 0 || seq >= c->g.max_seqs) return c->fail(DFLASH_EINVAL, "bad sequence");
+  c->len[seq] = 0;
+  c->first[seq] = 0;
+  return DFLASH_OK;
+}
+
+int dflash_ctx_span(const dflash_ctx* c, int32_t seq, int64_t* first, int64_t* end) {
+  if (!c || !first || !end || seq < 0 || seq >= c->g.max_seqs) return DFLASH_EINVAL;
+  *first = c->first[seq];
+  *end = c->first[seq] + c->len[seq];
+  return DFLASH_OK;
+}
+
+int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
+                         float* logits) {
+  if (!c) return DFLASH_EINVAL;
+  StageTimer t(c, DFLASH_STAGE_BLOCK);
+  return block_common(c, n_seqs, seqs, anchors, h, logits, false);
+}
+
+int dflash_time_stage(dflash_ctx* c, int32_t stage) {
+  if (!c || stage > DFLASH_STAGE_APPEND) return DFLASH_EINVAL;
+  c->timed_stage = stage < 0 ? -1 : stage;
+  return DFLASH_OK;
+}
+
+int dflash_read_timing(dflash_ctx* c, double* total_ms, int64_t* count) {
+  if (!c || !total_ms || !count) return DFLASH_EINVAL;
+  double tot = 0.0;
+  const size_t pairs = c->ev_used / 2;
+  for (size_t i = 0; i < pairs; i++) {
+    TRY_HIP(c, hipEventSynchronize(c->ev_pool[2 * i + 1]), "timing sync");
+    float ms = 0.f;
+    TRY_HIP(c, hipEventElapsedTime(&ms, c->ev_pool[2 * i], c->ev_pool[2 * i + 1]), "timing");
+    tot += ms;
+  }
+  c->ev_used = 0;
+  *total_ms = tot;
+  *count = (int64_t)pairs;
+  return DFLASH_OK;
+}
+
+int dflash_block_hidden(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
+                        float* hidden) {
+  if (!c) return DFLASH_EINVAL;
+  return block_common(c, n_seqs, seqs, anchors, h, hidden, true);
+}
+
+const char* dflash_last_error(const dflash_ctx* c) { return c ? c->err.c_str() : g_create_err.c_str(); }
+
+void dflash_destroy(dflash_ctx* c) { delete c; }
+
+int dflash_read_kv(const dflash_ctx* c, int32_t layer, int32_t seq, int32_t row0, int32_t n, float* k, float* v) {
+  if (!c || !k || !v) return DFLASH_EINVAL;
+  const dflash_geometry& g = c->g;
+  if (layer < 0 || layer >= g.layers || seq < 0 || seq >= g.max_seqs || row0 < 0 || n < 0 || row0 + n > g.max_ctx)
+    return DFLASH_EINVAL;
+  if (n == 0) return DFLASH_OK;
+  const size_t hd = g.head_dim, kvh = g.kv_heads;
+  const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd;
+  for (size_t h = 0; h < kvh; h++) {
+    const size_t src = (size_t)layer * layer_cache + (((size_t)seq * kvh + h) * g.max_ctx + row0) * hd;
+    hipError_t e = hipMemcpy2DAsync(k + h * hd, kvh * hd * 4, c->at<float>(c->lay.kc) + src, hd * 4, hd * 4, n,
+                                    hipMemcpyDeviceToDevice, c->st);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(v + h * hd, kvh * hd * 4, c->at<float>(c->lay.vc) + src, hd * 4, hd * 4, n,
+                           hipMemcpyDeviceToDevice, c->st);
+    if (e != hipSuccess) return DFLASH_EHIP;
+  }
+  return DFLASH_OK;
+}
+
+int dflash_quant_act(const float* x, int32_t rows, int32_t cols, int8_t* q, float* d, void* stream) {
+  if (!x || !q || !d || rows < 0 || cols <= 0 || cols % 32) return DFLASH_EINVAL;
+  if (rows == 0) return DFLASH_OK;
+  return launch_quant_rows(x, rows, cols, q, d, (hipStream_t)stream) == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
+}
+
+int dflash_packed_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* bytes) {
+  if (!bytes || !is_fmt(fmt) || rows <= 0 || cols <= 0 || rows % 16) return DFLASH_EINVAL;
+  if (fmt != DFLASH_F32 && cols % 128) return DFLASH_EINVAL;
+  *bytes = packed_bytes(fmt, rows, cols);
+  return DFLASH_OK;
+}
+
+int dflash_pack(int32_t fmt, int32_t rows, int32_t cols, dflash_matrix w, void* packed, void* stream) {
+  size_t b;
+  if (dflash_packed_bytes(fmt, rows, cols, &b) || !packed || !w.codes || (fmt != DFLASH_F32 && !w.scales))
+    return DFLASH_EINVAL;
+  return launch_pack(fmt, w.codes, w.scales, rows, cols, packed, 0, 1, (hipStream_t)stream) == hipSuccess
+             ? DFLASH_OK
+             : DFLASH_EHIP;
+}
+
+// scratch: padded activations [Mpad][cols] int8, their scales [cols/32][Mpad] f32, partials.
+int dflash_gemm_scratch_bytes(int32_t rows, int32_t cols, int32_t m, int32_t splits, size_t* bytes) {
+  if (!bytes || rows <= 0 || cols <= 0 || cols % 128 || rows % 16 || m < 1 || m > MROWS) return DFLASH_EINVAL;
+  const int Mpad = round16(m);
+  const int s = splits > 0 ? normalize_splits(cols, splits) : choose_splits(rows, cols, Mpad);
+  *bytes = align256((size_t)Mpad * cols) + align256((size_t)(cols / 32) * Mpad * 4) + (size_t)s * Mpad * rows * 4;
+  return DFLASH_OK;
+}
+
+int dflash_gemm(int32_t fmt, const void* packed, int32_t rows, int32_t cols, const int8_t* xq, const float* dx,
+                int32_t m, float* y, int32_t splits, void* scratch, void* stream) {
+  size_t need;
+  if ((fmt != DFLASH_Q4_32 && fmt != DFLASH_Q8_32) || !packed || !xq || !dx || !y || !scratch ||
+      dflash_gemm_scratch_bytes(rows, cols, m, splits, &need))
+    return DFLASH_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  const int Mpad = round16(m);
+  const int s = splits > 0 ? normalize_splits(cols, splits) : choose_splits(rows, cols, Mpad);
+  int8_t* xp = (int8_t*)scratch;
+  float* dT = (float*)((uint8_t*)scratch + align256((size_t)Mpad * cols));
+  float* part = (float*)((uint8_t*)dT + align256((size_t)(cols / 32) * Mpad * 4));
+  if (hipMemsetAsync(xp, 0, (size_t)Mpad * cols, st) != hipSuccess) return DFLASH_EHIP;
+  if (hipMemcpyAsync(xp, xq, (size_t)m * cols, hipMemcpyDeviceToDevice, st) != hipSuccess) return DFLASH_EHIP;
+  if (launch_transpose_scales(dx, m, cols / 32, Mpad, dT, st) != hipSuccess) return DFLASH_EHIP;
+  if (launch_gemm_q(fmt, packed, rows, cols, xp, dT, Mpad, s, part, false, 0, 0, st) != hipSuccess) return DFLASH_EHIP;
+  return launch_norm_act(part, s, Mpad, nullptr, nullptr, nullptr, 0.f, m, m, rows, false, nullptr, nullptr, y, st) ==
+                 hipSuccess
+             ? DFLASH_OK
+             : DFLASH_EHIP;
+}
+
+int dflash_group_sums(int32_t fmt, const void* packed, int32_t rows, int32_t cols, const int8_t* xq, int32_t m,
+                      int32_t* sums, void* scratch, void* stream) {
+  size_t need;
+  if ((fmt != DFLASH_Q4_32 && fmt != DFLASH_Q8_32) || !packed || !xq || !sums || !scratch ||
+      dflash_gemm_scratch_bytes(rows, cols, m, 1, &need))
+    return DFLASH_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  const int Mpad = round16(m);
+  int8_t* xp = (int8_t*)scratch;
+  if (hipMemsetAsync(xp, 0, (size_t)Mpad * cols, st) != hipSuccess) return DFLASH_EHIP;
+  if (hipMemcpyAsync(xp, xq, (size_t)m * cols, hipMemcpyDeviceToDevice, st) != hipSuccess) return DFLASH_EHIP;
+  return launch_group_sums(fmt, packed, rows, cols, xp, Mpad, m, sums, st) == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+// Block-vs-context attention (cortiq-engine "dflash.rs", Drafter::block: each q head j reads
+// kv head j / rep; its keys and values are the context rows before the anchor followed by the
+// block's own rows, with no causal mask; s = (q . k) * hd^-0.5, softmax, y = sum p v).
+//
+// The pages' device kernel (gpu_wgpu/dflash_dev.rs, dflash_attn) writes every score to a global
+// scratch and re-reads it; here the context is split into chunks, each workgroup keeps a
+// running (max, sum, acc) per query in registers (online softmax), and a merge combines the
+// chunks.  A workgroup serves one (sequence, kv head, chunk) with one wave per q head of the
+// group; the 16 block rows of a head are the 16 columns of v_mfma_f32_16x16x4f32 tiles:
+//   S^T[key][q] = K . Q^T   (A = 16 keys staged in LDS, B = the wave's queries in registers)
+//   Y^T[d][q]  += V^T . P^T (A = 16-dim slices of V from LDS, B = the wave's probabilities,
+//                            already in the accumulator layout of S^T)
+// so the probabilities never leave registers.  Context K/V is f32 [slot][kvh][max_ctx][hd].
+#include "common.h"
+
+namespace dfl {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int HD>
+__global__ __launch_bounds__(1024) void k_attn_partial(AttnShape a, SeqInfo si, const float* __restrict__ q,
+                                                      const float* __restrict__ kb, const float* __restrict__ vb,
+                                                      const float* __restrict__ kc, const float* __restrict__ vc,
+                                                      float* __restrict__ part, float* __restrict__ ml) {
+  constexpr int KS = HD + 4;  // padded LDS key row (floats)
+  __shared__ __attribute__((aligned(16))) float Ks[16 * KS];
+  __shared__ __attribute__((aligned(16))) float Vs[16 * KS];
+  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int nctx = si.nctx[s];
+  const int nch = (nctx + a.ck - 1) / a.ck;
+  if (c > nch) return;  // the whole workgroup: this sequence has fewer chunks
+  const int rep = a.nh / a.kvh;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int quarter = lane >> 4, col = lane & 15;
+  const bool blockchunk = c == nch;
+  const int k0 = blockchunk ? 0 : c * a.ck;
+  const int kend = blockchunk ? a.B : min(nctx, (c + 1) * a.ck);
+  const float *Kbase, *Vbase;
+  size_t kstride;
+  if (blockchunk) {
+    Kbase = kb + ((size_t)s * a.B * a.kvh + g) * HD;
+    Vbase = vb + ((size_t)s * a.B * a.kvh + g) * HD;
+    kstride = (size_t)a.kvh * HD;
+  } else {
+    Kbase = kc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
+    Vbase = vc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
+    kstride = HD;
+  }
+  const int j = g * rep + w;
+  v4f qr[HD / 16];
+#pragma unroll
+  for (int i4 = 0; i4 < HD / 16; i4++)
+    qr[i4] = col < a.B ? *(const v4f*)(q + ((size_t)(s * a.B + col) * a.nh + j) * HD + 16 * i4 + 4 * quarter)
+                       : (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  v4f acc[HD / 16];
+#pragma unroll
+  for (int dt = 0; dt < HD / 16; dt++) acc[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = k0; t0 < kend; t0 += 16) {
+    __syncthreads();
+    for (int i = tid; i < 16 * (HD / 4); i += blockDim.x) {
+      const int r = i / (HD / 4), c4 = i % (HD / 4);
+      const int key = t0 + r;
+      v4f kv = (v4f){0.f, 0.f, 0.f, 0.f}, vv = kv;
+      if (key < kend) {
+        kv = *(const v4f*)(Kbase + (size_t)key * kstride + 4 * c4);
+        vv = *(const v4f*)(Vbase + (size_t)key * kstride + 4 * c4);
+      }
+      *(v4f*)(Ks + r * KS + 4 * c4) = kv;
+      *(v4f*)(Vs + r * KS + 4 * c4) = vv;
+    }
+    __syncthreads();
+    v4f st0 = (v4f){0.f, 0.f, 0.f, 0.f}, st1 = st0;
+#pragma unroll
+    for (int i4 = 0; i4 < HD / 16; i4++) {
+      const v4f kv = *(const v4f*)(Ks + col * KS + 16 * i4 + 4 * quarter);
+      st0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[0], qr[i4][0], st0, 0, 0, 0);
+      st1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[1], qr[i4][1], st1, 0, 0, 0);
+      st0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[2], qr[i4][2], st0, 0, 0, 0);
+      st1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[3], qr[i4][3], st1, 0, 0, 0);
+    }
+    const v4f st = st0 + st1;
+    float p[4], mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int key = t0 + 4 * quarter + r;
+      p[r] = key < kend ? st[r] * a.scale : -INFINITY;
+      mx = fmaxf(mx, p[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float corr = expf(m_run - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      p[r] = expf(p[r] - m_new);
+      ps += p[r];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; dt++) {
+      acc[dt] *= corr;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float va = Vs[(4 * quarter + i) * KS + 64 * (dt >> 2) + 4 * col + (dt & 3)];
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va, p[i], acc[dt], 0, 0, 0);
+      }
+    }
+  }
+  if (col >= a.B) return;
+  const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + w) * 16 + col;
+  float* dst = part + prow * HD;
+#pragma unroll
+  for (int d4 = 0; d4 < HD / 64; d4++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      // accumulator (dt = 4*d4 + e, row 4*quarter + r) holds dim 64*d4 + 16*quarter + 4*r + e
+      const v4f v = (v4f){acc[4 * d4][r], acc[4 * d4 + 1][r], acc[4 * d4 + 2][r], acc[4 * d4 + 3][r]};
+      *(v4f*)(dst + 64 * d4 + 16 * quarter + 4 * r) = v;
+    }
+  if (quarter == 0) {
+    ml[prow * 2] = m_run;
+    ml[prow * 2 + 1] = l_run;
+  }
+}
+
+__device__ __forceinline__ void emit_q8(float y, size_t qi, int8_t* __restrict__ xq, float* __restrict__ dx,
+                                        size_t di, int lane) {
+  float amax = fabsf(y);
+#pragma unroll
+  for (int o = 16; o; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+  int8_t qv = 0;
+  float d = 0.f;
+  if (amax > 0.f) {
+    d = amax / 127.0f;
+    const float inv = 127.0f / amax;
+    float r = __builtin_rintf(y * inv);
+    r = fminf(fmaxf(r, -127.f), 127.f);
+    qv = (int8_t)r;
+  }
+  xq[qi] = qv;
+  if ((lane & 31) == 0) dx[di] = d;
+}
+
+// One wave per (q head, block row, sequence): combine the chunks' (max, sum, acc).
+template <int HD, bool QUANT>
+__global__ __launch_bounds__(64) void k_attn_merge(AttnShape a, SeqInfo si, const float* __restrict__ part,
+                                                  const float* __restrict__ ml, int Mpad, int8_t* __restrict__ xq,
+                                                  float* __restrict__ dxT, float* __restrict__ xf) {
+  const int j = blockIdx.x, r = blockIdx.y, s = blockIdx.z, lane = threadIdx.x;
+  const int rep = a.nh / a.kvh, g = j / rep, w = j % rep;
+  const int nch = (si.nctx[s] + a.ck - 1) / a.ck;
+  const size_t base = (((size_t)s * a.kvh + g) * a.maxch) * rep;
+  float mx = -INFINITY;
+  for (int c = 0; c <= nch; c++) mx = fmaxf(mx, ml[(((base + (size_t)c * rep + w) * 16) + r) * 2]);
+  float L = 0.f, y[HD / 64];
+#pragma unroll
+  for (int t = 0; t < HD / 64; t++) y[t] = 0.f;
+  for (int c = 0; c <= nch; c++) {
+    const size_t row = (base + (size_t)c * rep + w) * 16 + r;
+    const float e = expf(ml[row * 2] - mx);
+    L += ml[row * 2 + 1] * e;
+#pragma unroll
+    for (int t = 0; t < HD / 64; t++) y[t] += part[row * HD + lane + 64 * t] * e;
+  }
+  const float invL = 1.0f / L;
+  const int m = s * a.B + r;
+  const size_t qd = (size_t)a.nh * HD;
+#pragma unroll
+  for (int t = 0; t < HD / 64; t++) {
+    const float v = y[t] * invL;
+    const size_t colx = (size_t)j * HD + lane + 64 * t;
+    if (QUANT)
+      emit_q8(v, (size_t)m * qd + colx, xq, dxT, (colx >> 5) * Mpad + m, lane);
+    else
+      xf[(size_t)m * qd + colx] = v;
+  }
+}
+
+template <int HD>
+static hipError_t attn_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
+                          const float* kc, const float* vc, float* part, float* ml, int Mpad, bool quant, int8_t* xq,
+                          float* dxT, float* xf, hipStream_t st) {
+  int maxn = 0;
+  for (int i = 0; i < si.n; i++) {
+    const int nch = (si.nctx[i] + a.ck - 1) / a.ck;
+    if (nch > maxn) maxn = nch;
+  }
+  if (maxn + 1 > a.maxch) return hipErrorInvalidValue;
+  const int rep = a.nh / a.kvh;
+  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn + 1, a.kvh, si.n), dim3(64 * rep), 0, st, a, si, q, kb, vb, kc,
+                     vc, part, ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (quant)
+    hipLaunchKernelGGL((k_attn_merge<HD, true>), dim3(a.nh, a.B, si.n), dim3(64), 0, st, a, si, part, ml, Mpad, xq,
+                       dxT, xf);
+  else
+    hipLaunchKernelGGL((k_attn_merge<HD, false>), dim3(a.nh, a.B, si.n), dim3(64), 0, st, a, si, part, ml, Mpad, xq,
+                       dxT, xf);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
+                            const float* kc, const float* vc, float* part, float* ml, int Mpad, bool quant,
+                            int8_t* xq, float* dxT, float* xf, hipStream_t st) {
+  if (a.nh % a.kvh || a.nh / a.kvh > 16 || a.B > 16 || a.ck % 16 || a.ck <= 0) return hipErrorInvalidValue;
+  if (a.hd == 64) return attn_hd<64>(a, si, q, kb, vb, kc, vc, part, ml, Mpad, quant, xq, dxT, xf, st);
+  if (a.hd == 128) return attn_hd<128>(a, si, q, kb, vb, kc, vc, part, ml, Mpad, quant, xq, dxT, xf, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dfl

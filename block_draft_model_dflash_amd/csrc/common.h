@@ -1,0 +1,99 @@
+// Internal declarations of the gfx950 DFlash library: packed weight layout, kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dfl {
+
+enum Fmt { F32 = 0, Q4 = 1, Q8 = 2 };
+
+// Packed ("tiled") quantized weights.  A superblock covers 16 output rows (an n-tile) and 128
+// input columns (4 groups of 32).  Superblocks are stored [n-tile][k-block], so one wave
+// streams one n-tile's row of superblocks front to back.
+//
+// Q4 superblock, 1152 bytes:
+//   bytes [0, 1024): 64 lanes x 16 bytes.  Lane l's dword j (group g = 4*kb + j) holds the
+//     codes of row 16*t + l%16, columns k0 = 32*g + 8*(l/16) .. k0+7: byte b keeps column
+//     k0+b in its low nibble and column k0+4+b in its high nibble (two's complement nibbles).
+//     (dword << 4) & 0xF0F0F0F0 then gives 16*q of columns k0..k0+3 as signed bytes and
+//     dword & 0xF0F0F0F0 gives 16*q of k0+4..k0+7: the B operand of one 16x16x32 int8 MFMA.
+//   bytes [1024, 1152): f16 scales [16 rows][4 groups].
+// Q8 superblock, 2176 bytes:
+//   bytes [0, 1024): lane l 16 bytes = groups j = 0, 1 (8 codes each, columns k0..k0+7);
+//   bytes [1024, 2048): the same for groups 2, 3; bytes [2048, 2176): f16 scales [16][4].
+// F32 matrices stay row-major [rows][cols] (rows permuted the same way as tiles below).
+constexpr int SB_Q4 = 1152, SB_Q8 = 2176;
+constexpr int SB_SCALES_Q4 = 1024, SB_SCALES_Q8 = 2048;
+
+inline size_t packed_bytes(int fmt, long rows, long cols) {
+  if (fmt == F32) return (size_t)rows * cols * 4;
+  return (size_t)(rows / 16) * (cols / 128) * (fmt == Q4 ? SB_Q4 : SB_Q8);
+}
+
+constexpr int MAX_SEQS_ARG = 64;  // sequences of one block call (max_seqs*block <= 128)
+
+// Per-call sequence table passed by value to the block kernels.
+struct SeqInfo {
+  int n;                        // sequences in this call
+  int slot[MAX_SEQS_ARG];       // cache slot of each
+  int nctx[MAX_SEQS_ARG];       // context rows each attends to (index 0 .. nctx-1)
+  long long pos0[MAX_SEQS_ARG]; // position of block row 0 (the anchor)
+};
+
+// ---- launchers (return the launch's hipError_t) ----
+
+// Repack a canonical matrix into tiles; destination n-tile of source tile t is
+// tile_off + t * tile_stride (used to concatenate and interleave matrices).
+hipError_t launch_pack(int fmt, const void* codes, const void* scales, int rows, int cols, void* out, long tile_off,
+                       long tile_stride, hipStream_t st);
+
+// Quantized weight-streaming GEMM.  xq [Mpad][K] int8 (rows >= M zero or ignored), dxT
+// [K/32][Mpad] f32.  direct: out[m*out_ld + n] for m < m_store; else out is [S][Mpad][N].
+hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int Mpad,
+                         int splits, float* out, bool direct, int out_ld, int m_store, hipStream_t st);
+// Number of K slices the GEMM uses for a shape when the caller does not fix it, and the
+// number it really uses for a requested count (slices of whole 128-column blocks).
+int choose_splits(int N, int K, int Mpad);
+int normalize_splits(int K, int s);
+hipError_t launch_group_sums(int fmt, const void* W, int N, int K, const int8_t* xq, int Mpad, int M,
+                             int32_t* sums, hipStream_t st);
+// f32 GEMM: x [Mpad][K] f32; same output conventions (S = 1).
+hipError_t launch_gemm_f32(const float* W, int N, int K, const float* x, int Mpad, int M, float* out, bool direct,
+                           int out_ld, int m_store, hipStream_t st);
+
+// Activation producers.  Every one writes rows [0, Mpad): rows >= M are zero.  quant: xq
+// [Mpad][N] int8 + dxT [N/32][Mpad]; else xf [Mpad][N] f32.
+//
+// v = (resid ? resid[m] : 0) + sum_{s<S} src[(s*src_mstride + m)*N + i]; h_out (optional)
+// receives v; with a norm weight w the row is RMSNormed first.
+hipError_t launch_norm_act(const float* src, int S, int src_mstride, const float* resid, float* h_out,
+                           const float* w, float eps, int M, int Mpad, int N, bool quant, int8_t* xq, float* dxT,
+                           float* xf, hipStream_t st);
+// a = silu(gate) * up from the interleaved gate|up partials [S][Mpad][2I].
+hipError_t launch_swiglu_act(const float* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
+                             float* xf, hipStream_t st);
+// q/k/v of the block rows from the fused projection partials [S][Mpad][qd + 2 kvd]:
+// q-norm / k-norm, RoPE at si.pos0[m / B] + m % B.
+hipError_t launch_qkv_epilogue(const float* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
+                               int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
+                               float* q, float* k, float* v, hipStream_t st);
+// Context rows into the cache from the all-layer K|V partials [S][Mpad][L * 2 kvd].
+hipError_t launch_kv_append(const float* part, int S, int Mpad, int n, int layers, int kvh, int hd,
+                            const float* k_norms, const float* inv_freq, float eps, long long pos0, int row0,
+                            int slot, int max_seqs, int max_ctx, float* kc, float* vc, hipStream_t st);
+
+// Attention of the block rows over context + block keys, split over context chunks.
+struct AttnShape {
+  int nh, kvh, hd, B, max_ctx, max_seqs, ck, maxch;
+  float scale;
+};
+hipError_t launch_attention(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
+                            const float* kc, const float* vc, float* part, float* ml, int Mpad, bool quant,
+                            int8_t* xq, float* dxT, float* xf, hipStream_t st);
+
+hipError_t launch_inv_freq(double theta, int hd, float* out, hipStream_t st);
+hipError_t launch_quant_rows(const float* x, int rows, int cols, int8_t* q, float* d, hipStream_t st);
+hipError_t launch_transpose_scales(const float* d, int rows, int groups, int Mpad, float* dT, hipStream_t st);
+
+}  // namespace dfl

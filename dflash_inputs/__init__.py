@@ -69,6 +69,7 @@ class Config:
     taps_std: float = 1.0
     emb_std: float = 0.02
     seed: int = 1000
+    weight_seed: int = 0  # seed of the weights when they are another workload's drafter (0: seed)
 
     @property
     def tap_width(self) -> int:
@@ -95,10 +96,11 @@ CONFIGS = {
                       Q4_32, Q8_32, Q8_32, seed=1002),
     "qwen3_8b": Config("qwen3_8b", 5, 4096, 32, 8, 128, 12288, 5, 151936, 16, 4096,
                        Q4_32, Q8_32, Q8_32, seed=1003),
+    # the same 8B-shaped drafter (its weights drawn from seed 1003) over other contexts
     "qwen3_8b_long": Config("qwen3_8b_long", 5, 4096, 32, 8, 128, 12288, 5, 151936, 16, 32768,
-                            Q4_32, Q8_32, Q8_32, append_per_block=16, seed=1004),
+                            Q4_32, Q8_32, Q8_32, append_per_block=16, seed=1004, weight_seed=1003),
     "qwen3_8b_batch8": Config("qwen3_8b_batch8", 5, 4096, 32, 8, 128, 12288, 5, 151936, 16, 8192,
-                              Q4_32, Q8_32, Q8_32, n_seqs=8, seed=1005),
+                              Q4_32, Q8_32, Q8_32, n_seqs=8, seed=1005, weight_seed=1003),
 }
 CONFIG_ORDER = ["tiny_f32", "small_q", "qwen3_8b", "qwen3_8b_long", "qwen3_8b_batch8"]
 
@@ -164,7 +166,7 @@ def _draw_matrix(cfg: Config, index: int, rows: int, cols: int, fmt: int, chunk_
     codes_parts, scale_parts = [], []
     for c0 in range(0, rows, chunk_rows):
         n = min(chunk_rows, rows - c0)
-        r = _rng(cfg.seed, _S_WEIGHT, index * 100003 + c0 // chunk_rows)
+        r = _rng(cfg.weight_seed or cfg.seed, _S_WEIGHT, index * 100003 + c0 // chunk_rows)
         w = r.standard_normal((n, cols), dtype=np.float32) * np.float32(cfg.weight_std)
         c, s = quantize_rows(w, fmt)
         codes_parts.append(c)
@@ -176,7 +178,7 @@ def _draw_matrix(cfg: Config, index: int, rows: int, cols: int, fmt: int, chunk_
 
 
 def _norm_vec(cfg: Config, index: int, n: int) -> np.ndarray:
-    r = _rng(cfg.seed, _S_NORM, index)
+    r = _rng(cfg.weight_seed or cfg.seed, _S_NORM, index)
     return (np.float32(cfg.norm_mean) + r.standard_normal(n, dtype=np.float32) * np.float32(cfg.norm_std)).astype(np.float32)
 
 
@@ -242,7 +244,7 @@ def make_block_input(cfg: Config, seq: int, index: int) -> np.ndarray:
     """Block rows [anchor, MASK, ..., MASK] as embeddings: row 0 the anchor token's (fresh per
     block), rows 1.. the mask token's (one vector per drafter), each N(0, emb_std)."""
     a = _rng(cfg.seed, _S_ANCHOR, seq * 1_000_003 + index).standard_normal(cfg.hidden, dtype=np.float32)
-    m = _rng(cfg.seed, _S_MASK, 0).standard_normal(cfg.hidden, dtype=np.float32)
+    m = _rng(cfg.weight_seed or cfg.seed, _S_MASK, 0).standard_normal(cfg.hidden, dtype=np.float32)
     h = np.empty((cfg.block, cfg.hidden), dtype=np.float32)
     h[0] = a * np.float32(cfg.emb_std)
     h[1:] = m * np.float32(cfg.emb_std)

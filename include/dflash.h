@@ -1,0 +1,201 @@
+/* dflash.h -- C ABI of the MI355X (gfx950) DFlash 2 block-drafter library.
+ *
+ * What it computes (cortiq-engine "dflash.rs", module header; Drafter::settle_rows and
+ * Drafter::block): a drafter of a few Qwen3-shaped layers keeps, per position of its context,
+ *     t   = RMSNorm(FC . taps, hidden_norm)            taps = the target's tapped layer outputs
+ *     K_l = RoPE(RMSNorm(Wk_l . t, k_norm_l), pos)     V_l = Wv_l . t        for every layer l
+ * and a block of rows [anchor, MASK, ..., MASK] at positions a, a+1, ... runs through the
+ * layers (RMSNorm, Wq/Wk/Wv, q/k RMSNorm, RoPE, attention over the context before a and the
+ * block's own rows -- not causal --, Wo + residual, RMSNorm, SwiGLU MLP + residual), then
+ * logits = Head . RMSNorm(h, norm) for every block row (row j >= 1 drafts position a + j).
+ *
+ * Matrices come in three formats (the pages name a 4-bit and an 8-bit format without their
+ * bytes, gpu_wgpu/dflash_dev.rs kind_of; these layouts are this library's contract):
+ *   DFLASH_F32    float [rows][cols], activations stay f32;
+ *   DFLASH_Q4_32  per row and group of 32 columns one IEEE f16 scale d and 32 signed 4-bit
+ *                 codes q (weight = d*q): codes uint8 [rows][cols/2], column 2j in the low
+ *                 nibble of byte j; scales f16 [rows][cols/32];
+ *   DFLASH_Q8_32  the same with int8 codes [rows][cols].
+ * Before a quantized matrix the activations are quantized per row and group of 32 (A8_32):
+ *   amax = max|x|; d = amax/127 and inv = 127/amax (f32 divisions);
+ *   q = clamp(rint(x*inv), -127, 127) (f32 product, ties to even); amax == 0 -> d = 0, q = 0.
+ * The quantized product sums q_w*q_x exactly per group and scales each group's sum by
+ * d_w*d_x (gpu_wgpu/dflash_dev.rs, Dev::q4: int8 activations per group of 32).
+ *
+ * Conventions for every call:
+ *  - Device pointers are device-global memory of the GPU current when dflash_create ran
+ *    (e.g. torch tensors' data_ptr()); host pointers are marked "host".
+ *  - All GPU work of a ctx is enqueued on its stream (dflash_create / dflash_set_stream) and
+ *    nothing synchronizes except dflash_create; a call returns once its work is enqueued.
+ *  - Every call checks its arguments on the host before enqueueing anything and, on error,
+ *    returns a negative status with the ctx state unchanged (dflash_last_error says why).
+ *  - The library never allocates device memory: the caller hands dflash_create one workspace
+ *    buffer (packed weights, K/V cache, activations) and owns it, the taps, block inputs and
+ *    logits.  Borrowed buffers must stay valid until the work enqueued on them has run.
+ *  - Not thread safe: one ctx is used by one host thread at a time.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dflash_status {
+  DFLASH_OK = 0,
+  DFLASH_EINVAL = -1,    /* a bad argument (null pointer, out-of-range index, ...) */
+  DFLASH_ECAPACITY = -2, /* the context would exceed max_ctx rows of a sequence */
+  DFLASH_EHIP = -3,      /* the HIP runtime reported an error */
+  DFLASH_ENOTSUP = -4    /* a geometry outside the kernels' limits */
+};
+
+enum dflash_format { DFLASH_F32 = 0, DFLASH_Q4_32 = 1, DFLASH_Q8_32 = 2 };
+
+/* The drafter's geometry (cortiq-engine dflash.rs, struct Geometry, minus the row
+ * convolutions, the selector, windows and target binding) plus the cache's capacity.
+ * Limits: layers >= 1; 2 <= block <= 16; heads % kv_heads == 0 and heads/kv_heads <= 16;
+ * head_dim 64 or 128; hidden, heads*head_dim, intermediate and n_taps*hidden multiples of 128
+ * (of 4 for f32 matrices); vocab a multiple of 16; max_seqs*block <= 128; max_ctx >= 0. */
+typedef struct {
+  double rope_theta; /* RoPE base (inv_freq[i] = theta^(-2i/head_dim)) */
+  double eps;        /* RMSNorm epsilon, applied in f32 */
+  int32_t layers, hidden, heads, kv_heads, head_dim, intermediate, vocab, block, n_taps;
+  int32_t body_fmt; /* Wq, Wk, Wv, Wo, gate, up, down */
+  int32_t fc_fmt;   /* FC [hidden][n_taps*hidden] */
+  int32_t head_fmt; /* head [vocab][hidden] */
+  int32_t max_seqs; /* independent sequences (separate contexts, shared weights) */
+  int32_t max_ctx;  /* context rows a sequence can hold */
+} dflash_geometry;
+
+/* A matrix in the canonical layout above (device pointers; scales NULL for DFLASH_F32). */
+typedef struct {
+  const void* codes;
+  const void* scales;
+} dflash_matrix;
+
+typedef struct {
+  const float *in_norm, *post_norm; /* [hidden] */
+  const float *q_norm, *k_norm;     /* [head_dim] */
+  dflash_matrix q;                  /* [heads*head_dim][hidden] */
+  dflash_matrix k, v;               /* [kv_heads*head_dim][hidden] */
+  dflash_matrix o;                  /* [hidden][heads*head_dim] */
+  dflash_matrix gate, up;           /* [intermediate][hidden] */
+  dflash_matrix down;               /* [hidden][intermediate] */
+} dflash_layer_weights;
+
+typedef struct {
+  dflash_matrix fc, head;
+  const float *hidden_norm, *norm;   /* [hidden] */
+  const dflash_layer_weights* layer; /* host array [layers] */
+} dflash_weights;
+
+typedef struct dflash_ctx dflash_ctx;
+
+/* Bytes of workspace dflash_create needs for g (packed weights, the K/V cache of max_seqs x
+ * max_ctx rows in f32, activations).  *bytes receives the size. */
+int dflash_workspace_bytes(const dflash_geometry* g, size_t* bytes);
+
+/* Build a drafter: checks g, carves `workspace` (device, >= dflash_workspace_bytes, 256-byte
+ * aligned), repacks every matrix of w into the kernels' tiled layout inside it, copies the norm
+ * weights, computes the RoPE table, and waits for that work on `stream` (a hipStream_t, or NULL
+ * for the default stream) so w may be freed on return.  Every sequence starts empty at
+ * position 0.  *out receives the ctx (free it with dflash_destroy; the workspace stays the
+ * caller's). */
+int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* workspace, size_t bytes, void* stream,
+                  dflash_ctx** out);
+
+/* Later calls enqueue on `stream` (hipStream_t; NULL = default stream). */
+int dflash_set_stream(dflash_ctx* c, void* stream);
+
+/* Add context rows (cortiq-engine dflash.rs, Drafter::push_context / queue_context /
+ * settle_rows): `taps` is device [n][n_taps*hidden] f32, the rows of positions pos..pos+n-1.
+ * If first <= pos <= first+len, positions >= pos are forgotten first; if pos < first or
+ * pos > first+len the sequence starts over with first = pos.  Each row's K and V (every
+ * layer, k-norm and RoPE at its absolute position) go to the device cache at index
+ * position - first.  n == 0 only applies that bookkeeping.  DFLASH_ECAPACITY if the sequence
+ * would pass max_ctx rows (nothing changes then). */
+int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps, int32_t n);
+
+/* Forget positions >= pos of a sequence (dflash.rs, Drafter::truncate); the first stays. */
+int dflash_ctx_truncate(dflash_ctx* c, int32_t seq, int64_t pos);
+
+/* Empty a sequence and set its first position to 0 (dflash.rs, Drafter::reset). */
+int dflash_ctx_reset(dflash_ctx* c, int32_t seq);
+
+/* host *first, *end receive the positions a sequence holds: [first, end). */
+int dflash_ctx_span(const dflash_ctx* c, int32_t seq, int64_t* first, int64_t* end);
+
+/* One block for each of n_seqs distinct sequences (dflash.rs, Drafter::block, and the head of
+ * the module header): seqs and anchors are host [n_seqs]; h is device [n_seqs][block][hidden]
+ * f32, the rows' embeddings ([anchor, MASK...]) at positions anchors[i]+r; logits receives
+ * device [n_seqs][block][vocab] f32 for every block row.  Layer l of sequence s attends to its
+ * context positions [first, clamp(min(anchor, first+len), >= first)) and to all block rows.
+ * The context is not modified. */
+int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors,
+                         const float* h, float* logits);
+
+/* The same block, stopping after the final RMSNorm: hidden receives device
+ * [n_seqs][block][hidden] f32 (the rows the head reads; a diagnostic of the block body). */
+int dflash_block_hidden(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors,
+                        const float* h, float* hidden);
+
+/* The last error message of c (or of the last failed dflash_create when c is NULL);
+ * valid until the next call on c. */
+const char* dflash_last_error(const dflash_ctx* c);
+
+void dflash_destroy(dflash_ctx* c);
+
+/* ---- unit entry points (tests and microbenchmarks); each enqueues on `stream` ---- */
+
+/* A8_32 of rows x rows: x device [rows][cols] f32 -> q device [rows][cols] int8 and
+ * d device [rows][cols/32] f32.  cols % 32 == 0. */
+int dflash_quant_act(const float* x, int32_t rows, int32_t cols, int8_t* q, float* d, void* stream);
+
+/* Bytes of the tiled (packed) form of a [rows][cols] matrix of format fmt. */
+int dflash_packed_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* bytes);
+
+/* Repack a canonical matrix (device) into the tiled form (device, dflash_packed_bytes). */
+int dflash_pack(int32_t fmt, int32_t rows, int32_t cols, dflash_matrix w, void* packed, void* stream);
+
+/* y device [m][rows] f32 = W . x through the production weight-streaming kernel, for a packed
+ * quantized W and A8_32 activations xq device [m][cols] int8, dx device [m][cols/32] f32;
+ * splits: 0 = the library's choice, else the number of K slices.  m <= 128.
+ * `scratch` is device memory of at least splits*ceil16(m)*rows*4 + 32*cols*ceil16(m)*... bytes:
+ * pass dflash_gemm_scratch_bytes(). */
+int dflash_gemm_scratch_bytes(int32_t rows, int32_t cols, int32_t m, int32_t splits, size_t* bytes);
+int dflash_gemm(int32_t fmt, const void* packed, int32_t rows, int32_t cols, const int8_t* xq, const float* dx,
+                int32_t m, float* y, int32_t splits, void* scratch, void* stream);
+
+/* Exact per-group integer sums of the same kernel: sums device [m][rows][cols/32] int32,
+ * sum over the group of q_w*q_x (the quantized product's integer accumulators). */
+int dflash_group_sums(int32_t fmt, const void* packed, int32_t rows, int32_t cols, const int8_t* xq, int32_t m,
+                      int32_t* sums, void* scratch, void* stream);
+
+/* Stage timing (the pages time a block's stages with GPU timestamps; here HIP events on the
+ * ctx stream).  dflash_time_stage(c, stage) brackets every later launch of one stage with an
+ * event pair (stage < 0 stops); dflash_read_timing waits for the recorded pairs and returns
+ * their summed milliseconds and count, then forgets them.  Stages: */
+enum dflash_stage {
+  DFLASH_STAGE_HEAD = 0,      /* the head's matrix product (logits) */
+  DFLASH_STAGE_QKV = 1,       /* every layer's Wq|Wk|Wv product */
+  DFLASH_STAGE_ATTENTION = 2, /* every layer's attention (chunks + merge) */
+  DFLASH_STAGE_O = 3,         /* every layer's Wo product */
+  DFLASH_STAGE_GATE_UP = 4,   /* every layer's gate|up product */
+  DFLASH_STAGE_DOWN = 5,      /* every layer's down product */
+  DFLASH_STAGE_BLOCK = 6,     /* the whole block call */
+  DFLASH_STAGE_APPEND = 7     /* the whole append call */
+};
+int dflash_time_stage(dflash_ctx* c, int32_t stage);
+int dflash_read_timing(dflash_ctx* c, double* total_ms, int64_t* count);
+
+/* Copy K and V of context rows row0..row0+n-1 (index = position - first) of one layer and
+ * sequence into device k, v [n][kv_heads][head_dim] f32 (a read-back of the cache). */
+int dflash_read_kv(const dflash_ctx* c, int32_t layer, int32_t seq, int32_t row0, int32_t n, float* k, float* v);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

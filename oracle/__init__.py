@@ -94,7 +94,8 @@ def lib(path: str | None = None):
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        L.og_set_threads(int(os.environ.get("DFLASH_ORACLE_THREADS", os.cpu_count() or 1)))
+        # at most 16 threads: the CPU share of a one-GPU machine, whatever the host reports
+        L.og_set_threads(int(os.environ.get("DFLASH_ORACLE_THREADS", min(16, os.cpu_count() or 1))))
         _lib = L
     return _lib
 

@@ -1,0 +1,85 @@
+"""The C-ABI library builds for gfx950, loads on a CPU-only host and exports every entry point
+include/dflash.h declares; host-side argument checks (no GPU call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import block_draft_model_dflash_amd as D
+import dflash_inputs as di
+from block_draft_model_dflash_amd.drafter import geometry
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(D.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = D.lib()
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing
+
+
+def test_library_is_built_for_gfx950():
+    data = open(D.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+@pytest.mark.parametrize("key", di.CONFIG_ORDER)
+def test_workspace_sizes_of_the_workloads(key):
+    c = di.CONFIGS[key]
+    g = geometry(c, c.ctx + 64, c.n_seqs)
+    n = D.dflash_workspace_bytes(g)
+    # at least the packed weights and the f32 K/V cache
+    ab = di.algorithmic_bytes(c)
+    cache = 2 * c.layers * c.n_seqs * (c.ctx + 64) * c.kv_dim * 4
+    assert n >= ab["body"] + ab["head"] + cache
+
+
+@pytest.mark.parametrize("change,code", [
+    ({"head_dim": 96}, D.DFLASH_ENOTSUP),
+    ({"heads": 6, "kv_heads": 4}, D.DFLASH_EINVAL),
+    ({"block": 1}, D.DFLASH_EINVAL),
+    ({"block": 17}, D.DFLASH_ENOTSUP),
+    ({"hidden": 4000}, D.DFLASH_ENOTSUP),
+    ({"layers": 0}, D.DFLASH_EINVAL),
+    ({"body_fmt": 7}, D.DFLASH_EINVAL),
+])
+def test_geometry_checks(change, code):
+    c = di.CONFIGS["small_q"].replace(**change)
+    g = geometry(c, 600, 1)
+    with pytest.raises(D.DFlashError) as e:
+        D.dflash_workspace_bytes(g)
+    assert e.value.code == code
+    assert "geometry" in D.dflash_last_error(None)
+
+
+def test_too_many_rows_refused():
+    c = di.CONFIGS["qwen3_8b"]
+    with pytest.raises(D.DFlashError) as e:
+        D.dflash_workspace_bytes(geometry(c, 100, 9))  # 9 sequences x 16 rows > 128
+    assert e.value.code == D.DFLASH_ENOTSUP
+
+
+def test_null_arguments_refused_before_any_gpu_work():
+    L = D.lib()
+    g = geometry(di.CONFIGS["tiny_f32"], 128, 1)
+    out = C.c_void_p()
+    assert L.dflash_create(C.byref(g), None, None, 0, None, C.byref(out)) == D.DFLASH_EINVAL
+    assert L.dflash_ctx_append(None, 0, 0, None, 0) == D.DFLASH_EINVAL
+    assert L.dflash_block_forward(None, 1, None, None, None, None) == D.DFLASH_EINVAL
+    assert L.dflash_quant_act(None, 1, 32, None, None, None) == D.DFLASH_EINVAL
+    n = C.c_size_t()
+    assert L.dflash_packed_bytes(D.DFLASH_Q4_32, 16, 100, C.byref(n)) == D.DFLASH_EINVAL
+    assert L.dflash_packed_bytes(D.DFLASH_Q4_32, 32, 256, C.byref(n)) == 0 and n.value == 2 * 2 * 1152
+    assert L.dflash_packed_bytes(D.DFLASH_Q8_32, 16, 128, C.byref(n)) == 0 and n.value == 2176
+    assert L.dflash_gemm_scratch_bytes(64, 256, 129, 0, C.byref(n)) == D.DFLASH_EINVAL

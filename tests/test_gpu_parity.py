@@ -1,0 +1,129 @@
+"""Whole-path parity through the C ABI: context append (K/V cache) and block logits of the GPU
+library against the CPU oracle on the same seeded inputs.
+
+Bar (the drafter's stated tolerance): logits max |d| <= 2e-3 * max |logit| and top-1 agreement
+>= 99.9% of rows; the K/V cache is held to the same relative bound.  The f32 workload has no
+quantizer, so it is held to 1e-5, the f32 rounding of a few layers."""
+import numpy as np
+import pytest
+
+import dflash_inputs as di
+import oracle
+from gpu_common import logits_parity, rel_err, say, weights_for
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+TINY = di.CONFIGS["tiny_f32"]
+SHARP = TINY.replace(key="tiny_f32_sharp", norm_mean=1.0, taps_std=1.0, emb_std=1.0, seed=2001)
+QTINY = di.Config("q_tiny", 2, 256, 4, 2, 64, 512, 2, 1024, 8, 40, di.Q4_32, di.Q8_32, di.Q8_32, seed=2002)
+SMALL = di.CONFIGS["small_q"]
+Q8B = di.CONFIGS["qwen3_8b"]
+
+
+def _pair(cfg, ctx, max_ctx, n_seqs=1, first=0):
+    from block_draft_model_dflash_amd import Drafter
+
+    w = weights_for(cfg)
+    om = oracle.Model(cfg, w, max_ctx=max_ctx, max_seqs=n_seqs)
+    say(f"{cfg.key}: create on the GPU")
+    gm = Drafter(cfg, w, max_ctx=max_ctx, max_seqs=n_seqs)
+    for s in range(n_seqs):
+        taps = di.make_taps(cfg, s, first, ctx)
+        say(f"{cfg.key}: append {ctx} rows to sequence {s} (oracle)")
+        assert om.append(s, first, taps) == 0
+        say(f"{cfg.key}: append {ctx} rows to sequence {s} (GPU)")
+        gm.append(s, first, taps)
+    torch.cuda.synchronize()
+    return w, om, gm
+
+
+def _kv_check(cfg, om, gm, seq, rows, tol):
+    for li in range(cfg.layers):
+        for r0, n in rows:
+            ko, vo = om.read_kv(li, seq, r0, n)
+            kg, vg = gm.read_kv(li, seq, r0, n)
+            torch.cuda.synchronize()
+            ek, ev = rel_err(kg.cpu().numpy(), ko), rel_err(vg.cpu().numpy(), vo)
+            assert ek <= tol and ev <= tol, (li, r0, ek, ev)
+
+
+def _blocks(cfg, om, gm, cases, tol, top1_min):
+    rels, agree = [], []
+    for seqs, anchors, index in cases:
+        h = np.stack([di.make_block_input(cfg, s, index) for s in seqs])
+        say(f"{cfg.key}: block seqs={list(seqs)} anchors={list(anchors)}")
+        got = gm.block_forward(list(seqs), list(anchors), h)
+        torch.cuda.synchronize()
+        ref = om.block_forward(list(seqs), list(anchors), h)
+        rel, top1 = logits_parity(got.cpu().numpy(), ref)
+        say(f"{cfg.key}: rel {rel:.3e} top1 {top1:.4f}")
+        rels.append(rel)
+        agree.append(top1)
+        assert rel <= tol
+    assert np.mean(agree) >= top1_min
+
+
+@pytest.mark.parametrize("cfg", [TINY, SHARP], ids=lambda c: c.key)
+def test_f32_drafter(cfg):
+    _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64, first=100)
+    _kv_check(cfg, om, gm, 0, [(0, cfg.ctx)], 1e-5)
+    cases = [((0,), (100 + cfg.ctx,), 0), ((0,), (100 + cfg.ctx - 9,), 1), ((0,), (100 + cfg.ctx + 5,), 2),
+             ((0,), (50,), 3)]  # an anchor before the first position: no context at all
+    _blocks(cfg, om, gm, cases, 1e-5, 1.0)
+
+
+def test_quantized_small_two_sequences_ragged():
+    cfg = QTINY.replace(n_seqs=2)
+    _, om, gm = _pair(cfg, 37, 100, n_seqs=2)  # 37 rows: two tiles and a ragged tail
+    for m in (om, gm):
+        m.append(1, 500, di.make_taps(cfg, 1, 500, 21))  # a gap: sequence 1 starts over at 500
+    _kv_check(cfg, om, gm, 0, [(0, 37)], 2e-3)
+    _kv_check(cfg, om, gm, 1, [(0, 21)], 2e-3)
+    _blocks(cfg, om, gm, [((0, 1), (37, 521), 0), ((1, 0), (510, 30), 1), ((1,), (600, ), 2)], 2e-3, 0.999)
+
+
+def test_append_chunking_truncate_and_empty_on_gpu():
+    """Rows are independent: any chunking gives the same cache bits; truncate + re-append is
+    a no-op; n = 0 only moves the bookkeeping."""
+    from block_draft_model_dflash_amd import Drafter
+
+    cfg = QTINY
+    w = weights_for(cfg)
+    taps = di.make_taps(cfg, 0, 0, 300)
+    a = Drafter(cfg, w, max_ctx=320)
+    a.append(0, 0, taps)
+    b = Drafter(cfg, w, max_ctx=320)
+    for c0, c1 in [(0, 1), (1, 129), (129, 130), (130, 300)]:
+        b.append(0, c0, taps[c0:c1])
+    b.truncate(0, 200)
+    assert b.span(0) == (0, 200)
+    b.append(0, 200, taps[200:])
+    b.append(0, 300, np.zeros((0, cfg.tap_width), np.float32))
+    assert b.span(0) == (0, 300)
+    for li in range(cfg.layers):
+        ka, va = a.read_kv(li, 0, 0, 300)
+        kb, vb = b.read_kv(li, 0, 0, 300)
+        torch.cuda.synchronize()
+        assert torch.equal(ka, kb) and torch.equal(va, vb)
+    from block_draft_model_dflash_amd import DFlashError
+
+    with pytest.raises(DFlashError):
+        b.append(0, 290, di.make_taps(cfg, 0, 0, 40))  # 330 rows > 320
+    assert b.span(0) == (0, 300)
+
+
+def test_small_quantized_drafter():
+    cfg = SMALL
+    _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64)
+    _kv_check(cfg, om, gm, 0, [(0, 64), (448, 64)], 2e-3)
+    _blocks(cfg, om, gm, [((0,), (cfg.ctx,), i) for i in range(3)], 2e-3, 0.999)
+
+
+@pytest.mark.timeout(600)
+def test_qwen3_8b_shaped_drafter():
+    """The 8B-shaped drafter at its full size: 4096 context rows, 16-row blocks, 151936 vocab."""
+    cfg = Q8B
+    _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64)
+    _kv_check(cfg, om, gm, 0, [(0, 32), (2000, 16), (4064, 32)], 2e-3)
+    _blocks(cfg, om, gm, [((0,), (cfg.ctx,), i) for i in range(2)], 2e-3, 0.999)

@@ -1,0 +1,109 @@
+"""GPU unit parity through the C ABI: the activation quantizer and the quantized product's
+integer accumulators are bit-exact against the oracle on identical inputs; the product itself
+agrees to its f32 rounding bound."""
+import numpy as np
+import pytest
+
+import block_draft_model_dflash_amd as D
+import dflash_inputs as di
+import oracle
+from gpu_common import say
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _st():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _acts(rng, rows, cols):
+    x = rng.standard_normal((rows, cols)) * np.repeat(10.0 ** rng.uniform(-3, 2, (rows, cols // 32)), 32, axis=1)
+    x = x.astype(np.float32)
+    if cols >= 64:
+        x[0, 32:64] = 0.0  # a zero group
+    x[-1, :4] = [127.0, 2.5, -3.5, 0.5]  # exact ties under d = 1
+    x[-1, 4:32] = 0.0
+    return x
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (7, 256), (16, 4096), (130, 2048), (3, 20480)])
+def test_quant_act_bit_exact(rows, cols):
+    say(f"quant_act rows={rows} cols={cols}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = _acts(rng, rows, cols)
+    q, d = oracle.quant_act(x)
+    gq = torch.empty((rows, cols), dtype=torch.int8, device="cuda")
+    gd = torch.empty((rows, cols // 32), dtype=torch.float32, device="cuda")
+    D.dflash_quant_act(_dev(x).data_ptr(), rows, cols, gq.data_ptr(), gd.data_ptr(), _st())
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cpu().numpy(), q)
+    assert np.array_equal(gd.cpu().numpy(), d)
+
+
+def _matrix(rng, fmt, rows, cols, full_range=True):
+    """Codes over the whole range the decoder accepts (-8..7 / -128..127) and positive scales."""
+    scales = (rng.uniform(0.5, 2.0, (rows, cols // 32)) * 0.01).astype(np.float16)
+    if fmt == di.Q4_32:
+        codes = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    else:
+        codes = rng.integers(-128 if full_range else -127, 128, (rows, cols), dtype=np.int16).astype(np.int8)
+    return {"fmt": fmt, "rows": rows, "cols": cols, "codes": codes, "scales": scales}
+
+
+def _packed(mat):
+    n = D.dflash_packed_bytes(mat["fmt"], mat["rows"], mat["cols"])
+    p = torch.empty(n, dtype=torch.uint8, device="cuda")
+    c, s = _dev(mat["codes"]), _dev(mat["scales"])
+    D.dflash_pack(mat["fmt"], mat["rows"], mat["cols"], c.data_ptr(), s.data_ptr(), p.data_ptr(), _st())
+    torch.cuda.synchronize()
+    return p
+
+
+SHAPES = [(16, 128, 1), (48, 384, 5), (64, 256, 16), (32, 512, 33), (16, 128, 128), (80, 1024, 100)]
+
+
+@pytest.mark.parametrize("fmt", [di.Q4_32, di.Q8_32], ids=["q4", "q8"])
+@pytest.mark.parametrize("rows,cols,m", SHAPES)
+def test_group_sums_bit_exact(fmt, rows, cols, m):
+    say(f"group_sums fmt={fmt} rows={rows} cols={cols} m={m}")
+    rng = np.random.default_rng(rows + cols + m + fmt)
+    mat = _matrix(rng, fmt, rows, cols)
+    xq = rng.integers(-127, 128, (m, cols), dtype=np.int16).astype(np.int8)
+    ref = oracle.group_sums(mat, xq)
+    p = _packed(mat)
+    scratch = torch.empty(D.dflash_gemm_scratch_bytes(rows, cols, m, 1), dtype=torch.uint8, device="cuda")
+    sums = torch.empty((m, rows, cols // 32), dtype=torch.int32, device="cuda")
+    D.dflash_group_sums(fmt, p.data_ptr(), rows, cols, _dev(xq).data_ptr(), m, sums.data_ptr(), scratch.data_ptr(),
+                        _st())
+    torch.cuda.synchronize()
+    assert np.array_equal(sums.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("fmt", [di.Q4_32, di.Q8_32], ids=["q4", "q8"])
+@pytest.mark.parametrize("rows,cols,m", SHAPES)
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_gemm_within_f32_rounding(fmt, rows, cols, m, splits):
+    say(f"gemm fmt={fmt} rows={rows} cols={cols} m={m} splits={splits}")
+    rng = np.random.default_rng(rows * 3 + cols + m + fmt + splits)
+    mat = _matrix(rng, fmt, rows, cols)
+    x = _acts(rng, m, cols)
+    xq, dx = oracle.quant_act(x)
+    ref = oracle.matmul_q(mat, xq, dx).astype(np.float64)
+    # bound of the f32 accumulation: (groups + 2) ulps of sum |d_w d_x s_g|
+    s = oracle.group_sums(mat, xq).astype(np.float64)
+    dw = mat["scales"].astype(np.float64)
+    mag = np.einsum("mrg,rg,mg->mr", np.abs(s), dw, dx.astype(np.float64))
+    tol = (cols // 32 + 2) * 2.0 ** -23 * mag + 1e-30
+    p = _packed(mat)
+    scratch = torch.empty(D.dflash_gemm_scratch_bytes(rows, cols, m, splits), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, rows), dtype=torch.float32, device="cuda")
+    D.dflash_gemm(fmt, p.data_ptr(), rows, cols, _dev(xq).data_ptr(), _dev(dx).data_ptr(), m, y.data_ptr(), splits,
+                  scratch.data_ptr(), _st())
+    torch.cuda.synchronize()
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= tol), float((err / tol).max())
