@@ -7,6 +7,11 @@
 // context rows); "gpu_wgpu/dflash_dev.rs" -- dflash_qk (q/k rms then rotation, one workgroup
 // a head and row).  A8_32 (int8 per row and group of 32): amax, d = amax/127, inv = 127/amax,
 // q = clamp(rint(x*inv)), all f32 and correctly rounded (hipcc keeps IEEE division/sqrt).
+//
+// Every value stored as f32 is the rounding of an f64 evaluation (matrix products arrive as
+// f64 partial sums; SwiGLU and the rotation are evaluated in f64), so it is the correctly
+// rounded f32 of its step; the f32 steps the pages fix (the RMSNorm scale and products, the
+// RoPE angle, the quantizer) are done in f32 exactly as written.
 #include "common.h"
 
 namespace dfl {
@@ -41,14 +46,22 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   return t;
 }
 
-// v = resid + sum of S partial slices; optional write-back; optional RMSNorm; then A8_32 or f32.
-// dx element of (row m, group g) at g*dxg + m*dxm.
+// f32 of the sum of S f64 partial slices of element (m, col): one rounding.
+__device__ __forceinline__ float reduce_parts(const double* __restrict__ part, int S, int mstride, int m, size_t N,
+                                              size_t col) {
+  double o = part[(size_t)m * N + col];
+  for (int s = 1; s < S; s++) o += part[((size_t)s * mstride + m) * N + col];
+  return (float)o;
+}
+
+// v = resid + o; optional write-back; optional RMSNorm; then A8_32 or f32.  The dx element of
+// (row m, group g) sits at g*dxg + m*dxm.
 template <bool NORM, bool QUANT>
-__global__ __launch_bounds__(256) void k_norm_act(const float* __restrict__ src, int S, int src_mstride,
-                                                 const float* __restrict__ resid, float* __restrict__ h_out,
-                                                 const float* __restrict__ w, float eps, int M, int N,
-                                                 int8_t* __restrict__ xq, float* __restrict__ dx, int dxg, int dxm,
-                                                 float* __restrict__ xf) {
+__global__ __launch_bounds__(256) void k_norm_act(const double* __restrict__ part, const float* __restrict__ x, int S,
+                                                 int part_mstride, const float* __restrict__ resid,
+                                                 float* __restrict__ h_out, const float* __restrict__ w, float eps,
+                                                 int M, int N, int8_t* __restrict__ xq, float* __restrict__ dx,
+                                                 int dxg, int dxm, float* __restrict__ xf) {
   extern __shared__ float row[];  // N floats when NORM
   __shared__ double red[4];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
@@ -65,8 +78,7 @@ __global__ __launch_bounds__(256) void k_norm_act(const float* __restrict__ src,
   }
   double ss = 0.0;
   for (int i = tid; i < N; i += 256) {
-    float o = src[(size_t)m * N + i];
-    for (int s = 1; s < S; s++) o += src[((size_t)s * src_mstride + m) * N + i];
+    const float o = part ? reduce_parts(part, S, part_mstride, m, N, i) : x[(size_t)m * N + i];
     const float v = resid ? resid[(size_t)m * N + i] + o : o;
     if (h_out) h_out[(size_t)m * N + i] = v;
     if (NORM) {
@@ -91,48 +103,40 @@ __global__ __launch_bounds__(256) void k_norm_act(const float* __restrict__ src,
   }
 }
 
-hipError_t launch_norm_act(const float* src, int S, int src_mstride, const float* resid, float* h_out,
-                           const float* w, float eps, int M, int Mpad, int N, bool quant, int8_t* xq, float* dxT,
-                           float* xf, hipStream_t st) {
-  const size_t lds = w ? (size_t)N * 4 : 0;
-  if (lds > 96 * 1024 || N % 32) return hipErrorInvalidValue;
-  dim3 g(Mpad), b(256);
-  if (w && quant) {
-    static bool attr = false;
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_norm_act<true, true>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
-    hipLaunchKernelGGL((k_norm_act<true, true>), g, b, lds, st, src, S, src_mstride, resid, h_out, w, eps, M, N, xq,
-                       dxT, Mpad, 1, xf);
-  } else if (w) {
-    static bool attr = false;
-    if (!attr) {
-      hipError_t e = hipFuncSetAttribute((const void*)k_norm_act<true, false>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-      if (e != hipSuccess) return e;
-      attr = true;
-    }
-    hipLaunchKernelGGL((k_norm_act<true, false>), g, b, lds, st, src, S, src_mstride, resid, h_out, w, eps, M, N, xq,
-                       dxT, Mpad, 1, xf);
-  } else if (quant) {
-    hipLaunchKernelGGL((k_norm_act<false, true>), g, b, 0, st, src, S, src_mstride, resid, h_out, w, eps, M, N, xq,
-                       dxT, Mpad, 1, xf);
-  } else {
-    hipLaunchKernelGGL((k_norm_act<false, false>), g, b, 0, st, src, S, src_mstride, resid, h_out, w, eps, M, N, xq,
-                       dxT, Mpad, 1, xf);
-  }
+template <bool NORM, bool QUANT>
+static hipError_t norm_act_inst(const double* part, const float* x, int S, int part_mstride, const float* resid,
+                                float* h_out, const float* w, float eps, int M, int grid, int N, int8_t* xq,
+                                float* dx, int dxg, int dxm, float* xf, hipStream_t st) {
+  const size_t lds = NORM ? (size_t)N * 4 : 0;
+  hipError_t e = allow_lds((const void*)k_norm_act<NORM, QUANT>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_norm_act<NORM, QUANT>), dim3(grid), dim3(256), lds, st, part, x, S, part_mstride, resid, h_out,
+                     w, eps, M, N, xq, dx, dxg, dxm, xf);
   return hipGetLastError();
+}
+
+hipError_t launch_norm_act(const double* part, const float* x, int S, int part_mstride, const float* resid,
+                           float* h_out, const float* w, float eps, int M, int Mpad, int N, bool quant, int8_t* xq,
+                           float* dxT, float* xf, hipStream_t st) {
+  if ((w && (size_t)N * 4 > 96 * 1024) || (quant && N % 32) || (!part && !x)) return hipErrorInvalidValue;
+  if (w && quant)
+    return norm_act_inst<true, true>(part, x, S, part_mstride, resid, h_out, w, eps, M, Mpad, N, xq, dxT, Mpad, 1, xf,
+                                     st);
+  if (w)
+    return norm_act_inst<true, false>(part, x, S, part_mstride, resid, h_out, w, eps, M, Mpad, N, xq, dxT, Mpad, 1, xf,
+                                      st);
+  if (quant)
+    return norm_act_inst<false, true>(part, x, S, part_mstride, resid, h_out, w, eps, M, Mpad, N, xq, dxT, Mpad, 1, xf,
+                                      st);
+  return norm_act_inst<false, false>(part, x, S, part_mstride, resid, h_out, w, eps, M, Mpad, N, xq, dxT, Mpad, 1, xf,
+                                     st);
 }
 
 // A8_32 of plain rows with scales in row order [rows][cols/32] (a unit entry point).
 hipError_t launch_quant_rows(const float* x, int rows, int cols, int8_t* q, float* d, hipStream_t st) {
   if (cols % 32) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_norm_act<false, true>), dim3(rows), dim3(256), 0, st, x, 1, rows, (const float*)nullptr,
-                     (float*)nullptr, (const float*)nullptr, 0.f, rows, cols, q, d, 1, cols / 32, (float*)nullptr);
-  return hipGetLastError();
+  return norm_act_inst<false, true>(nullptr, x, 1, rows, nullptr, nullptr, nullptr, 0.f, rows, rows, cols, q, d, 1,
+                                    cols / 32, nullptr, st);
 }
 
 __global__ void k_transpose_scales(const float* __restrict__ d, int rows, int groups, int Mpad,
@@ -149,10 +153,11 @@ hipError_t launch_transpose_scales(const float* d, int rows, int groups, int Mpa
   return hipGetLastError();
 }
 
-// a = silu(g) * u.  Gate and up share n-tiles pairwise: column (i/16)*32 + i%16 is gate row i,
-// 16 further the up row i.  Grid (ceil(I/1024), Mpad).
+// a = silu(g) * u with g, u the f32 products, evaluated in f64.  Gate and up share n-tiles
+// pairwise: column (i/16)*32 + i%16 is gate row i, 16 further the up row i.  Grid
+// (ceil(I/1024), Mpad).
 template <bool QUANT>
-__global__ __launch_bounds__(256) void k_swiglu_act(const float* __restrict__ part, int S, int M, int Mpad, int I,
+__global__ __launch_bounds__(256) void k_swiglu_act(const double* __restrict__ part, int S, int M, int Mpad, int I,
                                                    int8_t* __restrict__ xq, float* __restrict__ dxT,
                                                    float* __restrict__ xf) {
   const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
@@ -163,12 +168,9 @@ __global__ __launch_bounds__(256) void k_swiglu_act(const float* __restrict__ pa
     float a = 0.f;
     if (m < M) {
       const size_t gc = (size_t)(i >> 4) * 32 + (i & 15);
-      float g = part[(size_t)m * N2 + gc], u = part[(size_t)m * N2 + gc + 16];
-      for (int s = 1; s < S; s++) {
-        g += part[((size_t)s * Mpad + m) * N2 + gc];
-        u += part[((size_t)s * Mpad + m) * N2 + gc + 16];
-      }
-      a = g / (1.0f + expf(-g)) * u;
+      const double g = reduce_parts(part, S, Mpad, m, N2, gc);
+      const double u = reduce_parts(part, S, Mpad, m, N2, gc + 16);
+      a = (float)(g / (1.0 + exp(-g)) * u);
     }
     if (QUANT)
       emit_q(a, (size_t)m * I + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(256) void k_swiglu_act(const float* __restrict__ pa
   }
 }
 
-hipError_t launch_swiglu_act(const float* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
+hipError_t launch_swiglu_act(const double* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
                              float* xf, hipStream_t st) {
   if (I % 32) return hipErrorInvalidValue;
   dim3 g((unsigned)((I + 1023) / 1024), (unsigned)Mpad);
@@ -188,7 +190,9 @@ hipError_t launch_swiglu_act(const float* part, int S, int M, int Mpad, int I, b
   return hipGetLastError();
 }
 
-// RMSNorm of one head (threads d < hd of a 128-thread block) then its rotation to `pos`.
+// RMSNorm of one head (threads d < hd of a 128-thread block), then its rotation to `pos`: the
+// angle is the f32 product f32(pos) * inv_freq[i]; its cosine and sine and the rotation are
+// evaluated in f64 and rounded once.
 __device__ __forceinline__ float head_norm_rope(float x, int d, int hd, const float* __restrict__ w, float eps,
                                                 const float* __restrict__ inv_freq, long long pos, float* ybuf,
                                                 double* red) {
@@ -206,14 +210,15 @@ __device__ __forceinline__ float head_norm_rope(float x, int d, int hd, const fl
   const int half = hd >> 1;
   const int i = d < half ? d : d - half;
   const float ang = (float)pos * inv_freq[i];
-  float sn, cs;
-  sincosf(ang, &sn, &cs);
-  return d < half ? y * cs - ybuf[d + half] * sn : y * cs + ybuf[d - half] * sn;
+  double sn, cs;
+  sincos((double)ang, &sn, &cs);
+  const double a = (double)y;
+  return d < half ? (float)(a * cs - (double)ybuf[d + half] * sn) : (float)(a * cs + (double)ybuf[d - half] * sn);
 }
 
 // Grid (nh + 2 kvh heads, M rows), block 128.  Columns of the fused projection: q heads, then
 // k heads, then v heads, hd each.
-__global__ __launch_bounds__(128) void k_qkv_epilogue(const float* __restrict__ part, int S, int Mpad, int B,
+__global__ __launch_bounds__(128) void k_qkv_epilogue(const double* __restrict__ part, int S, int Mpad, int B,
                                                      SeqInfo si, int nh, int kvh, int hd,
                                                      const float* __restrict__ q_norm,
                                                      const float* __restrict__ k_norm,
@@ -225,11 +230,7 @@ __global__ __launch_bounds__(128) void k_qkv_epilogue(const float* __restrict__ 
   const int head = blockIdx.x, m = blockIdx.y, d = threadIdx.x;
   const size_t N = (size_t)(nh + 2 * kvh) * hd;
   const size_t col = (size_t)head * hd + d;
-  float x = 0.f;
-  if (d < hd) {
-    x = part[(size_t)m * N + col];
-    for (int s = 1; s < S; s++) x += part[((size_t)s * Mpad + m) * N + col];
-  }
+  const float x = d < hd ? reduce_parts(part, S, Mpad, m, N, col) : 0.f;
   if (head >= nh + kvh) {
     if (d < hd) v[((size_t)m * kvh + (head - nh - kvh)) * hd + d] = x;
     return;
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(128) void k_qkv_epilogue(const float* __restrict__ 
   }
 }
 
-hipError_t launch_qkv_epilogue(const float* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
+hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
                                int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
                                float* q, float* k, float* v, hipStream_t st) {
   if (hd > 128 || hd % 2) return hipErrorInvalidValue;
@@ -256,7 +257,7 @@ hipError_t launch_qkv_epilogue(const float* part, int S, int Mpad, int M, int B,
 
 // Context append: grid (layers * 2 * kvh, n), block 128.  Columns of the all-layer K|V
 // projection: layer l's k heads then its v heads.  Cache layout [L][max_seqs][kvh][max_ctx][hd].
-__global__ __launch_bounds__(128) void k_kv_append(const float* __restrict__ part, int S, int Mpad, int layers,
+__global__ __launch_bounds__(128) void k_kv_append(const double* __restrict__ part, int S, int Mpad, int layers,
                                                   int kvh, int hd, const float* __restrict__ k_norms,
                                                   const float* __restrict__ inv_freq, float eps, long long pos0,
                                                   int row0, int slot, int max_seqs, int max_ctx,
@@ -267,11 +268,7 @@ __global__ __launch_bounds__(128) void k_kv_append(const float* __restrict__ par
   const int l = unit / (2 * kvh), rem = unit % (2 * kvh), kind = rem / kvh, h = rem % kvh;
   const size_t kvd = (size_t)kvh * hd, N = (size_t)layers * 2 * kvd;
   const size_t col = ((size_t)l * 2 + kind) * kvd + (size_t)h * hd + d;
-  float x = 0.f;
-  if (d < hd) {
-    x = part[(size_t)i * N + col];
-    for (int s = 1; s < S; s++) x += part[((size_t)s * Mpad + i) * N + col];
-  }
+  const float x = d < hd ? reduce_parts(part, S, Mpad, i, N, col) : 0.f;
   const size_t dst = ((((size_t)l * max_seqs + slot) * kvh + h) * max_ctx + (size_t)(row0 + i)) * hd + d;
   if (kind == 1) {
     if (d < hd) vc[dst] = x;
@@ -281,7 +278,7 @@ __global__ __launch_bounds__(128) void k_kv_append(const float* __restrict__ par
   if (d < hd) kc[dst] = out;
 }
 
-hipError_t launch_kv_append(const float* part, int S, int Mpad, int n, int layers, int kvh, int hd,
+hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
                             const float* k_norms, const float* inv_freq, float eps, long long pos0, int row0,
                             int slot, int max_seqs, int max_ctx, float* kc, float* vc, hipStream_t st) {
   if (hd > 128 || hd % 2) return hipErrorInvalidValue;

@@ -26,7 +26,12 @@ constexpr int APPEND_CHUNK = 128;  // context rows per append pass (8 row tiles 
 constexpr int MROWS = 128;         // activation rows the workspace holds
 constexpr int MAXCH = 65;          // attention chunks per (sequence, kv head), block chunk included
 
-thread_local std::string g_create_err;
+thread_local std::string g_create_err;  // last error of a call without a ctx
+
+int unit_fail(int code, const char* what, hipError_t e = hipSuccess) {
+  g_create_err = std::string(what) + (e != hipSuccess ? std::string(": ") + hipGetErrorString(e) : std::string());
+  return code;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int round16(int x) { return (x + 15) & ~15; }
@@ -138,10 +143,10 @@ void plan(const dflash_geometry* g, Layout* L) {
   need(g->body_fmt, 2 * I, H);
   need(g->body_fmt, H, I);
   L->part_floats = pf;
-  L->part = take(pf * 4);
+  L->part = take(pf * 8);  // f64 partial sums
   const size_t arows = (size_t)g->max_seqs * kvh * MAXCH * rep * 16;
-  L->apart = take(arows * hd * 4);
-  L->aml = take(arows * 2 * 4);
+  L->apart = take(arows * hd * 8);
+  L->aml = take(arows * 2 * 8);
   L->total = off;
 }
 
@@ -215,7 +220,7 @@ bool bodyq(const dflash_ctx* c) { return c->g.body_fmt != DFLASH_F32; }
 
 // One matrix product over the activations prepared by the previous producer.  Returns the
 // number of K slices written to the partial buffer (1 when direct).
-int run_gemm(dflash_ctx* c, int fmt, size_t woff, int N, int K, int Mpad, int M, float* out, bool direct, int out_ld,
+int run_gemm(dflash_ctx* c, int fmt, size_t woff, int N, int K, int Mpad, int M, void* out, bool direct, int out_ld,
              int m_store, int* slices) {
   const void* W = c->ws + woff;
   if (fmt == DFLASH_F32) {
@@ -275,7 +280,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   const float eps = (float)g.eps;
   const Layout& L = c->lay;
   float* hbuf = c->at<float>(L.h);
-  float* part = c->at<float>(L.part);
+  double* part = c->at<double>(L.part);
   int8_t* xq = c->at<int8_t>(L.xq);
   float* dxT = c->at<float>(L.dxT);
   float* xf = c->at<float>(L.xf);
@@ -302,8 +307,8 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
 
   TRY_HIP(c, hipMemcpyAsync(hbuf, h, (size_t)M * H * 4, hipMemcpyDeviceToDevice, c->st), "copy block rows");
   TRY_HIP(c,
-          launch_norm_act(hbuf, 1, Mpad, nullptr, nullptr, c->at<float>(L.in_norm), eps, M, Mpad, H, bq, xq, dxT, xf,
-                          c->st),
+          launch_norm_act(nullptr, hbuf, 1, Mpad, nullptr, nullptr, c->at<float>(L.in_norm), eps, M, Mpad, H, bq, xq,
+                          dxT, xf, c->st),
           "in-norm");
   const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd;
   for (int l = 0; l < NL; l++) {
@@ -322,7 +327,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
       TRY_HIP(c,
             launch_attention(as, si, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
                              c->at<float>(L.kc) + (size_t)l * layer_cache, c->at<float>(L.vc) + (size_t)l * layer_cache,
-                             c->at<float>(L.apart), c->at<float>(L.aml), Mpad, bq, xq, dxT, xf, c->st),
+                             c->at<double>(L.apart), c->at<double>(L.aml), Mpad, bq, xq, dxT, xf, c->st),
               "attention");
     }
     {
@@ -330,8 +335,8 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
       if ((rc = run_gemm(c, g.body_fmt, L.o[l], H, qd, Mpad, M, part, false, 0, 0, &S))) return rc;
     }
     TRY_HIP(c,
-            launch_norm_act(part, S, Mpad, hbuf, hbuf, c->at<float>(L.post_norm) + (size_t)l * H, eps, M, Mpad, H, bq,
-                            xq, dxT, xf, c->st),
+            launch_norm_act(part, nullptr, S, Mpad, hbuf, hbuf, c->at<float>(L.post_norm) + (size_t)l * H, eps, M,
+                            Mpad, H, bq, xq, dxT, xf, c->st),
             "o residual + post-norm");
     {
       StageTimer t(c, DFLASH_STAGE_GATE_UP);
@@ -345,7 +350,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
     const bool last = l + 1 == NL;
     const float* nw = last ? c->at<float>(L.norm) : c->at<float>(L.in_norm) + (size_t)(l + 1) * H;
     const bool nq = last ? (!hidden_only && g.head_fmt != DFLASH_F32) : bq;
-    TRY_HIP(c, launch_norm_act(part, S, Mpad, hbuf, hbuf, nw, eps, M, Mpad, H, nq, xq, dxT, xf, c->st),
+    TRY_HIP(c, launch_norm_act(part, nullptr, S, Mpad, hbuf, hbuf, nw, eps, M, Mpad, H, nq, xq, dxT, xf, c->st),
             "down residual + next norm");
   }
   if (hidden_only) {
@@ -486,7 +491,7 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
   const int H = g.hidden, T = g.n_taps * g.hidden, kvd = g.kv_heads * g.head_dim, NL = g.layers;
   const float eps = (float)g.eps;
   const Layout& L = c->lay;
-  float* part = c->at<float>(L.part);
+  double* part = c->at<double>(L.part);
   int8_t* xq = c->at<int8_t>(L.xq);
   float* dxT = c->at<float>(L.dxT);
   float* xf = c->at<float>(L.xf);
@@ -496,7 +501,9 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
     const float* rows = taps + (size_t)c0 * T;
     int S = 1, rc;
     if (g.fc_fmt != DFLASH_F32) {
-      TRY_HIP(c, launch_norm_act(rows, 1, Mpad, nullptr, nullptr, nullptr, eps, nn, Mpad, T, true, xq, dxT, xf, c->st),
+      TRY_HIP(c,
+              launch_norm_act(nullptr, rows, 1, Mpad, nullptr, nullptr, nullptr, eps, nn, Mpad, T, true, xq, dxT, xf,
+                              c->st),
               "taps quant");
       rc = run_gemm(c, g.fc_fmt, L.fc, H, T, Mpad, nn, part, false, 0, 0, &S);
     } else {
@@ -506,8 +513,8 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
     }
     if (rc) return rc;
     TRY_HIP(c,
-            launch_norm_act(part, S, Mpad, nullptr, nullptr, c->at<float>(L.hidden_norm), eps, nn, Mpad, H, bodyq(c),
-                            xq, dxT, xf, c->st),
+            launch_norm_act(part, nullptr, S, Mpad, nullptr, nullptr, c->at<float>(L.hidden_norm), eps, nn, Mpad, H,
+                            bodyq(c), xq, dxT, xf, c->st),
             "hidden norm");
     if ((rc = run_gemm(c, g.body_fmt, L.kvall, NL * 2 * kvd, H, Mpad, nn, part, false, 0, 0, &S))) return rc;
     TRY_HIP(c,
@@ -605,9 +612,10 @@ int dflash_read_kv(const dflash_ctx* c, int32_t layer, int32_t seq, int32_t row0
 }
 
 int dflash_quant_act(const float* x, int32_t rows, int32_t cols, int8_t* q, float* d, void* stream) {
-  if (!x || !q || !d || rows < 0 || cols <= 0 || cols % 32) return DFLASH_EINVAL;
+  if (!x || !q || !d || rows < 0 || cols <= 0 || cols % 32) return unit_fail(DFLASH_EINVAL, "quant_act: arguments");
   if (rows == 0) return DFLASH_OK;
-  return launch_quant_rows(x, rows, cols, q, d, (hipStream_t)stream) == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
+  hipError_t e = launch_quant_rows(x, rows, cols, q, d, (hipStream_t)stream);
+  return e == hipSuccess ? DFLASH_OK : unit_fail(DFLASH_EHIP, "quant_act", e);
 }
 
 int dflash_packed_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* bytes) {
@@ -620,10 +628,9 @@ int dflash_packed_bytes(int32_t fmt, int32_t rows, int32_t cols, size_t* bytes) 
 int dflash_pack(int32_t fmt, int32_t rows, int32_t cols, dflash_matrix w, void* packed, void* stream) {
   size_t b;
   if (dflash_packed_bytes(fmt, rows, cols, &b) || !packed || !w.codes || (fmt != DFLASH_F32 && !w.scales))
-    return DFLASH_EINVAL;
-  return launch_pack(fmt, w.codes, w.scales, rows, cols, packed, 0, 1, (hipStream_t)stream) == hipSuccess
-             ? DFLASH_OK
-             : DFLASH_EHIP;
+    return unit_fail(DFLASH_EINVAL, "pack: arguments");
+  hipError_t e = launch_pack(fmt, w.codes, w.scales, rows, cols, packed, 0, 1, (hipStream_t)stream);
+  return e == hipSuccess ? DFLASH_OK : unit_fail(DFLASH_EHIP, "pack", e);
 }
 
 // scratch: padded activations [Mpad][cols] int8, their scales [cols/32][Mpad] f32, partials.
@@ -631,7 +638,7 @@ int dflash_gemm_scratch_bytes(int32_t rows, int32_t cols, int32_t m, int32_t spl
   if (!bytes || rows <= 0 || cols <= 0 || cols % 128 || rows % 16 || m < 1 || m > MROWS) return DFLASH_EINVAL;
   const int Mpad = round16(m);
   const int s = splits > 0 ? normalize_splits(cols, splits) : choose_splits(rows, cols, Mpad);
-  *bytes = align256((size_t)Mpad * cols) + align256((size_t)(cols / 32) * Mpad * 4) + (size_t)s * Mpad * rows * 4;
+  *bytes = align256((size_t)Mpad * cols) + align256((size_t)(cols / 32) * Mpad * 4) + (size_t)s * Mpad * rows * 8;
   return DFLASH_OK;
 }
 
@@ -640,21 +647,25 @@ int dflash_gemm(int32_t fmt, const void* packed, int32_t rows, int32_t cols, con
   size_t need;
   if ((fmt != DFLASH_Q4_32 && fmt != DFLASH_Q8_32) || !packed || !xq || !dx || !y || !scratch ||
       dflash_gemm_scratch_bytes(rows, cols, m, splits, &need))
-    return DFLASH_EINVAL;
+    return unit_fail(DFLASH_EINVAL, "gemm: arguments");
   hipStream_t st = (hipStream_t)stream;
   const int Mpad = round16(m);
   const int s = splits > 0 ? normalize_splits(cols, splits) : choose_splits(rows, cols, Mpad);
   int8_t* xp = (int8_t*)scratch;
   float* dT = (float*)((uint8_t*)scratch + align256((size_t)Mpad * cols));
-  float* part = (float*)((uint8_t*)dT + align256((size_t)(cols / 32) * Mpad * 4));
-  if (hipMemsetAsync(xp, 0, (size_t)Mpad * cols, st) != hipSuccess) return DFLASH_EHIP;
-  if (hipMemcpyAsync(xp, xq, (size_t)m * cols, hipMemcpyDeviceToDevice, st) != hipSuccess) return DFLASH_EHIP;
-  if (launch_transpose_scales(dx, m, cols / 32, Mpad, dT, st) != hipSuccess) return DFLASH_EHIP;
-  if (launch_gemm_q(fmt, packed, rows, cols, xp, dT, Mpad, s, part, false, 0, 0, st) != hipSuccess) return DFLASH_EHIP;
-  return launch_norm_act(part, s, Mpad, nullptr, nullptr, nullptr, 0.f, m, m, rows, false, nullptr, nullptr, y, st) ==
-                 hipSuccess
-             ? DFLASH_OK
-             : DFLASH_EHIP;
+  double* part = (double*)((uint8_t*)dT + align256((size_t)(cols / 32) * Mpad * 4));
+  hipError_t e;
+  if ((e = hipMemsetAsync(xp, 0, (size_t)Mpad * cols, st)) != hipSuccess) return unit_fail(DFLASH_EHIP, "gemm: clear", e);
+  if ((e = hipMemcpyAsync(xp, xq, (size_t)m * cols, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+    return unit_fail(DFLASH_EHIP, "gemm: copy", e);
+  if ((e = launch_transpose_scales(dx, m, cols / 32, Mpad, dT, st)) != hipSuccess)
+    return unit_fail(DFLASH_EHIP, "gemm: scales", e);
+  if ((e = launch_gemm_q(fmt, packed, rows, cols, xp, dT, Mpad, s, part, false, 0, 0, st)) != hipSuccess)
+    return unit_fail(DFLASH_EHIP, "gemm: kernel", e);
+  if ((e = launch_norm_act(part, nullptr, s, Mpad, nullptr, nullptr, nullptr, 0.f, m, m, rows, false, nullptr, nullptr,
+                           y, st)) != hipSuccess)
+    return unit_fail(DFLASH_EHIP, "gemm: reduce", e);
+  return DFLASH_OK;
 }
 
 int dflash_group_sums(int32_t fmt, const void* packed, int32_t rows, int32_t cols, const int8_t* xq, int32_t m,
@@ -662,13 +673,18 @@ int dflash_group_sums(int32_t fmt, const void* packed, int32_t rows, int32_t col
   size_t need;
   if ((fmt != DFLASH_Q4_32 && fmt != DFLASH_Q8_32) || !packed || !xq || !sums || !scratch ||
       dflash_gemm_scratch_bytes(rows, cols, m, 1, &need))
-    return DFLASH_EINVAL;
+    return unit_fail(DFLASH_EINVAL, "group_sums: arguments");
   hipStream_t st = (hipStream_t)stream;
   const int Mpad = round16(m);
   int8_t* xp = (int8_t*)scratch;
-  if (hipMemsetAsync(xp, 0, (size_t)Mpad * cols, st) != hipSuccess) return DFLASH_EHIP;
-  if (hipMemcpyAsync(xp, xq, (size_t)m * cols, hipMemcpyDeviceToDevice, st) != hipSuccess) return DFLASH_EHIP;
-  return launch_group_sums(fmt, packed, rows, cols, xp, Mpad, m, sums, st) == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
+  hipError_t e;
+  if ((e = hipMemsetAsync(xp, 0, (size_t)Mpad * cols, st)) != hipSuccess)
+    return unit_fail(DFLASH_EHIP, "group_sums: clear", e);
+  if ((e = hipMemcpyAsync(xp, xq, (size_t)m * cols, hipMemcpyDeviceToDevice, st)) != hipSuccess)
+    return unit_fail(DFLASH_EHIP, "group_sums: copy", e);
+  if ((e = launch_group_sums(fmt, packed, rows, cols, xp, Mpad, m, sums, st)) != hipSuccess)
+    return unit_fail(DFLASH_EHIP, "group_sums: kernel", e);
+  return DFLASH_OK;
 }
 
 }  // extern "C"

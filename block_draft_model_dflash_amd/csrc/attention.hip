@@ -6,22 +6,30 @@
 // scratch and re-reads it; here the context is split into chunks, each workgroup keeps a
 // running (max, sum, acc) per query in registers (online softmax), and a merge combines the
 // chunks.  A workgroup serves one (sequence, kv head, chunk) with one wave per q head of the
-// group; the 16 block rows of a head are the 16 columns of v_mfma_f32_16x16x4f32 tiles:
+// group; the 16 block rows of a head are the 16 columns of v_mfma_f64_16x16x4f64 tiles:
 //   S^T[key][q] = K . Q^T   (A = 16 keys staged in LDS, B = the wave's queries in registers)
 //   Y^T[d][q]  += V^T . P^T (A = 16-dim slices of V from LDS, B = the wave's probabilities,
 //                            already in the accumulator layout of S^T)
 // so the probabilities never leave registers.  Context K/V is f32 [slot][kvh][max_ctx][hd].
+// Lane layout of the f64 16x16x4 MFMA: lane l gives A[l%16][l/16] and B[l/16][l%16] and holds
+// D[l/16 + 4r][l%16] in accumulator slot r (rows interleaved, unlike the f32 16x16 forms).
+//
+// Scores, softmax and values are evaluated in f64 (the f32 keys, values and queries are exact
+// in f64) and the output is rounded once to f32: it feeds an int8 quantizer, where a value one
+// ulp off flips codes that the following layers amplify, so it has to be the correctly rounded
+// result that any exact evaluation gives.
 #include "common.h"
 
 namespace dfl {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef double v4d __attribute__((ext_vector_type(4)));
 
 template <int HD>
-__global__ __launch_bounds__(1024) void k_attn_partial(AttnShape a, SeqInfo si, const float* __restrict__ q,
-                                                      const float* __restrict__ kb, const float* __restrict__ vb,
-                                                      const float* __restrict__ kc, const float* __restrict__ vc,
-                                                      float* __restrict__ part, float* __restrict__ ml) {
+__global__ __launch_bounds__(256) void k_attn_partial(AttnShape a, SeqInfo si, const float* __restrict__ q,
+                                                     const float* __restrict__ kb, const float* __restrict__ vb,
+                                                     const float* __restrict__ kc, const float* __restrict__ vc,
+                                                     double* __restrict__ part, double* __restrict__ ml) {
   constexpr int KS = HD + 4;  // padded LDS key row (floats)
   __shared__ __attribute__((aligned(16))) float Ks[16 * KS];
   __shared__ __attribute__((aligned(16))) float Vs[16 * KS];
@@ -29,7 +37,7 @@ __global__ __launch_bounds__(1024) void k_attn_partial(AttnShape a, SeqInfo si, 
   const int nctx = si.nctx[s];
   const int nch = (nctx + a.ck - 1) / a.ck;
   if (c > nch) return;  // the whole workgroup: this sequence has fewer chunks
-  const int rep = a.nh / a.kvh;
+  const int rep = a.nh / a.kvh, waves = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int quarter = lane >> 4, col = lane & 15;
   const bool blockchunk = c == nch;
@@ -46,86 +54,94 @@ __global__ __launch_bounds__(1024) void k_attn_partial(AttnShape a, SeqInfo si, 
     Vbase = vc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
     kstride = HD;
   }
-  const int j = g * rep + w;
-  v4f qr[HD / 16];
+  // the group's q heads, `waves` at a time (one per wave); the chunk's keys are re-staged per
+  // round when a group has more heads than the workgroup has waves
+  for (int h0 = 0; h0 < rep; h0 += waves) {
+    const int hw = h0 + w;  // this wave's head within the group
+    const bool live = hw < rep;
+    const int j = g * rep + (live ? hw : 0);
+    v4f qr[HD / 16];
 #pragma unroll
-  for (int i4 = 0; i4 < HD / 16; i4++)
-    qr[i4] = col < a.B ? *(const v4f*)(q + ((size_t)(s * a.B + col) * a.nh + j) * HD + 16 * i4 + 4 * quarter)
-                       : (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  v4f acc[HD / 16];
+    for (int i4 = 0; i4 < HD / 16; i4++)
+      qr[i4] = col < a.B ? *(const v4f*)(q + ((size_t)(s * a.B + col) * a.nh + j) * HD + 16 * i4 + 4 * quarter)
+                         : (v4f){0.f, 0.f, 0.f, 0.f};
+    double m_run = -INFINITY, l_run = 0.0;
+    v4d acc[HD / 16];
 #pragma unroll
-  for (int dt = 0; dt < HD / 16; dt++) acc[dt] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < HD / 16; dt++) acc[dt] = (v4d){0.0, 0.0, 0.0, 0.0};
 
-  for (int t0 = k0; t0 < kend; t0 += 16) {
-    __syncthreads();
-    for (int i = tid; i < 16 * (HD / 4); i += blockDim.x) {
-      const int r = i / (HD / 4), c4 = i % (HD / 4);
-      const int key = t0 + r;
-      v4f kv = (v4f){0.f, 0.f, 0.f, 0.f}, vv = kv;
-      if (key < kend) {
-        kv = *(const v4f*)(Kbase + (size_t)key * kstride + 4 * c4);
-        vv = *(const v4f*)(Vbase + (size_t)key * kstride + 4 * c4);
+    for (int t0 = k0; t0 < kend; t0 += 16) {
+      __syncthreads();
+      for (int i = tid; i < 16 * (HD / 4); i += blockDim.x) {
+        const int r = i / (HD / 4), c4 = i % (HD / 4);
+        const int key = t0 + r;
+        v4f kv = (v4f){0.f, 0.f, 0.f, 0.f}, vv = kv;
+        if (key < kend) {
+          kv = *(const v4f*)(Kbase + (size_t)key * kstride + 4 * c4);
+          vv = *(const v4f*)(Vbase + (size_t)key * kstride + 4 * c4);
+        }
+        *(v4f*)(Ks + r * KS + 4 * c4) = kv;
+        *(v4f*)(Vs + r * KS + 4 * c4) = vv;
       }
-      *(v4f*)(Ks + r * KS + 4 * c4) = kv;
-      *(v4f*)(Vs + r * KS + 4 * c4) = vv;
-    }
-    __syncthreads();
-    v4f st0 = (v4f){0.f, 0.f, 0.f, 0.f}, st1 = st0;
+      __syncthreads();
+      if (!live) continue;
+      v4d st0 = (v4d){0.0, 0.0, 0.0, 0.0}, st1 = st0;
 #pragma unroll
-    for (int i4 = 0; i4 < HD / 16; i4++) {
-      const v4f kv = *(const v4f*)(Ks + col * KS + 16 * i4 + 4 * quarter);
-      st0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[0], qr[i4][0], st0, 0, 0, 0);
-      st1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[1], qr[i4][1], st1, 0, 0, 0);
-      st0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[2], qr[i4][2], st0, 0, 0, 0);
-      st1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[3], qr[i4][3], st1, 0, 0, 0);
-    }
-    const v4f st = st0 + st1;
-    float p[4], mx = -INFINITY;
+      for (int i4 = 0; i4 < HD / 16; i4++) {
+        const v4f kv = *(const v4f*)(Ks + col * KS + 16 * i4 + 4 * quarter);
+        st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[0], (double)qr[i4][0], st0, 0, 0, 0);
+        st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[1], (double)qr[i4][1], st1, 0, 0, 0);
+        st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[2], (double)qr[i4][2], st0, 0, 0, 0);
+        st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[3], (double)qr[i4][3], st1, 0, 0, 0);
+      }
+      double p[4], mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int key = t0 + 4 * quarter + r;
-      p[r] = key < kend ? st[r] * a.scale : -INFINITY;
-      mx = fmaxf(mx, p[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float corr = expf(m_run - m_new);
-    float ps = 0.f;
+      for (int r = 0; r < 4; r++) {
+        const int key = t0 + quarter + 4 * r;  // accumulator slot r holds key row quarter + 4r
+        p[r] = key < kend ? (st0[r] + st1[r]) * (double)a.scale : -INFINITY;
+        mx = fmax(mx, p[r]);
+      }
+      mx = fmax(mx, __shfl_xor(mx, 16));
+      mx = fmax(mx, __shfl_xor(mx, 32));
+      const double m_new = fmax(m_run, mx);
+      const double corr = exp(m_run - m_new);
+      double ps = 0.0;
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      p[r] = expf(p[r] - m_new);
-      ps += p[r];
-    }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l_run = l_run * corr + ps;
-    m_run = m_new;
+      for (int r = 0; r < 4; r++) {
+        p[r] = exp(p[r] - m_new);
+        ps += p[r];
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run = l_run * corr + ps;
+      m_run = m_new;
 #pragma unroll
-    for (int dt = 0; dt < HD / 16; dt++) {
-      acc[dt] *= corr;
+      for (int dt = 0; dt < HD / 16; dt++) {
+        acc[dt] *= corr;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float va = Vs[(4 * quarter + i) * KS + 64 * (dt >> 2) + 4 * col + (dt & 3)];
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va, p[i], acc[dt], 0, 0, 0);
+        for (int i = 0; i < 4; i++) {
+          // step i pairs the probabilities of slot i (keys quarter + 4i) with those keys' values
+          const float va = Vs[(4 * i + quarter) * KS + 64 * (dt >> 2) + 4 * col + (dt & 3)];
+          acc[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va, p[i], acc[dt], 0, 0, 0);
+        }
       }
     }
-  }
-  if (col >= a.B) return;
-  const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + w) * 16 + col;
-  float* dst = part + prow * HD;
+    if (!live || col >= a.B) continue;
+    const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + hw) * 16 + col;
+    double* dst = part + prow * HD;
 #pragma unroll
-  for (int d4 = 0; d4 < HD / 64; d4++)
+    for (int d4 = 0; d4 < HD / 64; d4++)
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      // accumulator (dt = 4*d4 + e, row 4*quarter + r) holds dim 64*d4 + 16*quarter + 4*r + e
-      const v4f v = (v4f){acc[4 * d4][r], acc[4 * d4 + 1][r], acc[4 * d4 + 2][r], acc[4 * d4 + 3][r]};
-      *(v4f*)(dst + 64 * d4 + 16 * quarter + 4 * r) = v;
+      for (int r = 0; r < 4; r++) {
+        // accumulator (dt = 4*d4 + e, slot r) is row quarter + 4r of tile dt: dim 64*d4 + 16*r + 4*quarter + e
+        double* o = dst + 64 * d4 + 16 * r + 4 * quarter;
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = acc[4 * d4 + e][r];
+      }
+    if (quarter == 0) {
+      ml[prow * 2] = m_run;
+      ml[prow * 2 + 1] = l_run;
     }
-  if (quarter == 0) {
-    ml[prow * 2] = m_run;
-    ml[prow * 2 + 1] = l_run;
   }
 }
 
@@ -149,31 +165,30 @@ __device__ __forceinline__ void emit_q8(float y, size_t qi, int8_t* __restrict__
 
 // One wave per (q head, block row, sequence): combine the chunks' (max, sum, acc).
 template <int HD, bool QUANT>
-__global__ __launch_bounds__(64) void k_attn_merge(AttnShape a, SeqInfo si, const float* __restrict__ part,
-                                                  const float* __restrict__ ml, int Mpad, int8_t* __restrict__ xq,
+__global__ __launch_bounds__(64) void k_attn_merge(AttnShape a, SeqInfo si, const double* __restrict__ part,
+                                                  const double* __restrict__ ml, int Mpad, int8_t* __restrict__ xq,
                                                   float* __restrict__ dxT, float* __restrict__ xf) {
   const int j = blockIdx.x, r = blockIdx.y, s = blockIdx.z, lane = threadIdx.x;
   const int rep = a.nh / a.kvh, g = j / rep, w = j % rep;
   const int nch = (si.nctx[s] + a.ck - 1) / a.ck;
   const size_t base = (((size_t)s * a.kvh + g) * a.maxch) * rep;
-  float mx = -INFINITY;
-  for (int c = 0; c <= nch; c++) mx = fmaxf(mx, ml[(((base + (size_t)c * rep + w) * 16) + r) * 2]);
-  float L = 0.f, y[HD / 64];
+  double mx = -INFINITY;
+  for (int c = 0; c <= nch; c++) mx = fmax(mx, ml[(((base + (size_t)c * rep + w) * 16) + r) * 2]);
+  double L = 0.0, y[HD / 64];
 #pragma unroll
-  for (int t = 0; t < HD / 64; t++) y[t] = 0.f;
+  for (int t = 0; t < HD / 64; t++) y[t] = 0.0;
   for (int c = 0; c <= nch; c++) {
     const size_t row = (base + (size_t)c * rep + w) * 16 + r;
-    const float e = expf(ml[row * 2] - mx);
+    const double e = exp(ml[row * 2] - mx);
     L += ml[row * 2 + 1] * e;
 #pragma unroll
     for (int t = 0; t < HD / 64; t++) y[t] += part[row * HD + lane + 64 * t] * e;
   }
-  const float invL = 1.0f / L;
   const int m = s * a.B + r;
   const size_t qd = (size_t)a.nh * HD;
 #pragma unroll
   for (int t = 0; t < HD / 64; t++) {
-    const float v = y[t] * invL;
+    const float v = (float)(y[t] / L);
     const size_t colx = (size_t)j * HD + lane + 64 * t;
     if (QUANT)
       emit_q8(v, (size_t)m * qd + colx, xq, dxT, (colx >> 5) * Mpad + m, lane);
@@ -184,7 +199,7 @@ __global__ __launch_bounds__(64) void k_attn_merge(AttnShape a, SeqInfo si, cons
 
 template <int HD>
 static hipError_t attn_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
-                          const float* kc, const float* vc, float* part, float* ml, int Mpad, bool quant, int8_t* xq,
+                          const float* kc, const float* vc, double* part, double* ml, int Mpad, bool quant, int8_t* xq,
                           float* dxT, float* xf, hipStream_t st) {
   int maxn = 0;
   for (int i = 0; i < si.n; i++) {
@@ -193,7 +208,8 @@ static hipError_t attn_hd(const AttnShape& a, const SeqInfo& si, const float* q,
   }
   if (maxn + 1 > a.maxch) return hipErrorInvalidValue;
   const int rep = a.nh / a.kvh;
-  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn + 1, a.kvh, si.n), dim3(64 * rep), 0, st, a, si, q, kb, vb, kc,
+  const int waves = rep < 4 ? rep : 4;
+  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn + 1, a.kvh, si.n), dim3(64 * waves), 0, st, a, si, q, kb, vb, kc,
                      vc, part, ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -207,7 +223,7 @@ static hipError_t attn_hd(const AttnShape& a, const SeqInfo& si, const float* q,
 }
 
 hipError_t launch_attention(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
-                            const float* kc, const float* vc, float* part, float* ml, int Mpad, bool quant,
+                            const float* kc, const float* vc, double* part, double* ml, int Mpad, bool quant,
                             int8_t* xq, float* dxT, float* xf, hipStream_t st) {
   if (a.nh % a.kvh || a.nh / a.kvh > 16 || a.B > 16 || a.ck % 16 || a.ck <= 0) return hipErrorInvalidValue;
   if (a.hd == 64) return attn_hd<64>(a, si, q, kb, vb, kc, vc, part, ml, Mpad, quant, xq, dxT, xf, st);

@@ -49,9 +49,11 @@ hipError_t launch_pack(int fmt, const void* codes, const void* scales, int rows,
                        long tile_stride, hipStream_t st);
 
 // Quantized weight-streaming GEMM.  xq [Mpad][K] int8 (rows >= M zero or ignored), dxT
-// [K/32][Mpad] f32.  direct: out[m*out_ld + n] for m < m_store; else out is [S][Mpad][N].
+// [K/32][Mpad] f32.  direct: out is f32, out[m*out_ld + n] for m < m_store; else out is the
+// f64 partial sums [S][Mpad][N] of the S K-slices (consumers add them in slice order and
+// round once to f32).
 hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int Mpad,
-                         int splits, float* out, bool direct, int out_ld, int m_store, hipStream_t st);
+                         int splits, void* out, bool direct, int out_ld, int m_store, hipStream_t st);
 // Number of K slices the GEMM uses for a shape when the caller does not fix it, and the
 // number it really uses for a requested count (slices of whole 128-column blocks).
 int choose_splits(int N, int K, int Mpad);
@@ -59,27 +61,28 @@ int normalize_splits(int K, int s);
 hipError_t launch_group_sums(int fmt, const void* W, int N, int K, const int8_t* xq, int Mpad, int M,
                              int32_t* sums, hipStream_t st);
 // f32 GEMM: x [Mpad][K] f32; same output conventions (S = 1).
-hipError_t launch_gemm_f32(const float* W, int N, int K, const float* x, int Mpad, int M, float* out, bool direct,
+hipError_t launch_gemm_f32(const float* W, int N, int K, const float* x, int Mpad, int M, void* out, bool direct,
                            int out_ld, int m_store, hipStream_t st);
 
 // Activation producers.  Every one writes rows [0, Mpad): rows >= M are zero.  quant: xq
 // [Mpad][N] int8 + dxT [N/32][Mpad]; else xf [Mpad][N] f32.
 //
-// v = (resid ? resid[m] : 0) + sum_{s<S} src[(s*src_mstride + m)*N + i]; h_out (optional)
-// receives v; with a norm weight w the row is RMSNormed first.
-hipError_t launch_norm_act(const float* src, int S, int src_mstride, const float* resid, float* h_out,
-                           const float* w, float eps, int M, int Mpad, int N, bool quant, int8_t* xq, float* dxT,
-                           float* xf, hipStream_t st);
+// v = (resid ? resid[m] : 0) + o, o = f32(sum_{s<S} part[(s*part_mstride + m)*N + i]) (f64
+// partials) or, with part NULL, o = x[m*N + i] (f32 rows); h_out (optional) receives v; with a
+// norm weight w the row is RMSNormed first.
+hipError_t launch_norm_act(const double* part, const float* x, int S, int part_mstride, const float* resid,
+                           float* h_out, const float* w, float eps, int M, int Mpad, int N, bool quant, int8_t* xq,
+                           float* dxT, float* xf, hipStream_t st);
 // a = silu(gate) * up from the interleaved gate|up partials [S][Mpad][2I].
-hipError_t launch_swiglu_act(const float* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
+hipError_t launch_swiglu_act(const double* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
                              float* xf, hipStream_t st);
 // q/k/v of the block rows from the fused projection partials [S][Mpad][qd + 2 kvd]:
 // q-norm / k-norm, RoPE at si.pos0[m / B] + m % B.
-hipError_t launch_qkv_epilogue(const float* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
+hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
                                int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
                                float* q, float* k, float* v, hipStream_t st);
 // Context rows into the cache from the all-layer K|V partials [S][Mpad][L * 2 kvd].
-hipError_t launch_kv_append(const float* part, int S, int Mpad, int n, int layers, int kvh, int hd,
+hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
                             const float* k_norms, const float* inv_freq, float eps, long long pos0, int row0,
                             int slot, int max_seqs, int max_ctx, float* kc, float* vc, hipStream_t st);
 
@@ -89,8 +92,13 @@ struct AttnShape {
   float scale;
 };
 hipError_t launch_attention(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
-                            const float* kc, const float* vc, float* part, float* ml, int Mpad, bool quant,
+                            const float* kc, const float* vc, double* part, double* ml, int Mpad, bool quant,
                             int8_t* xq, float* dxT, float* xf, hipStream_t st);
+
+// Dynamic LDS a workgroup may use on the current device (queried once per device), and a
+// helper that raises a kernel's dynamic-LDS limit when a launch needs more than the default.
+size_t max_dynamic_lds();
+hipError_t allow_lds(const void* kernel, size_t bytes);
 
 hipError_t launch_inv_freq(double theta, int hd, float* out, hipStream_t st);
 hipError_t launch_quant_rows(const float* x, int rows, int cols, int8_t* q, float* d, hipStream_t st);

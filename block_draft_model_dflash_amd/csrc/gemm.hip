@@ -10,12 +10,19 @@
 // away.  The int8 activation block and its scales are staged once per workgroup in LDS and
 // shared by the workgroup's four waves; K is split across blockIdx.y when the weight has few
 // n-tiles (partial sums [S][Mpad][N] are reduced by the consumer kernel, in slice order).
+//
+// The rescale accumulates in f64: d_w*d_x is exact in f64 and so is its product with a Q4 group
+// sum, so each output is the f32 rounding of (nearly) the exact sum, the same value a plain f64
+// evaluation gives.  Every product feeds an int8 quantizer downstream, and a value one ulp off
+// there flips codes that the following layers amplify to percent-level differences in the
+// logits; correctly rounded outputs keep two implementations on the same codes.
 #include "common.h"
 
 namespace dfl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef double v2d __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
@@ -63,20 +70,21 @@ __device__ __forceinline__ float w_scale(const Super<FMT>& r, int j) {
   return f16_to_f32(w >> (16 * (j & 1)));
 }
 
-constexpr int PF = 4;            // superblocks in flight per wave
-constexpr int LDS_COLS_X16 = 4096;  // K columns staged per chunk x (Mpad/16) rows-of-16
+constexpr int PF = 4;  // superblocks in flight per wave
+// LDS budget of one workgroup's activation chunk: two workgroups fit a 160 KB CU
+constexpr size_t LDS_BUDGET = 76 * 1024;
 
 template <int FMT, int MT>
 __global__ __launch_bounds__(256) void k_gemm_q(const uint8_t* __restrict__ W, int N, int K,
                                                const int8_t* __restrict__ xq, const float* __restrict__ dxT,
-                                               int kbps, int kcb, float* __restrict__ out, int direct, int out_ld,
+                                               int kbps, int kcb, void* __restrict__ out, int direct, int out_ld,
                                                int m_store) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MR = MT * 16;
   constexpr int SBB = FMT == Q4 ? SB_Q4 : SB_Q8;
   const int ASTR = kcb * 128 + 16;  // padded LDS row: rows land 4 banks apart
   int8_t* A = (int8_t*)smem;
-  float* DX = (float*)(smem + MR * ASTR);  // [kcb*4 groups][MR]
+  double* DX = (double*)(smem + MR * ASTR);  // [kcb*4 groups][MR], activation scales in f64
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntile = blockIdx.x * 4 + wave;
   const bool active = ntile < (N >> 4);
@@ -86,9 +94,11 @@ __global__ __launch_bounds__(256) void k_gemm_q(const uint8_t* __restrict__ W, i
   const uint8_t* wt = W + (size_t)ntile * KB * SBB;
   const int quarter = lane >> 4, row16 = lane & 15;
 
-  v4f acc[MT];
+  double acc[MT][4];
 #pragma unroll
-  for (int mt = 0; mt < MT; mt++) acc[mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) acc[mt][r] = 0.0;
 
   for (int c0 = kb0; c0 < kb1; c0 += kcb) {
     const int c1 = min(c0 + kcb, kb1);
@@ -101,7 +111,7 @@ __global__ __launch_bounds__(256) void k_gemm_q(const uint8_t* __restrict__ W, i
     }
     const int ng = ncols >> 5;
     const float* dsrc = dxT + (size_t)c0 * 4 * MR;
-    for (int i = tid; i < ng * MR; i += 256) DX[i] = dsrc[i];
+    for (int i = tid; i < ng * MR; i += 256) DX[i] = (double)dsrc[i];
     __syncthreads();
     if (active) {
       for (int kb = c0; kb < c1; kb += PF) {
@@ -116,14 +126,18 @@ __global__ __launch_bounds__(256) void k_gemm_q(const uint8_t* __restrict__ W, i
 #pragma unroll
             for (int j = 0; j < 4; j++) {
               const long b = b_operand(r[p], j);
-              const float dw = w_scale<FMT>(r[p], j);
+              const double dw = (double)w_scale<FMT>(r[p], j);
               const int col = kk * 128 + 32 * j + 8 * quarter;
 #pragma unroll
               for (int mt = 0; mt < MT; mt++) {
                 const long a = *(const long*)(A + (mt * 16 + row16) * ASTR + col);
                 const v4i s = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (v4i){0, 0, 0, 0}, 0, 0, 0);
-                const v4f dx = *(const v4f*)(DX + (kk * 4 + j) * MR + mt * 16 + 4 * quarter);
-                acc[mt] += __builtin_convertvector(s, v4f) * (dw * dx);
+                const double* dxp = DX + (kk * 4 + j) * MR + mt * 16 + 4 * quarter;
+                const v2d d01 = *(const v2d*)dxp, d23 = *(const v2d*)(dxp + 2);
+                acc[mt][0] = __builtin_fma((double)s[0], dw * d01[0], acc[mt][0]);
+                acc[mt][1] = __builtin_fma((double)s[1], dw * d01[1], acc[mt][1]);
+                acc[mt][2] = __builtin_fma((double)s[2], dw * d23[0], acc[mt][2]);
+                acc[mt][3] = __builtin_fma((double)s[3], dw * d23[1], acc[mt][3]);
               }
             }
           }
@@ -132,18 +146,18 @@ __global__ __launch_bounds__(256) void k_gemm_q(const uint8_t* __restrict__ W, i
     }
   }
   if (!active) return;
-  const float post = FMT == Q4 ? 0.0625f : 1.0f;  // Q4 codes entered the MFMA as 16*q
+  const double post = FMT == Q4 ? 0.0625 : 1.0;  // Q4 codes entered the MFMA as 16*q
   const int n = ntile * 16 + row16;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int m = mt * 16 + 4 * quarter + r;
-      const float v = acc[mt][r] * post;
+      const double v = acc[mt][r] * post;
       if (direct) {
-        if (m < m_store) out[(size_t)m * out_ld + n] = v;
+        if (m < m_store) ((float*)out)[(size_t)m * out_ld + n] = (float)v;
       } else {
-        out[((size_t)blockIdx.y * MR + m) * N + n] = v;
+        ((double*)out)[((size_t)blockIdx.y * MR + m) * N + n] = v;
       }
     }
   }
@@ -195,20 +209,19 @@ int choose_splits(int N, int K, int Mpad) {
 }
 
 template <int FMT, int MT>
-static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, int splits, float* out,
+static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, int splits, void* out,
                             bool direct, int out_ld, int m_store, hipStream_t st) {
   const int KB = K / 128;
   const int kbps = ceil_div(KB, splits);
-  const int kcb_max = LDS_COLS_X16 / 128 / MT;
+  // per 128-column block: MT*16 rows of 128 codes + 4 groups x MT*16 f64 scales; row padding
+  size_t budget = max_dynamic_lds();
+  if (budget > LDS_BUDGET) budget = LDS_BUDGET;
+  int kcb_max = (int)((budget - (size_t)256 * MT) / ((size_t)2560 * MT));
+  if (kcb_max < 1) kcb_max = 1;
   const int kcb = kbps < kcb_max ? kbps : kcb_max;
-  const size_t lds = (size_t)MT * 16 * (kcb * 128 + 16) + (size_t)kcb * 4 * MT * 16 * 4;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q<FMT, MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       96 * 1024);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  const size_t lds = (size_t)MT * 16 * (kcb * 128 + 16) + (size_t)kcb * 4 * MT * 16 * 8;
+  hipError_t e = allow_lds((const void*)k_gemm_q<FMT, MT>, lds);
+  if (e != hipSuccess) return e;
   dim3 grid((unsigned)ceil_div(N / 16, 4), (unsigned)ceil_div(KB, kbps));
   hipLaunchKernelGGL((k_gemm_q<FMT, MT>), grid, dim3(256), lds, st, (const uint8_t*)W, N, K, xq, dxT, kbps, kcb, out,
                      direct ? 1 : 0, out_ld, m_store);
@@ -217,7 +230,7 @@ static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const
 
 template <int FMT>
 static hipError_t gemm_fmt(const void* W, int N, int K, const int8_t* xq, const float* dxT, int Mpad, int splits,
-                           float* out, bool direct, int out_ld, int m_store, hipStream_t st) {
+                           void* out, bool direct, int out_ld, int m_store, hipStream_t st) {
   switch (Mpad / 16) {
     case 1: return gemm_inst<FMT, 1>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
     case 2: return gemm_inst<FMT, 2>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
@@ -232,7 +245,7 @@ static hipError_t gemm_fmt(const void* W, int N, int K, const int8_t* xq, const 
 }
 
 hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int Mpad,
-                         int splits, float* out, bool direct, int out_ld, int m_store, hipStream_t st) {
+                         int splits, void* out, bool direct, int out_ld, int m_store, hipStream_t st) {
   if (N % 16 || K % 128 || Mpad % 16 || Mpad < 16 || Mpad > 128) return hipErrorInvalidValue;
   splits = normalize_splits(K, splits);
   if (direct && splits != 1) return hipErrorInvalidValue;
@@ -254,30 +267,31 @@ hipError_t launch_group_sums(int fmt, const void* W, int N, int K, const int8_t*
   return hipGetLastError();
 }
 
-// f32 matrices (the unquantized drafter): one wave per output row, lanes across K.
+// f32 matrices (the unquantized drafter): one wave per output row, lanes across K, products
+// and sums in f64 (f32 x f32 is exact in f64), one rounding at the end.
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ W, int N, int K,
                                                  const float* __restrict__ x, int Mpad, int M,
-                                                 float* __restrict__ out, int direct, int out_ld, int m_store) {
+                                                 void* __restrict__ out, int direct, int out_ld, int m_store) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = blockIdx.x * 4 + wave;
   if (n >= N) return;
   const float* w = W + (size_t)n * K;
   for (int m = 0; m < Mpad; m++) {
-    float acc = 0.f;
+    double acc = 0.0;
     if (m < M)
-      for (int k = lane; k < K; k += 64) acc += w[k] * x[(size_t)m * K + k];
+      for (int k = lane; k < K; k += 64) acc = __builtin_fma((double)w[k], (double)x[(size_t)m * K + k], acc);
     for (int o = 32; o; o >>= 1) acc += __shfl_xor(acc, o);
     if (lane == 0) {
       if (direct) {
-        if (m < m_store) out[(size_t)m * out_ld + n] = acc;
+        if (m < m_store) ((float*)out)[(size_t)m * out_ld + n] = (float)acc;
       } else {
-        out[(size_t)m * N + n] = acc;
+        ((double*)out)[(size_t)m * N + n] = acc;
       }
     }
   }
 }
 
-hipError_t launch_gemm_f32(const float* W, int N, int K, const float* x, int Mpad, int M, float* out, bool direct,
+hipError_t launch_gemm_f32(const float* W, int N, int K, const float* x, int Mpad, int M, void* out, bool direct,
                            int out_ld, int m_store, hipStream_t st) {
   hipLaunchKernelGGL(k_gemm_f32, dim3((unsigned)ceil_div(N, 4)), dim3(256), 0, st, W, N, K, x, Mpad, M, out,
                      direct ? 1 : 0, out_ld, m_store);

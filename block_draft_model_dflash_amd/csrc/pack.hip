@@ -68,6 +68,25 @@ hipError_t launch_pack(int fmt, const void* codes, const void* scales, int rows,
   return hipGetLastError();
 }
 
+size_t max_dynamic_lds() {
+  static size_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+      v = 64 * 1024;
+    cached[dev] = (size_t)v;
+  }
+  return cached[dev];
+}
+
+hipError_t allow_lds(const void* kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  if (bytes > max_dynamic_lds()) return hipErrorInvalidValue;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 // inv_freq[i] = theta^(-2i/hd) in f64, stored f32 (cortiq-engine dflash.rs, Drafter::new).
 __global__ void k_inv_freq(double theta, int hd, float* out) {
   const int i = threadIdx.x;
