@@ -46,27 +46,37 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   return t;
 }
 
-// f32 of the sum of S f64 partial slices of element (m, col): one rounding.
+// f32 of the sum of S f64 partial slices of element (m, col): one rounding.  The slices are
+// loaded together (they are independent) and added in slice order.
+constexpr int MAX_SLICES = 16;
 __device__ __forceinline__ float reduce_parts(const double* __restrict__ part, int S, int mstride, int m, size_t N,
                                               size_t col) {
-  double o = part[(size_t)m * N + col];
-  for (int s = 1; s < S; s++) o += part[((size_t)s * mstride + m) * N + col];
+  double v[MAX_SLICES];
+#pragma unroll
+  for (int s = 0; s < MAX_SLICES; s++) v[s] = s < S ? part[((size_t)s * mstride + m) * N + col] : 0.0;
+  double o = v[0];
+#pragma unroll
+  for (int s = 1; s < MAX_SLICES; s++)
+    if (s < S) o += v[s];
   return (float)o;
 }
+
+constexpr int ROW_THREADS = 1024;  // one workgroup per row, 16 waves
 
 // v = resid + o; optional write-back; optional RMSNorm; then A8_32 or f32.  The dx element of
 // (row m, group g) sits at g*dxg + m*dxm.
 template <bool NORM, bool QUANT>
-__global__ __launch_bounds__(256) void k_norm_act(const double* __restrict__ part, const float* __restrict__ x, int S,
-                                                 int part_mstride, const float* __restrict__ resid,
-                                                 float* __restrict__ h_out, const float* __restrict__ w, float eps,
-                                                 int M, int N, int8_t* __restrict__ xq, float* __restrict__ dx,
-                                                 int dxg, int dxm, float* __restrict__ xf) {
+__global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restrict__ part,
+                                                         const float* __restrict__ x, int S, int part_mstride,
+                                                         const float* __restrict__ resid, float* __restrict__ h_out,
+                                                         const float* __restrict__ w, float eps, int M, int N,
+                                                         int8_t* __restrict__ xq, float* __restrict__ dx, int dxg,
+                                                         int dxm, float* __restrict__ xf) {
   extern __shared__ float row[];  // N floats when NORM
-  __shared__ double red[4];
+  __shared__ double red[ROW_THREADS / 64];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   if (m >= M) {
-    for (int i = tid; i < N; i += 256) {
+    for (int i = tid; i < N; i += ROW_THREADS) {
       if (QUANT) {
         xq[(size_t)m * N + i] = 0;
         if ((lane & 31) == 0) dx[(size_t)(i >> 5) * dxg + (size_t)m * dxm] = 0.f;
@@ -77,7 +87,7 @@ __global__ __launch_bounds__(256) void k_norm_act(const double* __restrict__ par
     return;
   }
   double ss = 0.0;
-  for (int i = tid; i < N; i += 256) {
+  for (int i = tid; i < N; i += ROW_THREADS) {
     const float o = part ? reduce_parts(part, S, part_mstride, m, N, i) : x[(size_t)m * N + i];
     const float v = resid ? resid[(size_t)m * N + i] + o : o;
     if (h_out) h_out[(size_t)m * N + i] = v;
@@ -93,7 +103,7 @@ __global__ __launch_bounds__(256) void k_norm_act(const double* __restrict__ par
   if (!NORM) return;
   ss = block_sum_f64(ss, red);
   const float sc = 1.0f / sqrtf((float)(ss / (double)N) + eps);
-  for (int i = tid; i < N; i += 256) {
+  for (int i = tid; i < N; i += ROW_THREADS) {
     const float t = row[i] * sc;
     const float y = t * w[i];
     if (QUANT)
@@ -110,15 +120,16 @@ static hipError_t norm_act_inst(const double* part, const float* x, int S, int p
   const size_t lds = NORM ? (size_t)N * 4 : 0;
   hipError_t e = allow_lds((const void*)k_norm_act<NORM, QUANT>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_norm_act<NORM, QUANT>), dim3(grid), dim3(256), lds, st, part, x, S, part_mstride, resid, h_out,
-                     w, eps, M, N, xq, dx, dxg, dxm, xf);
+  hipLaunchKernelGGL((k_norm_act<NORM, QUANT>), dim3(grid), dim3(ROW_THREADS), lds, st, part, x, S, part_mstride, resid,
+                     h_out, w, eps, M, N, xq, dx, dxg, dxm, xf);
   return hipGetLastError();
 }
 
 hipError_t launch_norm_act(const double* part, const float* x, int S, int part_mstride, const float* resid,
                            float* h_out, const float* w, float eps, int M, int Mpad, int N, bool quant, int8_t* xq,
                            float* dxT, float* xf, hipStream_t st) {
-  if ((w && (size_t)N * 4 > 96 * 1024) || (quant && N % 32) || (!part && !x)) return hipErrorInvalidValue;
+  if ((w && (size_t)N * 4 > 96 * 1024) || (quant && N % 32) || (!part && !x) || S > MAX_SLICES)
+    return hipErrorInvalidValue;
   if (w && quant)
     return norm_act_inst<true, true>(part, x, S, part_mstride, resid, h_out, w, eps, M, Mpad, N, xq, dxT, Mpad, 1, xf,
                                      st);
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(256) void k_swiglu_act(const double* __restrict__ p
 
 hipError_t launch_swiglu_act(const double* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
                              float* xf, hipStream_t st) {
-  if (I % 32) return hipErrorInvalidValue;
+  if (I % 32 || S > MAX_SLICES) return hipErrorInvalidValue;
   dim3 g((unsigned)((I + 1023) / 1024), (unsigned)Mpad);
   if (quant)
     hipLaunchKernelGGL(k_swiglu_act<true>, g, dim3(256), 0, st, part, S, M, Mpad, I, xq, dxT, xf);
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(128) void k_qkv_epilogue(const double* __restrict__
 hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
                                int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
                                float* q, float* k, float* v, hipStream_t st) {
-  if (hd > 128 || hd % 2) return hipErrorInvalidValue;
+  if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_qkv_epilogue, dim3(nh + 2 * kvh, M), dim3(128), 0, st, part, S, Mpad, B, si, nh, kvh, hd,
                      q_norm, k_norm, inv_freq, eps, q, k, v);
   return hipGetLastError();
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(128) void k_kv_append(const double* __restrict__ pa
 hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
                             const float* k_norms, const float* inv_freq, float eps, long long pos0, int row0,
                             int slot, int max_seqs, int max_ctx, float* kc, float* vc, hipStream_t st) {
-  if (hd > 128 || hd % 2) return hipErrorInvalidValue;
+  if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_kv_append, dim3(layers * 2 * kvh, n), dim3(128), 0, st, part, S, Mpad, layers, kvh, hd,
                      k_norms, inv_freq, eps, pos0, row0, slot, max_seqs, max_ctx, kc, vc);
   return hipGetLastError();

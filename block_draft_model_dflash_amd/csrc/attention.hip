@@ -25,8 +25,10 @@ namespace dfl {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 
+constexpr int ATTN_THREADS = 256;  // four waves: one q head each per round
+
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_partial(AttnShape a, SeqInfo si, const float* __restrict__ q,
+__global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqInfo si, const float* __restrict__ q,
                                                      const float* __restrict__ kb, const float* __restrict__ vb,
                                                      const float* __restrict__ kc, const float* __restrict__ vc,
                                                      double* __restrict__ part, double* __restrict__ ml) {
@@ -37,7 +39,9 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnShape a, SeqInfo si, c
   const int nctx = si.nctx[s];
   const int nch = (nctx + a.ck - 1) / a.ck;
   if (c > nch) return;  // the whole workgroup: this sequence has fewer chunks
-  const int rep = a.nh / a.kvh, waves = blockDim.x >> 6;
+  const int rep = a.nh / a.kvh;
+  constexpr int waves = ATTN_THREADS / 64;
+  constexpr int NL = 16 * (HD / 4) / ATTN_THREADS;  // float4 of K (and of V) each thread stages per tile
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int quarter = lane >> 4, col = lane & 15;
   const bool blockchunk = c == nch;
@@ -70,20 +74,33 @@ __global__ __launch_bounds__(256) void k_attn_partial(AttnShape a, SeqInfo si, c
 #pragma unroll
     for (int dt = 0; dt < HD / 16; dt++) acc[dt] = (v4d){0.0, 0.0, 0.0, 0.0};
 
+    // the next tile's keys and values travel to registers while the current one is computed
+    v4f pk[NL], pv[NL];
+    auto fetch = [&](int t) {
+#pragma unroll
+      for (int u = 0; u < NL; u++) {
+        const int i = tid + u * ATTN_THREADS;
+        const int r = i / (HD / 4), c4 = i % (HD / 4);
+        const int key = t + r;
+        pk[u] = pv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+        if (key < kend) {
+          pk[u] = *(const v4f*)(Kbase + (size_t)key * kstride + 4 * c4);
+          pv[u] = *(const v4f*)(Vbase + (size_t)key * kstride + 4 * c4);
+        }
+      }
+    };
+    fetch(k0);
     for (int t0 = k0; t0 < kend; t0 += 16) {
       __syncthreads();
-      for (int i = tid; i < 16 * (HD / 4); i += blockDim.x) {
+#pragma unroll
+      for (int u = 0; u < NL; u++) {
+        const int i = tid + u * ATTN_THREADS;
         const int r = i / (HD / 4), c4 = i % (HD / 4);
-        const int key = t0 + r;
-        v4f kv = (v4f){0.f, 0.f, 0.f, 0.f}, vv = kv;
-        if (key < kend) {
-          kv = *(const v4f*)(Kbase + (size_t)key * kstride + 4 * c4);
-          vv = *(const v4f*)(Vbase + (size_t)key * kstride + 4 * c4);
-        }
-        *(v4f*)(Ks + r * KS + 4 * c4) = kv;
-        *(v4f*)(Vs + r * KS + 4 * c4) = vv;
+        *(v4f*)(Ks + r * KS + 4 * c4) = pk[u];
+        *(v4f*)(Vs + r * KS + 4 * c4) = pv[u];
       }
       __syncthreads();
+      if (t0 + 16 < kend) fetch(t0 + 16);
       if (!live) continue;
       v4d st0 = (v4d){0.0, 0.0, 0.0, 0.0}, st1 = st0;
 #pragma unroll
@@ -163,37 +180,57 @@ __device__ __forceinline__ void emit_q8(float y, size_t qi, int8_t* __restrict__
   if ((lane & 31) == 0) dx[di] = d;
 }
 
-// One wave per (q head, block row, sequence): combine the chunks' (max, sum, acc).
+// One workgroup of four waves per (q head, block row, sequence) combines the chunks' (max,
+// sum, acc): the lanes first find the largest chunk maximum, then wave w adds the chunks
+// c = w mod 4 weighted by exp(m_c - max), and the four waves' sums are added in wave order.
+constexpr int MERGE_WAVES = 4;
 template <int HD, bool QUANT>
-__global__ __launch_bounds__(64) void k_attn_merge(AttnShape a, SeqInfo si, const double* __restrict__ part,
-                                                  const double* __restrict__ ml, int Mpad, int8_t* __restrict__ xq,
-                                                  float* __restrict__ dxT, float* __restrict__ xf) {
-  const int j = blockIdx.x, r = blockIdx.y, s = blockIdx.z, lane = threadIdx.x;
-  const int rep = a.nh / a.kvh, g = j / rep, w = j % rep;
-  const int nch = (si.nctx[s] + a.ck - 1) / a.ck;
+__global__ __launch_bounds__(64 * MERGE_WAVES) void k_attn_merge(AttnShape a, SeqInfo si,
+                                                                const double* __restrict__ part,
+                                                                const double* __restrict__ ml, int Mpad,
+                                                                int8_t* __restrict__ xq, float* __restrict__ dxT,
+                                                                float* __restrict__ xf) {
+  __shared__ double ys[MERGE_WAVES][HD];
+  __shared__ double ls[MERGE_WAVES];
+  const int j = blockIdx.x, r = blockIdx.y, s = blockIdx.z, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rep = a.nh / a.kvh, g = j / rep, hw = j % rep;
+  const int nch = (si.nctx[s] + a.ck - 1) / a.ck;  // context chunks; chunk nch is the block's own rows
   const size_t base = (((size_t)s * a.kvh + g) * a.maxch) * rep;
+  auto row_of = [&](int c) { return (base + (size_t)c * rep + hw) * 16 + r; };
   double mx = -INFINITY;
-  for (int c = 0; c <= nch; c++) mx = fmax(mx, ml[(((base + (size_t)c * rep + w) * 16) + r) * 2]);
+  for (int c = lane; c <= nch; c += 64) mx = fmax(mx, ml[row_of(c) * 2]);
+#pragma unroll
+  for (int o = 32; o; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
   double L = 0.0, y[HD / 64];
 #pragma unroll
   for (int t = 0; t < HD / 64; t++) y[t] = 0.0;
-  for (int c = 0; c <= nch; c++) {
-    const size_t row = (base + (size_t)c * rep + w) * 16 + r;
+#pragma unroll 4
+  for (int c = w; c <= nch; c += MERGE_WAVES) {
+    const size_t row = row_of(c);
     const double e = exp(ml[row * 2] - mx);
     L += ml[row * 2 + 1] * e;
 #pragma unroll
     for (int t = 0; t < HD / 64; t++) y[t] += part[row * HD + lane + 64 * t] * e;
   }
+#pragma unroll
+  for (int t = 0; t < HD / 64; t++) ys[w][lane + 64 * t] = y[t];
+  if (lane == 0) ls[w] = L;
+  __syncthreads();
+  if (w != 0) return;
+  double Lt = ls[0];
+  for (int v = 1; v < MERGE_WAVES; v++) Lt += ls[v];
   const int m = s * a.B + r;
   const size_t qd = (size_t)a.nh * HD;
 #pragma unroll
   for (int t = 0; t < HD / 64; t++) {
-    const float v = (float)(y[t] / L);
+    double yt = ys[0][lane + 64 * t];
+    for (int v = 1; v < MERGE_WAVES; v++) yt += ys[v][lane + 64 * t];
+    const float val = (float)(yt / Lt);
     const size_t colx = (size_t)j * HD + lane + 64 * t;
     if (QUANT)
-      emit_q8(v, (size_t)m * qd + colx, xq, dxT, (colx >> 5) * Mpad + m, lane);
+      emit_q8(val, (size_t)m * qd + colx, xq, dxT, (colx >> 5) * Mpad + m, lane);
     else
-      xf[(size_t)m * qd + colx] = v;
+      xf[(size_t)m * qd + colx] = val;
   }
 }
 
@@ -207,18 +244,16 @@ static hipError_t attn_hd(const AttnShape& a, const SeqInfo& si, const float* q,
     if (nch > maxn) maxn = nch;
   }
   if (maxn + 1 > a.maxch) return hipErrorInvalidValue;
-  const int rep = a.nh / a.kvh;
-  const int waves = rep < 4 ? rep : 4;
-  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn + 1, a.kvh, si.n), dim3(64 * waves), 0, st, a, si, q, kb, vb, kc,
-                     vc, part, ml);
+  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn + 1, a.kvh, si.n), dim3(ATTN_THREADS), 0, st, a, si, q, kb, vb,
+                     kc, vc, part, ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (quant)
-    hipLaunchKernelGGL((k_attn_merge<HD, true>), dim3(a.nh, a.B, si.n), dim3(64), 0, st, a, si, part, ml, Mpad, xq,
-                       dxT, xf);
+    hipLaunchKernelGGL((k_attn_merge<HD, true>), dim3(a.nh, a.B, si.n), dim3(64 * MERGE_WAVES), 0, st, a, si, part,
+                       ml, Mpad, xq, dxT, xf);
   else
-    hipLaunchKernelGGL((k_attn_merge<HD, false>), dim3(a.nh, a.B, si.n), dim3(64), 0, st, a, si, part, ml, Mpad, xq,
-                       dxT, xf);
+    hipLaunchKernelGGL((k_attn_merge<HD, false>), dim3(a.nh, a.B, si.n), dim3(64 * MERGE_WAVES), 0, st, a, si, part,
+                       ml, Mpad, xq, dxT, xf);
   return hipGetLastError();
 }
 

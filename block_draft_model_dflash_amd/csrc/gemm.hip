@@ -51,6 +51,22 @@ __device__ __forceinline__ void super_load(const uint8_t* sb, int lane, Super<Q8
   r.s = *(const uint2*)(sb + SB_SCALES_Q8 + 8 * (lane & 15));
 }
 
+// The same through a buffer resource covering one wave's superblocks: a superblock past the
+// resource's end reads as zeros and costs no memory traffic, so a load ring needs no branches.
+constexpr int RSRC_WORD3 = 0x00020000;  // raw (untyped) buffer access, gfx9-family encoding
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, RSRC_WORD3);
+}
+__device__ __forceinline__ void super_load(__amdgpu_buffer_rsrc_t rs, int off, int lane, Super<Q4>& r) {
+  r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * lane, 0, 0));
+  r.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + SB_SCALES_Q4 + 8 * (lane & 15), 0, 0));
+}
+__device__ __forceinline__ void super_load(__amdgpu_buffer_rsrc_t rs, int off, int lane, Super<Q8>& r) {
+  r.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * lane, 0, 0));
+  r.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 + 16 * lane, 0, 0));
+  r.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + SB_SCALES_Q8 + 8 * (lane & 15), 0, 0));
+}
+
 __device__ __forceinline__ uint32_t pick(uint4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
 
 // B operand of group j: 8 signed bytes, columns k0..k0+7 of the lane's row.  Q4 gives 16*q.
@@ -70,23 +86,31 @@ __device__ __forceinline__ float w_scale(const Super<FMT>& r, int j) {
   return f16_to_f32(w >> (16 * (j & 1)));
 }
 
-constexpr int PF = 4;  // superblocks in flight per wave
-// LDS budget of one workgroup's activation chunk: two workgroups fit a 160 KB CU
+// superblocks in flight per wave (a register ring): deep for the block's few rows, shallower
+// when the accumulators of many row tiles take the registers
+constexpr int PF = 8;
+template <int MT>
+struct Ring {
+  static constexpr int depth = MT <= 2 ? 8 : MT <= 4 ? 4 : 2;
+};
+// LDS budget of one workgroup's activation chunk (int8 rows and their scales): two
+// workgroups fit a 160 KB CU
 constexpr size_t LDS_BUDGET = 76 * 1024;
 
-template <int FMT, int MT>
-__global__ __launch_bounds__(256) void k_gemm_q(const uint8_t* __restrict__ W, int N, int K,
-                                               const int8_t* __restrict__ xq, const float* __restrict__ dxT,
-                                               int kbps, int kcb, void* __restrict__ out, int direct, int out_ld,
-                                               int m_store) {
+template <int FMT, int MT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_q(const uint8_t* __restrict__ W, int N, int K,
+                                                      const int8_t* __restrict__ xq,
+                                                      const float* __restrict__ dxT, int kbps, int kcb,
+                                                      void* __restrict__ out, int direct, int out_ld, int m_store) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MR = MT * 16;
   constexpr int SBB = FMT == Q4 ? SB_Q4 : SB_Q8;
+  constexpr int NT = 64 * WAVES;
   const int ASTR = kcb * 128 + 16;  // padded LDS row: rows land 4 banks apart
   int8_t* A = (int8_t*)smem;
-  double* DX = (double*)(smem + MR * ASTR);  // [kcb*4 groups][MR], activation scales in f64
+  float* DX = (float*)(smem + MR * ASTR);  // [kcb*4 groups][MR] activation scales (exact in f64)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntile = blockIdx.x * 4 + wave;
+  const int ntile = blockIdx.x * WAVES + wave;
   const bool active = ntile < (N >> 4);
   const int KB = K >> 7;
   const int kb0 = blockIdx.y * kbps;
@@ -100,48 +124,50 @@ __global__ __launch_bounds__(256) void k_gemm_q(const uint8_t* __restrict__ W, i
 #pragma unroll
     for (int r = 0; r < 4; r++) acc[mt][r] = 0.0;
 
+  constexpr int RD = Ring<MT>::depth;
+  Super<FMT> r[RD];
   for (int c0 = kb0; c0 < kb1; c0 += kcb) {
     const int c1 = min(c0 + kcb, kb1);
     const int ncols = (c1 - c0) * 128;
-    __syncthreads();
+    if (c0 != kb0) __syncthreads();  // the previous chunk's LDS reads are done
+    // the weights' ring is filled first, so their HBM latency overlaps the activations' staging
+    const __amdgpu_buffer_rsrc_t rs = wave_rsrc(wt, active ? c1 * SBB : 0);
+#pragma unroll
+    for (int p = 0; p < RD; p++) super_load(rs, (c0 + p) * SBB, lane, r[p]);
     const int v16 = ncols >> 4;
-    for (int i = tid; i < MR * v16; i += 256) {
-      const int r = i / v16, c = i - r * v16;
-      *(uint4*)(A + r * ASTR + c * 16) = *(const uint4*)(xq + (size_t)r * K + (size_t)c0 * 128 + c * 16);
+    for (int i = tid; i < MR * v16; i += NT) {
+      const int rr = i / v16, c = i - rr * v16;
+      *(uint4*)(A + rr * ASTR + c * 16) = *(const uint4*)(xq + (size_t)rr * K + (size_t)c0 * 128 + c * 16);
     }
     const int ng = ncols >> 5;
     const float* dsrc = dxT + (size_t)c0 * 4 * MR;
-    for (int i = tid; i < ng * MR; i += 256) DX[i] = (double)dsrc[i];
+    for (int i = tid; i < ng * MR; i += NT) DX[i] = dsrc[i];
     __syncthreads();
-    if (active) {
-      for (int kb = c0; kb < c1; kb += PF) {
-        Super<FMT> r[PF];
+    if (!active) continue;
+    for (int kb = c0; kb < c1; kb += RD) {
 #pragma unroll
-        for (int p = 0; p < PF; p++)
-          if (kb + p < c1) super_load(wt + (size_t)(kb + p) * SBB, lane, r[p]);
+      for (int p = 0; p < RD; p++) {
+        if (kb + p < c1) {
+          const int kk = kb + p - c0;
+#pragma unroll MT <= 2 ? 4 : 1
+          for (int j = 0; j < 4; j++) {
+            const long b = b_operand(r[p], j);
+            const double dw = (double)w_scale<FMT>(r[p], j);
+            const int col = kk * 128 + 32 * j + 8 * quarter;
 #pragma unroll
-        for (int p = 0; p < PF; p++) {
-          if (kb + p < c1) {
-            const int kk = kb + p - c0;
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-              const long b = b_operand(r[p], j);
-              const double dw = (double)w_scale<FMT>(r[p], j);
-              const int col = kk * 128 + 32 * j + 8 * quarter;
-#pragma unroll
-              for (int mt = 0; mt < MT; mt++) {
-                const long a = *(const long*)(A + (mt * 16 + row16) * ASTR + col);
-                const v4i s = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (v4i){0, 0, 0, 0}, 0, 0, 0);
-                const double* dxp = DX + (kk * 4 + j) * MR + mt * 16 + 4 * quarter;
-                const v2d d01 = *(const v2d*)dxp, d23 = *(const v2d*)(dxp + 2);
-                acc[mt][0] = __builtin_fma((double)s[0], dw * d01[0], acc[mt][0]);
-                acc[mt][1] = __builtin_fma((double)s[1], dw * d01[1], acc[mt][1]);
-                acc[mt][2] = __builtin_fma((double)s[2], dw * d23[0], acc[mt][2]);
-                acc[mt][3] = __builtin_fma((double)s[3], dw * d23[1], acc[mt][3]);
-              }
+            for (int mt = 0; mt < MT; mt++) {
+              const long a = *(const long*)(A + (mt * 16 + row16) * ASTR + col);
+              const v4i sm = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (v4i){0, 0, 0, 0}, 0, 0, 0);
+              const v4f dx = *(const v4f*)(DX + (kk * 4 + j) * MR + mt * 16 + 4 * quarter);
+              acc[mt][0] = __builtin_fma((double)sm[0], dw * (double)dx[0], acc[mt][0]);
+              acc[mt][1] = __builtin_fma((double)sm[1], dw * (double)dx[1], acc[mt][1]);
+              acc[mt][2] = __builtin_fma((double)sm[2], dw * (double)dx[2], acc[mt][2]);
+              acc[mt][3] = __builtin_fma((double)sm[3], dw * (double)dx[3], acc[mt][3]);
             }
           }
         }
+        // refill the slot with the superblock RD ahead (zeros, no traffic, past the chunk)
+        super_load(rs, (kb + p + RD) * SBB, lane, r[p]);
       }
     }
   }
@@ -197,34 +223,40 @@ int normalize_splits(int K, int s) {
   const int KB = K / 128;
   if (s < 1) s = 1;
   if (s > KB) s = KB;
+  if (s > 16) s = 16;  // the consumers add at most 16 slices
   const int kbps = ceil_div(KB, s);
   return ceil_div(KB, kbps);
 }
 
 int choose_splits(int N, int K, int Mpad) {
   (void)Mpad;
-  const int tiles = N / 16;
-  const int s = ceil_div(2048, tiles);  // about eight waves per CU over 256 CUs
-  return normalize_splits(K, s);
+  const int tiles = N / 16, KB = K / 128;
+  // A product with thousands of n-tiles streams its weights without splitting K; a smaller one
+  // gives each wave about PF superblocks, so all of its loads are in flight from the start.
+  if (tiles >= 4096) return 1;
+  // at least ~2048 waves (eight per CU), and at most 16 superblocks per wave
+  const int by_waves = ceil_div(2048, tiles), by_depth = ceil_div(KB, 2 * PF);
+  return normalize_splits(K, by_waves > by_depth ? by_waves : by_depth);
 }
 
 template <int FMT, int MT>
 static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, int splits, void* out,
                             bool direct, int out_ld, int m_store, hipStream_t st) {
+  constexpr int WAVES = 4;  // n-tiles sharing one LDS copy of the activations
   const int KB = K / 128;
   const int kbps = ceil_div(KB, splits);
-  // per 128-column block: MT*16 rows of 128 codes + 4 groups x MT*16 f64 scales; row padding
+  // per 128-column block: MT*16 rows of 128 codes + 4 groups x MT*16 f32 scales; row padding
   size_t budget = max_dynamic_lds();
   if (budget > LDS_BUDGET) budget = LDS_BUDGET;
-  int kcb_max = (int)((budget - (size_t)256 * MT) / ((size_t)2560 * MT));
+  int kcb_max = (int)((budget - (size_t)256 * MT) / ((size_t)2304 * MT));
   if (kcb_max < 1) kcb_max = 1;
   const int kcb = kbps < kcb_max ? kbps : kcb_max;
-  const size_t lds = (size_t)MT * 16 * (kcb * 128 + 16) + (size_t)kcb * 4 * MT * 16 * 8;
-  hipError_t e = allow_lds((const void*)k_gemm_q<FMT, MT>, lds);
+  const size_t lds = (size_t)MT * 16 * (kcb * 128 + 16) + (size_t)kcb * 4 * MT * 16 * 4;
+  hipError_t e = allow_lds((const void*)k_gemm_q<FMT, MT, WAVES>, lds);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)ceil_div(N / 16, 4), (unsigned)ceil_div(KB, kbps));
-  hipLaunchKernelGGL((k_gemm_q<FMT, MT>), grid, dim3(256), lds, st, (const uint8_t*)W, N, K, xq, dxT, kbps, kcb, out,
-                     direct ? 1 : 0, out_ld, m_store);
+  dim3 grid((unsigned)ceil_div(N / 16, WAVES), (unsigned)ceil_div(KB, kbps));
+  hipLaunchKernelGGL((k_gemm_q<FMT, MT, WAVES>), grid, dim3(64 * WAVES), lds, st, (const uint8_t*)W, N, K, xq, dxT,
+                     kbps, kcb, out, direct ? 1 : 0, out_ld, m_store);
   return hipGetLastError();
 }
 

@@ -2,7 +2,6 @@
 oracle and the GPU library fed the same seeded inputs, and the parity measures."""
 from __future__ import annotations
 
-import functools
 import sys
 import time
 
@@ -15,12 +14,27 @@ def say(*a):
     print("[gpu-test]", *a, file=sys.stderr, flush=True)
 
 
-@functools.lru_cache(maxsize=2)
+_GEOM = ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "n_taps", "vocab", "body_fmt", "fc_fmt",
+         "head_fmt", "weight_std", "norm_mean", "norm_std")
+
+
+def drafter_key(cfg: di.Config):
+    """Workloads that share a drafter (same weight seed and shapes) share its weights."""
+    return (cfg.weight_seed or cfg.seed,) + tuple(getattr(cfg, n) for n in _GEOM)
+
+
+_WEIGHTS: dict = {}
+
+
 def weights_for(cfg: di.Config) -> dict:
-    t = time.time()
-    w = di.make_weights(cfg)
-    say(f"weights of {cfg.key}: {time.time() - t:.1f} s")
-    return w
+    key = drafter_key(cfg)
+    if key not in _WEIGHTS:
+        if len(_WEIGHTS) >= 2:
+            _WEIGHTS.pop(next(iter(_WEIGHTS)))
+        t = time.time()
+        _WEIGHTS[key] = di.make_weights(cfg)
+        say(f"weights of {cfg.key}: {time.time() - t:.1f} s")
+    return _WEIGHTS[key]
 
 
 def logits_parity(got: np.ndarray, ref: np.ndarray):

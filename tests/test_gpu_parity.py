@@ -19,9 +19,11 @@ SHARP = TINY.replace(key="tiny_f32_sharp", norm_mean=1.0, taps_std=1.0, emb_std=
 QTINY = di.Config("q_tiny", 2, 256, 4, 2, 64, 512, 2, 1024, 8, 40, di.Q4_32, di.Q8_32, di.Q8_32, seed=2002)
 SMALL = di.CONFIGS["small_q"]
 Q8B = di.CONFIGS["qwen3_8b"]
+LONG = di.CONFIGS["qwen3_8b_long"]
+BATCH = di.CONFIGS["qwen3_8b_batch8"]
 
 
-def _pair(cfg, ctx, max_ctx, n_seqs=1, first=0):
+def _pair(cfg, ctx, max_ctx, n_seqs=1, first=0, chunk=4096):
     from block_draft_model_dflash_amd import Drafter
 
     w = weights_for(cfg)
@@ -29,12 +31,13 @@ def _pair(cfg, ctx, max_ctx, n_seqs=1, first=0):
     say(f"{cfg.key}: create on the GPU")
     gm = Drafter(cfg, w, max_ctx=max_ctx, max_seqs=n_seqs)
     for s in range(n_seqs):
-        taps = di.make_taps(cfg, s, first, ctx)
-        say(f"{cfg.key}: append {ctx} rows to sequence {s} (oracle)")
-        assert om.append(s, first, taps) == 0
-        say(f"{cfg.key}: append {ctx} rows to sequence {s} (GPU)")
-        gm.append(s, first, taps)
-    torch.cuda.synchronize()
+        for p0 in range(0, ctx, chunk):
+            n = min(chunk, ctx - p0)
+            taps = di.make_taps(cfg, s, first + p0, n)
+            say(f"{cfg.key}: append rows {p0}..{p0 + n} of sequence {s}")
+            assert om.append(s, first + p0, taps) == 0
+            gm.append(s, first + p0, taps)
+            torch.cuda.synchronize()
     return w, om, gm
 
 
@@ -127,3 +130,32 @@ def test_qwen3_8b_shaped_drafter():
     _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64)
     _kv_check(cfg, om, gm, 0, [(0, 32), (2000, 16), (4064, 32)], 2e-3)
     _blocks(cfg, om, gm, [((0,), (cfg.ctx,), i) for i in range(2)], 2e-3, 0.999)
+
+
+@pytest.mark.timeout(900)
+def test_long_context_append_then_block():
+    """The long-context workload at its full size: a 32768-row context, then per step 16 new
+    context rows appended and a block anchored after them (the step the benchmark times)."""
+    cfg = LONG
+    _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64)
+    _kv_check(cfg, om, gm, 0, [(0, 16), (20000, 16), (32752, 16)], 2e-3)
+    for step in range(2):
+        p = cfg.ctx + step * cfg.append_per_block
+        taps = di.make_taps(cfg, 0, p, cfg.append_per_block)
+        assert om.append(0, p, taps) == 0
+        gm.append(0, p, taps)
+        _kv_check(cfg, om, gm, 0, [(p, cfg.append_per_block)], 2e-3)
+        _blocks(cfg, om, gm, [((0,), (p + cfg.append_per_block,), step)], 2e-3, 0.999)
+
+
+@pytest.mark.timeout(900)
+def test_eight_sequences_batched():
+    """The batched workload at its full size: 8 sequences of 8192 context rows, one block of
+    16 rows each in one call (128 rows through every matrix)."""
+    cfg = BATCH
+    _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64, n_seqs=cfg.n_seqs)
+    _kv_check(cfg, om, gm, 7, [(0, 16), (8176, 16)], 2e-3)
+    seqs = tuple(range(cfg.n_seqs))
+    _blocks(cfg, om, gm, [(seqs, (cfg.ctx,) * cfg.n_seqs, 0)], 2e-3, 0.999)
+    # a subset of the sequences, out of order and with different anchors
+    _blocks(cfg, om, gm, [((5, 2, 7), (cfg.ctx, cfg.ctx - 100, 4000), 1)], 2e-3, 0.999)
