@@ -128,13 +128,18 @@ def main() -> int:
     app = None
     if cfg.append_per_block:
         app = torch.from_numpy(np.stack([di.make_taps(cfg, 0, cfg.ctx + i * cfg.append_per_block,
-                                                      cfg.append_per_block) for i in range(K + W)])).cuda()
+                                                      cfg.append_per_block) for i in range(max(K, W))])).cuda()
     logits = torch.empty((cfg.n_seqs, cfg.block, cfg.vocab), dtype=torch.float32, device="cuda")
+
+    # the long-context workload grows the context by append_per_block rows per step; rewind()
+    # truncates it back to the prefill, and the next step appends right after it again
+    grown = [0]
 
     def step(i):
         if app is not None:
-            p = cfg.ctx + i * cfg.append_per_block
-            gm.append(0, p, app[i])
+            p = cfg.ctx + grown[0] * cfg.append_per_block
+            gm.append(0, p, app[grown[0]])
+            grown[0] += 1
             anchors = [p + cfg.append_per_block]
         else:
             anchors = [cfg.ctx] * cfg.n_seqs
@@ -143,6 +148,8 @@ def main() -> int:
     def rewind():
         if app is not None:
             gm.truncate(0, cfg.ctx)
+            grown[0] = 0
+            assert gm.span(0) == (0, cfg.ctx)
 
     for i in range(W):
         step(i)
@@ -158,6 +165,8 @@ def main() -> int:
         step(W + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if app is not None:  # every step extended the same context
+        assert gm.span(0) == (0, cfg.ctx + K * cfg.append_per_block), gm.span(0)
     head_ms, head_n = D.dflash_read_timing(gm.ctx)
     D.dflash_time_stage(gm.ctx, -1)
     ms = (t1 - t0) * 1e3 / K

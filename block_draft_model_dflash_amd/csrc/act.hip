@@ -143,6 +143,87 @@ hipError_t launch_norm_act(const double* part, const float* x, int S, int part_m
                                      st);
 }
 
+// RMSNorm + A8_32 (or f32) of rows whose sum of squares arrives in pieces: one workgroup per
+// (256 columns, row).  The pieces are added lane-strided then across the wave, the same order on
+// every run; s = 1/sqrt(f32(sum/N) + eps) and (h*s)*w in f32.  Rows >= M are written as zeros.
+constexpr int RMS_COLS = 256;
+template <bool QUANT>
+__global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ h, const double* __restrict__ ssq,
+                                                      int nparts, const float* __restrict__ w, float eps, int M,
+                                                      int Mpad, int N, int8_t* __restrict__ xq,
+                                                      float* __restrict__ dxT, float* __restrict__ xf) {
+  __shared__ float sc_sh;
+  const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int i = blockIdx.x * RMS_COLS + tid;
+  if (m >= M) {
+    if (i < N) {
+      if (QUANT) {
+        xq[(size_t)m * N + i] = 0;
+        if ((lane & 31) == 0) dxT[(size_t)(i >> 5) * Mpad + m] = 0.f;
+      } else {
+        xf[(size_t)m * N + i] = 0.f;
+      }
+    }
+    return;
+  }
+  if (tid < 64) {
+    double t = 0.0;
+    for (int p = lane; p < nparts; p += 64) t += ssq[(size_t)m * nparts + p];
+#pragma unroll
+    for (int o = 32; o; o >>= 1) t += __shfl_xor(t, o);
+    if (lane == 0) sc_sh = 1.0f / sqrtf((float)(t / (double)N) + eps);
+  }
+  __syncthreads();
+  if (i >= N) return;  // N is a multiple of 32: whole A8 groups leave together
+  const float sc = sc_sh;
+  const float y = (h[(size_t)m * N + i] * sc) * w[i];
+  if (QUANT)
+    emit_q(y, (size_t)m * N + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
+  else
+    xf[(size_t)m * N + i] = y;
+}
+
+hipError_t launch_rms_act(const float* h, const double* ssq, int nparts, const float* w, float eps, int M, int Mpad,
+                          int N, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st) {
+  if (N % 32 || M > Mpad || nparts < 1) return hipErrorInvalidValue;
+  dim3 g((unsigned)((N + RMS_COLS - 1) / RMS_COLS), (unsigned)Mpad);
+  if (quant)
+    hipLaunchKernelGGL(k_rms_act<true>, g, dim3(RMS_COLS), 0, st, h, ssq, nparts, w, eps, M, Mpad, N, xq, dxT, xf);
+  else
+    hipLaunchKernelGGL(k_rms_act<false>, g, dim3(RMS_COLS), 0, st, h, ssq, nparts, w, eps, M, Mpad, N, xq, dxT, xf);
+  return hipGetLastError();
+}
+
+// h = x and each row's sum of squares per 256 columns (f64, in a fixed order).
+__global__ __launch_bounds__(RMS_COLS) void k_copy_ssq(const float* __restrict__ x, float* __restrict__ h, int N,
+                                                       double* __restrict__ ssq) {
+  __shared__ double red[RMS_COLS / 64];
+  const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = blockIdx.x * RMS_COLS + tid;
+  double t = 0.0;
+  if (i < N) {
+    const float v = x[(size_t)m * N + i];
+    h[(size_t)m * N + i] = v;
+    t = (double)v * (double)v;
+  }
+#pragma unroll
+  for (int o = 32; o; o >>= 1) t += __shfl_xor(t, o);
+  if (lane == 0) red[wave] = t;
+  __syncthreads();
+  if (tid == 0) {
+    double s = red[0];
+    for (int k = 1; k < RMS_COLS / 64; k++) s += red[k];
+    ssq[(size_t)m * gridDim.x + blockIdx.x] = s;
+  }
+}
+
+hipError_t launch_copy_ssq(const float* x, float* h, int M, int N, double* ssq, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  dim3 g((unsigned)((N + RMS_COLS - 1) / RMS_COLS), (unsigned)M);
+  hipLaunchKernelGGL(k_copy_ssq, g, dim3(RMS_COLS), 0, st, x, h, N, ssq);
+  return hipGetLastError();
+}
+
 // A8_32 of plain rows with scales in row order [rows][cols/32] (a unit entry point).
 hipError_t launch_quant_rows(const float* x, int rows, int cols, int8_t* q, float* d, hipStream_t st) {
   if (cols % 32) return hipErrorInvalidValue;

@@ -24,7 +24,7 @@ namespace {
 
 constexpr int APPEND_CHUNK = 128;  // context rows per append pass (8 row tiles of 16)
 constexpr int MROWS = 128;         // activation rows the workspace holds
-constexpr int MAXCH = 65;          // attention chunks per (sequence, kv head), block chunk included
+constexpr int MAXCH = 64;          // attention chunks per (sequence, kv head)
 
 thread_local std::string g_create_err;  // last error of a call without a ctx
 
@@ -41,7 +41,7 @@ struct Layout {
   std::vector<size_t> qkv, o, gu, down;
   size_t hidden_norm, norm, in_norm, post_norm, q_norm, k_norm, inv_freq;
   size_t kc, vc;
-  size_t h, xq, dxT, xf, q, kb, vb, part, apart, aml;
+  size_t h, xq, dxT, xq2, dxT2, xf, q, kb, vb, part, ssq, apart, aml;
   size_t act_begin, total;
   size_t part_floats;
 };
@@ -83,8 +83,6 @@ int check_geometry(const dflash_geometry* g, std::string* err) {
   if (H * 4 > 96 * 1024) return fail(DFLASH_ENOTSUP, "hidden too wide for one workgroup's row");
   return DFLASH_OK;
 }
-
-int splits_for(int fmt, int N, int K) { return fmt == DFLASH_F32 ? 1 : choose_splits(N, K, MROWS); }
 
 void plan(const dflash_geometry* g, Layout* L) {
   const long H = g->hidden, qd = (long)g->heads * g->head_dim, kvd = (long)g->kv_heads * g->head_dim;
@@ -131,19 +129,18 @@ void plan(const dflash_geometry* g, Layout* L) {
   L->q = take((size_t)MROWS * qd * 4);
   L->kb = take((size_t)MROWS * kvd * 4);
   L->vb = take((size_t)MROWS * kvd * 4);
-  size_t pf = 0;
-  auto need = [&](int fmt, long N, long K) {
-    const size_t f = (size_t)splits_for(fmt, (int)N, (int)K) * MROWS * N;
-    if (f > pf) pf = f;
-  };
-  need(g->fc_fmt, H, T);
-  need(g->body_fmt, NL * 2 * kvd, H);
-  need(g->body_fmt, qd + 2 * kvd, H);
-  need(g->body_fmt, H, qd);
-  need(g->body_fmt, 2 * I, H);
-  need(g->body_fmt, H, I);
-  L->part_floats = pf;
-  L->part = take(pf * 8);  // f64 partial sums
+  // the second activation buffer: SwiGLU's output, read by down while gate|up's input stays put
+  L->xq2 = take((size_t)MROWS * I);
+  L->dxT2 = take((size_t)(I / 32) * MROWS * 4);
+  // f64 products of the projections that leave the GEMM unreduced (q|k|v, fc, the append's K|V)
+  long pn = H;
+  if (qd + 2 * kvd > pn) pn = qd + 2 * kvd;
+  if (NL * 2 * kvd > pn) pn = NL * 2 * kvd;
+  if (2 * I > pn) pn = 2 * I;  // the f32 drafter's gate|up
+  if (qd > pn) pn = qd;
+  L->part_floats = (size_t)MROWS * pn;
+  L->part = take(L->part_floats * 8);
+  L->ssq = take((size_t)MROWS * (H / 16 + 1) * 8);  // per-row sums of squares in pieces
   const size_t arows = (size_t)g->max_seqs * kvh * MAXCH * rep * 16;
   L->apart = take(arows * hd * 8);
   L->aml = take(arows * 2 * 8);
@@ -218,22 +215,27 @@ namespace {
 
 bool bodyq(const dflash_ctx* c) { return c->g.body_fmt != DFLASH_F32; }
 
-// One matrix product over the activations prepared by the previous producer.  Returns the
-// number of K slices written to the partial buffer (1 when direct).
-int run_gemm(dflash_ctx* c, int fmt, size_t woff, int N, int K, int Mpad, int M, void* out, bool direct, int out_ld,
-             int m_store, int* slices) {
-  const void* W = c->ws + woff;
-  if (fmt == DFLASH_F32) {
-    *slices = 1;
-    return c->hip(launch_gemm_f32((const float*)W, N, K, c->at<float>(c->lay.xf), Mpad, M, out, direct, out_ld,
-                                  m_store, c->st),
-                  "f32 gemm");
-  }
-  const int s = direct ? 1 : choose_splits(N, K, Mpad);
-  *slices = s;
-  return c->hip(launch_gemm_q(fmt, W, N, K, c->at<int8_t>(c->lay.xq), c->at<float>(c->lay.dxT), Mpad, s, out, direct,
-                              out_ld, m_store, c->st),
-                "quantized gemm");
+GemmOut gemm_out(int epi, int M, int Mpad) {
+  GemmOut o;
+  memset(&o, 0, sizeof o);
+  o.epi = epi;
+  o.M = M;
+  o.Mpad = Mpad;
+  return o;
+}
+
+// One quantized matrix product over activations (ax, ad) with the given epilogue.
+int run_gemm_q(dflash_ctx* c, int fmt, size_t woff, int N, int K, const int8_t* ax, const float* ad, const GemmOut& o,
+               const char* what) {
+  return c->hip(launch_gemm_q(fmt, c->ws + woff, N, K, ax, ad, -1, o, c->st), what);
+}
+
+// One f32 matrix product over the f32 activations xf: f64 products [Mpad][N] or f32 out.
+int run_gemm_f32(dflash_ctx* c, size_t woff, int N, int K, int Mpad, int M, void* out, bool direct, int out_ld,
+                 int m_store) {
+  return c->hip(launch_gemm_f32((const float*)(c->ws + woff), N, K, c->at<float>(c->lay.xf), Mpad, M, out, direct,
+                                out_ld, m_store, c->st),
+                "f32 gemm");
 }
 
 int check_weights(const dflash_geometry* g, const dflash_weights* w, std::string* err) {
@@ -298,68 +300,117 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   int nmax = 0;
   for (int i = 0; i < n_seqs; i++)
     if (si.nctx[i] > nmax) nmax = si.nctx[i];
-  int nch_target = 512 / (n_seqs * kvh);
-  if (nch_target < 1) nch_target = 1;
-  if (nch_target > MAXCH - 1) nch_target = MAXCH - 1;
-  int ck = round16((nmax + nch_target - 1) / nch_target);
-  if (ck < 16) ck = 16;
+  // about one workgroup per CU: n_seqs * kv heads * chunks ~ 256, chunks a multiple of 32 keys
+  // (the two key halves of a workgroup take alternate 16-key tiles)
+  int nch_target = (256 + n_seqs * kvh - 1) / (n_seqs * kvh);
+  if (nch_target > MAXCH) nch_target = MAXCH;
+  int ck = ((nmax + nch_target - 1) / nch_target + 31) / 32 * 32;
+  if (ck < 32) ck = 32;
   as.ck = ck;
 
-  TRY_HIP(c, hipMemcpyAsync(hbuf, h, (size_t)M * H * 4, hipMemcpyDeviceToDevice, c->st), "copy block rows");
+  double* ssq = c->at<double>(L.ssq);
+  int8_t* xq2 = c->at<int8_t>(L.xq2);
+  float* dxT2 = c->at<float>(L.dxT2);
+  const int fmt = g.body_fmt;
+  const int copy_parts = (H + 255) / 256, tile_parts = H / 16;
+
+  // h = the block rows; x = A8(RMSNorm(h, in_norm_0))
+  TRY_HIP(c, launch_copy_ssq(h, hbuf, M, H, ssq, c->st), "copy block rows");
   TRY_HIP(c,
-          launch_norm_act(nullptr, hbuf, 1, Mpad, nullptr, nullptr, c->at<float>(L.in_norm), eps, M, Mpad, H, bq, xq,
-                          dxT, xf, c->st),
+          launch_rms_act(hbuf, ssq, copy_parts, c->at<float>(L.in_norm), eps, M, Mpad, H, bq, xq, dxT, xf, c->st),
           "in-norm");
   const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd;
   for (int l = 0; l < NL; l++) {
-    int S = 1, rc;
+    int rc;
     {
       StageTimer t(c, DFLASH_STAGE_QKV);
-      if ((rc = run_gemm(c, g.body_fmt, L.qkv[l], qd + 2 * kvd, H, Mpad, M, part, false, 0, 0, &S))) return rc;
+      if (bq) {
+        GemmOut o = gemm_out(EPI_F64, M, Mpad);
+        o.y = part;
+        rc = run_gemm_q(c, fmt, L.qkv[l], qd + 2 * kvd, H, xq, dxT, o, "q|k|v");
+      } else {
+        rc = run_gemm_f32(c, L.qkv[l], qd + 2 * kvd, H, Mpad, M, part, false, 0, 0);
+      }
+      if (rc) return rc;
     }
     TRY_HIP(c,
-            launch_qkv_epilogue(part, S, Mpad, M, B, si, nh, kvh, hd, c->at<float>(L.q_norm) + (size_t)l * hd,
+            launch_qkv_epilogue(part, 1, Mpad, M, B, si, nh, kvh, hd, c->at<float>(L.q_norm) + (size_t)l * hd,
                                 c->at<float>(L.k_norm) + (size_t)l * hd, c->at<float>(L.inv_freq), eps,
                                 c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb), c->st),
             "q/k norm + rope");
     {
       StageTimer t(c, DFLASH_STAGE_ATTENTION);
       TRY_HIP(c,
-            launch_attention(as, si, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
-                             c->at<float>(L.kc) + (size_t)l * layer_cache, c->at<float>(L.vc) + (size_t)l * layer_cache,
-                             c->at<double>(L.apart), c->at<double>(L.aml), Mpad, bq, xq, dxT, xf, c->st),
+              launch_attention(as, si, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
+                               c->at<float>(L.kc) + (size_t)l * layer_cache,
+                               c->at<float>(L.vc) + (size_t)l * layer_cache, c->at<double>(L.apart),
+                               c->at<double>(L.aml), Mpad, bq, xq, dxT, xf, c->st),
               "attention");
-    }
-    {
-      StageTimer t(c, DFLASH_STAGE_O);
-      if ((rc = run_gemm(c, g.body_fmt, L.o[l], H, qd, Mpad, M, part, false, 0, 0, &S))) return rc;
-    }
-    TRY_HIP(c,
-            launch_norm_act(part, nullptr, S, Mpad, hbuf, hbuf, c->at<float>(L.post_norm) + (size_t)l * H, eps, M,
-                            Mpad, H, bq, xq, dxT, xf, c->st),
-            "o residual + post-norm");
-    {
-      StageTimer t(c, DFLASH_STAGE_GATE_UP);
-      if ((rc = run_gemm(c, g.body_fmt, L.gu[l], 2 * I, H, Mpad, M, part, false, 0, 0, &S))) return rc;
-    }
-    TRY_HIP(c, launch_swiglu_act(part, S, M, Mpad, I, bq, xq, dxT, xf, c->st), "swiglu");
-    {
-      StageTimer t(c, DFLASH_STAGE_DOWN);
-      if ((rc = run_gemm(c, g.body_fmt, L.down[l], H, I, Mpad, M, part, false, 0, 0, &S))) return rc;
     }
     const bool last = l + 1 == NL;
     const float* nw = last ? c->at<float>(L.norm) : c->at<float>(L.in_norm) + (size_t)(l + 1) * H;
     const bool nq = last ? (!hidden_only && g.head_fmt != DFLASH_F32) : bq;
-    TRY_HIP(c, launch_norm_act(part, nullptr, S, Mpad, hbuf, hbuf, nw, eps, M, Mpad, H, nq, xq, dxT, xf, c->st),
-            "down residual + next norm");
+    if (bq) {
+      // h += Wo y; x = A8(RMSNorm(h, post_norm)); a = A8(silu(gate x) * up x); h += down a
+      {
+        StageTimer t(c, DFLASH_STAGE_O);
+        GemmOut o = gemm_out(EPI_RESID, M, Mpad);
+        o.h = hbuf;
+        o.ssq = ssq;
+        if ((rc = run_gemm_q(c, fmt, L.o[l], H, qd, xq, dxT, o, "o + residual"))) return rc;
+      }
+      TRY_HIP(c,
+              launch_rms_act(hbuf, ssq, tile_parts, c->at<float>(L.post_norm) + (size_t)l * H, eps, M, Mpad, H, true,
+                             xq, dxT, xf, c->st),
+              "post-norm");
+      {
+        StageTimer t(c, DFLASH_STAGE_GATE_UP);
+        GemmOut o = gemm_out(EPI_SWIGLU, M, Mpad);
+        o.xq = xq2;
+        o.dxT = dxT2;
+        if ((rc = run_gemm_q(c, fmt, L.gu[l], 2 * I, H, xq, dxT, o, "gate|up + swiglu"))) return rc;
+      }
+      {
+        StageTimer t(c, DFLASH_STAGE_DOWN);
+        GemmOut o = gemm_out(EPI_RESID, M, Mpad);
+        o.h = hbuf;
+        o.ssq = ssq;
+        if ((rc = run_gemm_q(c, fmt, L.down[l], H, I, xq2, dxT2, o, "down + residual"))) return rc;
+      }
+      TRY_HIP(c, launch_rms_act(hbuf, ssq, tile_parts, nw, eps, M, Mpad, H, nq, xq, dxT, xf, c->st), "next norm");
+    } else {
+      {
+        StageTimer t(c, DFLASH_STAGE_O);
+        if ((rc = run_gemm_f32(c, L.o[l], H, qd, Mpad, M, part, false, 0, 0))) return rc;
+      }
+      TRY_HIP(c,
+              launch_norm_act(part, nullptr, 1, Mpad, hbuf, hbuf, c->at<float>(L.post_norm) + (size_t)l * H, eps, M,
+                              Mpad, H, false, xq, dxT, xf, c->st),
+              "o residual + post-norm");
+      {
+        StageTimer t(c, DFLASH_STAGE_GATE_UP);
+        if ((rc = run_gemm_f32(c, L.gu[l], 2 * I, H, Mpad, M, part, false, 0, 0))) return rc;
+      }
+      TRY_HIP(c, launch_swiglu_act(part, 1, M, Mpad, I, false, xq, dxT, xf, c->st), "swiglu");
+      {
+        StageTimer t(c, DFLASH_STAGE_DOWN);
+        if ((rc = run_gemm_f32(c, L.down[l], H, I, Mpad, M, part, false, 0, 0))) return rc;
+      }
+      TRY_HIP(c, launch_norm_act(part, nullptr, 1, Mpad, hbuf, hbuf, nw, eps, M, Mpad, H, nq, xq, dxT, xf, c->st),
+              "down residual + next norm");
+    }
   }
   if (hidden_only) {
     TRY_HIP(c, hipMemcpyAsync(out, xf, (size_t)M * H * 4, hipMemcpyDeviceToDevice, c->st), "copy hidden");
     return DFLASH_OK;
   }
-  int S = 1;
   StageTimer t(c, DFLASH_STAGE_HEAD);
-  return run_gemm(c, g.head_fmt, L.head, V, H, Mpad, M, out, true, V, M, &S);
+  if (g.head_fmt == DFLASH_F32) return run_gemm_f32(c, L.head, V, H, Mpad, M, out, true, V, M);
+  GemmOut o = gemm_out(EPI_F32, M, Mpad);
+  o.y = out;
+  o.ld = V;
+  o.m_store = M;
+  return run_gemm_q(c, g.head_fmt, L.head, V, H, xq, dxT, o, "head");
 }
 
 }  // namespace
@@ -499,26 +550,34 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
     const int nn = n - c0 < APPEND_CHUNK ? n - c0 : APPEND_CHUNK;
     const int Mpad = round16(nn);
     const float* rows = taps + (size_t)c0 * T;
-    int S = 1, rc;
+    int rc;
     if (g.fc_fmt != DFLASH_F32) {
       TRY_HIP(c,
               launch_norm_act(nullptr, rows, 1, Mpad, nullptr, nullptr, nullptr, eps, nn, Mpad, T, true, xq, dxT, xf,
                               c->st),
               "taps quant");
-      rc = run_gemm(c, g.fc_fmt, L.fc, H, T, Mpad, nn, part, false, 0, 0, &S);
+      GemmOut o = gemm_out(EPI_F64, nn, Mpad);
+      o.y = part;
+      rc = run_gemm_q(c, g.fc_fmt, L.fc, H, T, xq, dxT, o, "fc");
     } else {
-      S = 1;
       rc = c->hip(launch_gemm_f32((const float*)(c->ws + L.fc), H, T, rows, Mpad, nn, part, false, 0, 0, c->st),
                   "f32 gemm");
     }
     if (rc) return rc;
     TRY_HIP(c,
-            launch_norm_act(part, nullptr, S, Mpad, nullptr, nullptr, c->at<float>(L.hidden_norm), eps, nn, Mpad, H,
+            launch_norm_act(part, nullptr, 1, Mpad, nullptr, nullptr, c->at<float>(L.hidden_norm), eps, nn, Mpad, H,
                             bodyq(c), xq, dxT, xf, c->st),
             "hidden norm");
-    if ((rc = run_gemm(c, g.body_fmt, L.kvall, NL * 2 * kvd, H, Mpad, nn, part, false, 0, 0, &S))) return rc;
+    if (bodyq(c)) {
+      GemmOut o = gemm_out(EPI_F64, nn, Mpad);
+      o.y = part;
+      rc = run_gemm_q(c, g.body_fmt, L.kvall, NL * 2 * kvd, H, xq, dxT, o, "k|v of every layer");
+    } else {
+      rc = run_gemm_f32(c, L.kvall, NL * 2 * kvd, H, Mpad, nn, part, false, 0, 0);
+    }
+    if (rc) return rc;
     TRY_HIP(c,
-            launch_kv_append(part, S, Mpad, nn, NL, g.kv_heads, g.head_dim, c->at<float>(L.k_norm),
+            launch_kv_append(part, 1, Mpad, nn, NL, g.kv_heads, g.head_dim, c->at<float>(L.k_norm),
                              c->at<float>(L.inv_freq), eps, pos + c0, (int)(pos - first) + c0, seq, g.max_seqs,
                              g.max_ctx, c->at<float>(L.kc), c->at<float>(L.vc), c->st),
             "k/v into the cache");
@@ -633,12 +692,11 @@ int dflash_pack(int32_t fmt, int32_t rows, int32_t cols, dflash_matrix w, void* 
   return e == hipSuccess ? DFLASH_OK : unit_fail(DFLASH_EHIP, "pack", e);
 }
 
-// scratch: padded activations [Mpad][cols] int8, their scales [cols/32][Mpad] f32, partials.
+// scratch: padded activations [Mpad][cols] int8 and their scales [cols/32][Mpad] f32.
 int dflash_gemm_scratch_bytes(int32_t rows, int32_t cols, int32_t m, int32_t splits, size_t* bytes) {
-  if (!bytes || rows <= 0 || cols <= 0 || cols % 128 || rows % 16 || m < 1 || m > MROWS) return DFLASH_EINVAL;
+  if (!bytes || rows <= 0 || cols <= 0 || cols % 128 || rows % 16 || m < 1 || m > MROWS || splits < 0) return DFLASH_EINVAL;
   const int Mpad = round16(m);
-  const int s = splits > 0 ? normalize_splits(cols, splits) : choose_splits(rows, cols, Mpad);
-  *bytes = align256((size_t)Mpad * cols) + align256((size_t)(cols / 32) * Mpad * 4) + (size_t)s * Mpad * rows * 8;
+  *bytes = align256((size_t)Mpad * cols) + align256((size_t)(cols / 32) * Mpad * 4);
   return DFLASH_OK;
 }
 
@@ -650,21 +708,23 @@ int dflash_gemm(int32_t fmt, const void* packed, int32_t rows, int32_t cols, con
     return unit_fail(DFLASH_EINVAL, "gemm: arguments");
   hipStream_t st = (hipStream_t)stream;
   const int Mpad = round16(m);
-  const int s = splits > 0 ? normalize_splits(cols, splits) : choose_splits(rows, cols, Mpad);
+  // splits: 0 lets the library choose; 1 four n-tiles, one wave each; 2..7 four n-tiles x two
+  // k-waves per workgroup; 8 and more K split over the waves of one n-tile
+  const int layout = splits == 0 ? -1 : splits == 1 ? 2 : splits < 8 ? 0 : 1;
   int8_t* xp = (int8_t*)scratch;
   float* dT = (float*)((uint8_t*)scratch + align256((size_t)Mpad * cols));
-  double* part = (double*)((uint8_t*)dT + align256((size_t)(cols / 32) * Mpad * 4));
   hipError_t e;
   if ((e = hipMemsetAsync(xp, 0, (size_t)Mpad * cols, st)) != hipSuccess) return unit_fail(DFLASH_EHIP, "gemm: clear", e);
   if ((e = hipMemcpyAsync(xp, xq, (size_t)m * cols, hipMemcpyDeviceToDevice, st)) != hipSuccess)
     return unit_fail(DFLASH_EHIP, "gemm: copy", e);
   if ((e = launch_transpose_scales(dx, m, cols / 32, Mpad, dT, st)) != hipSuccess)
     return unit_fail(DFLASH_EHIP, "gemm: scales", e);
-  if ((e = launch_gemm_q(fmt, packed, rows, cols, xp, dT, Mpad, s, part, false, 0, 0, st)) != hipSuccess)
+  GemmOut o = gemm_out(EPI_F32, m, Mpad);
+  o.y = y;
+  o.ld = rows;
+  o.m_store = m;
+  if ((e = launch_gemm_q(fmt, packed, rows, cols, xp, dT, layout, o, st)) != hipSuccess)
     return unit_fail(DFLASH_EHIP, "gemm: kernel", e);
-  if ((e = launch_norm_act(part, nullptr, s, Mpad, nullptr, nullptr, nullptr, 0.f, m, m, rows, false, nullptr, nullptr,
-                           y, st)) != hipSuccess)
-    return unit_fail(DFLASH_EHIP, "gemm: reduce", e);
   return DFLASH_OK;
 }
 

@@ -3,10 +3,13 @@
 // block's own rows, with no causal mask; s = (q . k) * hd^-0.5, softmax, y = sum p v).
 //
 // The pages' device kernel (gpu_wgpu/dflash_dev.rs, dflash_attn) writes every score to a global
-// scratch and re-reads it; here the context is split into chunks, each workgroup keeps a
-// running (max, sum, acc) per query in registers (online softmax), and a merge combines the
-// chunks.  A workgroup serves one (sequence, kv head, chunk) with one wave per q head of the
-// group; the 16 block rows of a head are the 16 columns of v_mfma_f64_16x16x4f64 tiles:
+// scratch and re-reads it; here the context is split into chunks, each wave keeps a running
+// (max, sum, acc) per query in registers (online softmax), and a merge combines the chunks.
+// A workgroup serves one (sequence, kv head, chunk) with eight waves: wave w takes q head w % 4
+// of the group and the chunk's even (w < 4) or odd (w >= 4) 16-key tiles; the two halves of a
+// head are combined in LDS before the chunk's result is written.  The block's own rows form one
+// more tile at the end of the sequence's last chunk.  The 16 block rows of a head are the 16
+// columns of v_mfma_f64_16x16x4f64 tiles:
 //   S^T[key][q] = K . Q^T   (A = 16 keys staged in LDS, B = the wave's queries in registers)
 //   Y^T[d][q]  += V^T . P^T (A = 16-dim slices of V from LDS, B = the wave's probabilities,
 //                            already in the accumulator layout of S^T)
@@ -25,43 +28,52 @@ namespace dfl {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 
-constexpr int ATTN_THREADS = 256;  // four waves: one q head each per round
+constexpr int ATTN_HEADS = 4;                   // q heads served at once (one wave each per half)
+constexpr int ATTN_THREADS = 64 * 2 * ATTN_HEADS;  // two key halves
+
+// Chunks a sequence with n context rows takes: ceil(n / ck), and at least one for the block rows.
+__device__ __forceinline__ int attn_chunks(int nctx, int ck) { return nctx > 0 ? (nctx + ck - 1) / ck : 1; }
 
 template <int HD>
 __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqInfo si, const float* __restrict__ q,
-                                                     const float* __restrict__ kb, const float* __restrict__ vb,
-                                                     const float* __restrict__ kc, const float* __restrict__ vc,
-                                                     double* __restrict__ part, double* __restrict__ ml) {
-  constexpr int KS = HD + 4;  // padded LDS key row (floats)
-  __shared__ __attribute__((aligned(16))) float Ks[16 * KS];
-  __shared__ __attribute__((aligned(16))) float Vs[16 * KS];
+                                                               const float* __restrict__ kb,
+                                                               const float* __restrict__ vb,
+                                                               const float* __restrict__ kc,
+                                                               const float* __restrict__ vc,
+                                                               double* __restrict__ part, double* __restrict__ ml) {
+  constexpr int KS = HD + 4;           // padded LDS key row (floats)
+  constexpr int TILE = 16 * KS;        // one 16-key tile of K (or V)
+  constexpr int HALF = ATTN_THREADS / 2;
+  constexpr int NL = 16 * (HD / 4) / HALF;  // float4 of K (and of V) each thread stages per tile
+  constexpr int CD = 64;                    // dims combined per LDS round
+  constexpr int COMB = ATTN_HEADS * (16 * CD + 32);  // doubles: acc slice + (m, l) per row
+  constexpr int KV_BYTES = 2 * 2 * TILE * 4;
+  constexpr int LDS_BYTES = KV_BYTES > COMB * 8 ? KV_BYTES : COMB * 8;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int nctx = si.nctx[s];
-  const int nch = (nctx + a.ck - 1) / a.ck;
-  if (c > nch) return;  // the whole workgroup: this sequence has fewer chunks
+  const int nch = attn_chunks(nctx, a.ck);
+  if (c >= nch) return;  // the whole workgroup: this sequence has fewer chunks
   const int rep = a.nh / a.kvh;
-  constexpr int waves = ATTN_THREADS / 64;
-  constexpr int NL = 16 * (HD / 4) / ATTN_THREADS;  // float4 of K (and of V) each thread stages per tile
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int half = w / ATTN_HEADS, hw0 = w % ATTN_HEADS, htid = tid % HALF;
   const int quarter = lane >> 4, col = lane & 15;
-  const bool blockchunk = c == nch;
-  const int k0 = blockchunk ? 0 : c * a.ck;
-  const int kend = blockchunk ? a.B : min(nctx, (c + 1) * a.ck);
-  const float *Kbase, *Vbase;
-  size_t kstride;
-  if (blockchunk) {
-    Kbase = kb + ((size_t)s * a.B * a.kvh + g) * HD;
-    Vbase = vb + ((size_t)s * a.B * a.kvh + g) * HD;
-    kstride = (size_t)a.kvh * HD;
-  } else {
-    Kbase = kc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
-    Vbase = vc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
-    kstride = HD;
-  }
-  // the group's q heads, `waves` at a time (one per wave); the chunk's keys are re-staged per
-  // round when a group has more heads than the workgroup has waves
-  for (int h0 = 0; h0 < rep; h0 += waves) {
-    const int hw = h0 + w;  // this wave's head within the group
+  float* Ks = (float*)lds + half * 2 * TILE;
+  float* Vs = Ks + TILE;
+  const int k0 = c * a.ck, kend = min(nctx, k0 + a.ck);
+  const int nt_ctx = kend > k0 ? (kend - k0 + 15) / 16 : 0;
+  const int nt = nt_ctx + (c == nch - 1 ? 1 : 0);  // the last chunk also takes the block's rows
+  const int rounds = (nt + 1) / 2;
+  const float* Kctx = kc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
+  const float* Vctx = vc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
+  const float* Kblk = kb + ((size_t)s * a.B * a.kvh + g) * HD;
+  const float* Vblk = vb + ((size_t)s * a.B * a.kvh + g) * HD;
+  const size_t bstride = (size_t)a.kvh * HD;
+
+  // the group's q heads, ATTN_HEADS at a time; the chunk's keys are re-staged per round when a
+  // group has more heads than that
+  for (int h0 = 0; h0 < rep; h0 += ATTN_HEADS) {
+    const int hw = h0 + hw0;  // this wave's head within the group
     const bool live = hw < rep;
     const int j = g * rep + (live ? hw : 0);
     v4f qr[HD / 16];
@@ -74,34 +86,42 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
 #pragma unroll
     for (int dt = 0; dt < HD / 16; dt++) acc[dt] = (v4d){0.0, 0.0, 0.0, 0.0};
 
-    // the next tile's keys and values travel to registers while the current one is computed
+    // tile i of the chunk: context keys k0 + 16i.. while i < nt_ctx, else the block's rows; the
+    // next tile of this half travels to registers while the current one is computed
     v4f pk[NL], pv[NL];
-    auto fetch = [&](int t) {
+    auto fetch = [&](int i) {
 #pragma unroll
       for (int u = 0; u < NL; u++) {
-        const int i = tid + u * ATTN_THREADS;
-        const int r = i / (HD / 4), c4 = i % (HD / 4);
-        const int key = t + r;
+        const int e = htid + u * HALF;
+        const int r = e / (HD / 4), c4 = e % (HD / 4);
         pk[u] = pv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-        if (key < kend) {
-          pk[u] = *(const v4f*)(Kbase + (size_t)key * kstride + 4 * c4);
-          pv[u] = *(const v4f*)(Vbase + (size_t)key * kstride + 4 * c4);
+        if (i < nt_ctx) {
+          const int key = k0 + 16 * i + r;
+          if (key < kend) {
+            pk[u] = *(const v4f*)(Kctx + (size_t)key * HD + 4 * c4);
+            pv[u] = *(const v4f*)(Vctx + (size_t)key * HD + 4 * c4);
+          }
+        } else if (i < nt && r < a.B) {
+          pk[u] = *(const v4f*)(Kblk + (size_t)r * bstride + 4 * c4);
+          pv[u] = *(const v4f*)(Vblk + (size_t)r * bstride + 4 * c4);
         }
       }
     };
-    fetch(k0);
-    for (int t0 = k0; t0 < kend; t0 += 16) {
+    fetch(half);
+    for (int rd = 0; rd < rounds; rd++) {
+      const int i = 2 * rd + half;  // this half's tile in this round
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < NL; u++) {
-        const int i = tid + u * ATTN_THREADS;
-        const int r = i / (HD / 4), c4 = i % (HD / 4);
+        const int e = htid + u * HALF;
+        const int r = e / (HD / 4), c4 = e % (HD / 4);
         *(v4f*)(Ks + r * KS + 4 * c4) = pk[u];
         *(v4f*)(Vs + r * KS + 4 * c4) = pv[u];
       }
       __syncthreads();
-      if (t0 + 16 < kend) fetch(t0 + 16);
-      if (!live) continue;
+      if (i + 2 < nt) fetch(i + 2);
+      if (!live || i >= nt) continue;
+      const int nvalid = i < nt_ctx ? min(16, kend - (k0 + 16 * i)) : a.B;  // keys of this tile
       v4d st0 = (v4d){0.0, 0.0, 0.0, 0.0}, st1 = st0;
 #pragma unroll
       for (int i4 = 0; i4 < HD / 16; i4++) {
@@ -114,8 +134,8 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
       double p[4], mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int key = t0 + quarter + 4 * r;  // accumulator slot r holds key row quarter + 4r
-        p[r] = key < kend ? (st0[r] + st1[r]) * (double)a.scale : -INFINITY;
+        const int key = quarter + 4 * r;  // accumulator slot r holds key row quarter + 4r
+        p[r] = key < nvalid ? (st0[r] + st1[r]) * (double)a.scale : -INFINITY;
         mx = fmax(mx, p[r]);
       }
       mx = fmax(mx, __shfl_xor(mx, 16));
@@ -136,26 +156,58 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
       for (int dt = 0; dt < HD / 16; dt++) {
         acc[dt] *= corr;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          // step i pairs the probabilities of slot i (keys quarter + 4i) with those keys' values
-          const float va = Vs[(4 * i + quarter) * KS + 64 * (dt >> 2) + 4 * col + (dt & 3)];
-          acc[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va, p[i], acc[dt], 0, 0, 0);
+        for (int k = 0; k < 4; k++) {
+          // step k pairs the probabilities of slot k (keys quarter + 4k) with those keys' values
+          const float va = Vs[(4 * k + quarter) * KS + 64 * (dt >> 2) + 4 * col + (dt & 3)];
+          acc[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va, p[k], acc[dt], 0, 0, 0);
         }
       }
     }
-    if (!live || col >= a.B) continue;
+
+    // combine the halves: (m, l, acc) of the odd tiles join those of the even tiles through LDS,
+    // CD dims per round.  Half 0 always has tile 0, so its maximum is finite.
+    double* cb = (double*)lds + hw0 * (16 * CD + 32);
     const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + hw) * 16 + col;
-    double* dst = part + prow * HD;
+    double e0 = 1.0, e1 = 0.0;
+    for (int d0 = 0; d0 < HD; d0 += CD) {
+      __syncthreads();
+      if (half == 1 && live) {
 #pragma unroll
-    for (int d4 = 0; d4 < HD / 64; d4++)
+        for (int d4 = 0; d4 < CD / 64; d4++)
 #pragma unroll
-      for (int r = 0; r < 4; r++) {
-        // accumulator (dt = 4*d4 + e, slot r) is row quarter + 4r of tile dt: dim 64*d4 + 16*r + 4*quarter + e
-        double* o = dst + 64 * d4 + 16 * r + 4 * quarter;
+          for (int r = 0; r < 4; r++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = acc[4 * d4 + e][r];
+            for (int e = 0; e < 4; e++)
+              cb[col * CD + 64 * d4 + 16 * r + 4 * quarter + e] = acc[4 * ((d0 >> 6) + d4) + e][r];
+        if (d0 == 0 && quarter == 0) {
+          cb[16 * CD + 2 * col] = m_run;
+          cb[16 * CD + 2 * col + 1] = l_run;
+        }
       }
-    if (quarter == 0) {
+      __syncthreads();
+      if (half == 1 || !live) continue;
+      if (d0 == 0) {
+        const double m1 = cb[16 * CD + 2 * col], l1 = cb[16 * CD + 2 * col + 1];
+        const double m = fmax(m_run, m1);
+        e0 = exp(m_run - m);
+        e1 = m1 == -INFINITY ? 0.0 : exp(m1 - m);
+        l_run = l_run * e0 + l1 * e1;
+        m_run = m;
+      }
+      if (col >= a.B) continue;
+      double* dst = part + prow * HD + d0;
+#pragma unroll
+      for (int d4 = 0; d4 < CD / 64; d4++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          // accumulator (dt = 4*d4 + e, slot r) is row quarter + 4r of tile dt: dim 64*d4 + 16*r + 4*quarter + e
+          const int o = 64 * d4 + 16 * r + 4 * quarter;
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            dst[o + e] = acc[4 * ((d0 >> 6) + d4) + e][r] * e0 + cb[col * CD + o + e] * e1;
+        }
+    }
+    if (half == 0 && live && col < a.B && quarter == 0) {
       ml[prow * 2] = m_run;
       ml[prow * 2 + 1] = l_run;
     }
@@ -194,18 +246,18 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void k_attn_merge(AttnShape a, Se
   __shared__ double ls[MERGE_WAVES];
   const int j = blockIdx.x, r = blockIdx.y, s = blockIdx.z, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int rep = a.nh / a.kvh, g = j / rep, hw = j % rep;
-  const int nch = (si.nctx[s] + a.ck - 1) / a.ck;  // context chunks; chunk nch is the block's own rows
+  const int nch = attn_chunks(si.nctx[s], a.ck);
   const size_t base = (((size_t)s * a.kvh + g) * a.maxch) * rep;
   auto row_of = [&](int c) { return (base + (size_t)c * rep + hw) * 16 + r; };
   double mx = -INFINITY;
-  for (int c = lane; c <= nch; c += 64) mx = fmax(mx, ml[row_of(c) * 2]);
+  for (int c = lane; c < nch; c += 64) mx = fmax(mx, ml[row_of(c) * 2]);
 #pragma unroll
   for (int o = 32; o; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
   double L = 0.0, y[HD / 64];
 #pragma unroll
   for (int t = 0; t < HD / 64; t++) y[t] = 0.0;
 #pragma unroll 4
-  for (int c = w; c <= nch; c += MERGE_WAVES) {
+  for (int c = w; c < nch; c += MERGE_WAVES) {
     const size_t row = row_of(c);
     const double e = exp(ml[row * 2] - mx);
     L += ml[row * 2 + 1] * e;
@@ -240,11 +292,11 @@ static hipError_t attn_hd(const AttnShape& a, const SeqInfo& si, const float* q,
                           float* dxT, float* xf, hipStream_t st) {
   int maxn = 0;
   for (int i = 0; i < si.n; i++) {
-    const int nch = (si.nctx[i] + a.ck - 1) / a.ck;
+    const int nch = si.nctx[i] > 0 ? (si.nctx[i] + a.ck - 1) / a.ck : 1;
     if (nch > maxn) maxn = nch;
   }
-  if (maxn + 1 > a.maxch) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn + 1, a.kvh, si.n), dim3(ATTN_THREADS), 0, st, a, si, q, kb, vb,
+  if (maxn > a.maxch) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn, a.kvh, si.n), dim3(ATTN_THREADS), 0, st, a, si, q, kb, vb,
                      kc, vc, part, ml);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -48,19 +48,38 @@ struct SeqInfo {
 hipError_t launch_pack(int fmt, const void* codes, const void* scales, int rows, int cols, void* out, long tile_off,
                        long tile_stride, hipStream_t st);
 
-// Quantized weight-streaming GEMM.  xq [Mpad][K] int8 (rows >= M zero or ignored), dxT
-// [K/32][Mpad] f32.  direct: out is f32, out[m*out_ld + n] for m < m_store; else out is the
-// f64 partial sums [S][Mpad][N] of the S K-slices (consumers add them in slice order and
-// round once to f32).
-hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int Mpad,
-                         int splits, void* out, bool direct, int out_ld, int m_store, hipStream_t st);
-// Number of K slices the GEMM uses for a shape when the caller does not fix it, and the
-// number it really uses for a requested count (slices of whole 128-column blocks).
-int choose_splits(int N, int K, int Mpad);
-int normalize_splits(int K, int s);
+// Quantized weight-streaming GEMM: xq [Mpad][K] int8 (rows >= M zero), dxT [K/32][Mpad] f32
+// activation scales, y = W . x for the Mpad rows, then one epilogue:
+enum GemmEpi {
+  EPI_F64 = 0,    // double y[m*N + n] for m < Mpad
+  EPI_F32 = 1,    // float y[m*ld + n] for m < m_store
+  EPI_RESID = 2,  // h[m*N + n] += f32(y) for m < M; ssq[m*(N/16) + n/16] = sum of h^2 over the
+                  // 16 columns of n's tile (f64; 0 for rows >= M), m < Mpad
+  EPI_SWIGLU = 3  // N = 2I with gate|up interleaved by 16-column tiles: a = silu(gate) * up
+                  // (f64 from the f32 products, one rounding) -> A8_32 into xq [Mpad][I] and
+                  // dxT [I/32][Mpad], or f32 into xf [Mpad][I] when xq is null
+};
+struct GemmOut {
+  int epi;
+  int M, Mpad;
+  void* y;
+  int ld, m_store;
+  float* h;
+  double* ssq;
+  int8_t* xq;
+  float* dxT;
+  float* xf;
+};
+// layout < 0: chosen from the shape (0: four n-tiles x two k-waves per workgroup; 1: K split
+// over the waves of one (two) n-tile(s); 2: four n-tiles, one wave each); SwiGLU always uses
+// layout 0.
+hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int layout,
+                         const GemmOut& o, hipStream_t st);
+int gemm_layout(int N, int Mpad, int epi);
 hipError_t launch_group_sums(int fmt, const void* W, int N, int K, const int8_t* xq, int Mpad, int M,
                              int32_t* sums, hipStream_t st);
-// f32 GEMM: x [Mpad][K] f32; same output conventions (S = 1).
+// f32 GEMM: x [Mpad][K] f32.  direct: float out[m*out_ld + n] for m < m_store; else double
+// out[m*N + n] (one slice of partial sums, S = 1).
 hipError_t launch_gemm_f32(const float* W, int N, int K, const float* x, int Mpad, int M, void* out, bool direct,
                            int out_ld, int m_store, hipStream_t st);
 
@@ -69,10 +88,16 @@ hipError_t launch_gemm_f32(const float* W, int N, int K, const float* x, int Mpa
 //
 // v = (resid ? resid[m] : 0) + o, o = f32(sum_{s<S} part[(s*part_mstride + m)*N + i]) (f64
 // partials) or, with part NULL, o = x[m*N + i] (f32 rows); h_out (optional) receives v; with a
-// norm weight w the row is RMSNormed first.
+// norm weight w the row is RMSNormed first.  One workgroup per row.
 hipError_t launch_norm_act(const double* part, const float* x, int S, int part_mstride, const float* resid,
                            float* h_out, const float* w, float eps, int M, int Mpad, int N, bool quant, int8_t* xq,
                            float* dxT, float* xf, hipStream_t st);
+// RMSNorm + activation output of rows h [M][N] whose sums of squares arrive in nparts f64
+// pieces ssq[m*nparts + i]; many workgroups per row.
+hipError_t launch_rms_act(const float* h, const double* ssq, int nparts, const float* w, float eps, int M, int Mpad,
+                          int N, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st);
+// h = x (M rows of N) and the rows' sums of squares in N/256 pieces ssq[m*(N/256) + i].
+hipError_t launch_copy_ssq(const float* x, float* h, int M, int N, double* ssq, hipStream_t st);
 // a = silu(gate) * up from the interleaved gate|up partials [S][Mpad][2I].
 hipError_t launch_swiglu_act(const double* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
                              float* xf, hipStream_t st);

@@ -4,12 +4,14 @@
 // Dev::q4 / Dev::q8: int8 activations per group of 32 against the quantized weights).
 //
 // The block has 16..128 activation rows and thousands of weight rows, so the weights are the
-// stream: each wave owns one 16-row n-tile and walks its superblocks (common.h) front to back,
-// issuing PF 128-bit loads ahead.  One v_mfma_i32_16x16x32_i8 covers exactly one group of 32
-// for 16 rows x 16 columns, so the per-group rescale is applied to its integer result right
-// away.  The int8 activation block and its scales are staged once per workgroup in LDS and
-// shared by the workgroup's four waves; K is split across blockIdx.y when the weight has few
-// n-tiles (partial sums [S][Mpad][N] are reduced by the consumer kernel, in slice order).
+// stream: each wave owns one 16-row n-tile (and a share of its k-blocks) and walks its
+// superblocks (common.h) front to back with a ring of loads in flight.  One
+// v_mfma_i32_16x16x32_i8 covers exactly one group of 32 for 16 rows x 16 columns, so the
+// per-group rescale is applied to its integer result right away.  The int8 activation block and
+// its scales are staged in LDS and shared by the workgroup's waves.  A product with few n-tiles
+// splits K over the waves of one workgroup, which add their sums in LDS; the epilogue (the
+// residual add with the row's sum of squares, or SwiGLU with its A8 quantizer) runs in the same
+// kernel, so no partial sums travel through memory.
 //
 // The rescale accumulates in f64: d_w*d_x is exact in f64 and so is its product with a Q4 group
 // sum, so each output is the f32 rounding of (nearly) the exact sum, the same value a plain f64
@@ -86,36 +88,58 @@ __device__ __forceinline__ float w_scale(const Super<FMT>& r, int j) {
   return f16_to_f32(w >> (16 * (j & 1)));
 }
 
-// superblocks in flight per wave (a register ring): deep for the block's few rows, shallower
-// when the accumulators of many row tiles take the registers
-constexpr int PF = 8;
-template <int MT>
-struct Ring {
-  static constexpr int depth = MT <= 2 ? 8 : MT <= 4 ? 4 : 2;
-};
-// LDS budget of one workgroup's activation chunk (int8 rows and their scales): two
-// workgroups fit a 160 KB CU
-constexpr size_t LDS_BUDGET = 76 * 1024;
+// A8_32 of one element whose 32-element group sits in 32 consecutive lanes of the wave.
+__device__ __forceinline__ void emit_q32(float y, size_t qi, int8_t* __restrict__ xq, float* __restrict__ dx, size_t di,
+                                         int lane) {
+  float amax = fabsf(y);
+#pragma unroll
+  for (int o = 16; o; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+  int8_t q = 0;
+  float d = 0.f;
+  if (amax > 0.f) {
+    d = amax / 127.0f;
+    const float inv = 127.0f / amax;
+    float r = __builtin_rintf(y * inv);
+    r = fminf(fmaxf(r, -127.f), 127.f);
+    q = (int8_t)r;
+  }
+  xq[qi] = q;
+  if ((lane & 31) == 0) dx[di] = d;
+}
 
-template <int FMT, int MT, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void k_gemm_q(const uint8_t* __restrict__ W, int N, int K,
-                                                      const int8_t* __restrict__ xq,
-                                                      const float* __restrict__ dxT, int kbps, int kcb,
-                                                      void* __restrict__ out, int direct, int out_ld, int m_store) {
+// Register ring depth (superblocks in flight per wave) and the k-blocks one turn of the ring
+// covers across the workgroup's k-waves: about 32/MT k-blocks, so one turn's activations fit the
+// LDS chunk.
+template <int MT, int KW>
+struct Ring {
+  static constexpr int raw = 32 / MT / KW;
+  static constexpr int depth = raw < 1 ? 1 : raw > 8 ? 8 : raw;
+  static constexpr int step = depth * KW;
+};
+
+// One workgroup: NTW n-tiles x KW k-waves.  Wave (nt, kw) streams the superblocks kb = kw,
+// kw + KW, ... of n-tile blockIdx.x*NTW + nt through its register ring; the activations of a
+// chunk of kcb k-blocks (a multiple of the ring's step, so the ring runs on across chunks) are
+// staged in LDS and shared by all waves.  The k-waves' f64 sums are then added in wave order
+// through LDS (the same order on every run) and wave kw = 0 applies the epilogue.
+template <int FMT, int MT, int NTW, int KW>
+__global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restrict__ W, int N, int K,
+                                                         const int8_t* __restrict__ xq,
+                                                         const float* __restrict__ dxT, int kcb, GemmOut o) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MR = MT * 16;
   constexpr int SBB = FMT == Q4 ? SB_Q4 : SB_Q8;
-  constexpr int NT = 64 * WAVES;
+  constexpr int NT = 64 * NTW * KW;
+  constexpr int RD = Ring<MT, KW>::depth, STEP = Ring<MT, KW>::step;
   const int ASTR = kcb * 128 + 16;  // padded LDS row: rows land 4 banks apart
   int8_t* A = (int8_t*)smem;
-  float* DX = (float*)(smem + MR * ASTR);  // [kcb*4 groups][MR] activation scales (exact in f64)
+  float* DX = (float*)(smem + MR * ASTR);  // [kcb*4 groups][MR] activation scales
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntile = blockIdx.x * WAVES + wave;
+  const int nt = wave % NTW, kw = wave / NTW;
+  const int ntile = blockIdx.x * NTW + nt;
   const bool active = ntile < (N >> 4);
-  const int KB = K >> 7;
-  const int kb0 = blockIdx.y * kbps;
-  const int kb1 = min(kb0 + kbps, KB);
-  const uint8_t* wt = W + (size_t)ntile * KB * SBB;
+  const int KB = K >> 7, Mpad = o.Mpad;
+  const uint8_t* wt = W + (size_t)(active ? ntile : 0) * KB * SBB;
   const int quarter = lane >> 4, row16 = lane & 15;
 
   double acc[MT][4];
@@ -124,31 +148,58 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_q(const uint8_t* __restrict
 #pragma unroll
     for (int r = 0; r < 4; r++) acc[mt][r] = 0.0;
 
-  constexpr int RD = Ring<MT>::depth;
+  // the ring is filled before the first activations are staged, so the weights' HBM latency
+  // overlaps the staging; a superblock past the tile reads as zeros and costs nothing
+  const __amdgpu_buffer_rsrc_t rs = wave_rsrc(wt, active ? KB * SBB : 0);
   Super<FMT> r[RD];
-  for (int c0 = kb0; c0 < kb1; c0 += kcb) {
-    const int c1 = min(c0 + kcb, kb1);
-    const int ncols = (c1 - c0) * 128;
-    if (c0 != kb0) __syncthreads();  // the previous chunk's LDS reads are done
-    // the weights' ring is filled first, so their HBM latency overlaps the activations' staging
-    const __amdgpu_buffer_rsrc_t rs = wave_rsrc(wt, active ? c1 * SBB : 0);
 #pragma unroll
-    for (int p = 0; p < RD; p++) super_load(rs, (c0 + p) * SBB, lane, r[p]);
-    const int v16 = ncols >> 4;
-    for (int i = tid; i < MR * v16; i += NT) {
-      const int rr = i / v16, c = i - rr * v16;
-      *(uint4*)(A + rr * ASTR + c * 16) = *(const uint4*)(xq + (size_t)rr * K + (size_t)c0 * 128 + c * 16);
+  for (int p = 0; p < RD; p++) super_load(rs, (kw + p * KW) * SBB, lane, r[p]);
+  for (int c0 = 0; c0 < KB; c0 += kcb) {
+    const int c1 = min(c0 + kcb, KB);
+    const int ncols = (c1 - c0) * 128;
+    if (c0) __syncthreads();  // the previous chunk's LDS reads are done
+    // staging: SB loads are issued together, then stored, so their latencies overlap
+    constexpr int SB = 8;
+    const int v16 = ncols >> 4, nv = MR * v16;
+    for (int i0 = tid; i0 < nv; i0 += NT * SB) {
+      uint4 v[SB];
+#pragma unroll
+      for (int b = 0; b < SB; b++) {
+        const int i = i0 + b * NT;
+        const int rr = i / v16, c = i - rr * v16;
+        v[b] = (uint4){0u, 0u, 0u, 0u};
+        if (i < nv && rr < Mpad) v[b] = *(const uint4*)(xq + (size_t)rr * K + (size_t)c0 * 128 + c * 16);
+      }
+#pragma unroll
+      for (int b = 0; b < SB; b++) {
+        const int i = i0 + b * NT;
+        const int rr = i / v16, c = i - rr * v16;
+        if (i < nv) *(uint4*)(A + rr * ASTR + c * 16) = v[b];
+      }
     }
-    const int ng = ncols >> 5;
-    const float* dsrc = dxT + (size_t)c0 * 4 * MR;
-    for (int i = tid; i < ng * MR; i += NT) DX[i] = dsrc[i];
+    const int ng = ncols >> 5, nd = ng * MR;
+    for (int i0 = tid; i0 < nd; i0 += NT * SB) {
+      float v[SB];
+#pragma unroll
+      for (int b = 0; b < SB; b++) {
+        const int i = i0 + b * NT;
+        const int g = i / MR, m = i - g * MR;
+        v[b] = (i < nd && m < Mpad) ? dxT[(size_t)(c0 * 4 + g) * Mpad + m] : 0.f;
+      }
+#pragma unroll
+      for (int b = 0; b < SB; b++) {
+        const int i = i0 + b * NT;
+        if (i < nd) DX[i] = v[b];
+      }
+    }
     __syncthreads();
     if (!active) continue;
-    for (int kb = c0; kb < c1; kb += RD) {
+    for (int kb = c0 + kw; kb < c1; kb += STEP) {
 #pragma unroll
       for (int p = 0; p < RD; p++) {
-        if (kb + p < c1) {
-          const int kk = kb + p - c0;
+        const int kbp = kb + p * KW;
+        if (kbp < c1) {
+          const int kk = kbp - c0;
 #pragma unroll MT <= 2 ? 4 : 1
           for (int j = 0; j < 4; j++) {
             const long b = b_operand(r[p], j);
@@ -166,24 +217,81 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_q(const uint8_t* __restrict
             }
           }
         }
-        // refill the slot with the superblock RD ahead (zeros, no traffic, past the chunk)
-        super_load(rs, (kb + p + RD) * SBB, lane, r[p]);
+        // refill the slot with this wave's superblock one ring turn ahead
+        super_load(rs, (kbp + STEP) * SBB, lane, r[p]);
       }
     }
   }
-  if (!active) return;
+
+  // the k-waves' sums, added in wave order
+  if (KW > 1) {
+    __syncthreads();
+    double* red = (double*)smem;
+    if (kw > 0 && active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) red[((((kw - 1) * NTW + nt) * MT + mt) * 4 + q) * 64 + lane] = acc[mt][q];
+    __syncthreads();
+    if (kw == 0 && active)
+      for (int k = 1; k < KW; k++)
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) acc[mt][q] += red[((((k - 1) * NTW + nt) * MT + mt) * 4 + q) * 64 + lane];
+  }
   const double post = FMT == Q4 ? 0.0625 : 1.0;  // Q4 codes entered the MFMA as 16*q
   const int n = ntile * 16 + row16;
+
+  if (o.epi == EPI_SWIGLU) {
+    // NTW == 4: n-tiles gate(2b), up(2b), gate(2b+1), up(2b+1) of block b = blockIdx.x give the
+    // 32 columns 32b.. of a = silu(gate) * up, one A8 group per row
+    __syncthreads();
+    float* G = (float*)smem;  // [MR][64]: the four tiles' f32 products
+    if (kw == 0 && active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) G[(mt * 16 + 4 * quarter + q) * 64 + nt * 16 + row16] = (float)(acc[mt][q] * post);
+    __syncthreads();
+    const int I = N >> 1;
+    for (int i = tid; i < MR * 32; i += NT) {
+      const int m = i >> 5, j = i & 31;
+      if (m >= Mpad) break;  // whole 32-lane groups leave together
+      const int gc = (j >> 4) * 32 + (j & 15);
+      const double g = G[m * 64 + gc], u = G[m * 64 + gc + 16];
+      const float a = (float)(g / (1.0 + exp(-g)) * u);
+      const int c = blockIdx.x * 32 + j;
+      if (o.xq)
+        emit_q32(a, (size_t)m * I + c, o.xq, o.dxT, (size_t)(c >> 5) * Mpad + m, lane);
+      else
+        o.xf[(size_t)m * I + c] = a;
+    }
+    return;
+  }
+  if (kw != 0 || !active) return;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int m = mt * 16 + 4 * quarter + r;
-      const double v = acc[mt][r] * post;
-      if (direct) {
-        if (m < m_store) ((float*)out)[(size_t)m * out_ld + n] = (float)v;
-      } else {
-        ((double*)out)[((size_t)blockIdx.y * MR + m) * N + n] = v;
+    for (int q = 0; q < 4; q++) {
+      const int m = mt * 16 + 4 * quarter + q;
+      const double v = acc[mt][q] * post;
+      if (o.epi == EPI_F64) {
+        if (m < Mpad) ((double*)o.y)[(size_t)m * N + n] = v;
+      } else if (o.epi == EPI_F32) {
+        if (m < o.m_store) ((float*)o.y)[(size_t)m * o.ld + n] = (float)v;
+      } else {  // EPI_RESID: h += f32(v), and the tile's share of each row's sum of squares
+        double sq = 0.0;
+        if (m < o.M) {
+          const float hv = o.h[(size_t)m * N + n] + (float)v;
+          o.h[(size_t)m * N + n] = hv;
+          sq = (double)hv * (double)hv;
+        }
+        sq += __shfl_xor(sq, 1);
+        sq += __shfl_xor(sq, 2);
+        sq += __shfl_xor(sq, 4);
+        sq += __shfl_xor(sq, 8);
+        if (row16 == 0 && m < Mpad) o.ssq[(size_t)m * (N >> 4) + ntile] = sq;
       }
     }
   }
@@ -219,70 +327,74 @@ __global__ __launch_bounds__(256) void k_group_sums(const uint8_t* __restrict__ 
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-int normalize_splits(int K, int s) {
-  const int KB = K / 128;
-  if (s < 1) s = 1;
-  if (s > KB) s = KB;
-  if (s > 16) s = 16;  // the consumers add at most 16 slices
-  const int kbps = ceil_div(KB, s);
-  return ceil_div(KB, kbps);
-}
+// activation rows a launch handles: Mpad rounded up to 16, 32, 64 or 128
+static int gemm_mt(int Mpad) { return Mpad <= 16 ? 1 : Mpad <= 32 ? 2 : Mpad <= 64 ? 4 : 8; }
 
-int choose_splits(int N, int K, int Mpad) {
+int gemm_layout(int N, int Mpad, int epi) {
   (void)Mpad;
-  const int tiles = N / 16, KB = K / 128;
-  // A product with thousands of n-tiles streams its weights without splitting K; a smaller one
-  // gives each wave about PF superblocks, so all of its loads are in flight from the start.
-  if (tiles >= 4096) return 1;
-  // at least ~2048 waves (eight per CU), and at most 16 superblocks per wave
-  const int by_waves = ceil_div(2048, tiles), by_depth = ceil_div(KB, 2 * PF);
-  return normalize_splits(K, by_waves > by_depth ? by_waves : by_depth);
+  // thousands of n-tiles (the head, gate|up) stream without splitting K much; a product with
+  // few n-tiles splits K over eight (four) waves so every CU has about eight waves in flight
+  if (epi == EPI_SWIGLU) return 0;
+  return N / 16 >= 2048 ? 2 : 1;
 }
 
-template <int FMT, int MT>
-static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, int splits, void* out,
-                            bool direct, int out_ld, int m_store, hipStream_t st) {
-  constexpr int WAVES = 4;  // n-tiles sharing one LDS copy of the activations
+template <int FMT, int MT, int NTW, int KW>
+static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
+                            hipStream_t st) {
+  constexpr int MR = MT * 16, STEP = Ring<MT, KW>::step;
   const int KB = K / 128;
-  const int kbps = ceil_div(KB, splits);
-  // per 128-column block: MT*16 rows of 128 codes + 4 groups x MT*16 f32 scales; row padding
-  size_t budget = max_dynamic_lds();
-  if (budget > LDS_BUDGET) budget = LDS_BUDGET;
-  int kcb_max = (int)((budget - (size_t)256 * MT) / ((size_t)2304 * MT));
-  if (kcb_max < 1) kcb_max = 1;
-  const int kcb = kbps < kcb_max ? kbps : kcb_max;
-  const size_t lds = (size_t)MT * 16 * (kcb * 128 + 16) + (size_t)kcb * 4 * MT * 16 * 4;
-  hipError_t e = allow_lds((const void*)k_gemm_q<FMT, MT, WAVES>, lds);
+  // LDS of a chunk of kcb k-blocks: MR rows of kcb*128 codes (+16 B row padding) and kcb*4*MR
+  // f32 scales; about 76 KB so two workgroups share a CU
+  const size_t per_kb = (size_t)MR * 144;
+  int kcb = (int)((76 * 1024 - (size_t)MR * 16) / per_kb) / STEP * STEP;
+  if (kcb < STEP) kcb = STEP;
+  if (kcb > KB) kcb = KB;
+  size_t lds = (size_t)MR * (kcb * 128 + 16) + (size_t)kcb * 4 * MR * 4;
+  const size_t red = (size_t)(KW - 1) * NTW * MT * 4 * 64 * 8;
+  const size_t swg = (size_t)MR * 64 * 4;
+  if (red > lds) lds = red;
+  if (swg > lds) lds = swg;
+  if (lds > max_dynamic_lds()) return hipErrorInvalidValue;
+  hipError_t e = allow_lds((const void*)k_gemm_q<FMT, MT, NTW, KW>, lds);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)ceil_div(N / 16, WAVES), (unsigned)ceil_div(KB, kbps));
-  hipLaunchKernelGGL((k_gemm_q<FMT, MT, WAVES>), grid, dim3(64 * WAVES), lds, st, (const uint8_t*)W, N, K, xq, dxT,
-                     kbps, kcb, out, direct ? 1 : 0, out_ld, m_store);
+  dim3 grid((unsigned)ceil_div(N / 16, NTW));
+  hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW>), grid, dim3(64 * NTW * KW), lds, st, (const uint8_t*)W, N, K, xq,
+                     dxT, kcb, o);
   return hipGetLastError();
 }
 
-template <int FMT>
-static hipError_t gemm_fmt(const void* W, int N, int K, const int8_t* xq, const float* dxT, int Mpad, int splits,
-                           void* out, bool direct, int out_ld, int m_store, hipStream_t st) {
-  switch (Mpad / 16) {
-    case 1: return gemm_inst<FMT, 1>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
-    case 2: return gemm_inst<FMT, 2>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
-    case 3: return gemm_inst<FMT, 3>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
-    case 4: return gemm_inst<FMT, 4>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
-    case 5: return gemm_inst<FMT, 5>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
-    case 6: return gemm_inst<FMT, 6>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
-    case 7: return gemm_inst<FMT, 7>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
-    case 8: return gemm_inst<FMT, 8>(W, N, K, xq, dxT, splits, out, direct, out_ld, m_store, st);
-  }
-  return hipErrorInvalidValue;
+template <int FMT, int MT>
+static hipError_t gemm_mt_inst(int layout, const void* W, int N, int K, const int8_t* xq, const float* dxT,
+                               const GemmOut& o, hipStream_t st) {
+  if (layout == 0) return gemm_inst<FMT, MT, 4, 2>(W, N, K, xq, dxT, o, st);
+  if (layout == 2) return gemm_inst<FMT, MT, 4, 1>(W, N, K, xq, dxT, o, st);
+  if constexpr (MT <= 2)
+    return gemm_inst<FMT, MT, 1, 8>(W, N, K, xq, dxT, o, st);
+  else
+    return gemm_inst<FMT, MT, 2, 4>(W, N, K, xq, dxT, o, st);
 }
 
-hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int Mpad,
-                         int splits, void* out, bool direct, int out_ld, int m_store, hipStream_t st) {
-  if (N % 16 || K % 128 || Mpad % 16 || Mpad < 16 || Mpad > 128) return hipErrorInvalidValue;
-  splits = normalize_splits(K, splits);
-  if (direct && splits != 1) return hipErrorInvalidValue;
-  if (fmt == Q4) return gemm_fmt<Q4>(W, N, K, xq, dxT, Mpad, splits, out, direct, out_ld, m_store, st);
-  if (fmt == Q8) return gemm_fmt<Q8>(W, N, K, xq, dxT, Mpad, splits, out, direct, out_ld, m_store, st);
+template <int FMT>
+static hipError_t gemm_fmt(int layout, const void* W, int N, int K, const int8_t* xq, const float* dxT,
+                           const GemmOut& o, hipStream_t st) {
+  switch (gemm_mt(o.Mpad)) {
+    case 1: return gemm_mt_inst<FMT, 1>(layout, W, N, K, xq, dxT, o, st);
+    case 2: return gemm_mt_inst<FMT, 2>(layout, W, N, K, xq, dxT, o, st);
+    case 4: return gemm_mt_inst<FMT, 4>(layout, W, N, K, xq, dxT, o, st);
+    default: return gemm_mt_inst<FMT, 8>(layout, W, N, K, xq, dxT, o, st);
+  }
+}
+
+hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int layout,
+                         const GemmOut& o, hipStream_t st) {
+  if (N % 16 || K % 128 || o.Mpad % 16 || o.Mpad < 16 || o.Mpad > 128 || o.M > o.Mpad) return hipErrorInvalidValue;
+  if (o.epi == EPI_SWIGLU && (N % 64 || (!o.xq && !o.xf) || (o.xq && !o.dxT))) return hipErrorInvalidValue;
+  if ((o.epi == EPI_F64 || o.epi == EPI_F32) && !o.y) return hipErrorInvalidValue;
+  if (o.epi == EPI_RESID && (!o.h || !o.ssq)) return hipErrorInvalidValue;
+  if (layout < 0) layout = gemm_layout(N, o.Mpad, o.epi);
+  if (o.epi == EPI_SWIGLU) layout = 0;
+  if (fmt == Q4) return gemm_fmt<Q4>(layout, W, N, K, xq, dxT, o, st);
+  if (fmt == Q8) return gemm_fmt<Q8>(layout, W, N, K, xq, dxT, o, st);
   return hipErrorInvalidValue;
 }
 

@@ -162,9 +162,12 @@ int dflash_pack(int32_t fmt, int32_t rows, int32_t cols, dflash_matrix w, void* 
 
 /* y device [m][rows] f32 = W . x through the production weight-streaming kernel, for a packed
  * quantized W and A8_32 activations xq device [m][cols] int8, dx device [m][cols/32] f32;
- * splits: 0 = the library's choice, else the number of K slices.  m <= 128.  Each output is the
- * f32 rounding of the product's f64 accumulation.  `scratch` is device memory of at least
- * dflash_gemm_scratch_bytes() bytes (padded activations, their scales, f64 partial sums). */
+ * splits: how the kernel divides K among the waves of a workgroup: 0 = the library's choice,
+ * 1 = one wave per n-tile, 2..7 = two k-waves per group of four n-tiles, >= 8 = K split over
+ * the waves of one n-tile
+ * (negative: DFLASH_EINVAL).  m <= 128.  Each output is the f32 rounding of the product's f64
+ * accumulation, whatever the split.  `scratch` is device memory of at least
+ * dflash_gemm_scratch_bytes() bytes (padded activations and their scales). */
 int dflash_gemm_scratch_bytes(int32_t rows, int32_t cols, int32_t m, int32_t splits, size_t* bytes);
 int dflash_gemm(int32_t fmt, const void* packed, int32_t rows, int32_t cols, const int8_t* xq, const float* dx,
                 int32_t m, float* y, int32_t splits, void* scratch, void* stream);

@@ -66,6 +66,8 @@ def _packed(mat):
 
 
 SHAPES = [(16, 128, 1), (48, 384, 5), (64, 256, 16), (32, 512, 33), (16, 128, 128), (80, 1024, 100)]
+# K long enough for several activation chunks in LDS, the last one ragged (16, 48 and 128 rows)
+GEMM_SHAPES = SHAPES + [(64, 4608, 16), (48, 2560, 40), (32, 1152, 128)]
 
 
 @pytest.mark.parametrize("fmt", [di.Q4_32, di.Q8_32], ids=["q4", "q8"])
@@ -86,8 +88,8 @@ def test_group_sums_bit_exact(fmt, rows, cols, m):
 
 
 @pytest.mark.parametrize("fmt", [di.Q4_32, di.Q8_32], ids=["q4", "q8"])
-@pytest.mark.parametrize("rows,cols,m", SHAPES)
-@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("rows,cols,m", GEMM_SHAPES)
+@pytest.mark.parametrize("splits", [0, 1, 2, 8])
 def test_gemm_correctly_rounded(fmt, rows, cols, m, splits):
     """The product is the f32 rounding of its exact value, as the oracle's f64 evaluation: equal
     to the oracle's f32 except where the two f64 sums straddle a rounding boundary (rare), and
