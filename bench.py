@@ -22,6 +22,8 @@ if ROOT not in sys.path:
 
 METRIC = "ms per DFlash draft block + achieved HBM GB/s (% of peak), 8B-shaped drafter"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+F64_MFMA_PEAK_TFS = 78.6  # MI355X dense f64 matrix, published
+I8_MFMA_PEAK_OPS = 5.0e15  # MI355X dense int8 matrix, published
 
 
 def log(*a):
@@ -49,6 +51,47 @@ def head_bytes(cfg) -> int:
         w = cfg.vocab * (cfg.hidden // 32) * per
         x = rows * cfg.hidden + rows * (cfg.hidden // 32) * 4
     return w + x + rows * cfg.vocab * 4
+
+
+def attention_flops(cfg, nctx: int) -> int:
+    """Flops of one layer's attention of every sequence's block: per q head and block row, the
+    scores against nctx context keys + the block's own keys and the weighted sum of as many
+    values (2 flops per multiply-add each)."""
+    return 4 * cfg.n_seqs * cfg.block * cfg.heads * (nctx + cfg.block) * cfg.head_dim
+
+
+def int8_macs(cfg) -> int:
+    """Useful int8 multiply-adds of one step's quantized products (weights x activation rows):
+    every body matrix and the head for the block rows, plus FC and K|V of the appended rows."""
+    rows = cfg.n_seqs * cfg.block
+    H, qd, kvd, I = cfg.hidden, cfg.heads * cfg.head_dim, cfg.kv_heads * cfg.head_dim, cfg.intermediate
+    body = cfg.layers * ((qd + 2 * kvd) * H + H * qd + 2 * I * H + H * I)
+    macs = rows * (body + cfg.vocab * H)
+    if cfg.append_per_block:
+        n = cfg.append_per_block * cfg.n_seqs
+        macs += n * (H * cfg.n_taps * H + cfg.layers * 2 * kvd * H)
+    return macs
+
+
+def measured_traffic(kernel: str, workload: str, source: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary
+    profiles/<kernel>_<workload>_pmc.md (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known
+    size), or None when there is none or the kernel's source has changed since it was taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    src = os.path.join(ROOT, "block_draft_model_dflash_amd", "csrc", source)
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    text = open(path).read()
+    sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not sha or not val:
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != sha.group(1):
+        return None
+    return int(val.group(1))
 
 
 def cpu_baseline(cfg, weights, blocks: int = 2):
@@ -86,6 +129,8 @@ def main() -> int:
     ap.add_argument("--config", default="qwen3_8b", choices=di.CONFIG_ORDER)
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--stages", type=int, default=1, help="also time each stage in its own untimed pass")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed region, run one plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU; the path's multi-GPU sharding is a design "
@@ -156,9 +201,7 @@ def main() -> int:
     torch.cuda.synchronize()
     rewind()
 
-    # timed region: K steps; HIP events around the dominant kernel (the head) on the library's stream
-    D.dflash_time_stage(gm.ctx, D.DFLASH_STAGE_HEAD)
-    D.dflash_read_timing(gm.ctx)
+    # timed region: K steps, nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -167,15 +210,31 @@ def main() -> int:
     t1 = time.perf_counter()
     if app is not None:  # every step extended the same context
         assert gm.span(0) == (0, cfg.ctx + K * cfg.append_per_block), gm.span(0)
-    head_ms, head_n = D.dflash_read_timing(gm.ctx)
-    D.dflash_time_stage(gm.ctx, -1)
     ms = (t1 - t0) * 1e3 / K
-    head_avg_ms = head_ms / max(head_n, 1)
-    log(f"{ms:.4f} ms/step; head {head_avg_ms:.4f} ms x {head_n}")
+
+    # the same K steps again with HIP events (on the library's stream) around the head's product
+    # and around every layer's attention chunk kernel, the two largest kernels of the step; the
+    # event pairs cost a few microseconds per step, so this repetition is not the one in `value`
+    rewind()
+    D.dflash_time_stage(gm.ctx, -1)
+    D.dflash_time_stage(gm.ctx, D.DFLASH_STAGE_HEAD)
+    D.dflash_time_stage(gm.ctx, D.DFLASH_STAGE_ATTN_CHUNKS)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(K):
+        step(W + i)
+    torch.cuda.synchronize()
+    ms_events = (time.perf_counter() - t2) * 1e3 / K
+    head_ms, head_n = D.dflash_read_timing(gm.ctx, D.DFLASH_STAGE_HEAD)
+    attn_ms, attn_n = D.dflash_read_timing(gm.ctx, D.DFLASH_STAGE_ATTN_CHUNKS)
+    D.dflash_time_stage(gm.ctx, -1)
+    log(f"{ms:.4f} ms/step ({ms_events:.4f} with events); head {head_ms / max(head_n, 1):.4f} ms x {head_n}; "
+        f"attention chunks {attn_ms / max(attn_n, 1):.4f} ms x {attn_n}")
 
     stages = {}
     if args.stages:
-        names = {D.DFLASH_STAGE_QKV: "qkv", D.DFLASH_STAGE_ATTENTION: "attention", D.DFLASH_STAGE_O: "o",
+        names = {D.DFLASH_STAGE_QKV: "qkv", D.DFLASH_STAGE_ATTENTION: "attention",
+                 D.DFLASH_STAGE_ATTN_CHUNKS: "attention_chunks", D.DFLASH_STAGE_O: "o",
                  D.DFLASH_STAGE_GATE_UP: "gate_up", D.DFLASH_STAGE_DOWN: "down", D.DFLASH_STAGE_HEAD: "head",
                  D.DFLASH_STAGE_BLOCK: "block", D.DFLASH_STAGE_APPEND: "append"}
         for st, name in names.items():
@@ -183,19 +242,49 @@ def main() -> int:
                 continue
             rewind()
             D.dflash_time_stage(gm.ctx, st)
-            D.dflash_read_timing(gm.ctx)
             for i in range(K):
                 step(W + i)
-            tot, n = D.dflash_read_timing(gm.ctx)
+            tot, n = D.dflash_read_timing(gm.ctx, st)
             D.dflash_time_stage(gm.ctx, -1)
             stages[name] = round(tot / K, 5)  # ms per step, summed over the stage's launches
         log("stages ms/step:", stages)
 
+    if args.copy_probe_mib:
+        # a plain streaming kernel of known size (read n bytes, write n bytes): the reference
+        # against which the HBM byte counters of the other kernels are scaled
+        n = args.copy_probe_mib << 18  # f32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     ab = di.algorithmic_bytes(cfg, ctx_rows=cfg.ctx)
-    hb = head_bytes(cfg)
-    achieved = hb / (head_avg_ms * 1e-3) / 1e9
     block_gbs = ab["total"] / (ms * 1e-3) / 1e9
     rows = cfg.n_seqs * cfg.block
+    # the head: algorithmic bytes per launch / its average launch time (HBM roofline)
+    hb = head_bytes(cfg)
+    head_avg = head_ms / max(head_n, 1)
+    head_gbs = hb / (head_avg * 1e-3) / 1e9
+    head_line = {"bound": "hbm", "achieved": round(head_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(head_gbs / HBM_PEAK_GBS, 4),
+                 "traffic": measured_traffic("head_gemm", cfg.key, "gemm.hip"),
+                 "kernel": "k_gemm_q (head logits, Q8_32 x A8_32)", "bytes_per_launch": hb,
+                 "avg_launch_ms": round(head_avg, 5), "launches": head_n, "ms_per_step": round(head_ms / K, 5)}
+    # attention chunks: f64 MFMA flops per launch / its average launch time (f64 matrix roofline)
+    ctx_rows = [cfg.ctx + (i + 1) * cfg.append_per_block for i in range(K)] if app is not None else [cfg.ctx] * K
+    flops = sum(attention_flops(cfg, n) for n in ctx_rows) * cfg.layers
+    attn_avg = attn_ms / max(attn_n, 1)
+    attn_tf = flops / max(attn_n, 1) / (attn_avg * 1e-3) / 1e12
+    attn_line = {"bound": "mfma", "achieved": round(attn_tf, 2), "peak": F64_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                 "frac": round(attn_tf / F64_MFMA_PEAK_TFS, 4),
+                 "traffic": measured_traffic("attn_chunks", cfg.key, "attention.hip"),
+                 "kernel": "k_attn_partial (f64 MFMA scores, softmax and values)",
+                 "flops_per_launch": round(flops / max(attn_n, 1)), "avg_launch_ms": round(attn_avg, 5),
+                 "launches": attn_n, "ms_per_step": round(attn_ms / K, 5)}
+    # the dominant kernel of the step is the one with the larger share of the step's time
+    dominant, other = (attn_line, head_line) if attn_ms > head_ms else (head_line, attn_line)
     out = {
         "metric": METRIC,
         "value": round(ms, 5),
@@ -207,7 +296,7 @@ def main() -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8 (int8 MFMA on 4/8-bit weights) + f32",
+        "dtype": "i8 (int8 MFMA on 4/8-bit weights) + f64 (attention, rescale) + f32",
         "data": "synthetic",
         "config": {"workload": workload_name(cfg), "sequences": cfg.n_seqs, "block_rows": cfg.block,
                    "context_rows": cfg.ctx, "append_rows_per_step": cfg.append_per_block},
@@ -217,10 +306,10 @@ def main() -> int:
         "achieved_GBps_step": round(block_gbs, 1),
         "frac_of_hbm_peak_step": round(block_gbs / HBM_PEAK_GBS, 4),
         "gpu_prefill_rows_per_s": round(cfg.n_seqs * cfg.ctx / (prefill_ms * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_gemm_q<Q8_32> (head logits)", "bytes_per_launch": hb,
-                     "avg_launch_ms": round(head_avg_ms, 5), "launches": head_n},
+        "int8_mfma_util_step": round(int8_macs(cfg) * 2 / (ms * 1e-3) / I8_MFMA_PEAK_OPS, 5),
+        "roofline": dominant,
+        "roofline_next": other,
+        "ms_per_step_with_kernel_events": round(ms_events, 5),
         "stages_ms_per_step": stages,
     }
     if args.cpu_baseline and cfg.n_seqs == 1 and cfg.ctx <= 8192:

@@ -23,7 +23,7 @@ EXPORTS = [
     "dflash_gemm", "dflash_group_sums", "dflash_read_kv", "dflash_time_stage", "dflash_read_timing",
 ]
 (DFLASH_STAGE_HEAD, DFLASH_STAGE_QKV, DFLASH_STAGE_ATTENTION, DFLASH_STAGE_O, DFLASH_STAGE_GATE_UP, DFLASH_STAGE_DOWN,
- DFLASH_STAGE_BLOCK, DFLASH_STAGE_APPEND) = range(8)
+ DFLASH_STAGE_BLOCK, DFLASH_STAGE_APPEND, DFLASH_STAGE_ATTN_CHUNKS) = range(9)
 
 
 class dflash_geometry(C.Structure):
@@ -84,7 +84,7 @@ def lib():
             "dflash_group_sums": (i32, [i32, vp, i32, i32, vp, i32, vp, vp, vp]),
             "dflash_read_kv": (i32, [vp, i32, i32, i32, i32, vp, vp]),
             "dflash_time_stage": (i32, [vp, i32]),
-            "dflash_read_timing": (i32, [vp, C.POINTER(C.c_double), C.POINTER(i64)]),
+            "dflash_read_timing": (i32, [vp, i32, C.POINTER(C.c_double), C.POINTER(i64)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -200,10 +200,10 @@ def dflash_time_stage(ctx, stage: int) -> int:
     return _check(lib().dflash_time_stage(ctx, stage), ctx)
 
 
-def dflash_read_timing(ctx):
-    """(summed milliseconds, number of timed launches) since the last read."""
+def dflash_read_timing(ctx, stage: int):
+    """(summed milliseconds, number of timed launches) of one stage since its last read."""
     ms, n = C.c_double(), C.c_int64()
-    _check(lib().dflash_read_timing(ctx, C.byref(ms), C.byref(n)), ctx)
+    _check(lib().dflash_read_timing(ctx, stage, C.byref(ms), C.byref(n)), ctx)
     return ms.value, n.value
 
 

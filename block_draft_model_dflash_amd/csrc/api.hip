@@ -156,10 +156,11 @@ struct dflash_ctx {
   Layout lay;
   uint8_t* ws = nullptr;
   std::vector<int64_t> first, len;
-  // stage timing: event pairs recorded around one stage's launches
-  int timed_stage = -1;
+  // stage timing: event pairs recorded around the launches of the timed stages
+  unsigned timed_mask = 0;
   std::vector<hipEvent_t> ev_pool;  // created on first use, reused
   size_t ev_used = 0;
+  std::vector<int> ev_stage;  // stage of each recorded pair
 
   hipError_t mark() {  // record the next event of a pair
     if (ev_used == ev_pool.size()) {
@@ -203,8 +204,10 @@ struct dflash_ctx {
 struct StageTimer {
   dflash_ctx* c;
   bool on;
-  StageTimer(dflash_ctx* c_, int stage) : c(c_), on(c_->timed_stage == stage && c_->ev_used + 2 <= 65536) {
+  StageTimer(dflash_ctx* c_, int stage)
+      : c(c_), on(((c_->timed_mask >> stage) & 1u) && c_->ev_used + 2 <= 65536) {
     if (on && c->mark() != hipSuccess) on = false;
+    if (on) c->ev_stage.push_back(stage);
   }
   ~StageTimer() {
     if (on) (void)c->mark();
@@ -340,12 +343,19 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
             "q/k norm + rope");
     {
       StageTimer t(c, DFLASH_STAGE_ATTENTION);
+      {
+        StageTimer tc(c, DFLASH_STAGE_ATTN_CHUNKS);
+        TRY_HIP(c,
+                launch_attention_chunks(as, si, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
+                                        c->at<float>(L.kc) + (size_t)l * layer_cache,
+                                        c->at<float>(L.vc) + (size_t)l * layer_cache, c->at<double>(L.apart),
+                                        c->at<double>(L.aml), c->st),
+                "attention chunks");
+      }
       TRY_HIP(c,
-              launch_attention(as, si, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
-                               c->at<float>(L.kc) + (size_t)l * layer_cache,
-                               c->at<float>(L.vc) + (size_t)l * layer_cache, c->at<double>(L.apart),
-                               c->at<double>(L.aml), Mpad, bq, xq, dxT, xf, c->st),
-              "attention");
+              launch_attention_merge(as, si, c->at<double>(L.apart), c->at<double>(L.aml), Mpad, bq, xq, dxT, xf,
+                                     c->st),
+              "attention merge");
     }
     const bool last = l + 1 == NL;
     const float* nw = last ? c->at<float>(L.norm) : c->at<float>(L.in_norm) + (size_t)(l + 1) * H;
@@ -619,24 +629,43 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
 }
 
 int dflash_time_stage(dflash_ctx* c, int32_t stage) {
-  if (!c || stage > DFLASH_STAGE_APPEND) return DFLASH_EINVAL;
-  c->timed_stage = stage < 0 ? -1 : stage;
+  if (!c || stage > DFLASH_STAGE_LAST) return DFLASH_EINVAL;
+  if (stage < 0) {
+    c->timed_mask = 0;
+    c->ev_used = 0;
+    c->ev_stage.clear();
+  } else {
+    c->timed_mask |= 1u << stage;
+  }
   return DFLASH_OK;
 }
 
-int dflash_read_timing(dflash_ctx* c, double* total_ms, int64_t* count) {
-  if (!c || !total_ms || !count) return DFLASH_EINVAL;
+int dflash_read_timing(dflash_ctx* c, int32_t stage, double* total_ms, int64_t* count) {
+  if (!c || !total_ms || !count || stage < 0 || stage > DFLASH_STAGE_LAST) return DFLASH_EINVAL;
   double tot = 0.0;
+  int64_t n = 0;
   const size_t pairs = c->ev_used / 2;
   for (size_t i = 0; i < pairs; i++) {
+    if (c->ev_stage[i] != stage) continue;
     TRY_HIP(c, hipEventSynchronize(c->ev_pool[2 * i + 1]), "timing sync");
     float ms = 0.f;
     TRY_HIP(c, hipEventElapsedTime(&ms, c->ev_pool[2 * i], c->ev_pool[2 * i + 1]), "timing");
     tot += ms;
+    n++;
   }
-  c->ev_used = 0;
+  // forget the pairs once every stage that recorded some has been read: keep the others
+  bool others = false;
+  for (size_t i = 0; i < pairs; i++) {
+    if (c->ev_stage[i] == stage) c->ev_stage[i] = -1;
+    else if (c->ev_stage[i] >= 0) others = true;
+  }
+  if (!others) {
+    TRY_HIP(c, pairs ? hipEventSynchronize(c->ev_pool[2 * pairs - 1]) : hipSuccess, "timing sync");
+    c->ev_used = 0;
+    c->ev_stage.clear();
+  }
   *total_ms = tot;
-  *count = (int64_t)pairs;
+  *count = n;
   return DFLASH_OK;
 }
 

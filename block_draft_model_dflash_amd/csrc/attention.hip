@@ -287,19 +287,23 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void k_attn_merge(AttnShape a, Se
 }
 
 template <int HD>
-static hipError_t attn_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
-                          const float* kc, const float* vc, double* part, double* ml, int Mpad, bool quant, int8_t* xq,
-                          float* dxT, float* xf, hipStream_t st) {
+static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
+                                  const float* vb, const float* kc, const float* vc, double* part, double* ml,
+                                  hipStream_t st) {
   int maxn = 0;
   for (int i = 0; i < si.n; i++) {
     const int nch = si.nctx[i] > 0 ? (si.nctx[i] + a.ck - 1) / a.ck : 1;
     if (nch > maxn) maxn = nch;
   }
   if (maxn > a.maxch) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn, a.kvh, si.n), dim3(ATTN_THREADS), 0, st, a, si, q, kb, vb,
-                     kc, vc, part, ml);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn, a.kvh, si.n), dim3(ATTN_THREADS), 0, st, a, si, q, kb, vb, kc, vc,
+                     part, ml);
+  return hipGetLastError();
+}
+
+template <int HD>
+static hipError_t attn_merge_hd(const AttnShape& a, const SeqInfo& si, const double* part, const double* ml, int Mpad,
+                                bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st) {
   if (quant)
     hipLaunchKernelGGL((k_attn_merge<HD, true>), dim3(a.nh, a.B, si.n), dim3(64 * MERGE_WAVES), 0, st, a, si, part,
                        ml, Mpad, xq, dxT, xf);
@@ -309,13 +313,23 @@ static hipError_t attn_hd(const AttnShape& a, const SeqInfo& si, const float* q,
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
-                            const float* kc, const float* vc, double* part, double* ml, int Mpad, bool quant,
-                            int8_t* xq, float* dxT, float* xf, hipStream_t st) {
-  if (a.nh % a.kvh || a.nh / a.kvh > 16 || a.B > 16 || a.ck % 16 || a.ck <= 0) return hipErrorInvalidValue;
-  if (a.hd == 64) return attn_hd<64>(a, si, q, kb, vb, kc, vc, part, ml, Mpad, quant, xq, dxT, xf, st);
-  if (a.hd == 128) return attn_hd<128>(a, si, q, kb, vb, kc, vc, part, ml, Mpad, quant, xq, dxT, xf, st);
-  return hipErrorInvalidValue;
+static bool attn_shape_ok(const AttnShape& a) {
+  return !(a.nh % a.kvh || a.nh / a.kvh > 16 || a.B > 16 || a.ck % 32 || a.ck <= 0) && (a.hd == 64 || a.hd == 128);
+}
+
+hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
+                                   const float* vb, const float* kc, const float* vc, double* part, double* ml,
+                                   hipStream_t st) {
+  if (!attn_shape_ok(a)) return hipErrorInvalidValue;
+  if (a.hd == 64) return attn_partial_hd<64>(a, si, q, kb, vb, kc, vc, part, ml, st);
+  return attn_partial_hd<128>(a, si, q, kb, vb, kc, vc, part, ml, st);
+}
+
+hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const double* part, const double* ml,
+                                  int Mpad, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st) {
+  if (!attn_shape_ok(a)) return hipErrorInvalidValue;
+  if (a.hd == 64) return attn_merge_hd<64>(a, si, part, ml, Mpad, quant, xq, dxT, xf, st);
+  return attn_merge_hd<128>(a, si, part, ml, Mpad, quant, xq, dxT, xf, st);
 }
 
 }  // namespace dfl

@@ -178,21 +178,24 @@ int dflash_group_sums(int32_t fmt, const void* packed, int32_t rows, int32_t col
                       int32_t* sums, void* scratch, void* stream);
 
 /* Stage timing (the pages time a block's stages with GPU timestamps; here HIP events on the
- * ctx stream).  dflash_time_stage(c, stage) brackets every later launch of one stage with an
- * event pair (stage < 0 stops); dflash_read_timing waits for the recorded pairs and returns
- * their summed milliseconds and count, then forgets them.  Stages: */
+ * ctx stream).  dflash_time_stage(c, stage) adds a stage to the timed set (stage < 0 empties
+ * the set and forgets every recorded pair): each later launch of a timed stage is bracketed by
+ * an event pair.  dflash_read_timing(c, stage, ...) waits for that stage's recorded pairs and
+ * returns their summed milliseconds and count, then forgets them.  Stages: */
 enum dflash_stage {
-  DFLASH_STAGE_HEAD = 0,      /* the head's matrix product (logits) */
-  DFLASH_STAGE_QKV = 1,       /* every layer's Wq|Wk|Wv product */
-  DFLASH_STAGE_ATTENTION = 2, /* every layer's attention (chunks + merge) */
-  DFLASH_STAGE_O = 3,         /* every layer's Wo product */
-  DFLASH_STAGE_GATE_UP = 4,   /* every layer's gate|up product */
-  DFLASH_STAGE_DOWN = 5,      /* every layer's down product */
-  DFLASH_STAGE_BLOCK = 6,     /* the whole block call */
-  DFLASH_STAGE_APPEND = 7     /* the whole append call */
+  DFLASH_STAGE_HEAD = 0,        /* the head's matrix product (logits) */
+  DFLASH_STAGE_QKV = 1,         /* every layer's Wq|Wk|Wv product */
+  DFLASH_STAGE_ATTENTION = 2,   /* every layer's attention (chunks + merge) */
+  DFLASH_STAGE_O = 3,           /* every layer's Wo product (+ residual) */
+  DFLASH_STAGE_GATE_UP = 4,     /* every layer's gate|up product (+ SwiGLU) */
+  DFLASH_STAGE_DOWN = 5,        /* every layer's down product (+ residual) */
+  DFLASH_STAGE_BLOCK = 6,       /* the whole block call */
+  DFLASH_STAGE_APPEND = 7,      /* the whole append call */
+  DFLASH_STAGE_ATTN_CHUNKS = 8, /* every layer's attention chunk kernel alone (no merge) */
+  DFLASH_STAGE_LAST = 8
 };
 int dflash_time_stage(dflash_ctx* c, int32_t stage);
-int dflash_read_timing(dflash_ctx* c, double* total_ms, int64_t* count);
+int dflash_read_timing(dflash_ctx* c, int32_t stage, double* total_ms, int64_t* count);
 
 /* Copy K and V of context rows row0..row0+n-1 (index = position - first) of one layer and
  * sequence into device k, v [n][kv_heads][head_dim] f32 (a read-back of the cache). */
