@@ -1,7 +1,12 @@
 """The pins bite: plant plausible mistakes in a copy of the oracle's source (a dropped term, a
 wrong sign, index or operand), build each copy, and require some pin to fail on every one.
-Everything here runs on the CPU; the real oracle is restored afterwards."""
+Everything here runs on the CPU.  Each broken copy runs in a child process of its own: a
+planted indexing mistake can write past the oracle's buffers, and that must not corrupt the
+process that runs the other tests (a child that crashes has failed loudly: caught)."""
+import concurrent.futures as cf
 import os
+import subprocess
+import sys
 
 import pytest
 
@@ -67,12 +72,6 @@ CHECKS = [
 ]
 
 
-@pytest.fixture(scope="module")
-def restore_oracle():
-    yield
-    oracle.use_library(None)
-
-
 def _caught(fn, args) -> bool:
     try:
         fn(*args)
@@ -81,16 +80,51 @@ def _caught(fn, args) -> bool:
     return False
 
 
-@pytest.mark.parametrize("what,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_every_planted_mistake_fails_a_pin(what, old, new, tmp_path, restore_oracle):
-    src = open(oracle.SRC).read()
-    assert src.count(old) == 1, f"mutation site for '{what}' not unique in the oracle source"
-    path = os.path.join(tmp_path, "mutant.c")
+_CHILD = """
+import sys
+sys.path[:0] = {paths!r}
+import oracle
+oracle.use_library({so!r})
+import test_oracle_mutants as M
+for fn, args in M.CHECKS:
+    if M._caught(fn, args):
+        print("caught by", fn.__name__, flush=True)
+        sys.exit(0)
+sys.exit(1)
+"""
+
+
+def _run_mutant(src: str, what: str, old: str, new: str, work: str) -> str:
+    i = [m[0] for m in MUTANTS].index(what)
+    path = os.path.join(work, f"mutant{i}.c")
     with open(path, "w") as f:
         f.write(src.replace(old, new))
-    so = oracle.build(src=path, out=os.path.join(tmp_path, "libmutant.so"), opt="-O1")
-    oracle.use_library(so)
-    try:
-        assert any(_caught(fn, args) for fn, args in CHECKS), f"no pin caught: {what}"
-    finally:
-        oracle.use_library(None)
+    so = oracle.build(src=path, out=os.path.join(work, f"libmutant{i}.so"), opt="-O1")
+    here = os.path.dirname(os.path.abspath(__file__))
+    paths = [here, os.path.dirname(here)]
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _CHILD.format(paths=paths, so=so)], capture_output=True, text=True,
+                       env=env, timeout=600)
+    if r.returncode == 0:
+        return "caught"
+    if r.returncode < 0:
+        return f"crashed (signal {-r.returncode})"
+    return "not caught:\n" + r.stdout[-2000:] + r.stderr[-2000:]
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    src = open(oracle.SRC).read()
+    for what, old, _ in MUTANTS:
+        assert src.count(old) == 1, f"mutation site for '{what}' not unique in the oracle source"
+    work = str(tmp_path_factory.mktemp("mutants"))
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        futs = {what: ex.submit(_run_mutant, src, what, old, new, work) for what, old, new in MUTANTS}
+        return {what: f.result() for what, f in futs.items()}
+
+
+@pytest.mark.parametrize("what", [m[0] for m in MUTANTS])
+def test_every_planted_mistake_fails_a_pin(what, mutant_results):
+    res = mutant_results[what]
+    assert res == "caught" or res.startswith("crashed"), f"no pin caught: {what}: {res}"
