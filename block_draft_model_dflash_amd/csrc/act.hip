@@ -166,9 +166,21 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
     }
     return;
   }
+  // this column's value and weight travel while the row's scale is formed
+  const float hv = i < N ? h[(size_t)m * N + i] : 0.f, wv = i < N ? w[i] : 0.f;
   if (tid < 64) {
+    constexpr int PB = 8;  // pieces each lane loads at once
     double t = 0.0;
-    for (int p = lane; p < nparts; p += 64) t += ssq[(size_t)m * nparts + p];
+    for (int p0 = lane; p0 < nparts; p0 += 64 * PB) {
+      double v[PB];
+#pragma unroll
+      for (int b = 0; b < PB; b++) {
+        const int p = p0 + 64 * b;
+        v[b] = p < nparts ? ssq[(size_t)m * nparts + p] : 0.0;
+      }
+#pragma unroll
+      for (int b = 0; b < PB; b++) t += v[b];
+    }
 #pragma unroll
     for (int o = 32; o; o >>= 1) t += __shfl_xor(t, o);
     if (lane == 0) sc_sh = 1.0f / sqrtf((float)(t / (double)N) + eps);
@@ -176,7 +188,7 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
   __syncthreads();
   if (i >= N) return;  // N is a multiple of 32: whole A8 groups leave together
   const float sc = sc_sh;
-  const float y = (h[(size_t)m * N + i] * sc) * w[i];
+  const float y = (hv * sc) * wv;
   if (QUANT)
     emit_q(y, (size_t)m * N + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
   else

@@ -24,7 +24,7 @@ namespace {
 
 constexpr int APPEND_CHUNK = 128;  // context rows per append pass (8 row tiles of 16)
 constexpr int MROWS = 128;         // activation rows the workspace holds
-constexpr int MAXCH = 64;          // attention chunks per (sequence, kv head)
+constexpr int MAXCH = ATTN_MAXCH;  // attention chunks per (sequence, kv head)
 
 thread_local std::string g_create_err;  // last error of a call without a ctx
 
@@ -346,15 +346,14 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
       {
         StageTimer tc(c, DFLASH_STAGE_ATTN_CHUNKS);
         TRY_HIP(c,
-                launch_attention_chunks(as, si, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
-                                        c->at<float>(L.kc) + (size_t)l * layer_cache,
+                launch_attention_chunks(as, si, c->at<float>(L.q), c->at<float>(L.kc) + (size_t)l * layer_cache,
                                         c->at<float>(L.vc) + (size_t)l * layer_cache, c->at<double>(L.apart),
                                         c->at<double>(L.aml), c->st),
                 "attention chunks");
       }
       TRY_HIP(c,
-              launch_attention_merge(as, si, c->at<double>(L.apart), c->at<double>(L.aml), Mpad, bq, xq, dxT, xf,
-                                     c->st),
+              launch_attention_merge(as, si, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
+                                     c->at<double>(L.apart), c->at<double>(L.aml), Mpad, bq, xq, dxT, xf, c->st),
               "attention merge");
     }
     const bool last = l + 1 == NL;

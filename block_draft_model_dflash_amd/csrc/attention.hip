@@ -7,9 +7,10 @@
 // (max, sum, acc) per query in registers (online softmax), and a merge combines the chunks.
 // A workgroup serves one (sequence, kv head, chunk) with eight waves: wave w takes q head w % 4
 // of the group and the chunk's even (w < 4) or odd (w >= 4) 16-key tiles; the two halves of a
-// head are combined in LDS before the chunk's result is written.  The block's own rows form one
-// more tile at the end of the sequence's last chunk.  The 16 block rows of a head are the 16
-// columns of v_mfma_f64_16x16x4f64 tiles:
+// head are combined in LDS before the chunk's result is written.  The chunks hold context rows
+// only (so every key lane of the grid gets the same number of tiles); the block's own 16 keys,
+// a few thousand flops per (head, row), are scored by the merge, which then combines them with
+// the chunks.  The 16 block rows of a head are the 16 columns of v_mfma_f64_16x16x4f64 tiles:
 //   S^T[key][q] = K . Q^T   (A = 16 keys staged in LDS, B = the wave's queries in registers)
 //   Y^T[d][q]  += V^T . P^T (A = 16-dim slices of V from LDS, B = the wave's probabilities,
 //                            already in the accumulator layout of S^T)
@@ -31,13 +32,11 @@ typedef double v4d __attribute__((ext_vector_type(4)));
 constexpr int ATTN_HEADS = 4;                   // q heads served at once (one wave each per half)
 constexpr int ATTN_THREADS = 64 * 2 * ATTN_HEADS;  // two key halves
 
-// Chunks a sequence with n context rows takes: ceil(n / ck), and at least one for the block rows.
-__device__ __forceinline__ int attn_chunks(int nctx, int ck) { return nctx > 0 ? (nctx + ck - 1) / ck : 1; }
+// Chunks a sequence with n context rows takes (the block's own rows are the merge's part).
+__device__ __forceinline__ int attn_chunks(int nctx, int ck) { return nctx > 0 ? (nctx + ck - 1) / ck : 0; }
 
 template <int HD>
 __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqInfo si, const float* __restrict__ q,
-                                                               const float* __restrict__ kb,
-                                                               const float* __restrict__ vb,
                                                                const float* __restrict__ kc,
                                                                const float* __restrict__ vc,
                                                                double* __restrict__ part, double* __restrict__ ml) {
@@ -61,14 +60,10 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
   float* Ks = (float*)lds + half * 2 * TILE;
   float* Vs = Ks + TILE;
   const int k0 = c * a.ck, kend = min(nctx, k0 + a.ck);
-  const int nt_ctx = kend > k0 ? (kend - k0 + 15) / 16 : 0;
-  const int nt = nt_ctx + (c == nch - 1 ? 1 : 0);  // the last chunk also takes the block's rows
+  const int nt = (kend - k0 + 15) / 16;  // >= 1: every launched chunk holds context rows
   const int rounds = (nt + 1) / 2;
   const float* Kctx = kc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
   const float* Vctx = vc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
-  const float* Kblk = kb + ((size_t)s * a.B * a.kvh + g) * HD;
-  const float* Vblk = vb + ((size_t)s * a.B * a.kvh + g) * HD;
-  const size_t bstride = (size_t)a.kvh * HD;
 
   // the group's q heads, ATTN_HEADS at a time; the chunk's keys are re-staged per round when a
   // group has more heads than that
@@ -86,24 +81,19 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
 #pragma unroll
     for (int dt = 0; dt < HD / 16; dt++) acc[dt] = (v4d){0.0, 0.0, 0.0, 0.0};
 
-    // tile i of the chunk: context keys k0 + 16i.. while i < nt_ctx, else the block's rows; the
-    // next tile of this half travels to registers while the current one is computed
+    // tile i of the chunk: context keys k0 + 16i..; the next tile of this half travels to
+    // registers while the current one is computed
     v4f pk[NL], pv[NL];
     auto fetch = [&](int i) {
 #pragma unroll
       for (int u = 0; u < NL; u++) {
         const int e = htid + u * HALF;
         const int r = e / (HD / 4), c4 = e % (HD / 4);
+        const int key = k0 + 16 * i + r;
         pk[u] = pv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-        if (i < nt_ctx) {
-          const int key = k0 + 16 * i + r;
-          if (key < kend) {
-            pk[u] = *(const v4f*)(Kctx + (size_t)key * HD + 4 * c4);
-            pv[u] = *(const v4f*)(Vctx + (size_t)key * HD + 4 * c4);
-          }
-        } else if (i < nt && r < a.B) {
-          pk[u] = *(const v4f*)(Kblk + (size_t)r * bstride + 4 * c4);
-          pv[u] = *(const v4f*)(Vblk + (size_t)r * bstride + 4 * c4);
+        if (i < nt && key < kend) {
+          pk[u] = *(const v4f*)(Kctx + (size_t)key * HD + 4 * c4);
+          pv[u] = *(const v4f*)(Vctx + (size_t)key * HD + 4 * c4);
         }
       }
     };
@@ -121,7 +111,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
       __syncthreads();
       if (i + 2 < nt) fetch(i + 2);
       if (!live || i >= nt) continue;
-      const int nvalid = i < nt_ctx ? min(16, kend - (k0 + 16 * i)) : a.B;  // keys of this tile
+      const int nvalid = min(16, kend - (k0 + 16 * i));  // keys of this tile
       v4d st0 = (v4d){0.0, 0.0, 0.0, 0.0}, st1 = st0;
 #pragma unroll
       for (int i4 = 0; i4 < HD / 16; i4++) {
@@ -232,104 +222,175 @@ __device__ __forceinline__ void emit_q8(float y, size_t qi, int8_t* __restrict__
   if ((lane & 31) == 0) dx[di] = d;
 }
 
-// One workgroup of four waves per (q head, block row, sequence) combines the chunks' (max,
-// sum, acc): the lanes first find the largest chunk maximum, then wave w adds the chunks
-// c = w mod 4 weighted by exp(m_c - max), and the four waves' sums are added in wave order.
-constexpr int MERGE_WAVES = 4;
+// One workgroup per (q head, block row, sequence) finishes the row: it scores the block's own
+// keys (f64 dot products of the f32 query and keys, then the same scale), takes the common
+// maximum of those scores and of the chunks' maxima, and adds the block's values and the
+// chunks' partial sums with weights exp(m - max) in a fixed order.  Every load (the chunk
+// partials, the block's keys and values, the query) is issued before the first wait.
+constexpr int MERGE_THREADS = 256;
 template <int HD, bool QUANT>
-__global__ __launch_bounds__(64 * MERGE_WAVES) void k_attn_merge(AttnShape a, SeqInfo si,
-                                                                const double* __restrict__ part,
-                                                                const double* __restrict__ ml, int Mpad,
-                                                                int8_t* __restrict__ xq, float* __restrict__ dxT,
-                                                                float* __restrict__ xf) {
-  __shared__ double ys[MERGE_WAVES][HD];
-  __shared__ double ls[MERGE_WAVES];
-  const int j = blockIdx.x, r = blockIdx.y, s = blockIdx.z, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqInfo si, const float* __restrict__ q,
+                                                              const float* __restrict__ kb,
+                                                              const float* __restrict__ vb,
+                                                              const double* __restrict__ part,
+                                                              const double* __restrict__ ml, int Mpad,
+                                                              int8_t* __restrict__ xq, float* __restrict__ dxT,
+                                                              float* __restrict__ xf) {
+  constexpr int NG = MERGE_THREADS / HD;       // chunk groups: thread (d, gi) adds chunks gi, gi+NG, ...
+  constexpr int CPG = ATTN_MAXCH / NG;         // chunks per group at most
+  constexpr int KSL = HD / 16;                 // dims per thread of a block score (16 threads a key)
+  constexpr int VPG = 16 / NG;                 // block values per thread
+  __shared__ double s_sc[16];                  // block scores
+  __shared__ double s_e[16 + ATTN_MAXCH];      // weights: block keys, then chunks
+  __shared__ double s_y[NG][HD];
+  __shared__ double s_l;
+  const int j = blockIdx.x, r = blockIdx.y, s = blockIdx.z, tid = threadIdx.x, lane = tid & 63;
   const int rep = a.nh / a.kvh, g = j / rep, hw = j % rep;
   const int nch = attn_chunks(si.nctx[s], a.ck);
-  const size_t base = (((size_t)s * a.kvh + g) * a.maxch) * rep;
+  const int d = tid % HD, gi = tid / HD;
+  const size_t base = ((size_t)s * a.kvh + g) * a.maxch * rep;
   auto row_of = [&](int c) { return (base + (size_t)c * rep + hw) * 16 + r; };
-  double mx = -INFINITY;
-  for (int c = lane; c < nch; c += 64) mx = fmax(mx, ml[row_of(c) * 2]);
-#pragma unroll
-  for (int o = 32; o; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
-  double L = 0.0, y[HD / 64];
-#pragma unroll
-  for (int t = 0; t < HD / 64; t++) y[t] = 0.0;
-#pragma unroll 4
-  for (int c = w; c < nch; c += MERGE_WAVES) {
-    const size_t row = row_of(c);
-    const double e = exp(ml[row * 2] - mx);
-    L += ml[row * 2 + 1] * e;
-#pragma unroll
-    for (int t = 0; t < HD / 64; t++) y[t] += part[row * HD + lane + 64 * t] * e;
-  }
-#pragma unroll
-  for (int t = 0; t < HD / 64; t++) ys[w][lane + 64 * t] = y[t];
-  if (lane == 0) ls[w] = L;
-  __syncthreads();
-  if (w != 0) return;
-  double Lt = ls[0];
-  for (int v = 1; v < MERGE_WAVES; v++) Lt += ls[v];
   const int m = s * a.B + r;
-  const size_t qd = (size_t)a.nh * HD;
+
+  // loads, all unconditional (indices clamped into range; what lies past the end is not used)
+  // so they are in flight together
+  double accp[CPG];
+  const int clast = nch > 0 ? nch - 1 : 0;
 #pragma unroll
-  for (int t = 0; t < HD / 64; t++) {
-    double yt = ys[0][lane + 64 * t];
-    for (int v = 1; v < MERGE_WAVES; v++) yt += ys[v][lane + 64 * t];
-    const float val = (float)(yt / Lt);
-    const size_t colx = (size_t)j * HD + lane + 64 * t;
-    if (QUANT)
-      emit_q8(val, (size_t)m * qd + colx, xq, dxT, (colx >> 5) * Mpad + m, lane);
-    else
-      xf[(size_t)m * qd + colx] = val;
+  for (int k = 0; k < CPG; k++) {
+    const int c = min(gi + k * NG, clast);
+    accp[k] = nch > 0 ? part[row_of(c) * HD + d] : 0.0;
   }
+  const int key = tid >> 4, sl = tid & 15;
+  const int keyc = min(key, a.B - 1);
+  v4f qv[KSL / 4], kv[KSL / 4];
+#pragma unroll
+  for (int e = 0; e < KSL / 4; e++) {
+    qv[e] = *(const v4f*)(q + ((size_t)m * a.nh + j) * HD + sl * KSL + 4 * e);
+    kv[e] = *(const v4f*)(kb + ((size_t)(s * a.B + keyc) * a.kvh + g) * HD + sl * KSL + 4 * e);
+  }
+  float vv[VPG];
+#pragma unroll
+  for (int k = 0; k < VPG; k++) {
+    const int i = min(gi + NG * k, a.B - 1);
+    vv[k] = vb[((size_t)(s * a.B + i) * a.kvh + g) * HD + d];
+  }
+  const int cm = min(tid, clast);
+  double mc = ml[row_of(cm) * 2], lc = ml[row_of(cm) * 2 + 1];
+  if (tid >= nch) {
+    mc = -INFINITY;
+    lc = 0.0;
+  }
+
+  // the block's scores: f32 products are exact in f64
+  double sc = 0.0;
+#pragma unroll
+  for (int e = 0; e < KSL / 4; e++)
+#pragma unroll
+    for (int f = 0; f < 4; f++) sc += (double)qv[e][f] * (double)kv[e][f];
+  sc += __shfl_xor(sc, 1);
+  sc += __shfl_xor(sc, 2);
+  sc += __shfl_xor(sc, 4);
+  sc += __shfl_xor(sc, 8);
+  if (sl == 0 && key < a.B) s_sc[key] = sc * (double)a.scale;
+  if (tid < nch) s_e[16 + tid] = mc;
+  __syncthreads();
+
+  // the common maximum, the weights and the denominator (wave 0)
+  if (tid < 64) {
+    double mx = tid < a.B ? s_sc[tid] : -INFINITY;
+    if (tid < nch) mx = fmax(mx, s_e[16 + tid]);
+#pragma unroll
+    for (int o = 32; o; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    double lsum = 0.0;
+    if (tid < a.B) {
+      const double e = exp(s_sc[tid] - mx);
+      s_e[tid] = e;
+      lsum = e;
+    }
+    if (tid < nch) {
+      const double e = exp(mc - mx);
+      s_e[16 + tid] = e;
+      lsum += lc * e;
+    }
+#pragma unroll
+    for (int o = 32; o; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (tid == 0) s_l = lsum;
+  }
+  __syncthreads();
+
+  double y = 0.0;
+#pragma unroll
+  for (int k = 0; k < CPG; k++) {
+    const int c = gi + k * NG;
+    if (c < nch) y += accp[k] * s_e[16 + c];
+  }
+#pragma unroll
+  for (int k = 0; k < VPG; k++) {
+    const int i = gi + NG * k;
+    if (i < a.B) y += (double)vv[k] * s_e[i];
+  }
+  s_y[gi][d] = y;
+  __syncthreads();
+  if (gi != 0) return;  // threads d < HD: whole waves
+  double yt = s_y[0][d];
+#pragma unroll
+  for (int v = 1; v < NG; v++) yt += s_y[v][d];
+  const float val = (float)(yt / s_l);
+  const size_t qd = (size_t)a.nh * HD;
+  const size_t colx = (size_t)j * HD + d;
+  if (QUANT)
+    emit_q8(val, (size_t)m * qd + colx, xq, dxT, (colx >> 5) * Mpad + m, lane);
+  else
+    xf[(size_t)m * qd + colx] = val;
 }
 
 template <int HD>
-static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
-                                  const float* vb, const float* kc, const float* vc, double* part, double* ml,
-                                  hipStream_t st) {
+static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kc,
+                                  const float* vc, double* part, double* ml, hipStream_t st) {
   int maxn = 0;
   for (int i = 0; i < si.n; i++) {
-    const int nch = si.nctx[i] > 0 ? (si.nctx[i] + a.ck - 1) / a.ck : 1;
+    const int nch = si.nctx[i] > 0 ? (si.nctx[i] + a.ck - 1) / a.ck : 0;
     if (nch > maxn) maxn = nch;
   }
   if (maxn > a.maxch) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn, a.kvh, si.n), dim3(ATTN_THREADS), 0, st, a, si, q, kb, vb, kc, vc,
-                     part, ml);
+  if (maxn == 0) return hipSuccess;  // no sequence has context rows: the merge does it all
+  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn, a.kvh, si.n), dim3(ATTN_THREADS), 0, st, a, si, q, kc, vc, part,
+                     ml);
   return hipGetLastError();
 }
 
 template <int HD>
-static hipError_t attn_merge_hd(const AttnShape& a, const SeqInfo& si, const double* part, const double* ml, int Mpad,
-                                bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st) {
+static hipError_t attn_merge_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
+                                const float* vb, const double* part, const double* ml, int Mpad, bool quant,
+                                int8_t* xq, float* dxT, float* xf, hipStream_t st) {
   if (quant)
-    hipLaunchKernelGGL((k_attn_merge<HD, true>), dim3(a.nh, a.B, si.n), dim3(64 * MERGE_WAVES), 0, st, a, si, part,
-                       ml, Mpad, xq, dxT, xf);
+    hipLaunchKernelGGL((k_attn_merge<HD, true>), dim3(a.nh, a.B, si.n), dim3(MERGE_THREADS), 0, st, a, si, q, kb, vb,
+                       part, ml, Mpad, xq, dxT, xf);
   else
-    hipLaunchKernelGGL((k_attn_merge<HD, false>), dim3(a.nh, a.B, si.n), dim3(64 * MERGE_WAVES), 0, st, a, si, part,
-                       ml, Mpad, xq, dxT, xf);
+    hipLaunchKernelGGL((k_attn_merge<HD, false>), dim3(a.nh, a.B, si.n), dim3(MERGE_THREADS), 0, st, a, si, q, kb,
+                       vb, part, ml, Mpad, xq, dxT, xf);
   return hipGetLastError();
 }
 
 static bool attn_shape_ok(const AttnShape& a) {
-  return !(a.nh % a.kvh || a.nh / a.kvh > 16 || a.B > 16 || a.ck % 32 || a.ck <= 0) && (a.hd == 64 || a.hd == 128);
+  return !(a.nh % a.kvh || a.nh / a.kvh > 16 || a.B > 16 || a.ck % 32 || a.ck <= 0 || a.maxch > ATTN_MAXCH) &&
+         (a.hd == 64 || a.hd == 128);
 }
 
-hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
-                                   const float* vb, const float* kc, const float* vc, double* part, double* ml,
-                                   hipStream_t st) {
+hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const float* kc,
+                                   const float* vc, double* part, double* ml, hipStream_t st) {
   if (!attn_shape_ok(a)) return hipErrorInvalidValue;
-  if (a.hd == 64) return attn_partial_hd<64>(a, si, q, kb, vb, kc, vc, part, ml, st);
-  return attn_partial_hd<128>(a, si, q, kb, vb, kc, vc, part, ml, st);
+  if (a.hd == 64) return attn_partial_hd<64>(a, si, q, kc, vc, part, ml, st);
+  return attn_partial_hd<128>(a, si, q, kc, vc, part, ml, st);
 }
 
-hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const double* part, const double* ml,
-                                  int Mpad, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st) {
+hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
+                                  const float* vb, const double* part, const double* ml, int Mpad, bool quant,
+                                  int8_t* xq, float* dxT, float* xf, hipStream_t st) {
   if (!attn_shape_ok(a)) return hipErrorInvalidValue;
-  if (a.hd == 64) return attn_merge_hd<64>(a, si, part, ml, Mpad, quant, xq, dxT, xf, st);
-  return attn_merge_hd<128>(a, si, part, ml, Mpad, quant, xq, dxT, xf, st);
+  if (a.hd == 64) return attn_merge_hd<64>(a, si, q, kb, vb, part, ml, Mpad, quant, xq, dxT, xf, st);
+  return attn_merge_hd<128>(a, si, q, kb, vb, part, ml, Mpad, quant, xq, dxT, xf, st);
 }
 
 }  // namespace dfl

@@ -116,13 +116,15 @@ struct AttnShape {
   int nh, kvh, hd, B, max_ctx, max_seqs, ck, maxch;
   float scale;
 };
-// The chunk kernel writes per-chunk (max, sum, acc) in f64 to part/ml; the merge combines a
-// sequence's chunks per (q head, row) and writes the f32 result (A8 into xq/dxT, or f32 xf).
-hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
-                                   const float* vb, const float* kc, const float* vc, double* part, double* ml,
-                                   hipStream_t st);
-hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const double* part, const double* ml,
-                                  int Mpad, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st);
+// The chunk kernel writes per-chunk (max, sum, acc) of the context keys in f64 to part/ml; the
+// merge scores the block's own keys, combines them with a sequence's chunks per (q head, row)
+// and writes the f32 result (A8 into xq/dxT, or f32 xf).
+constexpr int ATTN_MAXCH = 64;  // context chunks per (sequence, kv head) at most
+hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const float* kc,
+                                   const float* vc, double* part, double* ml, hipStream_t st);
+hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
+                                  const float* vb, const double* part, const double* ml, int Mpad, bool quant,
+                                  int8_t* xq, float* dxT, float* xf, hipStream_t st);
 
 // Dynamic LDS a workgroup may use on the current device (queried once per device), and a
 // helper that raises a kernel's dynamic-LDS limit when a launch needs more than the default.

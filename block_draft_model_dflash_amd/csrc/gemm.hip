@@ -122,7 +122,12 @@ struct Ring {
 // chunk of kcb k-blocks (a multiple of the ring's step, so the ring runs on across chunks) are
 // staged in LDS and shared by all waves.  The k-waves' f64 sums are then added in wave order
 // through LDS (the same order on every run) and wave kw = 0 applies the epilogue.
-template <int FMT, int MT, int NTW, int KW>
+//
+// TURNS > 0: every chunk holds exactly TURNS ring turns (the last one may run past the tile,
+// where the slots read zeros), so the ring is straight-line code and the compiler counts the
+// loads in flight exactly; TURNS = 0 is the same with a runtime loop (shapes smaller than one
+// full chunk).
+template <int FMT, int MT, int NTW, int KW, int TURNS>
 __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restrict__ W, int N, int K,
                                                          const int8_t* __restrict__ xq,
                                                          const float* __restrict__ dxT, int kcb, GemmOut o) {
@@ -134,7 +139,9 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   const int ASTR = kcb * 128 + 16;  // padded LDS row: rows land 4 banks apart
   int8_t* A = (int8_t*)smem;
   float* DX = (float*)(smem + MR * ASTR);  // [kcb*4 groups][MR] activation scales
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across the wave: saying so keeps the weight tile's buffer
+  // resource in scalar registers (no per-lane descriptor loop around each load)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = wave % NTW, kw = wave / NTW;
   const int ntile = blockIdx.x * NTW + nt;
   const bool active = ntile < (N >> 4);
@@ -147,6 +154,18 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   for (int mt = 0; mt < MT; mt++)
 #pragma unroll
     for (int r = 0; r < 4; r++) acc[mt][r] = 0.0;
+
+  // the residual rows the epilogue adds to, loaded first (they are needed only at the end)
+  float hres[MT][4];
+  if (o.epi == EPI_RESID && kw == 0 && active) {
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int m = mt * 16 + 4 * quarter + q;
+        hres[mt][q] = m < o.M ? o.h[(size_t)m * N + ntile * 16 + row16] : 0.f;
+      }
+  }
 
   // the ring is filled before the first activations are staged, so the weights' HBM latency
   // overlaps the staging; a superblock past the tile reads as zeros and costs nothing
@@ -194,12 +213,19 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
     }
     __syncthreads();
     if (!active) continue;
-    for (int kb = c0 + kw; kb < c1; kb += STEP) {
+    // no branch in the ring: a chunk before the last holds whole ring turns (kcb is a multiple
+    // of STEP), so a slot past c1 only occurs past the tile's end, where it holds zeros and adds
+    // exactly 0 (its LDS reads are clamped into the staged range, which holds finite values)
+    constexpr int UNROLL = TURNS > 0 ? TURNS : 1;
+    const int turns = TURNS > 0 ? TURNS : (c1 - c0 - kw + STEP - 1) / STEP;
+#pragma unroll UNROLL
+    for (int t = 0; t < turns; t++) {
+      const int kb = c0 + kw + t * STEP;
 #pragma unroll
       for (int p = 0; p < RD; p++) {
         const int kbp = kb + p * KW;
-        if (kbp < c1) {
-          const int kk = kbp - c0;
+        {
+          const int kk = min(kbp, c1 - 1) - c0;
 #pragma unroll MT <= 2 ? 4 : 1
           for (int j = 0; j < 4; j++) {
             const long b = b_operand(r[p], j);
@@ -283,7 +309,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
       } else {  // EPI_RESID: h += f32(v), and the tile's share of each row's sum of squares
         double sq = 0.0;
         if (m < o.M) {
-          const float hv = o.h[(size_t)m * N + n] + (float)v;
+          const float hv = hres[mt][q] + (float)v;
           o.h[(size_t)m * N + n] = hv;
           sq = (double)hv * (double)hv;
         }
@@ -342,24 +368,32 @@ template <int FMT, int MT, int NTW, int KW>
 static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
                             hipStream_t st) {
   constexpr int MR = MT * 16, STEP = Ring<MT, KW>::step;
-  const int KB = K / 128;
   // LDS of a chunk of kcb k-blocks: MR rows of kcb*128 codes (+16 B row padding) and kcb*4*MR
   // f32 scales; about 76 KB so two workgroups share a CU
-  const size_t per_kb = (size_t)MR * 144;
-  int kcb = (int)((76 * 1024 - (size_t)MR * 16) / per_kb) / STEP * STEP;
-  if (kcb < STEP) kcb = STEP;
-  if (kcb > KB) kcb = KB;
+  constexpr size_t PER_KB = (size_t)MR * 144;
+  constexpr int KCB_FULL = (int)((76 * 1024 - (size_t)MR * 16) / PER_KB) / STEP * STEP;
+  constexpr int KCB = KCB_FULL < STEP ? STEP : KCB_FULL;
+  const int KB = K / 128;
+  const int kcb = KCB > KB ? KB : KCB;
   size_t lds = (size_t)MR * (kcb * 128 + 16) + (size_t)kcb * 4 * MR * 4;
   const size_t red = (size_t)(KW - 1) * NTW * MT * 4 * 64 * 8;
   const size_t swg = (size_t)MR * 64 * 4;
   if (red > lds) lds = red;
   if (swg > lds) lds = swg;
   if (lds > max_dynamic_lds()) return hipErrorInvalidValue;
-  hipError_t e = allow_lds((const void*)k_gemm_q<FMT, MT, NTW, KW>, lds);
+  // whole chunks of whole ring turns take the unrolled kernel
+  const bool unrolled = kcb == KCB && KCB % STEP == 0;
+  const void* kern = unrolled ? (const void*)k_gemm_q<FMT, MT, NTW, KW, KCB / STEP>
+                              : (const void*)k_gemm_q<FMT, MT, NTW, KW, 0>;
+  hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)ceil_div(N / 16, NTW));
-  hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW>), grid, dim3(64 * NTW * KW), lds, st, (const uint8_t*)W, N, K, xq,
-                     dxT, kcb, o);
+  if (unrolled)
+    hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW, KCB / STEP>), grid, dim3(64 * NTW * KW), lds, st,
+                       (const uint8_t*)W, N, K, xq, dxT, kcb, o);
+  else
+    hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW, 0>), grid, dim3(64 * NTW * KW), lds, st, (const uint8_t*)W, N, K,
+                       xq, dxT, kcb, o);
   return hipGetLastError();
 }
 
