@@ -40,8 +40,11 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
                                                                const float* __restrict__ kc,
                                                                const float* __restrict__ vc,
                                                                double* __restrict__ part, double* __restrict__ ml) {
-  constexpr int KS = HD + 4;           // padded LDS key row (floats)
-  constexpr int TILE = 16 * KS;        // one 16-key tile of K (or V)
+  // LDS rows: keys HD + 4 floats apart (each 16-lane group of a 128-bit read covers all banks),
+  // values HD + 1 apart (the 64 lanes' 32-bit reads of rows 4k + quarter, columns 4*col + e
+  // fall in 64 different banks)
+  constexpr int KS = HD + 4, VS = HD + 1;
+  constexpr int TILE = 16 * KS;        // one 16-key tile of K (V uses 16 * VS <= TILE)
   constexpr int HALF = ATTN_THREADS / 2;
   constexpr int NL = 16 * (HD / 4) / HALF;  // float4 of K (and of V) each thread stages per tile
   constexpr int CD = 64;                    // dims combined per LDS round
@@ -106,7 +109,8 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
         const int e = htid + u * HALF;
         const int r = e / (HD / 4), c4 = e % (HD / 4);
         *(v4f*)(Ks + r * KS + 4 * c4) = pk[u];
-        *(v4f*)(Vs + r * KS + 4 * c4) = pv[u];
+#pragma unroll
+        for (int f = 0; f < 4; f++) Vs[r * VS + 4 * c4 + f] = pv[u][f];
       }
       __syncthreads();
       if (i + 2 < nt) fetch(i + 2);
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
 #pragma unroll
         for (int k = 0; k < 4; k++) {
           // step k pairs the probabilities of slot k (keys quarter + 4k) with those keys' values
-          const float va = Vs[(4 * k + quarter) * KS + 64 * (dt >> 2) + 4 * col + (dt & 3)];
+          const float va = Vs[(4 * k + quarter) * VS + 64 * (dt >> 2) + 4 * col + (dt & 3)];
           acc[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va, p[k], acc[dt], 0, 0, 0);
         }
       }

@@ -59,14 +59,16 @@ constexpr int RSRC_WORD3 = 0x00020000;  // raw (untyped) buffer access, gfx9-fam
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const uint8_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, RSRC_WORD3);
 }
+// `off` (the superblock's byte offset) is the same for the whole wave and goes in the scalar
+// offset; only the lane's position within the superblock is a vector offset.
 __device__ __forceinline__ void super_load(__amdgpu_buffer_rsrc_t rs, int off, int lane, Super<Q4>& r) {
-  r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * lane, 0, 0));
-  r.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + SB_SCALES_Q4 + 8 * (lane & 15), 0, 0));
+  r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, off, 0));
+  r.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, SB_SCALES_Q4 + 8 * (lane & 15), off, 0));
 }
 __device__ __forceinline__ void super_load(__amdgpu_buffer_rsrc_t rs, int off, int lane, Super<Q8>& r) {
-  r.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * lane, 0, 0));
-  r.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 1024 + 16 * lane, 0, 0));
-  r.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + SB_SCALES_Q8 + 8 * (lane & 15), 0, 0));
+  r.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, off, 0));
+  r.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 + 16 * lane, off, 0));
+  r.s = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, SB_SCALES_Q8 + 8 * (lane & 15), off, 0));
 }
 
 __device__ __forceinline__ uint32_t pick(uint4 v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
@@ -130,7 +132,8 @@ struct Ring {
 template <int FMT, int MT, int NTW, int KW, int TURNS>
 __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restrict__ W, int N, int K,
                                                          const int8_t* __restrict__ xq,
-                                                         const float* __restrict__ dxT, int kcb, GemmOut o) {
+                                                         const float* __restrict__ dxT, int kcb, int RG,
+                                                         GemmOut o) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int MR = MT * 16;
   constexpr int SBB = FMT == Q4 ? SB_Q4 : SB_Q8;
@@ -143,7 +146,10 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   // resource in scalar registers (no per-lane descriptor loop around each load)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = wave % NTW, kw = wave / NTW;
-  const int ntile = blockIdx.x * NTW + nt;
+  // blockIdx.x = n-block * RG + row group: the row groups of one n-block are neighbours in the
+  // grid, so they ask for the same weights at about the same time (one HBM read, cache hits)
+  const int rg = blockIdx.x % RG, nb = blockIdx.x / RG, m0 = rg * MR;
+  const int ntile = nb * NTW + nt;
   const bool active = ntile < (N >> 4);
   const int KB = K >> 7, Mpad = o.Mpad;
   const uint8_t* wt = W + (size_t)(active ? ntile : 0) * KB * SBB;
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
     for (int mt = 0; mt < MT; mt++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int m = mt * 16 + 4 * quarter + q;
+        const int m = m0 + mt * 16 + 4 * quarter + q;
         hres[mt][q] = m < o.M ? o.h[(size_t)m * N + ntile * 16 + row16] : 0.f;
       }
   }
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
         const int i = i0 + b * NT;
         const int rr = i / v16, c = i - rr * v16;
         v[b] = (uint4){0u, 0u, 0u, 0u};
-        if (i < nv && rr < Mpad) v[b] = *(const uint4*)(xq + (size_t)rr * K + (size_t)c0 * 128 + c * 16);
+        if (i < nv && m0 + rr < Mpad) v[b] = *(const uint4*)(xq + (size_t)(m0 + rr) * K + (size_t)c0 * 128 + c * 16);
       }
 #pragma unroll
       for (int b = 0; b < SB; b++) {
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
       for (int b = 0; b < SB; b++) {
         const int i = i0 + b * NT;
         const int g = i / MR, m = i - g * MR;
-        v[b] = (i < nd && m < Mpad) ? dxT[(size_t)(c0 * 4 + g) * Mpad + m] : 0.f;
+        v[b] = (i < nd && m0 + m < Mpad) ? dxT[(size_t)(c0 * 4 + g) * Mpad + m0 + m] : 0.f;
       }
 #pragma unroll
       for (int b = 0; b < SB; b++) {
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   const int n = ntile * 16 + row16;
 
   if (o.epi == EPI_SWIGLU) {
-    // NTW == 4: n-tiles gate(2b), up(2b), gate(2b+1), up(2b+1) of block b = blockIdx.x give the
+    // NTW == 4: n-tiles gate(2b), up(2b), gate(2b+1), up(2b+1) of n-block b = nb give the
     // 32 columns 32b.. of a = silu(gate) * up, one A8 group per row
     __syncthreads();
     float* G = (float*)smem;  // [MR][64]: the four tiles' f32 products
@@ -282,12 +288,12 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
     __syncthreads();
     const int I = N >> 1;
     for (int i = tid; i < MR * 32; i += NT) {
-      const int m = i >> 5, j = i & 31;
+      const int ml = i >> 5, j = i & 31, m = m0 + ml;
       if (m >= Mpad) break;  // whole 32-lane groups leave together
       const int gc = (j >> 4) * 32 + (j & 15);
-      const double g = G[m * 64 + gc], u = G[m * 64 + gc + 16];
+      const double g = G[ml * 64 + gc], u = G[ml * 64 + gc + 16];
       const float a = (float)(g / (1.0 + exp(-g)) * u);
-      const int c = blockIdx.x * 32 + j;
+      const int c = nb * 32 + j;
       if (o.xq)
         emit_q32(a, (size_t)m * I + c, o.xq, o.dxT, (size_t)(c >> 5) * Mpad + m, lane);
       else
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const int m = mt * 16 + 4 * quarter + q;
+      const int m = m0 + mt * 16 + 4 * quarter + q;
       const double v = acc[mt][q] * post;
       if (o.epi == EPI_F64) {
         if (m < Mpad) ((double*)o.y)[(size_t)m * N + n] = v;
@@ -353,11 +359,18 @@ __global__ __launch_bounds__(256) void k_group_sums(const uint8_t* __restrict__ 
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// activation rows a launch handles: Mpad rounded up to 16, 32, 64 or 128
-static int gemm_mt(int Mpad) { return Mpad <= 16 ? 1 : Mpad <= 32 ? 2 : Mpad <= 64 ? 4 : 8; }
+// rows one workgroup takes: 16 for up to 16 rows; more rows are split into groups of 16 (or 32
+// rows for products whose workgroups hold four n-tiles), each its own workgroup, so the
+// activations a workgroup stages stay small and the weights are shared through the caches
+static int gemm_mt(int Mpad, int layout) {
+  if (Mpad <= 16) return 1;
+  return layout == 1 ? 1 : 2;
+}
 
 int gemm_layout(int N, int Mpad, int epi) {
-  (void)Mpad;
+  // more than 16 rows already give a product with few n-tiles several workgroups per n-block
+  // (one per row group): four n-tiles x two k-waves then beats splitting K eight ways
+  if (Mpad > 16 && epi != EPI_SWIGLU && N / 16 < 2048) return 0;
   // thousands of n-tiles (the head, gate|up) stream without splitting K much; a product with
   // few n-tiles splits K over eight (four) waves so every CU has about eight waves in flight
   if (epi == EPI_SWIGLU) return 0;
@@ -387,13 +400,14 @@ static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const
                               : (const void*)k_gemm_q<FMT, MT, NTW, KW, 0>;
   hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)ceil_div(N / 16, NTW));
+  const int RG = ceil_div(o.Mpad, MR);
+  dim3 grid((unsigned)(ceil_div(N / 16, NTW) * RG));
   if (unrolled)
     hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW, KCB / STEP>), grid, dim3(64 * NTW * KW), lds, st,
-                       (const uint8_t*)W, N, K, xq, dxT, kcb, o);
+                       (const uint8_t*)W, N, K, xq, dxT, kcb, RG, o);
   else
     hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW, 0>), grid, dim3(64 * NTW * KW), lds, st, (const uint8_t*)W, N, K,
-                       xq, dxT, kcb, o);
+                       xq, dxT, kcb, RG, o);
   return hipGetLastError();
 }
 
@@ -411,12 +425,8 @@ static hipError_t gemm_mt_inst(int layout, const void* W, int N, int K, const in
 template <int FMT>
 static hipError_t gemm_fmt(int layout, const void* W, int N, int K, const int8_t* xq, const float* dxT,
                            const GemmOut& o, hipStream_t st) {
-  switch (gemm_mt(o.Mpad)) {
-    case 1: return gemm_mt_inst<FMT, 1>(layout, W, N, K, xq, dxT, o, st);
-    case 2: return gemm_mt_inst<FMT, 2>(layout, W, N, K, xq, dxT, o, st);
-    case 4: return gemm_mt_inst<FMT, 4>(layout, W, N, K, xq, dxT, o, st);
-    default: return gemm_mt_inst<FMT, 8>(layout, W, N, K, xq, dxT, o, st);
-  }
+  if (gemm_mt(o.Mpad, layout) == 1) return gemm_mt_inst<FMT, 1>(layout, W, N, K, xq, dxT, o, st);
+  return gemm_mt_inst<FMT, 2>(layout, W, N, K, xq, dxT, o, st);
 }
 
 hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int layout,
