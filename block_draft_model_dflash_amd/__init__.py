@@ -21,6 +21,7 @@ EXPORTS = [
     "dflash_ctx_reset", "dflash_ctx_span", "dflash_block_forward", "dflash_block_hidden", "dflash_last_error",
     "dflash_destroy", "dflash_quant_act", "dflash_packed_bytes", "dflash_pack", "dflash_gemm_scratch_bytes",
     "dflash_gemm", "dflash_group_sums", "dflash_read_kv", "dflash_time_stage", "dflash_read_timing",
+    "dflash_top_k_scratch_bytes", "dflash_top_k", "dflash_select_scratch_bytes", "dflash_select",
 ]
 (DFLASH_STAGE_HEAD, DFLASH_STAGE_QKV, DFLASH_STAGE_ATTENTION, DFLASH_STAGE_O, DFLASH_STAGE_GATE_UP, DFLASH_STAGE_DOWN,
  DFLASH_STAGE_BLOCK, DFLASH_STAGE_APPEND, DFLASH_STAGE_ATTN_CHUNKS) = range(9)
@@ -85,6 +86,10 @@ def lib():
             "dflash_read_kv": (i32, [vp, i32, i32, i32, i32, vp, vp]),
             "dflash_time_stage": (i32, [vp, i32]),
             "dflash_read_timing": (i32, [vp, i32, C.POINTER(C.c_double), C.POINTER(i64)]),
+            "dflash_top_k_scratch_bytes": (i32, [i32, i32, i32, C.POINTER(sz)]),
+            "dflash_top_k": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "dflash_select_scratch_bytes": (i32, [i32, i32, i32, C.POINTER(sz)]),
+            "dflash_select": (i32, [vp, i32, i32, i32, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -205,6 +210,28 @@ def dflash_read_timing(ctx, stage: int):
     ms, n = C.c_double(), C.c_int64()
     _check(lib().dflash_read_timing(ctx, stage, C.byref(ms), C.byref(n)), ctx)
     return ms.value, n.value
+
+
+def dflash_top_k_scratch_bytes(rows: int, width: int, k: int) -> int:
+    n = C.c_size_t()
+    _check(lib().dflash_top_k_scratch_bytes(rows, width, k, C.byref(n)))
+    return n.value
+
+
+def dflash_top_k(x: int, rows: int, width: int, ld: int, k: int, vals: int, idx: int, scratch: int, stream) -> int:
+    return _check(lib().dflash_top_k(x, rows, width, ld, k, vals, idx, scratch, stream))
+
+
+def dflash_select_scratch_bytes(rows: int, width: int, top: int) -> int:
+    n = C.c_size_t()
+    _check(lib().dflash_select_scratch_bytes(rows, width, top, C.byref(n)))
+    return n.value
+
+
+def dflash_select(logits: int, rows: int, width: int, ld: int, hp: int, rank: int, pred: int, succ: int, vocab: int,
+                  top: int, anchor: int, chosen: int, plain: int, scratch: int, stream) -> int:
+    return _check(lib().dflash_select(logits, rows, width, ld, hp, rank, pred, succ, vocab, top, anchor, chosen, plain,
+                                      scratch, stream))
 
 
 from .drafter import Drafter  # noqa: E402,F401  (torch-backed convenience wrapper)

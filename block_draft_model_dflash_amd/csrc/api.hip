@@ -776,3 +776,49 @@ int dflash_group_sums(int32_t fmt, const void* packed, int32_t rows, int32_t col
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int dflash_top_k_scratch_bytes(int32_t rows, int32_t width, int32_t k, size_t* bytes) {
+  if (!bytes || rows < 1 || width < 1 || k < 1 || k > 64 || k > width) return DFLASH_EINVAL;
+  *bytes = top_k_scratch(rows, width, k);
+  return DFLASH_OK;
+}
+
+int dflash_top_k(const float* x, int32_t rows, int32_t width, int32_t ld, int32_t k, float* vals, int32_t* idx,
+                 void* scratch, void* stream) {
+  size_t need;
+  if (!x || !vals || !idx || !scratch || ld < width || dflash_top_k_scratch_bytes(rows, width, k, &need))
+    return unit_fail(DFLASH_EINVAL, "top_k: arguments");
+  float* pv = (float*)scratch;
+  int* pi = (int*)((uint8_t*)scratch + need / 2);
+  hipError_t e = launch_top_k(x, rows, width, ld, k, pv, pi, vals, idx, (hipStream_t)stream);
+  return e == hipSuccess ? DFLASH_OK : unit_fail(DFLASH_EHIP, "top_k", e);
+}
+
+int dflash_select_scratch_bytes(int32_t rows, int32_t width, int32_t top, size_t* bytes) {
+  size_t tk;
+  if (!bytes || dflash_top_k_scratch_bytes(rows, width, top, &tk)) return DFLASH_EINVAL;
+  *bytes = tk + 2 * align256((size_t)rows * top * 4);
+  return DFLASH_OK;
+}
+
+int dflash_select(const float* logits, int32_t rows, int32_t width, int32_t ld, const float* hp, int32_t rank,
+                  const uint16_t* pred, const uint16_t* succ, int32_t vocab, int32_t top, int32_t anchor,
+                  int32_t* chosen, int32_t* plain, void* scratch, void* stream) {
+  size_t need, tk;
+  if (!logits || !hp || !pred || !succ || !chosen || !plain || !scratch || ld < width || width > vocab ||
+      rank < 1 || rank > 4096 || anchor < 0 || anchor >= vocab || dflash_select_scratch_bytes(rows, width, top, &need))
+    return unit_fail(DFLASH_EINVAL, "select: arguments");
+  dflash_top_k_scratch_bytes(rows, width, top, &tk);
+  hipStream_t st = (hipStream_t)stream;
+  float* pv = (float*)scratch;
+  int* pi = (int*)((uint8_t*)scratch + tk / 2);
+  float* cv = (float*)((uint8_t*)scratch + tk);
+  int* ci = (int*)((uint8_t*)scratch + tk + align256((size_t)rows * top * 4));
+  hipError_t e = launch_top_k(logits, rows, width, ld, top, pv, pi, cv, ci, st);
+  if (e == hipSuccess) e = launch_select(cv, ci, rows, top, hp, rank, pred, succ, anchor, chosen, plain, st);
+  return e == hipSuccess ? DFLASH_OK : unit_fail(DFLASH_EHIP, "select", e);
+}
+
+}  // extern "C"

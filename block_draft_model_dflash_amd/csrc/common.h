@@ -131,6 +131,15 @@ hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const f
 size_t max_dynamic_lds();
 hipError_t allow_lds(const void* kernel, size_t bytes);
 
+// Candidate selection: per-row top T (chunk lists in part_v/part_i, top_k_scratch bytes), and
+// the greedy re-scoring of the draft rows' candidates (cv/ci [rows][T]).
+hipError_t launch_top_k(const float* x, int rows, int width, int ld, int T, float* part_v, int* part_i, float* vals,
+                        int* idx, hipStream_t st);
+size_t top_k_scratch(int rows, int width, int T);
+hipError_t launch_select(const float* cv, const int* ci, int rows, int T, const float* hp, int rank,
+                         const uint16_t* pred, const uint16_t* succ, int anchor, int* chosen, int* plain,
+                         hipStream_t st);
+
 hipError_t launch_inv_freq(double theta, int hd, float* out, hipStream_t st);
 hipError_t launch_quant_rows(const float* x, int rows, int cols, int8_t* q, float* d, hipStream_t st);
 hipError_t launch_transpose_scales(const float* d, int rows, int groups, int Mpad, float* dT, hipStream_t st);

@@ -38,7 +38,7 @@ F32, Q4_32, Q8_32 = 0, 1, 2
 FMT_NAMES = {F32: "f32", Q4_32: "q4_32", Q8_32: "q8_32"}
 
 # stream ids of SeedSequence([seed, stream, index])
-_S_WEIGHT, _S_NORM, _S_TAPS, _S_ANCHOR, _S_MASK = 1, 2, 3, 4, 5
+_S_WEIGHT, _S_NORM, _S_TAPS, _S_ANCHOR, _S_MASK, _S_SELECTOR = 1, 2, 3, 4, 5, 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -249,6 +249,18 @@ def make_block_input(cfg: Config, seq: int, index: int) -> np.ndarray:
     h[0] = a * np.float32(cfg.emb_std)
     h[1:] = m * np.float32(cfg.emb_std)
     return h
+
+
+def make_selector(cfg: Config, rank: int = 128, book_std: float = 0.1) -> dict:
+    """The candidate selector's tensors (the pages give no rank or top count for these workloads;
+    rank 128 is this project's choice): the hidden projection [rank][hidden] N(0, weight_std)
+    coded like the head, and the predecessor and successor codebooks, f16 [vocab][rank]
+    N(0, book_std)."""
+    sel = _draw_matrix(cfg, 10_000, rank, cfg.hidden, cfg.head_fmt)
+    r = _rng(cfg.weight_seed or cfg.seed, _S_SELECTOR, 0)
+    pred = (r.standard_normal((cfg.vocab, rank), dtype=np.float32) * book_std).astype(np.float16)
+    succ = (r.standard_normal((cfg.vocab, rank), dtype=np.float32) * book_std).astype(np.float16)
+    return {"sel": sel, "pred": pred, "succ": succ, "rank": rank}
 
 
 def algorithmic_bytes(cfg: Config, ctx_rows: int | None = None) -> dict:

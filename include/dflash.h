@@ -197,6 +197,34 @@ enum dflash_stage {
 int dflash_time_stage(dflash_ctx* c, int32_t stage);
 int dflash_read_timing(dflash_ctx* c, int32_t stage, double* total_ms, int64_t* count);
 
+/* ---- Candidate selection (cortiq-engine dflash.rs: top_k, Drafter::select_with) ----
+ *
+ * dflash_top_k: the k largest entries of each of `rows` rows of x (device f32, row r at
+ * x + r*ld, `width` entries, ld >= width) with their indices, largest first and, among equal
+ * values, the earlier index first (the order the pages' top_k list keeps).  vals device
+ * [rows][k] f32, idx device [rows][k] int32.  1 <= k <= min(width, 64); values must be finite.
+ * `scratch`: device memory of dflash_top_k_scratch_bytes() bytes.
+ *
+ * dflash_select: the draft tokens of `rows` rows from their logits (device, as for top_k; row j
+ * is the block row j + 1 when the anchor's row is left out) under the candidate selector:
+ * row j's candidates are its top `top` logits; candidate t scores, in f32 and in this order,
+ *   logit_t + (sum over r = 0, 1, ..., rank-1 of (pred[prev][r] * hp[j][r]) * succ[t][r])
+ * with every product and sum rounded on its own; the first candidate with the largest score is
+ * chosen and becomes prev for row j + 1 (prev = anchor, a token id, for row 0).  hp device
+ * [rows][rank] f32 (the selector's projection of the rows); pred/succ device [vocab][rank] f16
+ * bit patterns (the predecessor and successor codebooks); width <= vocab (candidates index the
+ * codebooks).  chosen/plain device [rows] int32: the chosen tokens and each row's own top token.
+ * 1 <= top <= 64, 1 <= rank <= 4096, 0 <= anchor < vocab.  `scratch`: device memory of
+ * dflash_select_scratch_bytes() bytes.  All four return DFLASH_EINVAL on bad arguments (nothing
+ * enqueued) and DFLASH_EHIP on a launch error; work goes on `stream` and is not waited for. */
+int dflash_top_k_scratch_bytes(int32_t rows, int32_t width, int32_t k, size_t* bytes);
+int dflash_top_k(const float* x, int32_t rows, int32_t width, int32_t ld, int32_t k, float* vals, int32_t* idx,
+                 void* scratch, void* stream);
+int dflash_select_scratch_bytes(int32_t rows, int32_t width, int32_t top, size_t* bytes);
+int dflash_select(const float* logits, int32_t rows, int32_t width, int32_t ld, const float* hp, int32_t rank,
+                  const uint16_t* pred, const uint16_t* succ, int32_t vocab, int32_t top, int32_t anchor,
+                  int32_t* chosen, int32_t* plain, void* scratch, void* stream);
+
 /* Copy K and V of context rows row0..row0+n-1 (index = position - first) of one layer and
  * sequence into device k, v [n][kv_heads][head_dim] f32 (a read-back of the cache). */
 int dflash_read_kv(const dflash_ctx* c, int32_t layer, int32_t seq, int32_t row0, int32_t n, float* k, float* v);

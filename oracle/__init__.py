@@ -89,6 +89,8 @@ def lib(path: str | None = None):
             "og_read_kv": (i32, [vp, i32, i32, i32, i32, vp, vp]),
             "og_block_forward": (i32, [vp, i32, vp, vp, vp, vp]),
             "og_block_hidden": (i32, [vp, i32, vp, vp, vp, vp]),
+            "og_top_k": (None, [vp, i32, i32, vp, vp]),
+            "og_select": (None, [vp, i32, i32, i32, vp, i32, vp, vp, i32, i32, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -216,6 +218,38 @@ def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     a = np.empty_like(g)
     lib().og_silu_mul(_p(g), _p(u), g.size, _p(a))
     return a
+
+
+def top_k(x: np.ndarray, k: int):
+    """dflash.rs top_k: the k largest of x with their indices, largest first (earlier index first
+    among equal values)."""
+    x = _c(x, np.float32).ravel()
+    if not 1 <= k <= x.size:
+        raise ValueError("k outside [1, len(x)]")
+    vals = np.empty(k, np.float32)
+    idx = np.empty(k, np.int32)
+    lib().og_top_k(_p(x), x.size, k, _p(vals), _p(idx))
+    return vals, idx
+
+
+def select(logits: np.ndarray, hp: np.ndarray, pred: np.ndarray, succ: np.ndarray, top: int, anchor: int):
+    """dflash.rs Drafter::select_with over logits [rows][width] (the draft rows), the selector's
+    rows hp [rows][rank] and the f16 codebooks [vocab][rank]: (chosen tokens, each row's top)."""
+    logits = _c(logits, np.float32)
+    hp = _c(hp, np.float32)
+    pred = _c(pred, np.float16).view(np.uint16)
+    succ = _c(succ, np.float16).view(np.uint16)
+    rows, width = logits.shape
+    rank = hp.shape[1]
+    if hp.shape[0] != rows or pred.shape[1] != rank or succ.shape != pred.shape or not 1 <= top <= width:
+        raise ValueError("select: shapes")
+    if not 0 <= anchor < pred.shape[0]:
+        raise ValueError("select: anchor token outside the codebooks")
+    chosen = np.empty(rows, np.int32)
+    plain = np.empty(rows, np.int32)
+    lib().og_select(_p(logits), rows, width, width, _p(hp), rank, _p(pred), _p(succ), top, anchor, _p(chosen),
+                    _p(plain))
+    return chosen, plain
 
 
 # ---- the drafter --------------------------------------------------------------------------

@@ -487,3 +487,58 @@ int og_block_forward(og_model* m, int n_seqs, const int32_t* seqs, const int64_t
   free(x);
   return 0;
 }
+
+/* ---- candidate selection ---- */
+
+/* dflash.rs, top_k: an ordered list of the best so far; a value enters after every kept value
+ * that is >= it, so equal values keep their index order. */
+void og_top_k(const float* x, int n, int k, float* vals, int32_t* idx) {
+  int len = 0;
+  for (int i = 0; i < n; i++) {
+    float v = x[i];
+    if (len == k && v <= vals[k - 1]) continue;
+    int at = 0;
+    while (at < len && vals[at] >= v) at++;
+    int end = len < k ? len : k - 1; /* the last entry falls off a full list */
+    for (int j = end; j > at; j--) {
+      vals[j] = vals[j - 1];
+      idx[j] = idx[j - 1];
+    }
+    vals[at] = v;
+    idx[at] = i;
+    if (len < k) len++;
+  }
+}
+
+static float f16f(uint16_t h) { return (float)og_f16_to_f64(h); }
+
+/* dflash.rs, Drafter::select_with (book rows through book_row: f16 to f32). */
+void og_select(const float* logits, int rows, int width, int ld, const float* hp, int rank,
+               const uint16_t* pred, const uint16_t* succ, int top, int32_t anchor, int32_t* chosen,
+               int32_t* plain) {
+  float* cv = (float*)malloc(sizeof(float) * (size_t)top);
+  int32_t* ci = (int32_t*)malloc(sizeof(int32_t) * (size_t)top);
+  float* pc = (float*)malloc(sizeof(float) * (size_t)rank);
+  int32_t prev = anchor;
+  for (int j = 0; j < rows; j++) {
+    og_top_k(logits + (size_t)j * ld, width, top, cv, ci);
+    plain[j] = ci[0];
+    for (int r = 0; r < rank; r++) pc[r] = f16f(pred[(size_t)prev * rank + r]) * hp[(size_t)j * rank + r];
+    float best = -INFINITY;
+    int32_t tok = ci[0];
+    for (int c = 0; c < top; c++) {
+      float sum = 0.0f;
+      for (int r = 0; r < rank; r++) sum = sum + pc[r] * f16f(succ[(size_t)ci[c] * rank + r]);
+      float sc = cv[c] + sum;
+      if (sc > best) {
+        best = sc;
+        tok = ci[c];
+      }
+    }
+    prev = tok;
+    chosen[j] = tok;
+  }
+  free(cv);
+  free(ci);
+  free(pc);
+}

@@ -86,6 +86,20 @@ int og_block_forward(og_model* m, int n_seqs, const int32_t* seqs, const int64_t
 int og_block_hidden(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                     float* hidden);
 
+/* ---- candidate selection (dflash.rs, top_k and Drafter::select_with) ---- */
+/* The k largest of x[0..n) with their indices, largest first; of equal values the earlier index
+ * comes first.  k <= n.  vals/idx [k]. */
+void og_top_k(const float* x, int n, int k, float* vals, int32_t* idx);
+/* Greedy left-to-right choice of the draft tokens of `rows` rows: row j's candidates are the top
+ * `top` of its logits (logits + j*ld, width entries); each is scored in f32 as
+ *   logit + sum_r (pred[prev][r] * hp[j][r]) * succ[tok][r]   (the sum from r = 0 upward)
+ * where prev is the token chosen for the row before (anchor for row 0) and pred/succ are f16 bit
+ * patterns [vocab][rank]; the first candidate with the largest score is chosen.  chosen/plain
+ * [rows] receive the chosen tokens and each row's own top token. */
+void og_select(const float* logits, int rows, int width, int ld, const float* hp, int rank,
+               const uint16_t* pred, const uint16_t* succ, int top, int32_t anchor, int32_t* chosen,
+               int32_t* plain);
+
 #ifdef __cplusplus
 }
 #endif

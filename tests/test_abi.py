@@ -83,3 +83,19 @@ def test_null_arguments_refused_before_any_gpu_work():
     assert L.dflash_packed_bytes(D.DFLASH_Q4_32, 32, 256, C.byref(n)) == 0 and n.value == 2 * 2 * 1152
     assert L.dflash_packed_bytes(D.DFLASH_Q8_32, 16, 128, C.byref(n)) == 0 and n.value == 2176
     assert L.dflash_gemm_scratch_bytes(64, 256, 129, 0, C.byref(n)) == D.DFLASH_EINVAL
+
+
+def test_selection_arguments_refused_before_any_gpu_work():
+    L = D.lib()
+    n = C.c_size_t()
+    assert L.dflash_top_k_scratch_bytes(2, 100, 0, C.byref(n)) == D.DFLASH_EINVAL
+    assert L.dflash_top_k_scratch_bytes(2, 100, 65, C.byref(n)) == D.DFLASH_EINVAL
+    assert L.dflash_top_k_scratch_bytes(2, 10, 11, C.byref(n)) == D.DFLASH_EINVAL
+    assert L.dflash_top_k_scratch_bytes(2, 151936, 16, C.byref(n)) == D.DFLASH_OK and n.value > 0
+    assert L.dflash_top_k(None, 2, 100, 100, 4, None, None, None, None) == D.DFLASH_EINVAL
+    assert L.dflash_select_scratch_bytes(15, 151936, 16, C.byref(n)) == D.DFLASH_OK
+    # width beyond the codebooks' vocabulary, anchor outside it, rank 0: refused
+    fake = 256  # never dereferenced: the checks come first
+    assert L.dflash_select(fake, 1, 200, 200, fake, 8, fake, fake, 100, 4, 0, fake, fake, fake, None) == D.DFLASH_EINVAL
+    assert L.dflash_select(fake, 1, 100, 100, fake, 8, fake, fake, 100, 4, 100, fake, fake, fake, None) == D.DFLASH_EINVAL
+    assert L.dflash_select(fake, 1, 100, 100, fake, 0, fake, fake, 100, 4, 0, fake, fake, fake, None) == D.DFLASH_EINVAL

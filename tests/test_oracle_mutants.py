@@ -13,6 +13,7 @@ import pytest
 import dflash_inputs as di
 import oracle
 import test_oracle_model as TM
+import test_oracle_select as TS
 import test_oracle_units as TU
 
 # (what the mistake is, text in dflash_oracle.c, its replacement)
@@ -50,9 +51,20 @@ MUTANTS = [
     ("a gap keeps the old first", "  if (pos > first + len || pos < first) {\n    first = pos;",
      "  if (pos > first + len || pos < first) {\n    first = first;"),
     ("softmax max not subtracted consistently", "s[j] = exp(s[j] - top);", "s[j] = exp(s[j] - top) * (j == 0 ? 2.0 : 1.0);"),
+    ("top-k keeps the later of equal values", "while (at < len && vals[at] >= v) at++;",
+     "while (at < len && vals[at] > v) at++;"),
+    ("the chain restarts at the anchor", "    prev = tok;\n    chosen[j] = tok;", "    prev = anchor;\n    chosen[j] = tok;"),
+    ("the last largest score wins", "if (sc > best) {", "if (sc >= best) {"),
+    ("predecessor read from the successor book", "pc[r] = f16f(pred[(size_t)prev * rank + r])",
+     "pc[r] = f16f(succ[(size_t)prev * rank + r])"),
 ]
 
 CHECKS = [
+    (TS.test_top_k_pages_worked_example, ()),
+    (TS.test_top_k_is_the_head_of_the_value_then_index_order, ()),
+    (TS.test_select_reduces_to_top_1, ()),
+    (TS.test_select_chooses_among_the_candidates_and_follows_the_chain, ()),
+    (TS.test_select_brute_force_small, ()),
     (TU.test_rmsnorm_against_torch, (4096,)),
     (TU.test_rope_against_transformers_rotate_half, (4095,)),
     (TU.test_rope_invariants, ()),
