@@ -129,6 +129,8 @@ def main() -> int:
     ap.add_argument("--config", default="qwen3_8b", choices=di.CONFIG_ORDER)
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--stages", type=int, default=1, help="also time each stage in its own untimed pass")
+    ap.add_argument("--selection", type=int, default=1,
+                    help="also time the candidate selection of one block's draft rows (top 16, rank 128)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -249,6 +251,33 @@ def main() -> int:
             stages[name] = round(tot / K, 5)  # ms per step, summed over the stage's launches
         log("stages ms/step:", stages)
 
+    # the candidate selection the pages run after the block (not part of the step): top 16 of the
+    # draft rows' logits and the greedy re-scoring with a rank-128 selector, timed on its own
+    sel_ms = None
+    if args.selection:
+        rank, top, nrow = 128, 16, cfg.block - 1
+        rng = np.random.default_rng(5)
+        hp = torch.from_numpy(rng.standard_normal((nrow, rank)).astype(np.float32)).cuda()
+        books = torch.from_numpy((rng.standard_normal((2, cfg.vocab, rank)) * 0.1).astype(np.float16).view(np.int16)).cuda()
+        chosen = torch.empty(nrow, dtype=torch.int32, device="cuda")
+        plain = torch.empty_like(chosen)
+        scr = torch.empty(D.dflash_select_scratch_bytes(nrow, cfg.vocab, top), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def sel():
+            D.dflash_select(logits.data_ptr() + cfg.vocab * 4, nrow, cfg.vocab, cfg.vocab, hp.data_ptr(), rank,
+                            books[0].data_ptr(), books[1].data_ptr(), cfg.vocab, top, 0, chosen.data_ptr(),
+                            plain.data_ptr(), scr.data_ptr(), stream)
+        for _ in range(3):
+            sel()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(K):
+            sel()
+        e1.record()
+        torch.cuda.synchronize()
+        sel_ms = e0.elapsed_time(e1) / K
+
     if args.copy_probe_mib:
         # a plain streaming kernel of known size (read n bytes, write n bytes): the reference
         # against which the HBM byte counters of the other kernels are scaled
@@ -311,6 +340,7 @@ def main() -> int:
         "roofline_next": other,
         "ms_per_step_with_kernel_events": round(ms_events, 5),
         "stages_ms_per_step": stages,
+        "selection_ms_per_block": None if sel_ms is None else round(sel_ms, 5),
     }
     if args.cpu_baseline and cfg.n_seqs == 1 and cfg.ctx <= 8192:
         out["cpu_baseline"] = cpu_baseline(cfg, weights)
