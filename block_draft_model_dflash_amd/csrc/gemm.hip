@@ -276,24 +276,26 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   const int n = ntile * 16 + row16;
 
   if (o.epi == EPI_SWIGLU) {
-    // NTW == 4: n-tiles gate(2b), up(2b), gate(2b+1), up(2b+1) of n-block b = nb give the
-    // 32 columns 32b.. of a = silu(gate) * up, one A8 group per row
+    // NTW = 4g: each group of four n-tiles gate(2b), up(2b), gate(2b+1), up(2b+1) (b = nb*NTW/4 +
+    // group) gives the 32 columns 32b.. of a = silu(gate) * up, one A8 group per row
+    constexpr int WC = NTW * 16, AC = NTW * 8;  // product columns and a columns of the workgroup
     __syncthreads();
-    float* G = (float*)smem;  // [MR][64]: the four tiles' f32 products
+    float* G = (float*)smem;  // [MR][WC]: the tiles' f32 products
     if (kw == 0 && active)
 #pragma unroll
       for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) G[(mt * 16 + 4 * quarter + q) * 64 + nt * 16 + row16] = (float)(acc[mt][q] * post);
+        for (int q = 0; q < 4; q++) G[(mt * 16 + 4 * quarter + q) * WC + nt * 16 + row16] = (float)(acc[mt][q] * post);
     __syncthreads();
     const int I = N >> 1;
-    for (int i = tid; i < MR * 32; i += NT) {
-      const int ml = i >> 5, j = i & 31, m = m0 + ml;
-      if (m >= Mpad) break;  // whole 32-lane groups leave together
-      const int gc = (j >> 4) * 32 + (j & 15);
-      const double g = G[ml * 64 + gc], u = G[ml * 64 + gc + 16];
+    for (int i = tid; i < MR * AC; i += NT) {
+      const int ml = i / AC, j = i % AC, m = m0 + ml;
+      if (m >= Mpad) break;  // whole 32-lane groups leave together (AC is a multiple of 32)
+      const int jj = j & 31;
+      const int gc = (j >> 5) * 64 + (jj >> 4) * 32 + (jj & 15);
+      const double g = G[ml * WC + gc], u = G[ml * WC + gc + 16];
       const float a = (float)(g / (1.0 + exp(-g)) * u);
-      const int c = nb * 32 + j;
+      const int c = nb * AC + j;
       if (o.xq)
         emit_q32(a, (size_t)m * I + c, o.xq, o.dxT, (size_t)(c >> 5) * Mpad + m, lane);
       else
@@ -371,6 +373,9 @@ int gemm_layout(int N, int Mpad, int epi) {
   // more than 16 rows already give a product with few n-tiles several workgroups per n-block
   // (one per row group): four n-tiles x two k-waves then beats splitting K eight ways
   if (Mpad > 16 && epi != EPI_SWIGLU && N / 16 < 2048) return 0;
+  // 16 rows and many n-tiles (the head, gate|up): eight n-tiles a workgroup, one wave each,
+  // stage the activations once for twice the weights
+  if (Mpad <= 16 && N / 16 >= 1024) return 3;
   // thousands of n-tiles (the head, gate|up) stream without splitting K much; a product with
   // few n-tiles splits K over eight (four) waves so every CU has about eight waves in flight
   if (epi == EPI_SWIGLU) return 0;
@@ -390,7 +395,7 @@ static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const
   const int kcb = KCB > KB ? KB : KCB;
   size_t lds = (size_t)MR * (kcb * 128 + 16) + (size_t)kcb * 4 * MR * 4;
   const size_t red = (size_t)(KW - 1) * NTW * MT * 4 * 64 * 8;
-  const size_t swg = (size_t)MR * 64 * 4;
+  const size_t swg = (size_t)MR * NTW * 16 * 4;
   if (red > lds) lds = red;
   if (swg > lds) lds = swg;
   if (lds > max_dynamic_lds()) return hipErrorInvalidValue;
@@ -416,6 +421,7 @@ static hipError_t gemm_mt_inst(int layout, const void* W, int N, int K, const in
                                const GemmOut& o, hipStream_t st) {
   if (layout == 0) return gemm_inst<FMT, MT, 4, 2>(W, N, K, xq, dxT, o, st);
   if (layout == 2) return gemm_inst<FMT, MT, 4, 1>(W, N, K, xq, dxT, o, st);
+  if (layout == 3) return gemm_inst<FMT, MT, 8, 1>(W, N, K, xq, dxT, o, st);
   if constexpr (MT <= 2)
     return gemm_inst<FMT, MT, 1, 8>(W, N, K, xq, dxT, o, st);
   else
@@ -436,7 +442,8 @@ hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq,
   if ((o.epi == EPI_F64 || o.epi == EPI_F32) && !o.y) return hipErrorInvalidValue;
   if (o.epi == EPI_RESID && (!o.h || !o.ssq)) return hipErrorInvalidValue;
   if (layout < 0) layout = gemm_layout(N, o.Mpad, o.epi);
-  if (o.epi == EPI_SWIGLU) layout = 0;
+  if (o.epi == EPI_SWIGLU && layout != 0 && layout != 3) layout = 0;  // whole groups of four n-tiles
+  if (o.epi == EPI_SWIGLU && layout == 3 && N % 128) layout = 0;
   if (fmt == Q4) return gemm_fmt<Q4>(layout, W, N, K, xq, dxT, o, st);
   if (fmt == Q8) return gemm_fmt<Q8>(layout, W, N, K, xq, dxT, o, st);
   return hipErrorInvalidValue;
