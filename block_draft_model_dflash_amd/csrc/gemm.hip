@@ -90,6 +90,24 @@ __device__ __forceinline__ float w_scale(const Super<FMT>& r, int j) {
   return f16_to_f32(w >> (16 * (j & 1)));
 }
 
+// x summed over the 16 lanes of each DPP row (lanes 16r..16r+15), every lane of the row getting
+// the same total: neighbours, then pairs within quads, then quads and half-rows mirrored onto
+// each other (a + b == b + a, so the mirrored partners hold equal sums).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xF, 0xF, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+__device__ __forceinline__ double row16_sum(double x) {
+  x += dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f64<0x141>(x);  // row_half_mirror
+  x += dpp_f64<0x140>(x);  // row_mirror
+  return x;
+}
+
 // A8_32 of one element whose 32-element group sits in 32 consecutive lanes of the wave.
 __device__ __forceinline__ void emit_q32(float y, size_t qi, int8_t* __restrict__ xq, float* __restrict__ dx, size_t di,
                                          int lane) {
@@ -161,67 +179,78 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
 #pragma unroll
     for (int r = 0; r < 4; r++) acc[mt][r] = 0.0;
 
-  // the residual rows the epilogue adds to, loaded first (they are needed only at the end)
-  float hres[MT][4];
-  if (o.epi == EPI_RESID && kw == 0 && active) {
+  // activations come through buffer resources that end at row Mpad (and at the last scale), so
+  // every staging load is unconditional: a row past the end reads as zeros, and a lane whose
+  // slot lies past the chunk loads something it then does not store
+  const __amdgpu_buffer_rsrc_t xr = wave_rsrc((const uint8_t*)xq, Mpad * K);
+  const __amdgpu_buffer_rsrc_t dr = wave_rsrc((const uint8_t*)dxT, (K >> 5) * Mpad * 4);
+  constexpr int SB = 8;  // 16-byte activation pieces (and scales) each thread has in flight
+  uint4 av[SB];
+  float dv[SB];
+  auto stage_load = [&](int c0, int c1, int i0) {
+    const int v16 = (c1 - c0) * 8;  // 16-byte pieces of a staged row
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++)
+    for (int b = 0; b < SB; b++) {
+      const int i = i0 + b * NT, rr = i / v16, c = i - rr * v16;
+      av[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, (m0 + rr) * K + c0 * 128 + c * 16, 0, 0));
+    }
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int m = m0 + mt * 16 + 4 * quarter + q;
-        hres[mt][q] = m < o.M ? o.h[(size_t)m * N + ntile * 16 + row16] : 0.f;
-      }
-  }
+    for (int b = 0; b < SB; b++) {  // scales of group c0*4 + g, row m0 + m ([group][Mpad])
+      const int i = i0 + b * NT, g = i / MR, m = i - g * MR;
+      dv[b] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, ((c0 * 4 + g) * Mpad + m0 + m) * 4, 0, 0));
+    }
+  };
+  // the stores are unconditional too (a conditional store would pull its load down next to it):
+  // a slot past the chunk writes row 0's padding or the scale array's spare word, never read
+  auto stage_store = [&](int c0, int c1, int i0) {
+    const int v16 = (c1 - c0) * 8, nv = MR * v16, nd = (c1 - c0) * 4 * MR;
+#pragma unroll
+    for (int b = 0; b < SB; b++) {
+      const int i = i0 + b * NT, rr = i / v16, c = i - rr * v16;
+      *(uint4*)(A + (i < nv ? rr * ASTR + c * 16 : kcb * 128)) = av[b];
+    }
+#pragma unroll
+    for (int b = 0; b < SB; b++) {  // a scale of a row past Mpad belongs to the next group: 0
+      const int i = i0 + b * NT, m = i % MR;
+      DX[i < nd ? i : kcb * 4 * MR] = m0 + m < Mpad ? dv[b] : 0.f;
+    }
+  };
 
-  // the ring is filled before the first activations are staged, so the weights' HBM latency
-  // overlaps the staging; a superblock past the tile reads as zeros and costs nothing
+  // the first chunk's activations are requested before the weights: loads return in order, so
+  // the staging then waits for them alone while the weights keep arriving
+  stage_load(0, min(kcb, KB), tid);
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the weights'
+
+  // the ring is filled before the activations are stored, so the weights' HBM latency overlaps
+  // the staging; a superblock past the tile reads as zeros and costs nothing
   const __amdgpu_buffer_rsrc_t rs = wave_rsrc(wt, active ? KB * SBB : 0);
   Super<FMT> r[RD];
 #pragma unroll
   for (int p = 0; p < RD; p++) super_load(rs, (kw + p * KW) * SBB, lane, r[p]);
-  for (int c0 = 0; c0 < KB; c0 += kcb) {
-    const int c1 = min(c0 + kcb, KB);
-    const int ncols = (c1 - c0) * 128;
-    if (c0) __syncthreads();  // the previous chunk's LDS reads are done
-    // staging: SB loads are issued together, then stored, so their latencies overlap
-    constexpr int SB = 8;
-    const int v16 = ncols >> 4, nv = MR * v16;
-    for (int i0 = tid; i0 < nv; i0 += NT * SB) {
-      uint4 v[SB];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // output slot s = 4*mt + q of the accumulators (rows m0 + 16*mt + 4*quarter + q, column
+  // row16 of the n-tile) is finished by k-wave s % KW
+  auto mine = [&](int s) { return KW == 1 || s % KW == kw; };
+
+  // the residual rows the epilogue adds to (needed only at the end), loaded without a branch
+  // (a branch around them would make every later wait count them as possibly missing): rows
+  // past M, and every row of another epilogue or of a tile past N, read as zeros
+  const __amdgpu_buffer_rsrc_t hr = wave_rsrc((const uint8_t*)o.h, o.epi == EPI_RESID && active ? o.M * N * 4 : 0);
+  float hres[MT][4];
 #pragma unroll
-      for (int b = 0; b < SB; b++) {
-        const int i = i0 + b * NT;
-        const int rr = i / v16, c = i - rr * v16;
-        v[b] = (uint4){0u, 0u, 0u, 0u};
-        if (i < nv && m0 + rr < Mpad) v[b] = *(const uint4*)(xq + (size_t)(m0 + rr) * K + (size_t)c0 * 128 + c * 16);
-      }
+  for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-      for (int b = 0; b < SB; b++) {
-        const int i = i0 + b * NT;
-        const int rr = i / v16, c = i - rr * v16;
-        if (i < nv) *(uint4*)(A + rr * ASTR + c * 16) = v[b];
-      }
+    for (int q = 0; q < 4; q++) {
+      const int m = m0 + mt * 16 + 4 * quarter + q;
+      hres[mt][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(hr, (m * N + ntile * 16 + row16) * 4, 0, 0));
     }
-    const int ng = ncols >> 5, nd = ng * MR;
-    for (int i0 = tid; i0 < nd; i0 += NT * SB) {
-      float v[SB];
-#pragma unroll
-      for (int b = 0; b < SB; b++) {
-        const int i = i0 + b * NT;
-        const int g = i / MR, m = i - g * MR;
-        v[b] = (i < nd && m0 + m < Mpad) ? dxT[(size_t)(c0 * 4 + g) * Mpad + m0 + m] : 0.f;
-      }
-#pragma unroll
-      for (int b = 0; b < SB; b++) {
-        const int i = i0 + b * NT;
-        if (i < nd) DX[i] = v[b];
-      }
-    }
-    __syncthreads();
-    if (!active) continue;
-    // no branch in the ring: a chunk before the last holds whole ring turns (kcb is a multiple
-    // of STEP), so a slot past c1 only occurs past the tile's end, where it holds zeros and adds
-    // exactly 0 (its LDS reads are clamped into the staged range, which holds finite values)
+
+  // the ring turns over the staged chunk [c0, c1).  No branch in the ring: a chunk before the
+  // last holds whole ring turns (kcb is a multiple of STEP), so a slot past c1 only occurs past
+  // the tile's end, where it holds zeros and adds exactly 0 (its LDS reads are clamped into the
+  // staged range, which holds finite values)
+  auto chunk = [&](int c0, int c1) {
     constexpr int UNROLL = TURNS > 0 ? TURNS : 1;
     const int turns = TURNS > 0 ? TURNS : (c1 - c0 - kw + STEP - 1) / STEP;
 #pragma unroll UNROLL
@@ -253,24 +282,52 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
         super_load(rs, (kbp + STEP) * SBB, lane, r[p]);
       }
     }
+  };
+
+  // the first chunk, its first batch of activations already on the way (straight-line code, so
+  // the stores wait for those loads alone)
+  {
+    const int c1 = min(kcb, KB);
+    stage_store(0, c1, tid);
+    for (int i0 = tid + NT * SB; i0 < MR * c1 * 8; i0 += NT * SB) {
+      stage_load(0, c1, i0);
+      stage_store(0, c1, i0);
+    }
+    __syncthreads();
+    if (active) chunk(0, c1);
+  }
+  for (int c0 = kcb; c0 < KB; c0 += kcb) {
+    const int c1 = min(c0 + kcb, KB);
+    __syncthreads();  // the previous chunk's LDS reads are done
+    for (int i0 = tid; i0 < MR * (c1 - c0) * 8; i0 += NT * SB) {
+      stage_load(c0, c1, i0);
+      stage_store(c0, c1, i0);
+    }
+    __syncthreads();
+    if (active) chunk(c0, c1);
   }
 
-  // the k-waves' sums, added in wave order
+  // the k-waves' sums: every wave leaves its partials in LDS, and k-wave s % KW adds slot s's
+  // in wave order (the same order on every run) and finishes it
   if (KW > 1) {
     __syncthreads();
     double* red = (double*)smem;
-    if (kw > 0 && active)
+    if (active)
 #pragma unroll
       for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) red[((((kw - 1) * NTW + nt) * MT + mt) * 4 + q) * 64 + lane] = acc[mt][q];
+        for (int q = 0; q < 4; q++) red[(((kw * NTW + nt) * MT + mt) * 4 + q) * 64 + lane] = acc[mt][q];
     __syncthreads();
-    if (kw == 0 && active)
-      for (int k = 1; k < KW; k++)
+    if (active)
 #pragma unroll
-        for (int mt = 0; mt < MT; mt++)
+      for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-          for (int q = 0; q < 4; q++) acc[mt][q] += red[((((k - 1) * NTW + nt) * MT + mt) * 4 + q) * 64 + lane];
+        for (int q = 0; q < 4; q++)
+          if (mine(4 * mt + q)) {
+            double v = red[((nt * MT + mt) * 4 + q) * 64 + lane];
+            for (int k = 1; k < KW; k++) v += red[(((k * NTW + nt) * MT + mt) * 4 + q) * 64 + lane];
+            acc[mt][q] = v;
+          }
   }
   const double post = FMT == Q4 ? 0.0625 : 1.0;  // Q4 codes entered the MFMA as 16*q
   const int n = ntile * 16 + row16;
@@ -281,11 +338,12 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
     constexpr int WC = NTW * 16, AC = NTW * 8;  // product columns and a columns of the workgroup
     __syncthreads();
     float* G = (float*)smem;  // [MR][WC]: the tiles' f32 products
-    if (kw == 0 && active)
+    if (active)
 #pragma unroll
       for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) G[(mt * 16 + 4 * quarter + q) * WC + nt * 16 + row16] = (float)(acc[mt][q] * post);
+        for (int q = 0; q < 4; q++)
+          if (mine(4 * mt + q)) G[(mt * 16 + 4 * quarter + q) * WC + nt * 16 + row16] = (float)(acc[mt][q] * post);
     __syncthreads();
     const int I = N >> 1;
     for (int i = tid; i < MR * AC; i += NT) {
@@ -303,11 +361,12 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
     }
     return;
   }
-  if (kw != 0 || !active) return;
+  if (!active) return;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
     for (int q = 0; q < 4; q++) {
+      if (!mine(4 * mt + q)) continue;
       const int m = m0 + mt * 16 + 4 * quarter + q;
       const double v = acc[mt][q] * post;
       if (o.epi == EPI_F64) {
@@ -321,10 +380,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
           o.h[(size_t)m * N + n] = hv;
           sq = (double)hv * (double)hv;
         }
-        sq += __shfl_xor(sq, 1);
-        sq += __shfl_xor(sq, 2);
-        sq += __shfl_xor(sq, 4);
-        sq += __shfl_xor(sq, 8);
+        sq = row16_sum(sq);
         if (row16 == 0 && m < Mpad) o.ssq[(size_t)m * (N >> 4) + ntile] = sq;
       }
     }
@@ -393,8 +449,8 @@ static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const
   constexpr int KCB = KCB_FULL < STEP ? STEP : KCB_FULL;
   const int KB = K / 128;
   const int kcb = KCB > KB ? KB : KCB;
-  size_t lds = (size_t)MR * (kcb * 128 + 16) + (size_t)kcb * 4 * MR * 4;
-  const size_t red = (size_t)(KW - 1) * NTW * MT * 4 * 64 * 8;
+  size_t lds = (size_t)MR * (kcb * 128 + 16) + (size_t)kcb * 4 * MR * 4 + 16;  // + the scales' spare word
+  const size_t red = KW > 1 ? (size_t)KW * NTW * MT * 4 * 64 * 8 : 0;  // every k-wave's partials
   const size_t swg = (size_t)MR * NTW * 16 * 4;
   if (red > lds) lds = red;
   if (swg > lds) lds = swg;
