@@ -303,9 +303,9 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   int nmax = 0;
   for (int i = 0; i < n_seqs; i++)
     if (si.nctx[i] > nmax) nmax = si.nctx[i];
-  // about one workgroup per CU: n_seqs * kv heads * chunks ~ 256, chunks a multiple of 32 keys
-  // (the two key halves of a workgroup take alternate 16-key tiles)
-  int nch_target = (256 + n_seqs * kvh - 1) / (n_seqs * kvh);
+  // about one workgroup per CU: n_seqs * q heads * chunks ~ 256 (a workgroup serves one q head
+  // of one chunk), chunks a multiple of 32 keys
+  int nch_target = (256 + n_seqs * nh - 1) / (n_seqs * nh);
   if (nch_target > MAXCH) nch_target = MAXCH;
   int ck = ((nmax + nch_target - 1) / nch_target + 31) / 32 * 32;
   if (ck < 32) ck = 32;

@@ -5,15 +5,19 @@
 // The pages' device kernel (gpu_wgpu/dflash_dev.rs, dflash_attn) writes every score to a global
 // scratch and re-reads it; here the context is split into chunks, each wave keeps a running
 // (max, sum, acc) per query in registers (online softmax), and a merge combines the chunks.
-// A workgroup serves one (sequence, kv head, chunk) with eight waves: wave w takes q head w % 4
-// of the group and the chunk's even (w < 4) or odd (w >= 4) 16-key tiles; the two halves of a
-// head are combined in LDS before the chunk's result is written.  The chunks hold context rows
-// only (so every key lane of the grid gets the same number of tiles); the block's own 16 keys,
-// a few thousand flops per (head, row), are scored by the merge, which then combines them with
-// the chunks.  The 16 block rows of a head are the 16 columns of v_mfma_f64_16x16x4f64 tiles:
-//   S^T[key][q] = K . Q^T   (A = 16 keys staged in LDS, B = the wave's queries in registers)
-//   Y^T[d][q]  += V^T . P^T (A = 16-dim slices of V from LDS, B = the wave's probabilities,
-//                            already in the accumulator layout of S^T)
+// A workgroup serves one (sequence, kv head, chunk, q head of the group).  Its eight waves take
+// the chunk's 16-key tiles in turn (wave w: tiles w, w + 8, ...), each straight from memory
+// into registers with the next tile's keys and values in flight while the current one is
+// computed, so the loop has no LDS staging and no barrier; the waves' (max, sum, acc) are then
+// combined in LDS in wave order and written once.  The q heads sharing a kv head read the
+// same tiles: their workgroups get ids 8 apart, which puts them on the same XCD (workgroups
+// go round-robin over the eight), where the tiles come from one L2.  The chunks hold context
+// rows only; the block's own 16 keys, a few thousand flops per (head, row), are scored by the
+// merge, which then combines them with the chunks.  The 16 block rows of a head are the 16
+// columns of v_mfma_f64_16x16x4f64 tiles:
+//   S^T[key][q] = K . Q^T   (A = 16 keys, B = the head's queries)
+//   Y^T[d][q]  += V^T . P^T (A = 16-dim slices of V, B = the probabilities, already in the
+//                            accumulator layout of S^T)
 // so the probabilities never leave registers.  Context K/V is f32 [slot][kvh][max_ctx][hd].
 // Lane layout of the f64 16x16x4 MFMA: lane l gives A[l%16][l/16] and B[l/16][l%16] and holds
 // D[l/16 + 4r][l%16] in accumulator slot r (rows interleaved, unlike the f32 16x16 forms).
@@ -29,182 +33,178 @@ namespace dfl {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef double v4d __attribute__((ext_vector_type(4)));
 
-constexpr int ATTN_HEADS = 4;                   // q heads served at once (one wave each per half)
-constexpr int ATTN_THREADS = 64 * 2 * ATTN_HEADS;  // two key halves
+constexpr int ATTN_WAVES = 8;
+constexpr int ATTN_THREADS = 64 * ATTN_WAVES;
 
 // Chunks a sequence with n context rows takes (the block's own rows are the merge's part).
 __device__ __forceinline__ int attn_chunks(int nctx, int ck) { return nctx > 0 ? (nctx + ck - 1) / ck : 0; }
 
+// LDS of the combine: every wave's (max, sum) per query and its acc, rows HD + 1 doubles apart
 template <int HD>
-__global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqInfo si, const float* __restrict__ q,
+constexpr size_t attn_comb_bytes() {
+  return (size_t)ATTN_WAVES * 16 * (HD + 1) * 8 + (size_t)ATTN_WAVES * 16 * 3 * 8;
+}
+// all of a workgroup's LDS: the combine, then the queries (16 rows of HD + 4 floats)
+template <int HD>
+constexpr size_t attn_lds_bytes() {
+  return attn_comb_bytes<HD>() + (size_t)16 * (HD + 4) * 4;
+}
+
+// Grid: ceil(tasks / 8) * 8 * rep workgroups for tasks (sequence, kv head, chunk) numbered
+// t = (s * kvh + g) * maxn + c; id = (t / 8) * 8 * rep + h * 8 + t % 8 serves q head g*rep + h.
+template <int HD>
+__global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqInfo si, int maxn,
+                                                               const float* __restrict__ q,
                                                                const float* __restrict__ kc,
                                                                const float* __restrict__ vc,
                                                                double* __restrict__ part, double* __restrict__ ml) {
-  // LDS rows: keys HD + 4 floats apart (each 16-lane group of a 128-bit read covers all banks),
-  // values HD + 1 apart (the 64 lanes' 32-bit reads of rows 4k + quarter, columns 4*col + e
-  // fall in 64 different banks)
-  constexpr int KS = HD + 4, VS = HD + 1;
-  constexpr int TILE = 16 * KS;        // one 16-key tile of K (V uses 16 * VS <= TILE)
-  constexpr int HALF = ATTN_THREADS / 2;
-  constexpr int NL = 16 * (HD / 4) / HALF;  // float4 of K (and of V) each thread stages per tile
-  constexpr int CD = 64;                    // dims combined per LDS round
-  constexpr int COMB = ATTN_HEADS * (16 * CD + 32);  // doubles: acc slice + (m, l) per row
-  constexpr int KV_BYTES = 2 * 2 * TILE * 4;
-  constexpr int LDS_BYTES = KV_BYTES > COMB * 8 ? KV_BYTES : COMB * 8;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  constexpr int NI = HD / 16;  // 16-dim slices: k-steps of the scores, output tiles of the values
+  constexpr int ND = HD / 64;  // 64-dim groups of a value row
+  constexpr int HDP = HD + 1;  // LDS row of a wave's acc (odd, so the 16 query rows spread over banks)
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int rep = a.nh / a.kvh, per = 8 * rep;
+  const int id = blockIdx.x, t = (id / per) * 8 + id % 8, h = (id % per) / 8;
+  if (t >= si.n * a.kvh * maxn) return;  // the whole workgroup: padding of the last group of 8
+  const int s = t / (a.kvh * maxn), g = (t / maxn) % a.kvh, c = t % maxn;
   const int nctx = si.nctx[s];
-  const int nch = attn_chunks(nctx, a.ck);
-  if (c >= nch) return;  // the whole workgroup: this sequence has fewer chunks
-  const int rep = a.nh / a.kvh;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int half = w / ATTN_HEADS, hw0 = w % ATTN_HEADS, htid = tid % HALF;
+  if (c >= attn_chunks(nctx, a.ck)) return;  // the whole workgroup: this sequence has fewer chunks
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int quarter = lane >> 4, col = lane & 15;
-  float* Ks = (float*)lds + half * 2 * TILE;
-  float* Vs = Ks + TILE;
+  const int j = g * rep + h;
   const int k0 = c * a.ck, kend = min(nctx, k0 + a.ck);
   const int nt = (kend - k0 + 15) / 16;  // >= 1: every launched chunk holds context rows
-  const int rounds = (nt + 1) / 2;
   const float* Kctx = kc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
   const float* Vctx = vc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
 
-  // the group's q heads, ATTN_HEADS at a time; the chunk's keys are re-staged per round when a
-  // group has more heads than that
-  for (int h0 = 0; h0 < rep; h0 += ATTN_HEADS) {
-    const int hw = h0 + hw0;  // this wave's head within the group
-    const bool live = hw < rep;
-    const int j = g * rep + (live ? hw : 0);
-    v4f qr[HD / 16];
+  // the head's queries in LDS (rows HD + 4 floats apart: the 16 rows of one 128-bit read fall
+  // in different banks), the B operand of the scores: q[row col][16*i4 + 4*quarter ..]
+  constexpr int QS = HD + 4;
+  float* Qs = (float*)(lds + attn_comb_bytes<HD>());
+  for (int e = tid; e < 16 * HD / 4; e += ATTN_THREADS) {
+    const int row = e / (HD / 4), c4 = e % (HD / 4);
+    const int rr = min(row, a.B - 1);  // rows past B: a copy of the last (their results are not kept)
+    *(v4f*)(Qs + row * QS + 4 * c4) = *(const v4f*)(q + ((size_t)(s * a.B + rr) * a.nh + j) * HD + 4 * c4);
+  }
+  __syncthreads();
+  double m_run = -INFINITY, l_run = 0.0;
+  v4d acc[NI];
 #pragma unroll
-    for (int i4 = 0; i4 < HD / 16; i4++)
-      qr[i4] = col < a.B ? *(const v4f*)(q + ((size_t)(s * a.B + col) * a.nh + j) * HD + 16 * i4 + 4 * quarter)
-                         : (v4f){0.f, 0.f, 0.f, 0.f};
-    double m_run = -INFINITY, l_run = 0.0;
-    v4d acc[HD / 16];
-#pragma unroll
-    for (int dt = 0; dt < HD / 16; dt++) acc[dt] = (v4d){0.0, 0.0, 0.0, 0.0};
+  for (int dt = 0; dt < NI; dt++) acc[dt] = (v4d){0.0, 0.0, 0.0, 0.0};
 
-    // tile i of the chunk: context keys k0 + 16i..; the next tile of this half travels to
-    // registers while the current one is computed
-    v4f pk[NL], pv[NL];
-    auto fetch = [&](int i) {
+  // a tile's operands, loaded unconditionally (keys past the chunk are clamped to its last key:
+  // their scores are masked, so their values are multiplied by 0):
+  //   kr[i4]    = K[key0 + col][16*i4 + 4*quarter ..]           (A of the scores)
+  //   vr[k][d4] = V[key0 + 4k + quarter][64*d4 + 4*col ..]      (A of the values, dims
+  //               64*d4 + 4*col + e of output tile dt = 4*d4 + e)
+  // (buffer loads: a plain load of read-only memory may be re-issued next to its use when
+  // registers run short, which would take the next tile out of flight)
+  v4f kr[NI], vr[4][ND];
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)Kctx, (short)0, kend * HD * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)Vctx, (short)0, kend * HD * 4, 0x00020000);
+  auto load_k = [&](int i) {
+    const int key = min(k0 + 16 * i + col, kend - 1);
 #pragma unroll
-      for (int u = 0; u < NL; u++) {
-        const int e = htid + u * HALF;
-        const int r = e / (HD / 4), c4 = e % (HD / 4);
-        const int key = k0 + 16 * i + r;
-        pk[u] = pv[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-        if (i < nt && key < kend) {
-          pk[u] = *(const v4f*)(Kctx + (size_t)key * HD + 4 * c4);
-          pv[u] = *(const v4f*)(Vctx + (size_t)key * HD + 4 * c4);
-        }
-      }
-    };
-    fetch(half);
-    for (int rd = 0; rd < rounds; rd++) {
-      const int i = 2 * rd + half;  // this half's tile in this round
-      __syncthreads();
+    for (int i4 = 0; i4 < NI; i4++)
+      kr[i4] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(kres, (key * HD + 16 * i4 + 4 * quarter) * 4, 0, 0));
+  };
+  auto load_v = [&](int i) {
 #pragma unroll
-      for (int u = 0; u < NL; u++) {
-        const int e = htid + u * HALF;
-        const int r = e / (HD / 4), c4 = e % (HD / 4);
-        *(v4f*)(Ks + r * KS + 4 * c4) = pk[u];
+    for (int k = 0; k < 4; k++) {
+      const int key = min(k0 + 16 * i + 4 * k + quarter, kend - 1);
 #pragma unroll
-        for (int f = 0; f < 4; f++) Vs[r * VS + 4 * c4 + f] = pv[u][f];
-      }
-      __syncthreads();
-      if (i + 2 < nt) fetch(i + 2);
-      if (!live || i >= nt) continue;
-      const int nvalid = min(16, kend - (k0 + 16 * i));  // keys of this tile
-      v4d st0 = (v4d){0.0, 0.0, 0.0, 0.0}, st1 = st0;
-#pragma unroll
-      for (int i4 = 0; i4 < HD / 16; i4++) {
-        const v4f kv = *(const v4f*)(Ks + col * KS + 16 * i4 + 4 * quarter);
-        st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[0], (double)qr[i4][0], st0, 0, 0, 0);
-        st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[1], (double)qr[i4][1], st1, 0, 0, 0);
-        st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[2], (double)qr[i4][2], st0, 0, 0, 0);
-        st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kv[3], (double)qr[i4][3], st1, 0, 0, 0);
-      }
-      double p[4], mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int key = quarter + 4 * r;  // accumulator slot r holds key row quarter + 4r
-        p[r] = key < nvalid ? (st0[r] + st1[r]) * (double)a.scale : -INFINITY;
-        mx = fmax(mx, p[r]);
-      }
-      mx = fmax(mx, __shfl_xor(mx, 16));
-      mx = fmax(mx, __shfl_xor(mx, 32));
-      const double m_new = fmax(m_run, mx);
-      const double corr = exp(m_run - m_new);
-      double ps = 0.0;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        p[r] = exp(p[r] - m_new);
-        ps += p[r];
-      }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l_run = l_run * corr + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < HD / 16; dt++) {
-        acc[dt] *= corr;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          // step k pairs the probabilities of slot k (keys quarter + 4k) with those keys' values
-          const float va = Vs[(4 * k + quarter) * VS + 64 * (dt >> 2) + 4 * col + (dt & 3)];
-          acc[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)va, p[k], acc[dt], 0, 0, 0);
-        }
-      }
+      for (int d4 = 0; d4 < ND; d4++)
+        vr[k][d4] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(vres, (key * HD + 64 * d4 + 4 * col) * 4, 0, 0));
     }
+  };
+  const int last = nt - 1;
+  // keys, then values, as in the loop (loads return in order: each wait then covers its own)
+  load_k(min(w, last));
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(min(w, last));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = w; i < nt; i += ATTN_WAVES) {
+    const int nvalid = min(16, kend - (k0 + 16 * i));  // keys of this tile
+    v4d st0 = (v4d){0.0, 0.0, 0.0, 0.0}, st1 = st0;
+#pragma unroll
+    for (int i4 = 0; i4 < NI; i4++) {
+      const v4f qv = *(const v4f*)(Qs + col * QS + 16 * i4 + 4 * quarter);
+      st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][0], (double)qv[0], st0, 0, 0, 0);
+      st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][1], (double)qv[1], st1, 0, 0, 0);
+      st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][2], (double)qv[2], st0, 0, 0, 0);
+      st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][3], (double)qv[3], st1, 0, 0, 0);
+    }
+    load_k(min(i + ATTN_WAVES, last));  // the next tile's keys travel during the softmax and values
+    double p[4], mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int key = quarter + 4 * r;  // accumulator slot r holds key row quarter + 4r
+      p[r] = key < nvalid ? (st0[r] + st1[r]) * (double)a.scale : -INFINITY;
+      mx = fmax(mx, p[r]);
+    }
+    mx = fmax(mx, __shfl_xor(mx, 16));
+    mx = fmax(mx, __shfl_xor(mx, 32));
+    const double m_new = fmax(m_run, mx);
+    const double corr = exp(m_run - m_new);
+    double ps = 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      p[r] = exp(p[r] - m_new);
+      ps += p[r];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * corr + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < NI; dt++) {
+      acc[dt] *= corr;
+#pragma unroll
+      for (int k = 0; k < 4; k++)  // step k pairs the probabilities of slot k with those keys' values
+        acc[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[k][dt >> 2][dt & 3], p[k], acc[dt], 0, 0, 0);
+    }
+    load_v(min(i + ATTN_WAVES, last));
+  }
 
-    // combine the halves: (m, l, acc) of the odd tiles join those of the even tiles through LDS,
-    // CD dims per round.  Half 0 always has tile 0, so its maximum is finite.
-    double* cb = (double*)lds + hw0 * (16 * CD + 32);
-    const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + hw) * 16 + col;
-    double e0 = 1.0, e1 = 0.0;
-    for (int d0 = 0; d0 < HD; d0 += CD) {
-      __syncthreads();
-      if (half == 1 && live) {
+  // combine the waves in wave order: M = the largest maximum (wave 0 has tile 0, so M is
+  // finite), e_w = exp(m_w - M) (0 for a wave without tiles), L = sum e_w l_w,
+  // acc = sum e_w acc_w
+  double* A = (double*)lds;                   // [wave][query][HDP]
+  double* MLs = A + ATTN_WAVES * 16 * HDP;    // [wave][query]: m, l, then e
 #pragma unroll
-        for (int d4 = 0; d4 < CD / 64; d4++)
+  for (int dt = 0; dt < NI; dt++)
 #pragma unroll
-          for (int r = 0; r < 4; r++)
-#pragma unroll
-            for (int e = 0; e < 4; e++)
-              cb[col * CD + 64 * d4 + 16 * r + 4 * quarter + e] = acc[4 * ((d0 >> 6) + d4) + e][r];
-        if (d0 == 0 && quarter == 0) {
-          cb[16 * CD + 2 * col] = m_run;
-          cb[16 * CD + 2 * col + 1] = l_run;
-        }
-      }
-      __syncthreads();
-      if (half == 1 || !live) continue;
-      if (d0 == 0) {
-        const double m1 = cb[16 * CD + 2 * col], l1 = cb[16 * CD + 2 * col + 1];
-        const double m = fmax(m_run, m1);
-        e0 = exp(m_run - m);
-        e1 = m1 == -INFINITY ? 0.0 : exp(m1 - m);
-        l_run = l_run * e0 + l1 * e1;
-        m_run = m;
-      }
-      if (col >= a.B) continue;
-      double* dst = part + prow * HD + d0;
-#pragma unroll
-      for (int d4 = 0; d4 < CD / 64; d4++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          // accumulator (dt = 4*d4 + e, slot r) is row quarter + 4r of tile dt: dim 64*d4 + 16*r + 4*quarter + e
-          const int o = 64 * d4 + 16 * r + 4 * quarter;
-#pragma unroll
-          for (int e = 0; e < 4; e++)
-            dst[o + e] = acc[4 * ((d0 >> 6) + d4) + e][r] * e0 + cb[col * CD + o + e] * e1;
-        }
+    for (int r = 0; r < 4; r++)  // slot r of tile dt: dim 64*(dt/4) + 16r + 4*quarter + dt%4
+      A[(w * 16 + col) * HDP + 64 * (dt >> 2) + 16 * r + 4 * quarter + (dt & 3)] = acc[dt][r];
+  if (quarter == 0) {
+    MLs[(w * 16 + col) * 3] = m_run;
+    MLs[(w * 16 + col) * 3 + 1] = l_run;
+  }
+  __syncthreads();
+  if (tid < 16) {  // one thread per query: the weights and the sum
+    double M = -INFINITY;
+    for (int v = 0; v < ATTN_WAVES; v++) M = fmax(M, MLs[(v * 16 + tid) * 3]);
+    double L = 0.0;
+    for (int v = 0; v < ATTN_WAVES; v++) {
+      const double mv = MLs[(v * 16 + tid) * 3];
+      const double e = mv == -INFINITY ? 0.0 : exp(mv - M);
+      MLs[(v * 16 + tid) * 3 + 2] = e;
+      L += MLs[(v * 16 + tid) * 3 + 1] * e;
     }
-    if (half == 0 && live && col < a.B && quarter == 0) {
-      ml[prow * 2] = m_run;
-      ml[prow * 2 + 1] = l_run;
+    const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + h) * 16 + tid;
+    if (tid < a.B) {
+      ml[prow * 2] = M;
+      ml[prow * 2 + 1] = L;
     }
+  }
+  __syncthreads();
+  for (int o = tid; o < 16 * HD; o += ATTN_THREADS) {
+    const int qq = o / HD, d = o % HD;
+    if (qq >= a.B) break;  // rows in order: the rest are past B too
+    double y = 0.0;
+#pragma unroll
+    for (int v = 0; v < ATTN_WAVES; v++) y += A[(v * 16 + qq) * HDP + d] * MLs[(v * 16 + qq) * 3 + 2];
+    const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + h) * 16 + qq;
+    part[prow * HD + d] = y;
   }
 }
 
@@ -359,8 +359,12 @@ static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const f
   }
   if (maxn > a.maxch) return hipErrorInvalidValue;
   if (maxn == 0) return hipSuccess;  // no sequence has context rows: the merge does it all
-  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(maxn, a.kvh, si.n), dim3(ATTN_THREADS), 0, st, a, si, q, kc, vc, part,
-                     ml);
+  const size_t lds = attn_lds_bytes<HD>();
+  hipError_t e = allow_lds((const void*)k_attn_partial<HD>, lds);
+  if (e != hipSuccess) return e;
+  const int tasks = si.n * a.kvh * maxn, rep = a.nh / a.kvh;
+  const int grid = (tasks + 7) / 8 * 8 * rep;
+  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(grid), dim3(ATTN_THREADS), lds, st, a, si, maxn, q, kc, vc, part, ml);
   return hipGetLastError();
 }
 
