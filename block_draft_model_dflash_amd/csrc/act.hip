@@ -13,30 +13,12 @@
 // rounded f32 of its step; the f32 steps the pages fix (the RMSNorm scale and products, the
 // RoPE angle, the quantizer) are done in f32 exactly as written.
 #include "common.h"
+#include "lanes.h"
 
 namespace dfl {
 
-// A8_32 of one element whose 32-element group sits in 32 consecutive lanes of the wave.
-__device__ __forceinline__ void emit_q(float y, size_t qi, int8_t* __restrict__ xq, float* __restrict__ dx,
-                                       size_t di, int lane) {
-  float amax = fabsf(y);
-#pragma unroll
-  for (int o = 16; o; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
-  int8_t q = 0;
-  float d = 0.f;
-  if (amax > 0.f) {
-    d = amax / 127.0f;
-    const float inv = 127.0f / amax;
-    float r = __builtin_rintf(y * inv);
-    r = fminf(fmaxf(r, -127.f), 127.f);
-    q = (int8_t)r;
-  }
-  xq[qi] = q;
-  if ((lane & 31) == 0) dx[di] = d;
-}
-
 __device__ __forceinline__ double block_sum_f64(double v, double* red) {
-  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o);
+  v = wave_sum_f64(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
@@ -95,7 +77,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restri
       row[i] = v;
       ss += (double)v * (double)v;
     } else if (QUANT) {
-      emit_q(v, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
+      emit_a8(v, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
     } else {
       xf[(size_t)m * N + i] = v;
     }
@@ -107,7 +89,7 @@ __global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restri
     const float t = row[i] * sc;
     const float y = t * w[i];
     if (QUANT)
-      emit_q(y, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
+      emit_a8(y, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
     else
       xf[(size_t)m * N + i] = y;
   }
@@ -181,8 +163,7 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
 #pragma unroll
       for (int b = 0; b < PB; b++) t += v[b];
     }
-#pragma unroll
-    for (int o = 32; o; o >>= 1) t += __shfl_xor(t, o);
+    t = wave_sum_f64(t);
     if (lane == 0) sc_sh = 1.0f / sqrtf((float)(t / (double)N) + eps);
   }
   __syncthreads();
@@ -190,7 +171,7 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
   const float sc = sc_sh;
   const float y = (hv * sc) * wv;
   if (QUANT)
-    emit_q(y, (size_t)m * N + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
+    emit_a8(y, (size_t)m * N + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
   else
     xf[(size_t)m * N + i] = y;
 }
@@ -218,8 +199,7 @@ __global__ __launch_bounds__(RMS_COLS) void k_copy_ssq(const float* __restrict__
     h[(size_t)m * N + i] = v;
     t = (double)v * (double)v;
   }
-#pragma unroll
-  for (int o = 32; o; o >>= 1) t += __shfl_xor(t, o);
+  t = wave_sum_f64(t);
   if (lane == 0) red[wave] = t;
   __syncthreads();
   if (tid == 0) {
@@ -277,7 +257,7 @@ __global__ __launch_bounds__(256) void k_swiglu_act(const double* __restrict__ p
       a = (float)(g / (1.0 + exp(-g)) * u);
     }
     if (QUANT)
-      emit_q(a, (size_t)m * I + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
+      emit_a8(a, (size_t)m * I + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
     else
       xf[(size_t)m * I + i] = a;
   }

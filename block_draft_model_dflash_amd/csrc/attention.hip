@@ -27,6 +27,7 @@
 // ulp off flips codes that the following layers amplify, so it has to be the correctly rounded
 // result that any exact evaluation gives.
 #include "common.h"
+#include "lanes.h"
 
 namespace dfl {
 
@@ -141,8 +142,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
       p[r] = key < nvalid ? (st0[r] + st1[r]) * (double)a.scale : -INFINITY;
       mx = fmax(mx, p[r]);
     }
-    mx = fmax(mx, __shfl_xor(mx, 16));
-    mx = fmax(mx, __shfl_xor(mx, 32));
+    mx = cross4_max_f64(mx);  // the same query's slots in the other three lane rows
     const double m_new = fmax(m_run, mx);
     const double corr = exp(m_run - m_new);
     double ps = 0.0;
@@ -151,8 +151,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
       p[r] = exp(p[r] - m_new);
       ps += p[r];
     }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    ps = cross4_sum_f64(ps);
     l_run = l_run * corr + ps;
     m_run = m_new;
 #pragma unroll
@@ -206,24 +205,6 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
     const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + h) * 16 + qq;
     part[prow * HD + d] = y;
   }
-}
-
-__device__ __forceinline__ void emit_q8(float y, size_t qi, int8_t* __restrict__ xq, float* __restrict__ dx,
-                                        size_t di, int lane) {
-  float amax = fabsf(y);
-#pragma unroll
-  for (int o = 16; o; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
-  int8_t qv = 0;
-  float d = 0.f;
-  if (amax > 0.f) {
-    d = amax / 127.0f;
-    const float inv = 127.0f / amax;
-    float r = __builtin_rintf(y * inv);
-    r = fminf(fmaxf(r, -127.f), 127.f);
-    qv = (int8_t)r;
-  }
-  xq[qi] = qv;
-  if ((lane & 31) == 0) dx[di] = d;
 }
 
 // One workgroup per (q head, block row, sequence) finishes the row: it scores the block's own
@@ -292,10 +273,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqIn
   for (int e = 0; e < KSL / 4; e++)
 #pragma unroll
     for (int f = 0; f < 4; f++) sc += (double)qv[e][f] * (double)kv[e][f];
-  sc += __shfl_xor(sc, 1);
-  sc += __shfl_xor(sc, 2);
-  sc += __shfl_xor(sc, 4);
-  sc += __shfl_xor(sc, 8);
+  sc = row16_sum_f64(sc);
   if (sl == 0 && key < a.B) s_sc[key] = sc * (double)a.scale;
   if (tid < nch) s_e[16 + tid] = mc;
   __syncthreads();
@@ -304,8 +282,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqIn
   if (tid < 64) {
     double mx = tid < a.B ? s_sc[tid] : -INFINITY;
     if (tid < nch) mx = fmax(mx, s_e[16 + tid]);
-#pragma unroll
-    for (int o = 32; o; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o));
+    mx = wave_max_f64(mx);
     double lsum = 0.0;
     if (tid < a.B) {
       const double e = exp(s_sc[tid] - mx);
@@ -317,8 +294,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqIn
       s_e[16 + tid] = e;
       lsum += lc * e;
     }
-#pragma unroll
-    for (int o = 32; o; o >>= 1) lsum += __shfl_xor(lsum, o);
+    lsum = wave_sum_f64(lsum);
     if (tid == 0) s_l = lsum;
   }
   __syncthreads();
@@ -344,7 +320,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqIn
   const size_t qd = (size_t)a.nh * HD;
   const size_t colx = (size_t)j * HD + d;
   if (QUANT)
-    emit_q8(val, (size_t)m * qd + colx, xq, dxT, (colx >> 5) * Mpad + m, lane);
+    emit_a8(val, (size_t)m * qd + colx, xq, dxT, (colx >> 5) * Mpad + m, lane);
   else
     xf[(size_t)m * qd + colx] = val;
 }

@@ -19,6 +19,7 @@
 // there flips codes that the following layers amplify to percent-level differences in the
 // logits; correctly rounded outputs keep two implementations on the same codes.
 #include "common.h"
+#include "lanes.h"
 
 namespace dfl {
 
@@ -88,43 +89,6 @@ template <int FMT>
 __device__ __forceinline__ float w_scale(const Super<FMT>& r, int j) {
   const uint32_t w = j < 2 ? r.s.x : r.s.y;
   return f16_to_f32(w >> (16 * (j & 1)));
-}
-
-// x summed over the 16 lanes of each DPP row (lanes 16r..16r+15), every lane of the row getting
-// the same total: neighbours, then pairs within quads, then quads and half-rows mirrored onto
-// each other (a + b == b + a, so the mirrored partners hold equal sums).
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double x) {
-  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
-  const unsigned lo = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)u, CTRL, 0xF, 0xF, false);
-  const unsigned hi = (unsigned)__builtin_amdgcn_mov_dpp((int)(unsigned)(u >> 32), CTRL, 0xF, 0xF, false);
-  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
-}
-__device__ __forceinline__ double row16_sum(double x) {
-  x += dpp_f64<0xB1>(x);   // quad_perm [1,0,3,2]
-  x += dpp_f64<0x4E>(x);   // quad_perm [2,3,0,1]
-  x += dpp_f64<0x141>(x);  // row_half_mirror
-  x += dpp_f64<0x140>(x);  // row_mirror
-  return x;
-}
-
-// A8_32 of one element whose 32-element group sits in 32 consecutive lanes of the wave.
-__device__ __forceinline__ void emit_q32(float y, size_t qi, int8_t* __restrict__ xq, float* __restrict__ dx, size_t di,
-                                         int lane) {
-  float amax = fabsf(y);
-#pragma unroll
-  for (int o = 16; o; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
-  int8_t q = 0;
-  float d = 0.f;
-  if (amax > 0.f) {
-    d = amax / 127.0f;
-    const float inv = 127.0f / amax;
-    float r = __builtin_rintf(y * inv);
-    r = fminf(fmaxf(r, -127.f), 127.f);
-    q = (int8_t)r;
-  }
-  xq[qi] = q;
-  if ((lane & 31) == 0) dx[di] = d;
 }
 
 // Register ring depth (superblocks in flight per wave) and the k-blocks one turn of the ring
@@ -355,7 +319,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
       const float a = (float)(g / (1.0 + exp(-g)) * u);
       const int c = nb * AC + j;
       if (o.xq)
-        emit_q32(a, (size_t)m * I + c, o.xq, o.dxT, (size_t)(c >> 5) * Mpad + m, lane);
+        emit_a8(a, (size_t)m * I + c, o.xq, o.dxT, (size_t)(c >> 5) * Mpad + m, lane);
       else
         o.xf[(size_t)m * I + c] = a;
     }
@@ -380,7 +344,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
           o.h[(size_t)m * N + n] = hv;
           sq = (double)hv * (double)hv;
         }
-        sq = row16_sum(sq);
+        sq = row16_sum_f64(sq);
         if (row16 == 0 && m < Mpad) o.ssq[(size_t)m * (N >> 4) + ntile] = sq;
       }
     }
