@@ -26,6 +26,7 @@ namespace dfl {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef double v2d __attribute__((ext_vector_type(2)));
+typedef double v4d __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
@@ -91,6 +92,18 @@ __device__ __forceinline__ float w_scale(const Super<FMT>& r, int j) {
   return f16_to_f32(w >> (16 * (j & 1)));
 }
 
+// Element type of the staged activation scales: f64 when eight n-tiles share them.
+template <int NTW>
+struct DxType {
+  using T = float;
+  using V = v4f;
+};
+template <>
+struct DxType<8> {
+  using T = double;
+  using V = v4d;
+};
+
 // Register ring depth (superblocks in flight per wave) and the k-blocks one turn of the ring
 // covers across the workgroup's k-waves: about 32/MT k-blocks, so one turn's activations fit the
 // LDS chunk.
@@ -123,7 +136,10 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   constexpr int RD = Ring<MT, KW>::depth, STEP = Ring<MT, KW>::step;
   const int ASTR = kcb * 128 + 16;  // padded LDS row: rows land 4 banks apart
   int8_t* A = (int8_t*)smem;
-  float* DX = (float*)(smem + MR * ASTR);  // [kcb*4 groups][MR] activation scales
+  // [kcb*4 groups][MR] activation scales; a workgroup of eight n-tiles keeps them as f64, so the
+  // conversion is done once at staging instead of once per n-tile in the loop
+  using DxT = typename DxType<NTW>::T;
+  DxT* DX = (DxT*)(smem + MR * ASTR);
   // the wave index is uniform across the wave: saying so keeps the weight tile's buffer
   // resource in scalar registers (no per-lane descriptor loop around each load)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -176,7 +192,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
 #pragma unroll
     for (int b = 0; b < SB; b++) {  // a scale of a row past Mpad belongs to the next group: 0
       const int i = i0 + b * NT, m = i % MR;
-      DX[i < nd ? i : kcb * 4 * MR] = m0 + m < Mpad ? dv[b] : 0.f;
+      DX[i < nd ? i : kcb * 4 * MR] = (DxT)(m0 + m < Mpad ? dv[b] : 0.f);
     }
   };
 
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
             for (int mt = 0; mt < MT; mt++) {
               const long a = *(const long*)(A + (mt * 16 + row16) * ASTR + col);
               const v4i sm = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (v4i){0, 0, 0, 0}, 0, 0, 0);
-              const v4f dx = *(const v4f*)(DX + (kk * 4 + j) * MR + mt * 16 + 4 * quarter);
+              const auto dx = *(const typename DxType<NTW>::V*)(DX + (kk * 4 + j) * MR + mt * 16 + 4 * quarter);
               acc[mt][0] = __builtin_fma((double)sm[0], dw * (double)dx[0], acc[mt][0]);
               acc[mt][1] = __builtin_fma((double)sm[1], dw * (double)dx[1], acc[mt][1]);
               acc[mt][2] = __builtin_fma((double)sm[2], dw * (double)dx[2], acc[mt][2]);
@@ -407,13 +423,16 @@ static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const
                             hipStream_t st) {
   constexpr int MR = MT * 16, STEP = Ring<MT, KW>::step;
   // LDS of a chunk of kcb k-blocks: MR rows of kcb*128 codes (+16 B row padding) and kcb*4*MR
-  // f32 scales; about 76 KB so two workgroups share a CU
-  constexpr size_t PER_KB = (size_t)MR * 144;
-  constexpr int KCB_FULL = (int)((76 * 1024 - (size_t)MR * 16) / PER_KB) / STEP * STEP;
+  // scales.  About 76 KB so two workgroups share a CU; a workgroup of eight n-tiles (one per CU
+  // by its registers) may take 96 KB for its f64 scales
+  constexpr size_t DXB = sizeof(typename DxType<NTW>::T);
+  constexpr size_t BUDGET = (NTW == 8 ? 96 : 76) * 1024;
+  constexpr size_t PER_KB = (size_t)MR * 128 + 4 * MR * DXB;
+  constexpr int KCB_FULL = (int)((BUDGET - (size_t)MR * 16 - 16) / PER_KB) / STEP * STEP;
   constexpr int KCB = KCB_FULL < STEP ? STEP : KCB_FULL;
   const int KB = K / 128;
   const int kcb = KCB > KB ? KB : KCB;
-  size_t lds = (size_t)MR * (kcb * 128 + 16) + (size_t)kcb * 4 * MR * 4 + 16;  // + the scales' spare word
+  size_t lds = (size_t)MR * (kcb * 128 + 16) + ((size_t)kcb * 4 * MR + 1) * DXB;  // + the scales' spare slot
   const size_t red = KW > 1 ? (size_t)KW * NTW * MT * 4 * 64 * 8 : 0;  // every k-wave's partials
   const size_t swg = (size_t)MR * NTW * 16 * 4;
   if (red > lds) lds = red;
