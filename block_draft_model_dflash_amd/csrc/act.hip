@@ -134,7 +134,6 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
                                                       int nparts, const float* __restrict__ w, float eps, int M,
                                                       int Mpad, int N, int8_t* __restrict__ xq,
                                                       float* __restrict__ dxT, float* __restrict__ xf) {
-  __shared__ float sc_sh;
   const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int i = blockIdx.x * RMS_COLS + tid;
   if (m >= M) {
@@ -148,27 +147,23 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
     }
     return;
   }
-  // this column's value and weight travel while the row's scale is formed
+  // this column's value and weight travel while the row's scale is formed; every wave forms the
+  // scale itself (the same loads and the same order of additions), so no wave waits for another
   const float hv = i < N ? h[(size_t)m * N + i] : 0.f, wv = i < N ? w[i] : 0.f;
-  if (tid < 64) {
-    constexpr int PB = 8;  // pieces each lane loads at once
-    double t = 0.0;
-    for (int p0 = lane; p0 < nparts; p0 += 64 * PB) {
-      double v[PB];
-#pragma unroll
-      for (int b = 0; b < PB; b++) {
-        const int p = p0 + 64 * b;
-        v[b] = p < nparts ? ssq[(size_t)m * nparts + p] : 0.0;
-      }
-#pragma unroll
-      for (int b = 0; b < PB; b++) t += v[b];
-    }
-    t = wave_sum_f64(t);
-    if (lane == 0) sc_sh = 1.0f / sqrtf((float)(t / (double)N) + eps);
+  double t = 0.0;
+  int p = lane;
+  for (; p + 192 < nparts; p += 256) {  // four pieces per lane in flight at once
+    const double v0 = ssq[(size_t)m * nparts + p], v1 = ssq[(size_t)m * nparts + p + 64];
+    const double v2 = ssq[(size_t)m * nparts + p + 128], v3 = ssq[(size_t)m * nparts + p + 192];
+    t += v0;
+    t += v1;
+    t += v2;
+    t += v3;
   }
-  __syncthreads();
+  for (; p < nparts; p += 64) t += ssq[(size_t)m * nparts + p];
+  t = wave_sum_f64(t);
   if (i >= N) return;  // N is a multiple of 32: whole A8 groups leave together
-  const float sc = sc_sh;
+  const float sc = 1.0f / sqrtf((float)(t / (double)N) + eps);
   const float y = (hv * sc) * wv;
   if (QUANT)
     emit_a8(y, (size_t)m * N + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
@@ -274,99 +269,99 @@ hipError_t launch_swiglu_act(const double* part, int S, int M, int Mpad, int I, 
   return hipGetLastError();
 }
 
-// RMSNorm of one head (threads d < hd of a 128-thread block), then its rotation to `pos`: the
-// angle is the f32 product f32(pos) * inv_freq[i]; its cosine and sine and the rotation are
-// evaluated in f64 and rounded once.
-__device__ __forceinline__ float head_norm_rope(float x, int d, int hd, const float* __restrict__ w, float eps,
-                                                const float* __restrict__ inv_freq, long long pos, float* ybuf,
-                                                double* red) {
-  double ss = d < hd ? (double)x * (double)x : 0.0;
-  ss = block_sum_f64(ss, red);
-  const float sc = 1.0f / sqrtf((float)(ss / (double)hd) + eps);
-  float y = 0.f;
-  if (d < hd) {
-    const float t = x * sc;
-    y = t * w[d];
-  }
-  ybuf[d] = y;
-  __syncthreads();
-  if (d >= hd) return 0.f;
+// Per-head RMSNorm then RoPE (cortiq-engine dflash.rs, Drafter::block / append: q_norm or k_norm
+// over the head's hd values, s = 1/sqrt(f32(sum x^2 / hd) + eps), y = (x*s)*w, then the rotation
+// of the pairs (d, d + hd/2) by the angle f32(pos) * inv_freq[d], an f32 product).  One wave per
+// (head, row): lane l holds dims l and l + hd/2 (hd <= 128), the pair the rotation mixes, so
+// nothing crosses lanes but the sum of squares.  The angle's cosine and sine and the rotation are
+// evaluated in f64 from the f32 y and rounded once.
+__device__ __forceinline__ void head_norm_rope(float x0, float x1, int lane, int hd, const float* __restrict__ w,
+                                               float eps, const float* __restrict__ inv_freq, long long pos,
+                                               float& o0, float& o1) {
   const int half = hd >> 1;
-  const int i = d < half ? d : d - half;
-  const float ang = (float)pos * inv_freq[i];
+  const bool on = lane < half;
+  double ss = on ? (double)x0 * (double)x0 + (double)x1 * (double)x1 : 0.0;
+  ss = wave_sum_f64(ss);
+  const float sc = 1.0f / sqrtf((float)(ss / (double)hd) + eps);
+  if (!on) return;
+  const float y0 = (x0 * sc) * w[lane], y1 = (x1 * sc) * w[lane + half];
+  const float ang = (float)pos * inv_freq[lane];
   double sn, cs;
   sincos((double)ang, &sn, &cs);
-  const double a = (double)y;
-  return d < half ? (float)(a * cs - (double)ybuf[d + half] * sn) : (float)(a * cs + (double)ybuf[d - half] * sn);
+  o0 = (float)((double)y0 * cs - (double)y1 * sn);
+  o1 = (float)((double)y1 * cs + (double)y0 * sn);
 }
 
-// Grid (nh + 2 kvh heads, M rows), block 128.  Columns of the fused projection: q heads, then
-// k heads, then v heads, hd each.
-__global__ __launch_bounds__(128) void k_qkv_epilogue(const double* __restrict__ part, int S, int Mpad, int B,
-                                                     SeqInfo si, int nh, int kvh, int hd,
-                                                     const float* __restrict__ q_norm,
-                                                     const float* __restrict__ k_norm,
-                                                     const float* __restrict__ inv_freq, float eps,
-                                                     float* __restrict__ q, float* __restrict__ k,
-                                                     float* __restrict__ v) {
-  __shared__ float ybuf[128];
-  __shared__ double red[2];
-  const int head = blockIdx.x, m = blockIdx.y, d = threadIdx.x;
+// Grid (nh + 2 kvh heads, M rows), one wave each.  Columns of the fused projection: q heads,
+// then k heads, then v heads, hd each.
+__global__ __launch_bounds__(64) void k_qkv_epilogue(const double* __restrict__ part, int S, int Mpad, int B,
+                                                    SeqInfo si, int nh, int kvh, int hd,
+                                                    const float* __restrict__ q_norm,
+                                                    const float* __restrict__ k_norm,
+                                                    const float* __restrict__ inv_freq, float eps,
+                                                    float* __restrict__ q, float* __restrict__ k,
+                                                    float* __restrict__ v) {
+  const int head = blockIdx.x, m = blockIdx.y, lane = threadIdx.x, half = hd >> 1;
   const size_t N = (size_t)(nh + 2 * kvh) * hd;
-  const size_t col = (size_t)head * hd + d;
-  const float x = d < hd ? reduce_parts(part, S, Mpad, m, N, col) : 0.f;
+  const size_t col = (size_t)head * hd + lane;
   if (head >= nh + kvh) {
-    if (d < hd) v[((size_t)m * kvh + (head - nh - kvh)) * hd + d] = x;
+    for (int d = lane; d < hd; d += 64)
+      v[((size_t)m * kvh + (head - nh - kvh)) * hd + d] = reduce_parts(part, S, Mpad, m, N, (size_t)head * hd + d);
     return;
   }
+  const bool on = lane < half;
+  const float x0 = on ? reduce_parts(part, S, Mpad, m, N, col) : 0.f;
+  const float x1 = on ? reduce_parts(part, S, Mpad, m, N, col + half) : 0.f;
   const long long pos = si.pos0[m / B] + (m % B);
   const bool isq = head < nh;
-  const float out = head_norm_rope(x, d, hd, isq ? q_norm : k_norm, eps, inv_freq, pos, ybuf, red);
-  if (d < hd) {
-    if (isq)
-      q[((size_t)m * nh + head) * hd + d] = out;
-    else
-      k[((size_t)m * kvh + (head - nh)) * hd + d] = out;
-  }
+  float o0 = 0.f, o1 = 0.f;
+  head_norm_rope(x0, x1, lane, hd, isq ? q_norm : k_norm, eps, inv_freq, pos, o0, o1);
+  if (!on) return;
+  float* dst = isq ? q + ((size_t)m * nh + head) * hd : k + ((size_t)m * kvh + (head - nh)) * hd;
+  dst[lane] = o0;
+  dst[lane + half] = o1;
 }
 
 hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
                                int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
                                float* q, float* k, float* v, hipStream_t st) {
   if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_qkv_epilogue, dim3(nh + 2 * kvh, M), dim3(128), 0, st, part, S, Mpad, B, si, nh, kvh, hd,
+  hipLaunchKernelGGL(k_qkv_epilogue, dim3(nh + 2 * kvh, M), dim3(64), 0, st, part, S, Mpad, B, si, nh, kvh, hd,
                      q_norm, k_norm, inv_freq, eps, q, k, v);
   return hipGetLastError();
 }
 
-// Context append: grid (layers * 2 * kvh, n), block 128.  Columns of the all-layer K|V
+// Context append: grid (layers * 2 * kvh, n), one wave each.  Columns of the all-layer K|V
 // projection: layer l's k heads then its v heads.  Cache layout [L][max_seqs][kvh][max_ctx][hd].
-__global__ __launch_bounds__(128) void k_kv_append(const double* __restrict__ part, int S, int Mpad, int layers,
-                                                  int kvh, int hd, const float* __restrict__ k_norms,
-                                                  const float* __restrict__ inv_freq, float eps, long long pos0,
-                                                  int row0, int slot, int max_seqs, int max_ctx,
-                                                  float* __restrict__ kc, float* __restrict__ vc) {
-  __shared__ float ybuf[128];
-  __shared__ double red[2];
-  const int unit = blockIdx.x, i = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(64) void k_kv_append(const double* __restrict__ part, int S, int Mpad, int layers,
+                                                 int kvh, int hd, const float* __restrict__ k_norms,
+                                                 const float* __restrict__ inv_freq, float eps, long long pos0,
+                                                 int row0, int slot, int max_seqs, int max_ctx,
+                                                 float* __restrict__ kc, float* __restrict__ vc) {
+  const int unit = blockIdx.x, i = blockIdx.y, lane = threadIdx.x, half = hd >> 1;
   const int l = unit / (2 * kvh), rem = unit % (2 * kvh), kind = rem / kvh, h = rem % kvh;
   const size_t kvd = (size_t)kvh * hd, N = (size_t)layers * 2 * kvd;
-  const size_t col = ((size_t)l * 2 + kind) * kvd + (size_t)h * hd + d;
-  const float x = d < hd ? reduce_parts(part, S, Mpad, i, N, col) : 0.f;
-  const size_t dst = ((((size_t)l * max_seqs + slot) * kvh + h) * max_ctx + (size_t)(row0 + i)) * hd + d;
+  const size_t col0 = ((size_t)l * 2 + kind) * kvd + (size_t)h * hd;
+  const size_t dst = ((((size_t)l * max_seqs + slot) * kvh + h) * max_ctx + (size_t)(row0 + i)) * hd;
   if (kind == 1) {
-    if (d < hd) vc[dst] = x;
+    for (int d = lane; d < hd; d += 64) vc[dst + d] = reduce_parts(part, S, Mpad, i, N, col0 + d);
     return;
   }
-  const float out = head_norm_rope(x, d, hd, k_norms + (size_t)l * hd, eps, inv_freq, pos0 + i, ybuf, red);
-  if (d < hd) kc[dst] = out;
+  const bool on = lane < half;
+  const float x0 = on ? reduce_parts(part, S, Mpad, i, N, col0 + lane) : 0.f;
+  const float x1 = on ? reduce_parts(part, S, Mpad, i, N, col0 + lane + half) : 0.f;
+  float o0 = 0.f, o1 = 0.f;
+  head_norm_rope(x0, x1, lane, hd, k_norms + (size_t)l * hd, eps, inv_freq, pos0 + i, o0, o1);
+  if (!on) return;
+  kc[dst + lane] = o0;
+  kc[dst + lane + half] = o1;
 }
 
 hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
                             const float* k_norms, const float* inv_freq, float eps, long long pos0, int row0,
                             int slot, int max_seqs, int max_ctx, float* kc, float* vc, hipStream_t st) {
   if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_kv_append, dim3(layers * 2 * kvh, n), dim3(128), 0, st, part, S, Mpad, layers, kvh, hd,
+  hipLaunchKernelGGL(k_kv_append, dim3(layers * 2 * kvh, n), dim3(64), 0, st, part, S, Mpad, layers, kvh, hd,
                      k_norms, inv_freq, eps, pos0, row0, slot, max_seqs, max_ctx, kc, vc);
   return hipGetLastError();
 }

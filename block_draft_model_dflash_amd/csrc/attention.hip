@@ -213,7 +213,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
 // chunks' partial sums with weights exp(m - max) in a fixed order.  Every load (the chunk
 // partials, the block's keys and values, the query) is issued before the first wait.
 constexpr int MERGE_THREADS = 256;
-template <int HD, bool QUANT>
+template <int HD, bool QUANT, int MAXC>
 __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqInfo si, const float* __restrict__ q,
                                                               const float* __restrict__ kb,
                                                               const float* __restrict__ vb,
@@ -222,11 +222,11 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqIn
                                                               int8_t* __restrict__ xq, float* __restrict__ dxT,
                                                               float* __restrict__ xf) {
   constexpr int NG = MERGE_THREADS / HD;       // chunk groups: thread (d, gi) adds chunks gi, gi+NG, ...
-  constexpr int CPG = ATTN_MAXCH / NG;         // chunks per group at most
+  constexpr int CPG = MAXC / NG;               // chunks per group at most (MAXC >= the call's chunks)
   constexpr int KSL = HD / 16;                 // dims per thread of a block score (16 threads a key)
   constexpr int VPG = 16 / NG;                 // block values per thread
   __shared__ double s_sc[16];                  // block scores
-  __shared__ double s_e[16 + ATTN_MAXCH];      // weights: block keys, then chunks
+  __shared__ double s_e[16 + MAXC];            // weights: block keys, then chunks
   __shared__ double s_y[NG][HD];
   __shared__ double s_l;
   const int j = blockIdx.x, r = blockIdx.y, s = blockIdx.z, tid = threadIdx.x, lane = tid & 63;
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqIn
   const int m = s * a.B + r;
 
   // loads, all unconditional (indices clamped into range; what lies past the end is not used)
-  // so they are in flight together
+  // so they are in flight together; the launch picks MAXC just above the call's chunk count
   double accp[CPG];
   const int clast = nch > 0 ? nch - 1 : 0;
 #pragma unroll
@@ -344,16 +344,34 @@ static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const f
   return hipGetLastError();
 }
 
+template <int HD, int MAXC>
+static void attn_merge_launch(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb, const float* vb,
+                              const double* part, const double* ml, int Mpad, bool quant, int8_t* xq, float* dxT,
+                              float* xf, hipStream_t st) {
+  if (quant)
+    hipLaunchKernelGGL((k_attn_merge<HD, true, MAXC>), dim3(a.nh, a.B, si.n), dim3(MERGE_THREADS), 0, st, a, si, q,
+                       kb, vb, part, ml, Mpad, xq, dxT, xf);
+  else
+    hipLaunchKernelGGL((k_attn_merge<HD, false, MAXC>), dim3(a.nh, a.B, si.n), dim3(MERGE_THREADS), 0, st, a, si, q,
+                       kb, vb, part, ml, Mpad, xq, dxT, xf);
+}
+
 template <int HD>
 static hipError_t attn_merge_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
                                 const float* vb, const double* part, const double* ml, int Mpad, bool quant,
                                 int8_t* xq, float* dxT, float* xf, hipStream_t st) {
-  if (quant)
-    hipLaunchKernelGGL((k_attn_merge<HD, true>), dim3(a.nh, a.B, si.n), dim3(MERGE_THREADS), 0, st, a, si, q, kb, vb,
-                       part, ml, Mpad, xq, dxT, xf);
+  int maxn = 0;
+  for (int i = 0; i < si.n; i++) {
+    const int nch = si.nctx[i] > 0 ? (si.nctx[i] + a.ck - 1) / a.ck : 0;
+    if (nch > maxn) maxn = nch;
+  }
+  if (maxn > ATTN_MAXCH) return hipErrorInvalidValue;
+  if (maxn <= 8)
+    attn_merge_launch<HD, 8>(a, si, q, kb, vb, part, ml, Mpad, quant, xq, dxT, xf, st);
+  else if (maxn <= 32)
+    attn_merge_launch<HD, 32>(a, si, q, kb, vb, part, ml, Mpad, quant, xq, dxT, xf, st);
   else
-    hipLaunchKernelGGL((k_attn_merge<HD, false>), dim3(a.nh, a.B, si.n), dim3(MERGE_THREADS), 0, st, a, si, q, kb,
-                       vb, part, ml, Mpad, xq, dxT, xf);
+    attn_merge_launch<HD, ATTN_MAXCH>(a, si, q, kb, vb, part, ml, Mpad, quant, xq, dxT, xf, st);
   return hipGetLastError();
 }
 

@@ -114,6 +114,30 @@ struct Ring {
   static constexpr int step = depth * KW;
 };
 
+// The four groups of superblock r against k-block kk of the staged activations: one
+// v_mfma_i32_16x16x32_i8 per group and m-tile, its exact int32 sums rescaled by d_w * d_x in f64.
+template <int FMT, int MT, int NTW>
+__device__ __forceinline__ void superblock_mfma(const Super<FMT>& r, const int8_t* A, int ASTR,
+                                                const typename DxType<NTW>::T* DX, int MR, int kk, int quarter,
+                                                int row16, double (&acc)[MT][4]) {
+#pragma unroll MT <= 2 ? 4 : 1
+  for (int j = 0; j < 4; j++) {
+    const long b = b_operand(r, j);
+    const double dw = (double)w_scale<FMT>(r, j);
+    const int col = kk * 128 + 32 * j + 8 * quarter;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      const long a = *(const long*)(A + (mt * 16 + row16) * ASTR + col);
+      const v4i sm = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (v4i){0, 0, 0, 0}, 0, 0, 0);
+      const auto dx = *(const typename DxType<NTW>::V*)(DX + (kk * 4 + j) * MR + mt * 16 + 4 * quarter);
+      acc[mt][0] = __builtin_fma((double)sm[0], dw * (double)dx[0], acc[mt][0]);
+      acc[mt][1] = __builtin_fma((double)sm[1], dw * (double)dx[1], acc[mt][1]);
+      acc[mt][2] = __builtin_fma((double)sm[2], dw * (double)dx[2], acc[mt][2]);
+      acc[mt][3] = __builtin_fma((double)sm[3], dw * (double)dx[3], acc[mt][3]);
+    }
+  }
+}
+
 // One workgroup: NTW n-tiles x KW k-waves.  Wave (nt, kw) streams the superblocks kb = kw,
 // kw + KW, ... of n-tile blockIdx.x*NTW + nt through its register ring; the activations of a
 // chunk of kcb k-blocks (a multiple of the ring's step, so the ring runs on across chunks) are
@@ -239,25 +263,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
 #pragma unroll
       for (int p = 0; p < RD; p++) {
         const int kbp = kb + p * KW;
-        {
-          const int kk = min(kbp, c1 - 1) - c0;
-#pragma unroll MT <= 2 ? 4 : 1
-          for (int j = 0; j < 4; j++) {
-            const long b = b_operand(r[p], j);
-            const double dw = (double)w_scale<FMT>(r[p], j);
-            const int col = kk * 128 + 32 * j + 8 * quarter;
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
-              const long a = *(const long*)(A + (mt * 16 + row16) * ASTR + col);
-              const v4i sm = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (v4i){0, 0, 0, 0}, 0, 0, 0);
-              const auto dx = *(const typename DxType<NTW>::V*)(DX + (kk * 4 + j) * MR + mt * 16 + 4 * quarter);
-              acc[mt][0] = __builtin_fma((double)sm[0], dw * (double)dx[0], acc[mt][0]);
-              acc[mt][1] = __builtin_fma((double)sm[1], dw * (double)dx[1], acc[mt][1]);
-              acc[mt][2] = __builtin_fma((double)sm[2], dw * (double)dx[2], acc[mt][2]);
-              acc[mt][3] = __builtin_fma((double)sm[3], dw * (double)dx[3], acc[mt][3]);
-            }
-          }
-        }
+        superblock_mfma<FMT, MT, NTW>(r[p], A, ASTR, DX, MR, min(kbp, c1 - 1) - c0, quarter, row16, acc);
         // refill the slot with this wave's superblock one ring turn ahead
         super_load(rs, (kbp + STEP) * SBB, lane, r[p]);
       }

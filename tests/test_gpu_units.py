@@ -91,6 +91,10 @@ def test_group_sums_bit_exact(fmt, rows, cols, m):
 @pytest.mark.parametrize("rows,cols,m", GEMM_SHAPES)
 @pytest.mark.parametrize("splits", [0, 1, 2, 8])
 def test_gemm_correctly_rounded(fmt, rows, cols, m, splits):
+    _check_gemm(fmt, rows, cols, m, splits)
+
+
+def _check_gemm(fmt, rows, cols, m, splits):
     """The product is the f32 rounding of its exact value, as the oracle's f64 evaluation: equal
     to the oracle's f32 except where the two f64 sums straddle a rounding boundary (rare), and
     never more than one ulp apart."""
@@ -119,3 +123,11 @@ def test_gemm_correctly_rounded(fmt, rows, cols, m, splits):
     ulp = np.spacing(np.abs(ref32)).astype(np.float64)
     assert np.all(err <= ulp)
     assert np.mean(got == ref32) >= 0.999
+
+
+# thousands of n-tiles with 16 activation rows: workgroups of eight n-tiles (ragged: 1025 tiles
+# are not a whole number of eight-tile blocks)
+@pytest.mark.parametrize("fmt", [di.Q4_32, di.Q8_32], ids=["q4", "q8"])
+@pytest.mark.parametrize("rows,cols,m", [(16400, 2048, 16), (16400, 4096, 3)])
+def test_gemm_many_tiles(fmt, rows, cols, m):
+    _check_gemm(fmt, rows, cols, m, 0)
