@@ -799,7 +799,7 @@ int dflash_top_k(const float* x, int32_t rows, int32_t width, int32_t ld, int32_
 int dflash_select_scratch_bytes(int32_t rows, int32_t width, int32_t top, size_t* bytes) {
   size_t tk;
   if (!bytes || dflash_top_k_scratch_bytes(rows, width, top, &tk)) return DFLASH_EINVAL;
-  *bytes = tk + 2 * align256((size_t)rows * top * 4);
+  *bytes = tk + 2 * align256((size_t)rows * top * 4) + align256(select_scratch(rows, top));
   return DFLASH_OK;
 }
 
@@ -816,8 +816,9 @@ int dflash_select(const float* logits, int32_t rows, int32_t width, int32_t ld, 
   int* pi = (int*)((uint8_t*)scratch + tk / 2);
   float* cv = (float*)((uint8_t*)scratch + tk);
   int* ci = (int*)((uint8_t*)scratch + tk + align256((size_t)rows * top * 4));
+  float* scores = (float*)((uint8_t*)scratch + tk + 2 * align256((size_t)rows * top * 4));
   hipError_t e = launch_top_k(logits, rows, width, ld, top, pv, pi, cv, ci, st);
-  if (e == hipSuccess) e = launch_select(cv, ci, rows, top, hp, rank, pred, succ, anchor, chosen, plain, st);
+  if (e == hipSuccess) e = launch_select(cv, ci, rows, top, hp, rank, pred, succ, anchor, chosen, plain, scores, st);
   return e == hipSuccess ? DFLASH_OK : unit_fail(DFLASH_EHIP, "select", e);
 }
 

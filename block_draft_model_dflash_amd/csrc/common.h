@@ -138,7 +138,8 @@ hipError_t launch_top_k(const float* x, int rows, int width, int ld, int T, floa
 size_t top_k_scratch(int rows, int width, int T);
 hipError_t launch_select(const float* cv, const int* ci, int rows, int T, const float* hp, int rank,
                          const uint16_t* pred, const uint16_t* succ, int anchor, int* chosen, int* plain,
-                         hipStream_t st);
+                         float* scores, hipStream_t st);
+size_t select_scratch(int rows, int T);
 
 hipError_t launch_inv_freq(double theta, int hd, float* out, hipStream_t st);
 hipError_t launch_quant_rows(const float* x, int rows, int cols, int8_t* q, float* d, hipStream_t st);

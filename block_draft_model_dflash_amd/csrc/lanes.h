@@ -128,3 +128,73 @@ __device__ __forceinline__ void emit_a8(float y, size_t qi, int8_t* __restrict__
 }
 
 }  // namespace dfl
+
+namespace dfl {
+
+// Arg-max in the order (larger value first, smaller index first among equal values): the order a
+// top-k list keeps.  Over distinct indices it is a strict total order, so every lane of the wave
+// ends with the same winner.
+__device__ __forceinline__ bool argmax_better(float av, int ai, float bv, int bi) {
+  return av > bv || (av == bv && ai < bi);
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& v, int& i) {
+  const float ov = dpp_f32<CTRL>(v);
+  const int oi = (int)dpp_u32<CTRL>((unsigned)i);
+  if (argmax_better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+__device__ __forceinline__ void argmax_pick(unsigned vl, unsigned vh, unsigned il, unsigned ih, float& v, int& i) {
+  const bool h = argmax_better(__uint_as_float(vh), (int)ih, __uint_as_float(vl), (int)il);
+  v = __uint_as_float(h ? vh : vl);
+  i = (int)(h ? ih : il);
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_dpp<DPP_XOR1>(v, i);
+  argmax_dpp<DPP_XOR2>(v, i);
+  argmax_dpp<DPP_HALF_MIRROR>(v, i);
+  argmax_dpp<DPP_MIRROR>(v, i);
+  unsigned vl, vh, il, ih;
+  swap16_u32(__float_as_uint(v), vl, vh);
+  swap16_u32((unsigned)i, il, ih);
+  argmax_pick(vl, vh, il, ih, v, i);
+  swap32_u32(__float_as_uint(v), vl, vh);
+  swap32_u32((unsigned)i, il, ih);
+  argmax_pick(vl, vh, il, ih, v, i);
+}
+
+}  // namespace dfl
+
+namespace dfl {
+
+// Maximum of a 64-bit unsigned key over the wave (every lane ends with it).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+  const unsigned lo = dpp_u32<CTRL>((unsigned)x), hi = dpp_u32<CTRL>((unsigned)(x >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+  unsigned long long y;
+  y = dpp_u64<DPP_XOR1>(x);
+  x = y > x ? y : x;
+  y = dpp_u64<DPP_XOR2>(x);
+  x = y > x ? y : x;
+  y = dpp_u64<DPP_HALF_MIRROR>(x);
+  x = y > x ? y : x;
+  y = dpp_u64<DPP_MIRROR>(x);
+  x = y > x ? y : x;
+  unsigned l0, h0, l1, h1;
+  swap16_u32((unsigned)x, l0, h0);
+  swap16_u32((unsigned)(x >> 32), l1, h1);
+  unsigned long long a = ((unsigned long long)l1 << 32) | l0, b = ((unsigned long long)h1 << 32) | h0;
+  x = a > b ? a : b;
+  swap32_u32((unsigned)x, l0, h0);
+  swap32_u32((unsigned)(x >> 32), l1, h1);
+  a = ((unsigned long long)l1 << 32) | l0;
+  b = ((unsigned long long)h1 << 32) | h0;
+  return a > b ? a : b;
+}
+
+}  // namespace dfl

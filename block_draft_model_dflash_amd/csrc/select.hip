@@ -10,6 +10,7 @@
 // same way.  The re-scoring repeats the pages' f32 arithmetic term by term, in their order and
 // without contraction, so its decisions are those of the reference evaluation.
 #include "common.h"
+#include "lanes.h"
 
 namespace dfl {
 
@@ -17,73 +18,71 @@ constexpr int TK_THREADS = 256;
 constexpr int TK_PER = 16;                       // elements each thread owns
 constexpr int TK_CHUNK = TK_THREADS * TK_PER;   // elements of one chunk
 
-__device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+// An element as one 64-bit key whose unsigned order is the top-k order: the high word is the
+// value's bits made monotone (-0 first made +0, so it ties with +0 as a float compare does), the
+// low word 0xffffffff - index, so among equal values the earlier index is larger.  Key 0: empty.
+__device__ __forceinline__ unsigned long long topk_key(float v, int i) {
+  const unsigned b = __float_as_uint(v + 0.0f);
+  const unsigned o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((unsigned long long)o << 32) | (0xffffffffu - (unsigned)i);
+}
+__device__ __forceinline__ void topk_decode(unsigned long long k, float& v, int& i) {
+  const unsigned o = (unsigned)(k >> 32);
+  v = k ? __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o) : -INFINITY;
+  i = k ? (int)(0xffffffffu - (unsigned)k) : -1;
 }
 
-// T rounds of a workgroup arg-max over the (v[e], ix[e]) of every thread (ix < 0: empty).
-// Round t's winner is written by thread 0 to out_v[t], out_i[t].
-__device__ void block_top(const float (&v)[TK_PER], const int (&ix)[TK_PER], int T, float* out_v, int* out_i) {
-  __shared__ float wv[2][TK_THREADS / 64];
-  __shared__ int wi[2][TK_THREADS / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  unsigned taken = 0;
+// T rounds of a wave-wide maximum over every lane's keys; the winner is cleared where it sits
+// (indices are distinct), and round t's winner goes to out[t] (0: the round found nothing).
+template <int PER>
+__device__ __forceinline__ void wave_top(unsigned long long (&key)[PER], int T, unsigned long long* out) {
+  const int lane = threadIdx.x & 63;
   for (int t = 0; t < T; t++) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    unsigned long long best = 0;
 #pragma unroll
-    for (int e = 0; e < TK_PER; e++)
-      if (ix[e] >= 0 && !((taken >> e) & 1u) && better(v[e], ix[e], bv, bi)) {
-        bv = v[e];
-        bi = ix[e];
-      }
+    for (int e = 0; e < PER; e++) best = key[e] > best ? key[e] : best;
+    best = wave_max_u64(best);
 #pragma unroll
-    for (int o = 32; o; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    const int slot = t & 1;  // alternate buffers: one barrier per round
-    if (lane == 0) {
-      wv[slot][wave] = bv;
-      wi[slot][wave] = bi;
-    }
-    __syncthreads();
-    bv = wv[slot][0];
-    bi = wi[slot][0];
-#pragma unroll
-    for (int w = 1; w < TK_THREADS / 64; w++)
-      if (better(wv[slot][w], wi[slot][w], bv, bi)) {
-        bv = wv[slot][w];
-        bi = wi[slot][w];
-      }
-#pragma unroll
-    for (int e = 0; e < TK_PER; e++)
-      if (ix[e] == bi) taken |= 1u << e;
-    if (tid == 0) {  // a round that found nothing (a short chunk) leaves index -1
-      out_v[t] = bv;
-      out_i[t] = bi == 0x7fffffff ? -1 : bi;
-    }
+    for (int e = 0; e < PER; e++) key[e] = key[e] == best ? 0ull : key[e];
+    if (lane == 0) out[t] = best;
   }
+}
+
+// The top T of the keys of the whole workgroup: each wave finds its own top T (no barrier
+// between rounds), then wave 0 finds the top T of those 4T keys.  Written by the first T lanes
+// of wave 0 to out_v, out_i (index -1 where there are fewer than T elements).
+__device__ void block_top(unsigned long long (&key)[TK_PER], int T, float* out_v, int* out_i) {
+  constexpr int NW = TK_THREADS / 64;
+  __shared__ unsigned long long lk[NW][64];
+  __shared__ unsigned long long ok[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  wave_top<TK_PER>(key, T, lk[wave]);
+  __syncthreads();
+  if (wave != 0) return;
+  unsigned long long ck[NW];
+#pragma unroll
+  for (int k = 0; k < NW; k++) {
+    const int j = lane + 64 * k, w = min(j / T, NW - 1), t = j % T;
+    ck[k] = j < NW * T ? lk[w][t] : 0ull;
+  }
+  wave_top<NW>(ck, T, ok);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // lane 0's stores before the lanes' loads
+  if (lane < T) topk_decode(ok[lane], out_v[lane], out_i[lane]);
 }
 
 // Grid (chunks, rows): the top T of elements [c*4096, (c+1)*4096) of row r.
 __global__ __launch_bounds__(TK_THREADS) void k_topk_chunk(const float* __restrict__ x, int width, int ld, int T,
                                                           float* __restrict__ pv, int* __restrict__ pi) {
   const int c = blockIdx.x, r = blockIdx.y, nch = gridDim.x, tid = threadIdx.x;
-  float v[TK_PER];
-  int ix[TK_PER];
+  unsigned long long key[TK_PER];
 #pragma unroll
   for (int e = 0; e < TK_PER; e++) {
     const int i = c * TK_CHUNK + e * TK_THREADS + tid;
-    ix[e] = i < width ? i : -1;
-    v[e] = i < width ? x[(size_t)r * ld + i] : -INFINITY;
+    const float v = x[(size_t)r * ld + min(i, width - 1)];
+    key[e] = i < width ? topk_key(v, i) : 0ull;
   }
   const size_t o = ((size_t)r * nch + c) * T;
-  block_top(v, ix, T, pv + o, pi + o);
+  block_top(key, T, pv + o, pi + o);
 }
 
 // Grid (rows): the top T of a row from its chunks' lists (nch * T <= 4096 entries).
@@ -91,16 +90,15 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_merge(const float* __restri
                                                           int nch, int T, float* __restrict__ vals,
                                                           int* __restrict__ idx) {
   const int r = blockIdx.x, tid = threadIdx.x, n = nch * T;
-  float v[TK_PER];
-  int ix[TK_PER];
+  unsigned long long key[TK_PER];
 #pragma unroll
   for (int e = 0; e < TK_PER; e++) {
-    const int j = e * TK_THREADS + tid;
-    const bool ok = j < n && pi[(size_t)r * n + j] >= 0;
-    ix[e] = ok ? pi[(size_t)r * n + j] : -1;
-    v[e] = ok ? pv[(size_t)r * n + j] : -INFINITY;
+    const int j = min(e * TK_THREADS + tid, n - 1);
+    const int i = pi[(size_t)r * n + j];
+    const float v = pv[(size_t)r * n + j];
+    key[e] = e * TK_THREADS + tid < n && i >= 0 ? topk_key(v, i) : 0ull;
   }
-  block_top(v, ix, T, vals + (size_t)r * T, idx + (size_t)r * T);
+  block_top(key, T, vals + (size_t)r * T, idx + (size_t)r * T);
 }
 
 hipError_t launch_top_k(const float* x, int rows, int width, int ld, int T, float* part_v, int* part_i, float* vals,
@@ -169,10 +167,121 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const float* __restrict_
   }
 }
 
+// The same re-scoring computed for every predecessor a row can have, then a chain of look-ups.
+// Row j's predecessor is the anchor (j = 0) or one of the T candidates of row j-1, so a
+// workgroup per row forms the score of every (predecessor option p, candidate c) pair with the
+// pages' arithmetic: pc = pred[p] * hp[j] (an f32 product per term), then candidate c's logit +
+// the f32 sum of pc[r] * succ[c][r] from r = 0 upward.  One thread a pair, so the T*T sequential
+// sums run side by side.  A single wave then walks the rows: the first largest score among
+// scores[j][prev] names row j's choice, which is row j+1's predecessor option.
+constexpr int SELP_THREADS = 256;
+size_t select_par_lds_bytes(int T, int rank) {
+  return (size_t)T * rank * 2 * 2 + (size_t)T * rank * 4 + (size_t)rank * 4 + (size_t)T * 8 * 2;
+}
+__global__ __launch_bounds__(SELP_THREADS) void k_select_scores(const float* __restrict__ cv,
+                                                               const int* __restrict__ ci, int T,
+                                                               const float* __restrict__ hp, int rank,
+                                                               const uint16_t* __restrict__ pred,
+                                                               const uint16_t* __restrict__ succ, int anchor,
+                                                               float* __restrict__ scores) {
+#pragma clang fp contract(off)
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int j = blockIdx.x, tid = threadIdx.x, np = j ? T : 1;
+  uint16_t* PV = (uint16_t*)lds;                // [np][rank] predecessor rows
+  uint16_t* SU = PV + (size_t)T * rank;         // [T][rank] successor rows
+  float* PC = (float*)(SU + (size_t)T * rank);  // [np][rank]
+  float* HP = PC + (size_t)T * rank;            // [rank]
+  int* PT = (int*)(HP + rank);                  // [T] predecessor tokens
+  int* ST = PT + T;                             // [T] candidate tokens
+  if (tid < T) {
+    PT[tid] = j ? max(ci[(j - 1) * T + tid], 0) : anchor;  // -1 only from non-finite logits
+    ST[tid] = max(ci[j * T + tid], 0);
+  }
+  for (int r = tid; r < rank; r += SELP_THREADS) HP[r] = hp[(size_t)j * rank + r];
+  __syncthreads();
+  for (int e = tid; e < np * rank; e += SELP_THREADS) PV[e] = pred[(size_t)PT[e / rank] * rank + e % rank];
+  for (int e = tid; e < T * rank; e += SELP_THREADS) SU[e] = succ[(size_t)ST[e / rank] * rank + e % rank];
+  __syncthreads();
+  for (int e = tid; e < np * rank; e += SELP_THREADS) PC[e] = f16_bits_to_f32(PV[e]) * HP[e % rank];
+  __syncthreads();
+  for (int e = tid; e < np * T; e += SELP_THREADS) {
+    const int pp = e / T, c = e % T;
+    const float* pc = PC + (size_t)pp * rank;
+    const uint16_t* su = SU + (size_t)c * rank;
+    float sum = 0.0f;
+    for (int r = 0; r < rank; r++) {
+      const float prod = pc[r] * f16_bits_to_f32(su[r]);  // rounded on its own (no contraction here)
+      sum = sum + prod;
+    }
+    scores[((size_t)j * T + pp) * T + c] = cv[j * T + c] + sum;
+  }
+}
+
+// One wave: row by row, the first largest of scores[j][prev][0..T) (prev: 0 for row 0, then the
+// previous row's choice).  The scores are first copied to LDS when they fit (STAGE), so each
+// step of the chain waits for LDS, not memory.
+constexpr int CHAIN_THREADS = 256;
+template <bool STAGE>
+__global__ __launch_bounds__(CHAIN_THREADS) void k_select_chain(const float* __restrict__ scores,
+                                                               const int* __restrict__ ci, int rows, int T,
+                                                               int* __restrict__ chosen, int* __restrict__ plain) {
+  extern __shared__ float sl[];
+  __shared__ int cl[16 * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const float* S = scores;
+  const int* C = ci;
+  if (STAGE) {  // all threads copy, eight loads each in flight; the candidate lists too
+    for (int e = tid; e < rows * T; e += CHAIN_THREADS) cl[e] = ci[e];
+    C = cl;
+    const int n = rows * T * T;
+    for (int base = tid; base < n; base += CHAIN_THREADS * 8) {
+      float v[8];
+#pragma unroll
+      for (int b = 0; b < 8; b++) v[b] = scores[min(base + b * CHAIN_THREADS, n - 1)];
+#pragma unroll
+      for (int b = 0; b < 8; b++)
+        if (base + b * CHAIN_THREADS < n) sl[base + b * CHAIN_THREADS] = v[b];
+    }
+    __syncthreads();
+    S = sl;
+  }
+  if (tid >= 64) return;
+  int prev = 0;
+  for (int j = 0; j < rows; j++) {
+    const float sc0 = lane < T ? S[((size_t)j * T + prev) * T + lane] : -INFINITY;  // T <= 64
+    float sc = sc0;
+    int c = lane;  // lanes >= T hold -inf behind every candidate
+    wave_argmax(sc, c);
+    c = c < T ? c : 0;  // (only a NaN score could leave a lane past T on top)
+    if (lane == 0) {
+      chosen[j] = max(C[j * T + c], 0);
+      plain[j] = C[j * T];
+    }
+    prev = c;
+  }
+}
+
+size_t select_scratch(int rows, int T) { return (size_t)rows * T * T * 4; }
+
 hipError_t launch_select(const float* cv, const int* ci, int rows, int T, const float* hp, int rank,
                          const uint16_t* pred, const uint16_t* succ, int anchor, int* chosen, int* plain,
-                         hipStream_t st) {
+                         float* scores, hipStream_t st) {
   if (T < 1 || T > 64 || rank < 1 || (size_t)rank * 4 > 48 * 1024) return hipErrorInvalidValue;
+  const size_t lds = select_par_lds_bytes(T, rank);
+  if (scores && lds <= max_dynamic_lds()) {
+    hipError_t e = allow_lds((const void*)k_select_scores, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_select_scores, dim3(rows), dim3(SELP_THREADS), lds, st, cv, ci, T, hp, rank, pred, succ,
+                       anchor, scores);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t sb = select_scratch(rows, T);
+    if (sb <= 48 * 1024 && rows * T <= 16 * 64)
+      hipLaunchKernelGGL(k_select_chain<true>, dim3(1), dim3(CHAIN_THREADS), sb, st, scores, ci, rows, T, chosen, plain);
+    else
+      hipLaunchKernelGGL(k_select_chain<false>, dim3(1), dim3(CHAIN_THREADS), 0, st, scores, ci, rows, T, chosen, plain);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_select, dim3(1), dim3(SEL_THREADS), (size_t)rank * 4, st, cv, ci, rows, T, hp, rank, pred, succ,
                      anchor, chosen, plain);
   return hipGetLastError();

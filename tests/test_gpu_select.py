@@ -72,7 +72,10 @@ def _gpu_select(logits, hp, pred, succ, top, anchor, ld=None):
     return chosen.cpu().numpy(), plain.cpu().numpy()
 
 
-@pytest.mark.parametrize("rows,vocab,rank,top", [(7, 1000, 32, 8), (15, 151936, 128, 16), (3, 50, 5, 50)])
+# scores for every predecessor option with the rows' tables in LDS (the first four), and the
+# sequential kernel when the tables exceed LDS (rank 4096 with 40 candidates)
+@pytest.mark.parametrize("rows,vocab,rank,top", [(7, 1000, 32, 8), (15, 151936, 128, 16), (3, 50, 5, 50),
+                                                 (15, 40000, 128, 64), (2, 100, 4096, 40)])
 def test_select_matches_the_oracle(rows, vocab, rank, top):
     rng = np.random.default_rng(rows * 7 + rank)
     say(f"select rows={rows} vocab={vocab} rank={rank} top={top}")
