@@ -45,10 +45,10 @@ template <int HD>
 constexpr size_t attn_comb_bytes() {
   return (size_t)ATTN_WAVES * 16 * (HD + 1) * 8 + (size_t)ATTN_WAVES * 16 * 3 * 8;
 }
-// all of a workgroup's LDS: the combine, then the queries (16 rows of HD + 4 floats)
+// all of a workgroup's LDS: the combine, then the queries (16 rows of HD + 2 doubles)
 template <int HD>
 constexpr size_t attn_lds_bytes() {
-  return attn_comb_bytes<HD>() + (size_t)16 * (HD + 4) * 4;
+  return attn_comb_bytes<HD>() + (size_t)16 * (HD + 2) * 8;
 }
 
 // Grid: ceil(tasks / 8) * 8 * rep workgroups for tasks (sequence, kv head, chunk) numbered
@@ -77,14 +77,16 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
   const float* Kctx = kc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
   const float* Vctx = vc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
 
-  // the head's queries in LDS (rows HD + 4 floats apart: the 16 rows of one 128-bit read fall
-  // in different banks), the B operand of the scores: q[row col][16*i4 + 4*quarter ..]
-  constexpr int QS = HD + 4;
-  float* Qs = (float*)(lds + attn_comb_bytes<HD>());
+  // the head's queries in LDS as f64 (converted once here, not once per tile; rows HD + 2
+  // doubles apart, so the 16 rows of one read fall in different banks), the B operand of the
+  // scores: q[row col][16*i4 + 4*quarter ..]
+  constexpr int QS = HD + 2;
+  double* Qs = (double*)(lds + attn_comb_bytes<HD>());
   for (int e = tid; e < 16 * HD / 4; e += ATTN_THREADS) {
     const int row = e / (HD / 4), c4 = e % (HD / 4);
     const int rr = min(row, a.B - 1);  // rows past B: a copy of the last (their results are not kept)
-    *(v4f*)(Qs + row * QS + 4 * c4) = *(const v4f*)(q + ((size_t)(s * a.B + rr) * a.nh + j) * HD + 4 * c4);
+    const v4f qv = *(const v4f*)(q + ((size_t)(s * a.B + rr) * a.nh + j) * HD + 4 * c4);
+    *(v4d*)(Qs + row * QS + 4 * c4) = (v4d){(double)qv[0], (double)qv[1], (double)qv[2], (double)qv[3]};
   }
   __syncthreads();
   double m_run = -INFINITY, l_run = 0.0;
@@ -128,11 +130,11 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
     v4d st0 = (v4d){0.0, 0.0, 0.0, 0.0}, st1 = st0;
 #pragma unroll
     for (int i4 = 0; i4 < NI; i4++) {
-      const v4f qv = *(const v4f*)(Qs + col * QS + 16 * i4 + 4 * quarter);
-      st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][0], (double)qv[0], st0, 0, 0, 0);
-      st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][1], (double)qv[1], st1, 0, 0, 0);
-      st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][2], (double)qv[2], st0, 0, 0, 0);
-      st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][3], (double)qv[3], st1, 0, 0, 0);
+      const v4d qv = *(const v4d*)(Qs + col * QS + 16 * i4 + 4 * quarter);
+      st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][0], qv[0], st0, 0, 0, 0);
+      st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][1], qv[1], st1, 0, 0, 0);
+      st0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][2], qv[2], st0, 0, 0, 0);
+      st1 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)kr[i4][3], qv[3], st1, 0, 0, 0);
     }
     load_k(min(i + ATTN_WAVES, last));  // the next tile's keys travel during the softmax and values
     double p[4], mx = -INFINITY;
@@ -144,7 +146,6 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
     }
     mx = cross4_max_f64(mx);  // the same query's slots in the other three lane rows
     const double m_new = fmax(m_run, mx);
-    const double corr = exp(m_run - m_new);
     double ps = 0.0;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -152,11 +153,19 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
       ps += p[r];
     }
     ps = cross4_sum_f64(ps);
-    l_run = l_run * corr + ps;
+    // after the first tiles the running maxima rarely move; where none of the wave's does,
+    // exp(m_run - m_new) is exactly 1, so the rescaling (an exact no-op then) is skipped
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      const double corr = exp(m_run - m_new);
+      l_run = l_run * corr + ps;
+#pragma unroll
+      for (int dt = 0; dt < NI; dt++) acc[dt] *= corr;
+    } else {
+      l_run = l_run + ps;
+    }
     m_run = m_new;
 #pragma unroll
     for (int dt = 0; dt < NI; dt++) {
-      acc[dt] *= corr;
 #pragma unroll
       for (int k = 0; k < 4; k++)  // step k pairs the probabilities of slot k with those keys' values
         acc[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[k][dt >> 2][dt & 3], p[k], acc[dt], 0, 0, 0);
