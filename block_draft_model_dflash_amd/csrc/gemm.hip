@@ -138,6 +138,95 @@ __device__ __forceinline__ void superblock_mfma(const Super<FMT>& r, const int8_
   }
 }
 
+// The end of a workgroup's product: the k-waves' sums, then the epilogue.  Every wave leaves its
+// partials in LDS and k-wave s % KW adds slot s's in wave order (the same order on every run)
+// and finishes it.  Output slot s = 4*mt + q of the accumulators is rows m0 + 16*mt + 4*quarter +
+// q, column row16 of n-tile ntile.
+template <int FMT, int MT, int NTW, int KW>
+__device__ __forceinline__ void gemm_finish(double (&acc)[MT][4], const float (&hres)[MT][4], uint8_t* smem,
+                                            const GemmOut& o, int N, int m0, int nb, int ntile, bool active,
+                                            int nt, int kw) {
+  constexpr int MR = MT * 16, NT = 64 * NTW * KW;
+  const int tid = threadIdx.x, lane = tid & 63, quarter = lane >> 4, row16 = lane & 15, Mpad = o.Mpad;
+  auto mine = [&](int s) { return KW == 1 || s % KW == kw; };
+  if (KW > 1) {
+    __syncthreads();
+    double* red = (double*)smem;
+    if (active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) red[(((kw * NTW + nt) * MT + mt) * 4 + q) * 64 + lane] = acc[mt][q];
+    __syncthreads();
+    if (active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          if (mine(4 * mt + q)) {
+            double v = red[((nt * MT + mt) * 4 + q) * 64 + lane];
+            for (int k = 1; k < KW; k++) v += red[(((k * NTW + nt) * MT + mt) * 4 + q) * 64 + lane];
+            acc[mt][q] = v;
+          }
+  }
+  const double post = FMT == Q4 ? 0.0625 : 1.0;  // Q4 codes entered the MFMA as 16*q
+  const int n = ntile * 16 + row16;
+
+  if (o.epi == EPI_SWIGLU) {
+    // NTW = 4g: each group of four n-tiles gate(2b), up(2b), gate(2b+1), up(2b+1) (b = nb*NTW/4 +
+    // group) gives the 32 columns 32b.. of a = silu(gate) * up, one A8 group per row
+    constexpr int WC = NTW * 16, AC = NTW * 8;  // product columns and a columns of the workgroup
+    __syncthreads();
+    float* G = (float*)smem;  // [MR][WC]: the tiles' f32 products
+    if (active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          if (mine(4 * mt + q)) G[(mt * 16 + 4 * quarter + q) * WC + nt * 16 + row16] = (float)(acc[mt][q] * post);
+    __syncthreads();
+    const int I = N >> 1;
+    for (int i = tid; i < MR * AC; i += NT) {
+      const int ml = i / AC, j = i % AC, m = m0 + ml;
+      if (m >= Mpad) break;  // whole 32-lane groups leave together (AC is a multiple of 32)
+      const int jj = j & 31;
+      const int gc = (j >> 5) * 64 + (jj >> 4) * 32 + (jj & 15);
+      const double g = G[ml * WC + gc], u = G[ml * WC + gc + 16];
+      const float a = (float)(g / (1.0 + exp(-g)) * u);
+      const int c = nb * AC + j;
+      if (o.xq)
+        emit_a8(a, (size_t)m * I + c, o.xq, o.dxT, (size_t)(c >> 5) * Mpad + m, lane);
+      else
+        o.xf[(size_t)m * I + c] = a;
+    }
+    return;
+  }
+  if (!active) return;
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      if (!mine(4 * mt + q)) continue;
+      const int m = m0 + mt * 16 + 4 * quarter + q;
+      const double v = acc[mt][q] * post;
+      if (o.epi == EPI_F64) {
+        if (m < Mpad) ((double*)o.y)[(size_t)m * N + n] = v;
+      } else if (o.epi == EPI_F32) {
+        if (m < o.m_store) ((float*)o.y)[(size_t)m * o.ld + n] = (float)v;
+      } else {  // EPI_RESID: h += f32(v), and the tile's share of each row's sum of squares
+        double sq = 0.0;
+        if (m < o.M) {
+          const float hv = hres[mt][q] + (float)v;
+          o.h[(size_t)m * N + n] = hv;
+          sq = (double)hv * (double)hv;
+        }
+        sq = row16_sum_f64(sq);
+        if (row16 == 0 && m < Mpad) o.ssq[(size_t)m * (N >> 4) + ntile] = sq;
+      }
+    }
+  }
+}
+
 // One workgroup: NTW n-tiles x KW k-waves.  Wave (nt, kw) streams the superblocks kb = kw,
 // kw + KW, ... of n-tile blockIdx.x*NTW + nt through its register ring; the activations of a
 // chunk of kcb k-blocks (a multiple of the ring's step, so the ring runs on across chunks) are
@@ -293,84 +382,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
     if (active) chunk(c0, c1);
   }
 
-  // the k-waves' sums: every wave leaves its partials in LDS, and k-wave s % KW adds slot s's
-  // in wave order (the same order on every run) and finishes it
-  if (KW > 1) {
-    __syncthreads();
-    double* red = (double*)smem;
-    if (active)
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) red[(((kw * NTW + nt) * MT + mt) * 4 + q) * 64 + lane] = acc[mt][q];
-    __syncthreads();
-    if (active)
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-          if (mine(4 * mt + q)) {
-            double v = red[((nt * MT + mt) * 4 + q) * 64 + lane];
-            for (int k = 1; k < KW; k++) v += red[(((k * NTW + nt) * MT + mt) * 4 + q) * 64 + lane];
-            acc[mt][q] = v;
-          }
-  }
-  const double post = FMT == Q4 ? 0.0625 : 1.0;  // Q4 codes entered the MFMA as 16*q
-  const int n = ntile * 16 + row16;
-
-  if (o.epi == EPI_SWIGLU) {
-    // NTW = 4g: each group of four n-tiles gate(2b), up(2b), gate(2b+1), up(2b+1) (b = nb*NTW/4 +
-    // group) gives the 32 columns 32b.. of a = silu(gate) * up, one A8 group per row
-    constexpr int WC = NTW * 16, AC = NTW * 8;  // product columns and a columns of the workgroup
-    __syncthreads();
-    float* G = (float*)smem;  // [MR][WC]: the tiles' f32 products
-    if (active)
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++)
-#pragma unroll
-        for (int q = 0; q < 4; q++)
-          if (mine(4 * mt + q)) G[(mt * 16 + 4 * quarter + q) * WC + nt * 16 + row16] = (float)(acc[mt][q] * post);
-    __syncthreads();
-    const int I = N >> 1;
-    for (int i = tid; i < MR * AC; i += NT) {
-      const int ml = i / AC, j = i % AC, m = m0 + ml;
-      if (m >= Mpad) break;  // whole 32-lane groups leave together (AC is a multiple of 32)
-      const int jj = j & 31;
-      const int gc = (j >> 5) * 64 + (jj >> 4) * 32 + (jj & 15);
-      const double g = G[ml * WC + gc], u = G[ml * WC + gc + 16];
-      const float a = (float)(g / (1.0 + exp(-g)) * u);
-      const int c = nb * AC + j;
-      if (o.xq)
-        emit_a8(a, (size_t)m * I + c, o.xq, o.dxT, (size_t)(c >> 5) * Mpad + m, lane);
-      else
-        o.xf[(size_t)m * I + c] = a;
-    }
-    return;
-  }
-  if (!active) return;
-#pragma unroll
-  for (int mt = 0; mt < MT; mt++) {
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      if (!mine(4 * mt + q)) continue;
-      const int m = m0 + mt * 16 + 4 * quarter + q;
-      const double v = acc[mt][q] * post;
-      if (o.epi == EPI_F64) {
-        if (m < Mpad) ((double*)o.y)[(size_t)m * N + n] = v;
-      } else if (o.epi == EPI_F32) {
-        if (m < o.m_store) ((float*)o.y)[(size_t)m * o.ld + n] = (float)v;
-      } else {  // EPI_RESID: h += f32(v), and the tile's share of each row's sum of squares
-        double sq = 0.0;
-        if (m < o.M) {
-          const float hv = hres[mt][q] + (float)v;
-          o.h[(size_t)m * N + n] = hv;
-          sq = (double)hv * (double)hv;
-        }
-        sq = row16_sum_f64(sq);
-        if (row16 == 0 && m < Mpad) o.ssq[(size_t)m * (N >> 4) + ntile] = sq;
-      }
-    }
-  }
+  gemm_finish<FMT, MT, NTW, KW>(acc, hres, smem, o, N, m0, nb, ntile, active, nt, kw);
 }
 
 // The integer accumulators of the same tiles: sums[m][n][g] for every group (Q4 shifted back).
