@@ -88,6 +88,9 @@ def lib(path: str | None = None):
             "og_ctx_span": (i32, [vp, i32, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
             "og_read_kv": (i32, [vp, i32, i32, i32, i32, vp, vp]),
             "og_block_forward": (i32, [vp, i32, vp, vp, vp, vp]),
+            "og_block_forward_rows": (i32, [vp, i32, vp, vp, vp, i32, vp]),
+            "og_set_layer_options": (i32, [vp, vp, vp]),
+            "og_dropped": (i64, [vp, i32, i32]),
             "og_block_hidden": (i32, [vp, i32, vp, vp, vp, vp]),
             "og_top_k": (None, [vp, i32, i32, vp, vp]),
             "og_select": (None, [vp, i32, i32, i32, vp, i32, vp, vp, i32, i32, vp, vp]),
@@ -324,12 +327,26 @@ class Model:
             raise ValueError(rc)
         return k, v
 
-    def block_forward(self, seqs, anchors, h: np.ndarray) -> np.ndarray:
+    def set_layer_options(self, windows=None, rotary=None) -> int:
+        """Per-layer windows (0: all positions) and rotary flags (0: no rotary position), before
+        any context row is held (dflash.rs Geometry::window_of / rotary)."""
+        L = self.cfg.layers
+        w = None if windows is None else np.ascontiguousarray(np.broadcast_to(np.asarray(windows, np.int32), (L,)))
+        r = None if rotary is None else np.ascontiguousarray(np.broadcast_to(np.asarray(rotary, np.int32), (L,)))
+        self._opts = (w, r)
+        return lib().og_set_layer_options(self.h, _p(w), _p(r))
+
+    def dropped(self, seq: int, layer: int) -> int:
+        return int(lib().og_dropped(self.h, seq, layer))
+
+    def block_forward(self, seqs, anchors, h: np.ndarray, head_rows: int | None = None) -> np.ndarray:
+        """Logits of every block row; with head_rows, over the head's first head_rows rows only."""
         seqs = np.asarray(seqs, np.int32)
         anchors = np.asarray(anchors, np.int64)
         h = _c(h, np.float32)
-        out = np.empty((len(seqs), self.cfg.block, self.cfg.vocab), np.float32)
-        rc = lib().og_block_forward(self.h, len(seqs), _p(seqs), _p(anchors), _p(h), _p(out))
+        n = self.cfg.vocab if head_rows is None else int(head_rows)
+        out = np.empty((len(seqs), self.cfg.block, n), np.float32)
+        rc = lib().og_block_forward_rows(self.h, len(seqs), _p(seqs), _p(anchors), _p(h), n, _p(out))
         if rc:
             raise ValueError(rc)
         return out

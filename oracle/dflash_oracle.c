@@ -207,7 +207,8 @@ void og_silu_mul(const float* g, const float* u, int n, float* a) {
 
 typedef struct {
   int64_t first, len;
-  float* k; /* [layers][max_ctx][kv_heads][head_dim] */
+  int64_t* dropped; /* [layers]: context rows a layer no longer holds (the oldest) */
+  float* k;         /* [layers][max_ctx][kv_heads][head_dim] */
   float* v;
 } og_seq;
 
@@ -216,6 +217,8 @@ struct og_model {
   og_weights w;
   og_layer* layers;
   float* inv_freq;
+  int32_t* window; /* [layers] positions a block row sees back, 0 = all */
+  int32_t* rotary; /* [layers] 0 = no rotary position */
   og_seq* seqs;
 };
 
@@ -235,8 +238,12 @@ og_model* og_create(const og_geometry* g, const og_weights* w) {
   m->w.layer = m->layers;
   m->inv_freq = (float*)malloc(sizeof(float) * (size_t)(g->head_dim / 2));
   og_inv_freq(g->rope_theta, g->head_dim, m->inv_freq);
+  m->window = (int32_t*)calloc((size_t)g->layers, sizeof(int32_t));
+  m->rotary = (int32_t*)malloc(sizeof(int32_t) * (size_t)g->layers);
+  for (int l = 0; l < g->layers; l++) m->rotary[l] = 1;
   m->seqs = (og_seq*)calloc((size_t)g->max_seqs, sizeof(og_seq));
   for (int s = 0; s < g->max_seqs; s++) {
+    m->seqs[s].dropped = (int64_t*)calloc((size_t)g->layers, sizeof(int64_t));
     m->seqs[s].k = (float*)calloc(seq_floats(g) ? seq_floats(g) : 1, sizeof(float));
     m->seqs[s].v = (float*)calloc(seq_floats(g) ? seq_floats(g) : 1, sizeof(float));
   }
@@ -246,13 +253,42 @@ og_model* og_create(const og_geometry* g, const og_weights* w) {
 void og_destroy(og_model* m) {
   if (!m) return;
   for (int s = 0; s < m->g.max_seqs; s++) {
+    free(m->seqs[s].dropped);
     free(m->seqs[s].k);
     free(m->seqs[s].v);
   }
   free(m->seqs);
+  free(m->rotary);
+  free(m->window);
   free(m->inv_freq);
   free(m->layers);
   free(m);
+}
+
+/* dflash.rs, Geometry::window_of and Geometry::rotary: the per-layer options */
+int og_set_layer_options(og_model* m, const int32_t* windows, const int32_t* rotary) {
+  for (int s = 0; s < m->g.max_seqs; s++)
+    if (m->seqs[s].len > 0) return -1;
+  for (int l = 0; l < m->g.layers; l++)
+    if (windows && windows[l] < 0) return -1;
+  for (int l = 0; l < m->g.layers; l++) {
+    m->window[l] = windows ? windows[l] : 0;
+    m->rotary[l] = rotary ? (rotary[l] != 0) : 1;
+  }
+  return 0;
+}
+
+int64_t og_dropped(const og_model* m, int seq, int layer) {
+  if (seq < 0 || seq >= m->g.max_seqs || layer < 0 || layer >= m->g.layers) return -1;
+  return m->seqs[seq].dropped[layer];
+}
+
+/* dflash.rs, Drafter::truncate: keep positions before pos (the first stays); a layer's dropped
+ * rows are clipped to what is kept */
+static void keep_rows(og_model* m, og_seq* s, int64_t keep) {
+  for (int l = 0; l < m->g.layers; l++)
+    if (s->dropped[l] > keep) s->dropped[l] = keep;
+  s->len = keep;
 }
 
 /* y[n][rows] = W . x[n] with x f32: A8_32 first when W is quantized */
@@ -283,8 +319,8 @@ int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
     len = pos - first;
   }
   if (len + n > g->max_ctx) return -2;
+  keep_rows(m, s, first == s->first ? len : 0); /* truncate(pos), or truncate(0) on a restart */
   s->first = first;
-  s->len = len;
   if (n == 0) return 0;
   /* dflash.rs, Drafter::settle_rows: t = rms(FC . taps, hidden_norm); every layer's k, v of t;
    * k = rotate(rms(k, k_norm), position); then the rows are kept. */
@@ -306,7 +342,7 @@ int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
       for (int h = 0; h < kvh; h++) {
         float* kh = k + (size_t)i * kvd + (size_t)h * hd;
         og_rmsnorm_row(kh, L->k_norm, hd, (float)g->eps, tmp);
-        og_rope_head(tmp, hd, p, m->inv_freq);
+        if (m->rotary[l]) og_rope_head(tmp, hd, p, m->inv_freq);
         size_t off = (((size_t)l * g->max_ctx + row) * kvh + h) * hd;
         memcpy(s->k + off, tmp, sizeof(float) * hd);
         memcpy(s->v + off, v + (size_t)i * kvd + (size_t)h * hd, sizeof(float) * hd);
@@ -314,6 +350,12 @@ int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
     }
   }
   s->len = len + n;
+  /* Drafter::settle_rows, at the end: a layer holding more than twice its window keeps only the
+   * last window's worth */
+  for (int l = 0; l < g->layers; l++) {
+    const int64_t w = m->window[l], held = s->len - s->dropped[l];
+    if (w > 0 && held > 2 * w) s->dropped[l] += held - w;
+  }
   free(tmp);
   free(v);
   free(k);
@@ -329,14 +371,14 @@ int og_ctx_truncate(og_model* m, int seq, int64_t pos) {
   int64_t keep = pos - s->first;
   if (keep < 0) keep = 0;
   if (keep > s->len) keep = s->len;
-  s->len = keep;
+  keep_rows(m, s, keep);
   return 0;
 }
 
 /* dflash.rs, Drafter::reset */
 int og_ctx_reset(og_model* m, int seq) {
   if (seq < 0 || seq >= m->g.max_seqs) return -1;
-  m->seqs[seq].len = 0;
+  keep_rows(m, &m->seqs[seq], 0);
   m->seqs[seq].first = 0;
   return 0;
 }
@@ -360,8 +402,8 @@ int og_read_kv(const og_model* m, int layer, int seq, int row0, int n, float* k,
 }
 
 /* dflash.rs, Drafter::block, for one sequence: rows [anchor, MASK...] at positions a, a+1, ...
- * pass every layer; returns the rows after the last norm.  Window 0 and every layer rotary
- * (the workloads declare no windows), and no row convolutions (the plain Qwen3 layer). */
+ * pass every layer; returns the rows after the last norm.  Per layer its window and rotary
+ * option; no row convolutions (the plain Qwen3 layer). */
 static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, float* out) {
   const og_geometry* g = &m->g;
   const int B = g->block, H = g->hidden, nh = g->heads, kvh = g->kv_heads, hd = g->head_dim;
@@ -369,12 +411,6 @@ static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, f
   const float eps = (float)g->eps;
   const float scale = powf((float)hd, -0.5f); /* Drafter::block: (hd as f32).powf(-0.5) */
   og_seq* s = &m->seqs[seq];
-  /* Drafter::block: the context rows before the anchor: lo = first, hi = clamp(min(anchor,
-   * first + len), >= lo) */
-  int64_t lo = s->first, hi = anchor < s->first + s->len ? anchor : s->first + s->len;
-  if (hi < lo) hi = lo;
-  const int nctx = (int)(hi - lo);
-  const int nk = nctx + B;
 
   float* h = (float*)malloc(sizeof(float) * (size_t)B * H);
   memcpy(h, h_in, sizeof(float) * (size_t)B * H);
@@ -391,6 +427,20 @@ static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, f
 
   for (int l = 0; l < g->layers; l++) {
     const og_layer* L = &m->layers[l];
+    /* Drafter::block: the layer's context rows before the anchor, as far back as its first row
+     * sees: base = first + dropped, hi = max(min(anchor, first + len), base), lo = base, or with
+     * a window w: clamp(anchor + 1 - w, base, hi) */
+    const int64_t w = m->window[l], base = s->first + s->dropped[l];
+    int64_t hi = anchor < s->first + s->len ? anchor : s->first + s->len;
+    if (hi < base) hi = base;
+    int64_t lo = base;
+    if (w > 0) {
+      lo = anchor + 1 - w;
+      if (lo < base) lo = base;
+      if (lo > hi) lo = hi;
+    }
+    const int nctx = (int)(hi - lo);
+    const int nk = nctx + B;
     for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, L->in_norm, H, eps, x + (size_t)r * H);
     mm(g->body_fmt, L->q, qd, H, x, B, q);
     mm(g->body_fmt, L->k, kvd, H, x, B, k);
@@ -399,13 +449,13 @@ static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, f
       for (int j = 0; j < nh; j++) {
         float* qh = q + (size_t)r * qd + (size_t)j * hd;
         og_rmsnorm_row(qh, L->q_norm, hd, eps, tmp);
-        og_rope_head(tmp, hd, anchor + r, m->inv_freq);
+        if (m->rotary[l]) og_rope_head(tmp, hd, anchor + r, m->inv_freq);
         memcpy(qh, tmp, sizeof(float) * hd);
       }
       for (int j = 0; j < kvh; j++) {
         float* kh = k + (size_t)r * kvd + (size_t)j * hd;
         og_rmsnorm_row(kh, L->k_norm, hd, eps, tmp);
-        og_rope_head(tmp, hd, anchor + r, m->inv_freq);
+        if (m->rotary[l]) og_rope_head(tmp, hd, anchor + r, m->inv_freq);
         memcpy(kh, tmp, sizeof(float) * hd);
       }
     }
@@ -417,7 +467,7 @@ static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, f
       float* vv = (float*)malloc(sizeof(float) * (size_t)nk * hd);
       float* qq = (float*)malloc(sizeof(float) * (size_t)hd);
       for (int c = 0; c < nctx; c++) {
-        size_t off = (((size_t)l * g->max_ctx + (size_t)c) * kvh + gi) * hd;
+        size_t off = (((size_t)l * g->max_ctx + (size_t)(lo - s->first + c)) * kvh + gi) * hd;
         memcpy(kk + (size_t)c * hd, s->k + off, sizeof(float) * hd);
         memcpy(vv + (size_t)c * hd, s->v + off, sizeof(float) * hd);
       }
@@ -427,8 +477,19 @@ static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, f
       }
       for (int j = gi * rep; j < (gi + 1) * rep; j++)
         for (int r = 0; r < B; r++) {
+          /* under a window, row r sees context positions from anchor + r + 1 - w on (the
+           * earlier ones are masked out); the block's own rows are all seen */
+          int64_t c0 = 0;
+          if (w > 0) {
+            int64_t from = anchor + r + 1 - w;
+            if (from < 0) from = 0;
+            c0 = from - lo;
+            if (c0 < 0) c0 = 0;
+            if (c0 > nctx) c0 = nctx;
+          }
           memcpy(qq, q + (size_t)r * qd + (size_t)j * hd, sizeof(float) * hd);
-          og_attend(qq, 1, kk, vv, nk, hd, scale, y + (size_t)r * qd + (size_t)j * hd, NULL);
+          og_attend(qq, 1, kk + (size_t)c0 * hd, vv + (size_t)c0 * hd, nk - (int)c0, hd, scale,
+                    y + (size_t)r * qd + (size_t)j * hd, NULL);
         }
       free(qq);
       free(vv);
@@ -475,17 +536,24 @@ int og_block_hidden(og_model* m, int n_seqs, const int32_t* seqs, const int64_t*
   return 0;
 }
 
-/* dflash.rs, module header: logits = head . norm(h); every block row gets its logits. */
-int og_block_forward(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
-                     float* logits) {
-  if (check_block_args(m, n_seqs, seqs, anchors)) return -1;
+/* dflash.rs, module header: logits = head . norm(h); every block row gets its logits.  The
+ * device block (Drafter::block_dev) may take the head's first rows only, a shortlist of the
+ * vocabulary: the same product over those rows. */
+int og_block_forward_rows(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
+                          int head_rows, float* logits) {
+  if (check_block_args(m, n_seqs, seqs, anchors) || head_rows < 1 || head_rows > m->g.vocab) return -1;
   const og_geometry* g = &m->g;
   size_t per = (size_t)g->block * g->hidden;
   float* x = (float*)malloc(sizeof(float) * per * (size_t)(n_seqs > 0 ? n_seqs : 1));
   for (int i = 0; i < n_seqs; i++) block_one(m, seqs[i], anchors[i], h + per * i, x + per * i);
-  if (n_seqs > 0) mm(g->head_fmt, m->w.head, g->vocab, g->hidden, x, n_seqs * g->block, logits);
+  if (n_seqs > 0) mm(g->head_fmt, m->w.head, head_rows, g->hidden, x, n_seqs * g->block, logits);
   free(x);
   return 0;
+}
+
+int og_block_forward(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
+                     float* logits) {
+  return og_block_forward_rows(m, n_seqs, seqs, anchors, h, m->g.vocab, logits);
 }
 
 /* ---- candidate selection ---- */

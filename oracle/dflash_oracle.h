@@ -79,9 +79,20 @@ int og_ctx_reset(og_model* m, int seq);
 int og_ctx_span(const og_model* m, int seq, int64_t* first, int64_t* end);
 /* K and V of context rows (index = position - first) for one layer: [n][kv_heads][head_dim] */
 int og_read_kv(const og_model* m, int layer, int seq, int row0, int n, float* k, float* v);
+/* Per-layer attention options (dflash.rs Geometry: window / windows, no_rope; window_of,
+ * rotary): windows[l] = positions a block row of layer l sees back (0: all), rotary[l] = 0 for a
+ * layer whose queries and keys carry no rotary position.  NULL keeps the default (0 / 1).
+ * Accepted only while every sequence holds no context rows (-1 otherwise, or on a negative
+ * window). */
+int og_set_layer_options(og_model* m, const int32_t* windows, const int32_t* rotary);
+/* rows of layer l's context that fell out of its window and were dropped (Drafter::settle_rows) */
+int64_t og_dropped(const og_model* m, int seq, int layer);
 /* logits[s][block][vocab] of the block rows h[s][block][hidden] anchored at anchors[s] */
 int og_block_forward(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                      float* logits);
+/* the same over the head's first head_rows rows (a shortlist): logits[s][block][head_rows] */
+int og_block_forward_rows(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
+                          int head_rows, float* logits);
 /* the same, stopping after the final norm: hidden[s][block][hidden] */
 int og_block_hidden(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                     float* hidden);

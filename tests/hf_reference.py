@@ -90,8 +90,9 @@ class HFDrafter:
         return F.linear(_a8_fake(x) if fmt != di.F32 else x, w)
 
     @torch.no_grad()
-    def context_kv(self, taps: np.ndarray, first: int):
-        """Per layer (K, V) of context rows at positions first.. as [1, kv, n, hd] float64."""
+    def context_kv(self, taps: np.ndarray, first: int, rotary=None):
+        """Per layer (K, V) of context rows at positions first.. as [1, kv, n, hd] float64 (a
+        layer with rotary[l] == 0 keeps its keys unrotated)."""
         c = self.cfg
         t = self._lin(torch.from_numpy(taps).double(), self.fc, c.fc_fmt)
         t = self.hidden_norm(t)
@@ -100,31 +101,37 @@ class HFDrafter:
         from transformers.models.qwen3.modeling_qwen3 import apply_rotary_pos_emb
 
         out = []
-        for L in self.layers:
+        for li, L in enumerate(self.layers):
             a = L.self_attn
             k = a.k_norm(a.k_proj(t[None]).view(1, n, c.kv_heads, c.head_dim)).transpose(1, 2)
             v = a.v_proj(t[None]).view(1, n, c.kv_heads, c.head_dim).transpose(1, 2)
-            _, k = apply_rotary_pos_emb(k, k, cos, sin)
+            if rotary is None or rotary[li]:
+                _, k = apply_rotary_pos_emb(k, k, cos, sin)
             out.append((k, v))
         return out
 
     @torch.no_grad()
-    def block_logits(self, kv, anchor: int, h: np.ndarray) -> np.ndarray:
+    def block_logits(self, kv, anchor: int, h: np.ndarray, masks=None, rotary=None) -> np.ndarray:
         """Logits of the block rows h [B][H] anchored at ``anchor`` over the context kv (the
-        rows before the anchor)."""
+        rows before the anchor; each layer's own length).  masks[l] (optional, [B][n_l] bool)
+        hides context keys from rows, as an additive -inf; a layer with rotary[l] == 0 takes
+        no rotary position (cos 1, sin 0)."""
         from transformers.cache_utils import DynamicCache
 
         c = self.cfg
         cache = DynamicCache()
         for li, (k, v) in enumerate(kv):
             cache.update(k.clone(), v.clone(), li)
-        nctx = kv[0][0].shape[2] if kv else 0
         B = h.shape[0]
         cos, sin = _cos_sin(np.arange(anchor, anchor + B), self.inv)
-        mask = torch.zeros(1, 1, B, nctx + B, dtype=torch.float64)
         x = torch.from_numpy(h).double()[None]
-        for L in self.layers:
-            x = L(x, attention_mask=mask, past_key_values=cache, use_cache=True, position_embeddings=(cos, sin))
+        for li, L in enumerate(self.layers):
+            nctx = kv[li][0].shape[2]
+            mask = torch.zeros(1, 1, B, nctx + B, dtype=torch.float64)
+            if masks is not None and masks[li] is not None:
+                mask[0, 0, :, :nctx][torch.from_numpy(np.asarray(masks[li], bool))] = -torch.inf
+            pe = (cos, sin) if rotary is None or rotary[li] else (torch.ones_like(cos), torch.zeros_like(sin))
+            x = L(x, attention_mask=mask, past_key_values=cache, use_cache=True, position_embeddings=pe)
             if isinstance(x, tuple):
                 x = x[0]
         x = self.norm(x)[0]

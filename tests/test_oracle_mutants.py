@@ -15,6 +15,7 @@ import oracle
 import test_oracle_model as TM
 import test_oracle_select as TS
 import test_oracle_units as TU
+import test_oracle_windows as TW
 
 # (what the mistake is, text in dflash_oracle.c, its replacement)
 MUTANTS = [
@@ -31,11 +32,22 @@ MUTANTS = [
     ("nibble order swapped", "int nib = (k & 1) ? (b >> 4) : (b & 15);", "int nib = (k & 1) ? (b & 15) : (b >> 4);"),
     ("unsigned nibbles", "return nib >= 8 ? nib - 16 : nib;", "return nib;"),
     ("attention scale dropped", "s[j] = dot * (double)scale;", "s[j] = dot;"),
-    ("wrong kv head for the context", "(((size_t)l * g->max_ctx + (size_t)c) * kvh + gi) * hd;",
-     "(((size_t)l * g->max_ctx + (size_t)c) * kvh + (kvh - 1 - gi)) * hd;"),
-    ("causal block rows", "og_attend(qq, 1, kk, vv, nk, hd, scale,", "og_attend(qq, 1, kk, vv, nctx + r + 1, hd, scale,"),
-    ("context past the anchor read", "int64_t lo = s->first, hi = anchor < s->first + s->len ? anchor : s->first + s->len;",
-     "int64_t lo = s->first, hi = s->first + s->len;"),
+    ("wrong kv head for the context", "(((size_t)l * g->max_ctx + (size_t)(lo - s->first + c)) * kvh + gi) * hd;",
+     "(((size_t)l * g->max_ctx + (size_t)(lo - s->first + c)) * kvh + (kvh - 1 - gi)) * hd;"),
+    ("causal block rows", "vv + (size_t)c0 * hd, nk - (int)c0, hd, scale,", "vv + (size_t)c0 * hd, nctx - (int)c0 + r + 1, hd, scale,"),
+    ("context past the anchor read", "int64_t hi = anchor < s->first + s->len ? anchor : s->first + s->len;",
+     "int64_t hi = s->first + s->len;"),
+    ("a row's window counted from the anchor row", "int64_t from = anchor + r + 1 - w;", "int64_t from = anchor + 1 - w;"),
+    ("window one position long", "int64_t from = anchor + r + 1 - w;", "int64_t from = anchor + r - w;"),
+    ("dropped rows still read", "base = s->first + s->dropped[l];", "base = s->first;"),
+    ("truncate keeps the dropped count", "if (s->dropped[l] > keep) s->dropped[l] = keep;", "(void)keep;"),
+    ("the drop keeps twice the window", "s->dropped[l] += held - w;", "s->dropped[l] += held - 2 * w;"),
+    ("a no-rope layer's context rotated", "if (m->rotary[l]) og_rope_head(tmp, hd, p, m->inv_freq);",
+     "og_rope_head(tmp, hd, p, m->inv_freq);"),
+    ("a no-rope layer's queries rotated", "og_rmsnorm_row(qh, L->q_norm, hd, eps, tmp);\n        if (m->rotary[l]) og_rope_head",
+     "og_rmsnorm_row(qh, L->q_norm, hd, eps, tmp);\n        if (1) og_rope_head"),
+    ("the shortlist takes the whole head", "mm(g->head_fmt, m->w.head, head_rows, g->hidden,",
+     "mm(g->head_fmt, m->w.head, head_rows > 16 ? head_rows - 16 : head_rows, g->hidden,"),
     ("silu sign", "a[i] = (float)(gv / (1.0 + exp(-gv)) * (double)u[i]);", "a[i] = (float)(gv / (1.0 + exp(gv)) * (double)u[i]);"),
     ("gate and up swapped", "og_silu_mul(gt, up, B * I, a);", "og_silu_mul(up, gt, B * I, a);"),
     ("attention residual dropped", "mm(g->body_fmt, L->o, H, qd, y, B, o);\n    for (size_t i = 0; i < (size_t)B * H; i++) h[i] = h[i] + o[i];",
@@ -81,6 +93,10 @@ CHECKS = [
     (TM.test_anchor_row_vs_draft_rows_non_causal, ()),
     (TM.test_context_past_the_anchor_is_not_read, ()),
     (TM.test_append_chunking_truncate_and_reset, ()),
+    (TW.test_windows_and_no_rope_match_transformers, ()),
+    (TW.test_window_drop_bookkeeping, ()),
+    (TW.test_no_rope_everywhere_is_position_free, ()),
+    (TW.test_shortlist_head_is_a_prefix, ()),
 ]
 
 
