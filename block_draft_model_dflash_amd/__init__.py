@@ -22,6 +22,7 @@ EXPORTS = [
     "dflash_destroy", "dflash_quant_act", "dflash_packed_bytes", "dflash_pack", "dflash_gemm_scratch_bytes",
     "dflash_gemm", "dflash_group_sums", "dflash_read_kv", "dflash_time_stage", "dflash_read_timing",
     "dflash_top_k_scratch_bytes", "dflash_top_k", "dflash_select_scratch_bytes", "dflash_select",
+    "dflash_set_layer_options", "dflash_ctx_dropped", "dflash_block_forward_rows",
 ]
 (DFLASH_STAGE_HEAD, DFLASH_STAGE_QKV, DFLASH_STAGE_ATTENTION, DFLASH_STAGE_O, DFLASH_STAGE_GATE_UP, DFLASH_STAGE_DOWN,
  DFLASH_STAGE_BLOCK, DFLASH_STAGE_APPEND, DFLASH_STAGE_ATTN_CHUNKS) = range(9)
@@ -74,6 +75,9 @@ def lib():
             "dflash_ctx_reset": (i32, [vp, i32]),
             "dflash_ctx_span": (i32, [vp, i32, C.POINTER(i64), C.POINTER(i64)]),
             "dflash_block_forward": (i32, [vp, i32, vp, vp, vp, vp]),
+            "dflash_block_forward_rows": (i32, [vp, i32, vp, vp, vp, i32, vp]),
+            "dflash_set_layer_options": (i32, [vp, vp, vp]),
+            "dflash_ctx_dropped": (i32, [vp, i32, i32, C.POINTER(i64)]),
             "dflash_block_hidden": (i32, [vp, i32, vp, vp, vp, vp]),
             "dflash_last_error": (C.c_char_p, [vp]),
             "dflash_destroy": (None, [vp]),
@@ -153,6 +157,26 @@ def _host_arrays(seqs, anchors):
 def dflash_block_forward(ctx, seqs, anchors, h: int, logits: int) -> int:
     n, s, a = _host_arrays(seqs, anchors)
     return _check(lib().dflash_block_forward(ctx, n, C.cast(s, C.c_void_p), C.cast(a, C.c_void_p), h, logits), ctx)
+
+
+def dflash_block_forward_rows(ctx, seqs, anchors, h: int, head_rows: int, logits: int) -> int:
+    n, s, a = _host_arrays(seqs, anchors)
+    return _check(lib().dflash_block_forward_rows(ctx, n, C.cast(s, C.c_void_p), C.cast(a, C.c_void_p), h,
+                                                  int(head_rows), logits), ctx)
+
+
+def dflash_set_layer_options(ctx, windows=None, rotary=None) -> int:
+    """windows / rotary: host sequences of one int per layer, or None for the defaults."""
+    w = None if windows is None else (C.c_int32 * len(windows))(*[int(x) for x in windows])
+    r = None if rotary is None else (C.c_int32 * len(rotary))(*[int(x) for x in rotary])
+    return _check(lib().dflash_set_layer_options(ctx, None if w is None else C.cast(w, C.c_void_p),
+                                                 None if r is None else C.cast(r, C.c_void_p)), ctx)
+
+
+def dflash_ctx_dropped(ctx, seq: int, layer: int) -> int:
+    d = C.c_int64()
+    _check(lib().dflash_ctx_dropped(ctx, seq, layer, C.byref(d)), ctx)
+    return d.value
 
 
 def dflash_block_hidden(ctx, seqs, anchors, h: int, hidden: int) -> int:

@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64) void k_qkv_epilogue(const double* __restrict__ 
                                                     SeqInfo si, int nh, int kvh, int hd,
                                                     const float* __restrict__ q_norm,
                                                     const float* __restrict__ k_norm,
-                                                    const float* __restrict__ inv_freq, float eps,
+                                                    const float* __restrict__ inv_freq, float eps, int rope,
                                                     float* __restrict__ q, float* __restrict__ k,
                                                     float* __restrict__ v) {
   const int head = blockIdx.x, m = blockIdx.y, lane = threadIdx.x, half = hd >> 1;
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(64) void k_qkv_epilogue(const double* __restrict__ 
   const long long pos = si.pos0[m / B] + (m % B);
   const bool isq = head < nh;
   float o0 = 0.f, o1 = 0.f;
-  head_norm_rope(x0, x1, lane, hd, isq ? q_norm : k_norm, eps, inv_freq, pos, o0, o1);
+  head_norm_rope(x0, x1, lane, hd, isq ? q_norm : k_norm, eps, inv_freq, pos, rope != 0, o0, o1);
   if (!on) return;
   float* dst = isq ? q + ((size_t)m * nh + head) * hd : k + ((size_t)m * kvh + (head - nh)) * hd;
   dst[lane] = o0;
@@ -287,10 +287,10 @@ __global__ __launch_bounds__(64) void k_qkv_epilogue(const double* __restrict__ 
 
 hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
                                int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
-                               float* q, float* k, float* v, hipStream_t st) {
+                               bool rope, float* q, float* k, float* v, hipStream_t st) {
   if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_qkv_epilogue, dim3(nh + 2 * kvh, M), dim3(64), 0, st, part, S, Mpad, B, si, nh, kvh, hd,
-                     q_norm, k_norm, inv_freq, eps, q, k, v);
+                     q_norm, k_norm, inv_freq, eps, (int)rope, q, k, v);
   return hipGetLastError();
 }
 
@@ -298,9 +298,10 @@ hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B
 // projection: layer l's k heads then its v heads.  Cache layout [L][max_seqs][kvh][max_ctx][hd].
 __global__ __launch_bounds__(64) void k_kv_append(const double* __restrict__ part, int S, int Mpad, int layers,
                                                  int kvh, int hd, const float* __restrict__ k_norms,
-                                                 const float* __restrict__ inv_freq, float eps, long long pos0,
-                                                 int row0, int slot, int max_seqs, int max_ctx,
-                                                 float* __restrict__ kc, float* __restrict__ vc) {
+                                                 const float* __restrict__ inv_freq, float eps,
+                                                 unsigned long long rot_mask, long long pos0, int row0, int slot,
+                                                 int max_seqs, int max_ctx, float* __restrict__ kc,
+                                                 float* __restrict__ vc) {
   const int unit = blockIdx.x, i = blockIdx.y, lane = threadIdx.x, half = hd >> 1;
   const int l = unit / (2 * kvh), rem = unit % (2 * kvh), kind = rem / kvh, h = rem % kvh;
   const size_t kvd = (size_t)kvh * hd, N = (size_t)layers * 2 * kvd;
@@ -314,18 +315,20 @@ __global__ __launch_bounds__(64) void k_kv_append(const double* __restrict__ par
   const float x0 = on ? reduce_parts(part, S, Mpad, i, N, col0 + lane) : 0.f;
   const float x1 = on ? reduce_parts(part, S, Mpad, i, N, col0 + lane + half) : 0.f;
   float o0 = 0.f, o1 = 0.f;
-  head_norm_rope(x0, x1, lane, hd, k_norms + (size_t)l * hd, eps, inv_freq, pos0 + i, o0, o1);
+  const bool rope = l >= 64 || ((rot_mask >> l) & 1ull);
+  head_norm_rope(x0, x1, lane, hd, k_norms + (size_t)l * hd, eps, inv_freq, pos0 + i, rope, o0, o1);
   if (!on) return;
   kc[dst + lane] = o0;
   kc[dst + lane + half] = o1;
 }
 
 hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
-                            const float* k_norms, const float* inv_freq, float eps, long long pos0, int row0,
-                            int slot, int max_seqs, int max_ctx, float* kc, float* vc, hipStream_t st) {
+                            const float* k_norms, const float* inv_freq, float eps, unsigned long long rot_mask,
+                            long long pos0, int row0, int slot, int max_seqs, int max_ctx, float* kc, float* vc,
+                            hipStream_t st) {
   if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_kv_append, dim3(layers * 2 * kvh, n), dim3(64), 0, st, part, S, Mpad, layers, kvh, hd,
-                     k_norms, inv_freq, eps, pos0, row0, slot, max_seqs, max_ctx, kc, vc);
+                     k_norms, inv_freq, eps, rot_mask, pos0, row0, slot, max_seqs, max_ctx, kc, vc);
   return hipGetLastError();
 }
 

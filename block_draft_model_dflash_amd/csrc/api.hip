@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -156,6 +157,18 @@ struct dflash_ctx {
   Layout lay;
   uint8_t* ws = nullptr;
   std::vector<int64_t> first, len;
+  // per-layer options (0 = every position; 1 = rotary) and, per (sequence, layer), the oldest
+  // context rows the layer dropped
+  std::vector<int32_t> window, rotary;
+  std::vector<int64_t> dropped;  // [max_seqs][layers]
+  unsigned long long rot_mask = ~0ull;  // bit l: layer l rotates (layers >= 64 always do)
+  int64_t& drop(int seq, int l) { return dropped[(size_t)seq * g.layers + l]; }
+  // Drafter::truncate: a layer's dropped rows are clipped to what a sequence keeps
+  void keep_rows(int seq, int64_t keep) {
+    for (int l = 0; l < g.layers; l++)
+      if (drop(seq, l) > keep) drop(seq, l) = keep;
+    len[seq] = keep;
+  }
   // stage timing: event pairs recorded around the launches of the timed stages
   unsigned timed_mask = 0;
   std::vector<hipEvent_t> ev_pool;  // created on first use, reused
@@ -259,8 +272,35 @@ int check_weights(const dflash_geometry* g, const dflash_weights* w, std::string
   return DFLASH_OK;
 }
 
+// The context keys layer l of each sequence attends to (dflash.rs, Drafter::block): base =
+// first + dropped, hi = max(min(anchor, first+len), base), lo = base or, under a window w,
+// clamp(anchor + 1 - w, base, hi); row r masks the keys before position anchor + r + 1 - w.
+// Cache rows are position - first; key index i of the call is cache row ctx0 + i.
+void layer_ranges(const dflash_ctx* c, int l, const int32_t* seqs, const int64_t* anchors, SeqInfo& si) {
+  const int64_t w = c->window[l];
+  for (int i = 0; i < si.n; i++) {
+    const int sq = seqs[i];
+    const int64_t first = c->first[sq], end = first + c->len[sq];
+    const int64_t base = first + c->dropped[(size_t)sq * c->g.layers + l];
+    int64_t hi = anchors[i] < end ? anchors[i] : end;
+    if (hi < base) hi = base;
+    int64_t lo = base;
+    if (w > 0) {
+      lo = anchors[i] + 1 - w;
+      if (lo < base) lo = base;
+      if (lo > hi) lo = hi;
+    }
+    si.ctx0[i] = (int)(lo - first);
+    si.nctx[i] = (int)(hi - lo);
+    int64_t m0 = w > 0 ? anchors[i] + 1 - w - lo : -(1ll << 30);
+    if (m0 < -(1ll << 30)) m0 = -(1ll << 30);
+    if (m0 > (1ll << 30)) m0 = 1ll << 30;
+    si.mask0[i] = (int)m0;
+  }
+}
+
 int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
-                 float* out, bool hidden_only) {
+                 float* out, bool hidden_only, int head_rows) {
   const dflash_geometry& g = c->g;
   if (n_seqs < 1 || n_seqs > g.max_seqs) return c->fail(DFLASH_EINVAL, "n_seqs %d outside [1, %d]", n_seqs, g.max_seqs);
   if (!seqs || !anchors || !h || !out) return c->fail(DFLASH_EINVAL, "null pointer");
@@ -272,11 +312,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
     for (int j = 0; j < i; j++)
       if (seqs[j] == seqs[i]) return c->fail(DFLASH_EINVAL, "sequence %d given twice", seqs[i]);
     if (anchors[i] < 0) return c->fail(DFLASH_EINVAL, "negative anchor");
-    const int64_t first = c->first[seqs[i]], end = first + c->len[seqs[i]];
-    int64_t hi = anchors[i] < end ? anchors[i] : end;
-    if (hi < first) hi = first;
     si.slot[i] = seqs[i];
-    si.nctx[i] = (int)(hi - first);
     si.pos0[i] = anchors[i];
   }
   const int B = g.block, H = g.hidden, nh = g.heads, kvh = g.kv_heads, hd = g.head_dim, NL = g.layers;
@@ -300,16 +336,17 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   as.max_seqs = g.max_seqs;
   as.maxch = MAXCH;
   as.scale = powf((float)hd, -0.5f);  // dflash.rs, Drafter::block: (hd as f32).powf(-0.5)
-  int nmax = 0;
-  for (int i = 0; i < n_seqs; i++)
-    if (si.nctx[i] > nmax) nmax = si.nctx[i];
   // about one workgroup per CU: n_seqs * q heads * chunks ~ 256 (a workgroup serves one q head
-  // of one chunk), chunks a multiple of 32 keys
+  // of one chunk), chunks a multiple of 32 keys; per layer, as its windows give it keys
   int nch_target = (256 + n_seqs * nh - 1) / (n_seqs * nh);
   if (nch_target > MAXCH) nch_target = MAXCH;
-  int ck = ((nmax + nch_target - 1) / nch_target + 31) / 32 * 32;
-  if (ck < 32) ck = 32;
-  as.ck = ck;
+  auto chunk_keys = [&]() {
+    int nmax = 0;
+    for (int i = 0; i < n_seqs; i++)
+      if (si.nctx[i] > nmax) nmax = si.nctx[i];
+    const int ck = ((nmax + nch_target - 1) / nch_target + 31) / 32 * 32;
+    return ck < 32 ? 32 : ck;
+  };
 
   double* ssq = c->at<double>(L.ssq);
   int8_t* xq2 = c->at<int8_t>(L.xq2);
@@ -339,8 +376,11 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
     TRY_HIP(c,
             launch_qkv_epilogue(part, 1, Mpad, M, B, si, nh, kvh, hd, c->at<float>(L.q_norm) + (size_t)l * hd,
                                 c->at<float>(L.k_norm) + (size_t)l * hd, c->at<float>(L.inv_freq), eps,
-                                c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb), c->st),
+                                c->rotary[l] != 0, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
+                                c->st),
             "q/k norm + rope");
+    layer_ranges(c, l, seqs, anchors, si);
+    as.ck = chunk_keys();
     {
       StageTimer t(c, DFLASH_STAGE_ATTENTION);
       {
@@ -413,13 +453,16 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
     TRY_HIP(c, hipMemcpyAsync(out, xf, (size_t)M * H * 4, hipMemcpyDeviceToDevice, c->st), "copy hidden");
     return DFLASH_OK;
   }
+  // the head's first head_rows rows (all V of them unless a shortlist is asked for): rows of
+  // the packed head are n-tiles stored front to back, so a shortlist is a prefix
   StageTimer t(c, DFLASH_STAGE_HEAD);
-  if (g.head_fmt == DFLASH_F32) return run_gemm_f32(c, L.head, V, H, Mpad, M, out, true, V, M);
+  const int HN = head_rows;
+  if (g.head_fmt == DFLASH_F32) return run_gemm_f32(c, L.head, HN, H, Mpad, M, out, true, HN, M);
   GemmOut o = gemm_out(EPI_F32, M, Mpad);
   o.y = out;
-  o.ld = V;
+  o.ld = HN;
   o.m_store = M;
-  return run_gemm_q(c, g.head_fmt, L.head, V, H, xq, dxT, o, "head");
+  return run_gemm_q(c, g.head_fmt, L.head, HN, H, xq, dxT, o, "head");
 }
 
 }  // namespace
@@ -472,6 +515,9 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* works
   c->st = (hipStream_t)stream;
   c->first.assign(g->max_seqs, 0);
   c->len.assign(g->max_seqs, 0);
+  c->window.assign(g->layers, 0);
+  c->rotary.assign(g->layers, 1);
+  c->dropped.assign((size_t)g->max_seqs * g->layers, 0);
   const long H = g->hidden, qd = (long)g->heads * g->head_dim, kvd = (long)g->kv_heads * g->head_dim;
   const long I = g->intermediate, T = (long)g->n_taps * g->hidden, V = g->vocab, hd = g->head_dim;
   auto fin = [&](int code) -> int {
@@ -545,8 +591,8 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
   if (len + n > g.max_ctx)
     return c->fail(DFLASH_ECAPACITY, "sequence %d: %lld + %d rows exceed max_ctx %d", seq, (long long)len, n,
                    g.max_ctx);
+  c->keep_rows(seq, first == c->first[seq] ? len : 0);  // truncate(pos), or truncate(0) on a restart
   c->first[seq] = first;
-  c->len[seq] = len;
   StageTimer timer(c, DFLASH_STAGE_APPEND);
   const int H = g.hidden, T = g.n_taps * g.hidden, kvd = g.kv_heads * g.head_dim, NL = g.layers;
   const float eps = (float)g.eps;
@@ -587,11 +633,17 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
     if (rc) return rc;
     TRY_HIP(c,
             launch_kv_append(part, 1, Mpad, nn, NL, g.kv_heads, g.head_dim, c->at<float>(L.k_norm),
-                             c->at<float>(L.inv_freq), eps, pos + c0, (int)(pos - first) + c0, seq, g.max_seqs,
-                             g.max_ctx, c->at<float>(L.kc), c->at<float>(L.vc), c->st),
+                             c->at<float>(L.inv_freq), eps, c->rot_mask, pos + c0, (int)(pos - first) + c0, seq,
+                             g.max_seqs, g.max_ctx, c->at<float>(L.kc), c->at<float>(L.vc), c->st),
             "k/v into the cache");
   }
   c->len[seq] = len + n;
+  // Drafter::settle_rows, at the end: a layer holding more than twice its window keeps only the
+  // last window's worth (the rows stay in the cache; they are never read again)
+  for (int l = 0; l < NL; l++) {
+    const int64_t w = c->window[l], held = c->len[seq] - c->drop(seq, l);
+    if (w > 0 && held > 2 * w) c->drop(seq, l) += held - w;
+  }
   return DFLASH_OK;
 }
 
@@ -601,15 +653,43 @@ int dflash_ctx_truncate(dflash_ctx* c, int32_t seq, int64_t pos) {
   int64_t keep = pos - c->first[seq];
   if (keep < 0) keep = 0;
   if (keep > c->len[seq]) keep = c->len[seq];
-  c->len[seq] = keep;
+  c->keep_rows(seq, keep);
   return DFLASH_OK;
 }
 
 int dflash_ctx_reset(dflash_ctx* c, int32_t seq) {
   if (!c) return DFLASH_EINVAL;
   if (seq < 0 || seq >= c->g.max_seqs) return c->fail(DFLASH_EINVAL, "bad sequence");
-  c->len[seq] = 0;
+  c->keep_rows(seq, 0);
   c->first[seq] = 0;
+  return DFLASH_OK;
+}
+
+int dflash_set_layer_options(dflash_ctx* c, const int32_t* windows, const int32_t* rotary) {
+  if (!c) return DFLASH_EINVAL;
+  const int NL = c->g.layers;
+  for (int s = 0; s < c->g.max_seqs; s++)
+    if (c->len[s] > 0) return c->fail(DFLASH_EINVAL, "layer options change only while no context is held");
+  unsigned long long mask = ~0ull;
+  for (int l = 0; l < NL; l++) {
+    if (windows && windows[l] < 0) return c->fail(DFLASH_EINVAL, "layer %d: negative window", l);
+    if (rotary && !rotary[l]) {
+      if (l >= 64) return c->fail(DFLASH_EINVAL, "layer %d: only the first 64 layers can be unrotated", l);
+      mask &= ~(1ull << l);
+    }
+  }
+  for (int l = 0; l < NL; l++) {
+    c->window[l] = windows ? windows[l] : 0;
+    c->rotary[l] = rotary ? (rotary[l] != 0) : 1;
+  }
+  c->rot_mask = mask;
+  std::fill(c->dropped.begin(), c->dropped.end(), 0);
+  return DFLASH_OK;
+}
+
+int dflash_ctx_dropped(const dflash_ctx* c, int32_t seq, int32_t layer, int64_t* dropped) {
+  if (!c || !dropped || seq < 0 || seq >= c->g.max_seqs || layer < 0 || layer >= c->g.layers) return DFLASH_EINVAL;
+  *dropped = c->dropped[(size_t)seq * c->g.layers + layer];
   return DFLASH_OK;
 }
 
@@ -624,7 +704,17 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
                          float* logits) {
   if (!c) return DFLASH_EINVAL;
   StageTimer t(c, DFLASH_STAGE_BLOCK);
-  return block_common(c, n_seqs, seqs, anchors, h, logits, false);
+  return block_common(c, n_seqs, seqs, anchors, h, logits, false, c->g.vocab);
+}
+
+int dflash_block_forward_rows(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors,
+                              const float* h, int32_t head_rows, float* logits) {
+  if (!c) return DFLASH_EINVAL;
+  if (head_rows != c->g.vocab && (head_rows < 16 || head_rows > c->g.vocab || head_rows % 16))
+    return c->fail(DFLASH_EINVAL, "head_rows %d: a multiple of 16 in [16, %d], or %d", head_rows, c->g.vocab,
+                   c->g.vocab);
+  StageTimer t(c, DFLASH_STAGE_BLOCK);
+  return block_common(c, n_seqs, seqs, anchors, h, logits, false, head_rows);
 }
 
 int dflash_time_stage(dflash_ctx* c, int32_t stage) {
@@ -671,7 +761,7 @@ int dflash_read_timing(dflash_ctx* c, int32_t stage, double* total_ms, int64_t* 
 int dflash_block_hidden(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                         float* hidden) {
   if (!c) return DFLASH_EINVAL;
-  return block_common(c, n_seqs, seqs, anchors, h, hidden, true);
+  return block_common(c, n_seqs, seqs, anchors, h, hidden, true, c->g.vocab);
 }
 
 const char* dflash_last_error(const dflash_ctx* c) { return c ? c->err.c_str() : g_create_err.c_str(); }

@@ -1,6 +1,8 @@
 // Block-vs-context attention (cortiq-engine "dflash.rs", Drafter::block: each q head j reads
-// kv head j / rep; its keys and values are the context rows before the anchor followed by the
-// block's own rows, with no causal mask; s = (q . k) * hd^-0.5, softmax, y = sum p v).
+// kv head j / rep; its keys and values are the layer's context rows before the anchor, as far
+// back as its window reaches, followed by the block's own rows, with no causal mask; under a
+// window, block row r masks the context positions before anchor + r + 1 - w;
+// s = (q . k) * hd^-0.5, softmax, y = sum p v).
 //
 // The pages' device kernel (gpu_wgpu/dflash_dev.rs, dflash_attn) writes every score to a global
 // scratch and re-reads it; here the context is split into chunks, each wave keeps a running
@@ -74,8 +76,12 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
   const int j = g * rep + h;
   const int k0 = c * a.ck, kend = min(nctx, k0 + a.ck);
   const int nt = (kend - k0 + 15) / 16;  // >= 1: every launched chunk holds context rows
-  const float* Kctx = kc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
-  const float* Vctx = vc + ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx * HD;
+  const float* Kctx = kc + (((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s]) * HD;
+  const float* Vctx = vc + (((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s]) * HD;
+  // under a window, query row col does not see the keys before index mask0 + col: their scores
+  // become -1e300, so exp() gives them exactly 0 beside any visible key; a chunk in which a row
+  // sees no key keeps the finite maximum -1e300, and the merge weights it by exp(-1e300 - m) = 0
+  const int kmin = si.mask0[s] + col;
 
   // the head's queries in LDS as f64 (converted once here, not once per tile; rows HD + 2
   // doubles apart, so the 16 rows of one read fall in different banks), the B operand of the
@@ -141,7 +147,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int key = quarter + 4 * r;  // accumulator slot r holds key row quarter + 4r
-      p[r] = key < nvalid ? (st0[r] + st1[r]) * (double)a.scale : -INFINITY;
+      p[r] = key < nvalid ? (k0 + 16 * i + key >= kmin ? (st0[r] + st1[r]) * (double)a.scale : -1e300) : -INFINITY;
       mx = fmax(mx, p[r]);
     }
     mx = cross4_max_f64(mx);  // the same query's slots in the other three lane rows

@@ -37,7 +37,9 @@ constexpr int MAX_SEQS_ARG = 64;  // sequences of one block call (max_seqs*block
 struct SeqInfo {
   int n;                        // sequences in this call
   int slot[MAX_SEQS_ARG];       // cache slot of each
-  int nctx[MAX_SEQS_ARG];       // context rows each attends to (index 0 .. nctx-1)
+  int ctx0[MAX_SEQS_ARG];       // cache row of its first context key (position - first)
+  int nctx[MAX_SEQS_ARG];       // context keys it attends to (cache rows ctx0 .. ctx0+nctx-1)
+  int mask0[MAX_SEQS_ARG];      // block row r does not see keys i < mask0 + r (a window)
   long long pos0[MAX_SEQS_ARG]; // position of block row 0 (the anchor)
 };
 
@@ -102,14 +104,16 @@ hipError_t launch_copy_ssq(const float* x, float* h, int M, int N, double* ssq, 
 hipError_t launch_swiglu_act(const double* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
                              float* xf, hipStream_t st);
 // q/k/v of the block rows from the fused projection partials [S][Mpad][qd + 2 kvd]:
-// q-norm / k-norm, RoPE at si.pos0[m / B] + m % B.
+// q-norm / k-norm, then (rope) RoPE at si.pos0[m / B] + m % B.
 hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
                                int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
-                               float* q, float* k, float* v, hipStream_t st);
-// Context rows into the cache from the all-layer K|V partials [S][Mpad][L * 2 kvd].
+                               bool rope, float* q, float* k, float* v, hipStream_t st);
+// Context rows into the cache from the all-layer K|V partials [S][Mpad][L * 2 kvd]; layer l's
+// keys are rotated when bit l of rot_mask is set (layers >= 64 always are).
 hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
-                            const float* k_norms, const float* inv_freq, float eps, long long pos0, int row0,
-                            int slot, int max_seqs, int max_ctx, float* kc, float* vc, hipStream_t st);
+                            const float* k_norms, const float* inv_freq, float eps, unsigned long long rot_mask,
+                            long long pos0, int row0, int slot, int max_seqs, int max_ctx, float* kc, float* vc,
+                            hipStream_t st);
 
 // Attention of the block rows over context + block keys, split over context chunks.
 struct AttnShape {

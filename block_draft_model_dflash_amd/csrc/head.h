@@ -24,13 +24,14 @@ __device__ __forceinline__ float reduce_parts(const double* __restrict__ part, i
 
 // Per-head RMSNorm then RoPE (cortiq-engine dflash.rs, Drafter::block / append: q_norm or k_norm
 // over the head's hd values, s = 1/sqrt(f32(sum x^2 / hd) + eps), y = (x*s)*w, then the rotation
-// of the pairs (d, d + hd/2) by the angle f32(pos) * inv_freq[d], an f32 product).  One wave per
+// of the pairs (d, d + hd/2) by the angle f32(pos) * inv_freq[d], an f32 product; a layer
+// without rotary positions, Geometry::rotary false, keeps y).  One wave per
 // (head, row): lane l holds dims l and l + hd/2 (hd <= 128), the pair the rotation mixes, so
 // nothing crosses lanes but the sum of squares.  The angle's cosine and sine and the rotation are
 // evaluated in f64 from the f32 y and rounded once.
 __device__ __forceinline__ void head_norm_rope(float x0, float x1, int lane, int hd, const float* __restrict__ w,
                                                float eps, const float* __restrict__ inv_freq, long long pos,
-                                               float& o0, float& o1) {
+                                               bool rope, float& o0, float& o1) {
   const int half = hd >> 1;
   const bool on = lane < half;
   double ss = on ? (double)x0 * (double)x0 + (double)x1 * (double)x1 : 0.0;
@@ -38,6 +39,11 @@ __device__ __forceinline__ void head_norm_rope(float x0, float x1, int lane, int
   const float sc = 1.0f / sqrtf((float)(ss / (double)hd) + eps);
   if (!on) return;
   const float y0 = (x0 * sc) * w[lane], y1 = (x1 * sc) * w[lane + half];
+  if (!rope) {
+    o0 = y0;
+    o1 = y1;
+    return;
+  }
   const float ang = (float)pos * inv_freq[lane];
   double sn, cs;
   sincos((double)ang, &sn, &cs);

@@ -6,10 +6,10 @@ import ctypes as C
 
 import numpy as np
 
-from . import (DFLASH_F32, dflash_block_forward, dflash_block_hidden, dflash_create, dflash_ctx_append,
-               dflash_ctx_reset, dflash_ctx_span, dflash_ctx_truncate, dflash_destroy, dflash_geometry,
-               dflash_layer_weights, dflash_matrix, dflash_read_kv, dflash_set_stream, dflash_weights,
-               dflash_workspace_bytes)
+from . import (DFLASH_F32, dflash_block_forward, dflash_block_forward_rows, dflash_block_hidden, dflash_create,
+               dflash_ctx_append, dflash_ctx_dropped, dflash_ctx_reset, dflash_ctx_span, dflash_ctx_truncate,
+               dflash_destroy, dflash_geometry, dflash_layer_weights, dflash_matrix, dflash_read_kv,
+               dflash_set_layer_options, dflash_set_stream, dflash_weights, dflash_workspace_bytes)
 
 GEOMETRY_FIELDS = ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab", "block", "n_taps",
                    "body_fmt", "fc_fmt", "head_fmt")
@@ -78,6 +78,14 @@ class Drafter:
         dflash_ctx_append(self.ctx, seq, pos, t.data_ptr() if n else None, n)
         self._last_inputs = t
 
+    def set_layer_options(self, windows=None, rotary=None) -> None:
+        L = self.g.layers
+        as_list = lambda x: None if x is None else [int(v) for v in np.broadcast_to(np.asarray(x), (L,))]
+        dflash_set_layer_options(self.ctx, as_list(windows), as_list(rotary))
+
+    def dropped(self, seq: int, layer: int) -> int:
+        return dflash_ctx_dropped(self.ctx, seq, layer)
+
     def truncate(self, seq: int, pos: int) -> None:
         dflash_ctx_truncate(self.ctx, seq, pos)
 
@@ -96,13 +104,18 @@ class Drafter:
         return k, v
 
     # -- blocks ----------------------------------------------------------------------------
-    def block_forward(self, seqs, anchors, h, out=None):
+    def block_forward(self, seqs, anchors, h, out=None, head_rows=None):
+        """Logits of every block row, over the head's first head_rows rows when given."""
         torch = self.torch
         t = self._f32(h)
+        n = self.g.vocab if head_rows is None else int(head_rows)
         if out is None:
-            out = torch.empty((len(seqs), self.g.block, self.g.vocab), dtype=torch.float32, device=self.device)
+            out = torch.empty((len(seqs), self.g.block, n), dtype=torch.float32, device=self.device)
         self._sync_stream()
-        dflash_block_forward(self.ctx, seqs, anchors, t.data_ptr(), out.data_ptr())
+        if head_rows is None:
+            dflash_block_forward(self.ctx, seqs, anchors, t.data_ptr(), out.data_ptr())
+        else:
+            dflash_block_forward_rows(self.ctx, seqs, anchors, t.data_ptr(), n, out.data_ptr())
         self._last_inputs = t
         return out
 

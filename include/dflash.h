@@ -119,6 +119,21 @@ int dflash_set_stream(dflash_ctx* c, void* stream);
  * would pass max_ctx rows (nothing changes then). */
 int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps, int32_t n);
 
+/* Per-layer attention options (dflash.rs, Geometry window / windows / no_rope with window_of
+ * and rotary): windows host [layers], positions a block row of that layer sees back (0: all of
+ * them; row r of a block anchored at a sees context positions >= a + r + 1 - w, and all block
+ * rows); rotary host [layers], 0 for a layer whose queries and keys carry no rotary position.
+ * NULL keeps the default (0, resp. 1 for every layer).  After every append a windowed layer
+ * holding more than twice its window drops its oldest rows down to one window
+ * (Drafter::settle_rows); dropped rows are never read again (a truncation clips the count to
+ * what it keeps).  The cache keeps its max_ctx rows per sequence: dropping frees no memory.
+ * Allowed only while no sequence holds context rows, and at most 64 layers may be unrotated;
+ * otherwise DFLASH_EINVAL with nothing changed. */
+int dflash_set_layer_options(dflash_ctx* c, const int32_t* windows, const int32_t* rotary);
+
+/* host *dropped receives how many of a sequence's oldest context rows layer `layer` dropped. */
+int dflash_ctx_dropped(const dflash_ctx* c, int32_t seq, int32_t layer, int64_t* dropped);
+
 /* Forget positions >= pos of a sequence (dflash.rs, Drafter::truncate); the first stays. */
 int dflash_ctx_truncate(dflash_ctx* c, int32_t seq, int64_t pos);
 
@@ -132,10 +147,19 @@ int dflash_ctx_span(const dflash_ctx* c, int32_t seq, int64_t* first, int64_t* e
  * the module header): seqs and anchors are host [n_seqs]; h is device [n_seqs][block][hidden]
  * f32, the rows' embeddings ([anchor, MASK...]) at positions anchors[i]+r; logits receives
  * device [n_seqs][block][vocab] f32 for every block row.  Layer l of sequence s attends to its
- * context positions [first, clamp(min(anchor, first+len), >= first)) and to all block rows.
+ * context positions [lo, hi) and to all block rows: base = first + the rows l dropped,
+ * hi = max(min(anchor, first+len), base), lo = base, or under a window w
+ * clamp(anchor + 1 - w, base, hi) with row r's positions before anchor + r + 1 - w masked.
  * The context is not modified. */
 int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors,
                          const float* h, float* logits);
+
+/* The same block with the head over its first head_rows rows only, a shortlist of the
+ * vocabulary (dflash.rs, Drafter::block_dev: the drafts' head over the table's first rows):
+ * logits receives device [n_seqs][block][head_rows] f32.  head_rows is a multiple of 16 in
+ * [16, vocab] (or vocab itself), else DFLASH_EINVAL. */
+int dflash_block_forward_rows(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors,
+                              const float* h, int32_t head_rows, float* logits);
 
 /* The same block, stopping after the final RMSNorm: hidden receives device
  * [n_seqs][block][hidden] f32 (the rows the head reads; a diagnostic of the block body). */
