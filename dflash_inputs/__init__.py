@@ -38,7 +38,7 @@ F32, Q4_32, Q8_32 = 0, 1, 2
 FMT_NAMES = {F32: "f32", Q4_32: "q4_32", Q8_32: "q8_32"}
 
 # stream ids of SeedSequence([seed, stream, index])
-_S_WEIGHT, _S_NORM, _S_TAPS, _S_ANCHOR, _S_MASK, _S_SELECTOR = 1, 2, 3, 4, 5, 6
+_S_WEIGHT, _S_NORM, _S_TAPS, _S_ANCHOR, _S_MASK, _S_SELECTOR, _S_CONV = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -70,6 +70,11 @@ class Config:
     emb_std: float = 0.02
     seed: int = 1000
     weight_seed: int = 0  # seed of the weights when they are another workload's drafter (0: seed)
+    # row convolutions around attention and the MLP (0: none, the plain Qwen3 layer): columns
+    # per kernel group, offsets per kernel, and the spread of the kernel projections' weights
+    conv_group: int = 0
+    conv_kernel: int = 0
+    conv_std: float = 0.0025
 
     @property
     def tap_width(self) -> int:
@@ -82,6 +87,11 @@ class Config:
     @property
     def kv_dim(self) -> int:
         return self.kv_heads * self.head_dim
+
+    @property
+    def conv_rows(self) -> int:
+        """Rows of a kernel projection: two stages x offsets x groups."""
+        return 2 * self.conv_kernel * (self.hidden // self.conv_group) if self.conv_kernel else 0
 
     def replace(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
@@ -161,13 +171,14 @@ def dequantize_rows(codes: np.ndarray, scales, fmt: int, cols: int) -> np.ndarra
     return q.astype(np.float64) * d
 
 
-def _draw_matrix(cfg: Config, index: int, rows: int, cols: int, fmt: int, chunk_rows: int = 8192):
+def _draw_matrix(cfg: Config, index: int, rows: int, cols: int, fmt: int, chunk_rows: int = 8192,
+                 std: float | None = None):
     """N(0, weight_std) [rows][cols] drawn in row chunks (each chunk its own stream), then coded."""
     codes_parts, scale_parts = [], []
     for c0 in range(0, rows, chunk_rows):
         n = min(chunk_rows, rows - c0)
         r = _rng(cfg.weight_seed or cfg.seed, _S_WEIGHT, index * 100003 + c0 // chunk_rows)
-        w = r.standard_normal((n, cols), dtype=np.float32) * np.float32(cfg.weight_std)
+        w = r.standard_normal((n, cols), dtype=np.float32) * np.float32(cfg.weight_std if std is None else std)
         c, s = quantize_rows(w, fmt)
         codes_parts.append(c)
         if s is not None:
@@ -183,6 +194,7 @@ def _norm_vec(cfg: Config, index: int, n: int) -> np.ndarray:
 
 
 MATRIX_NAMES = ["q", "k", "v", "o", "gate", "up", "down"]
+CONV_NAMES = ["attn_kp", "mlp_kp"]  # kernel projections of the attention and MLP convolutions
 NORM_NAMES = ["in_norm", "post_norm", "q_norm", "k_norm"]
 
 
@@ -201,6 +213,9 @@ def make_weights(cfg: Config, threads: int | None = None) -> dict:
         for mi, name in enumerate(MATRIX_NAMES):
             rows, cols = shapes[name]
             jobs[(li, name)] = (10 + li * 16 + mi, rows, cols, cfg.body_fmt)
+        if cfg.conv_kernel:  # kernel projections: the FC's format (Q8_32, or f32 unquantized)
+            for ci, name in enumerate(CONV_NAMES):
+                jobs[(li, name)] = (10 + li * 16 + 8 + ci, cfg.conv_rows, H, cfg.fc_fmt, 8192, cfg.conv_std)
     threads = threads or min(8, os.cpu_count() or 1)
     with _cf.ThreadPoolExecutor(max_workers=threads) as ex:
         futs = {k: ex.submit(_draw_matrix, cfg, *v) for k, v in jobs.items()}
@@ -213,8 +228,21 @@ def make_weights(cfg: Config, threads: int | None = None) -> dict:
         layer["post_norm"] = _norm_vec(cfg, 10 + li * 8 + 1, H)
         layer["q_norm"] = _norm_vec(cfg, 10 + li * 8 + 2, hd)
         layer["k_norm"] = _norm_vec(cfg, 10 + li * 8 + 3, hd)
+        if cfg.conv_kernel:
+            for ci, name in enumerate(CONV_NAMES):
+                layer[name] = mats[(li, name)]
+                layer[name.replace("_kp", "_base")] = _conv_base(cfg, li * 2 + ci)
         out["layers"].append(layer)
     return out
+
+
+def _conv_base(cfg: Config, index: int) -> np.ndarray:
+    """A convolution's static kernels [stage][offset][hidden]: 1 at offset 0 (the row itself) and
+    0 further back, plus N(0, weight_std), so each stage starts near the identity."""
+    r = _rng(cfg.weight_seed or cfg.seed, _S_CONV, index)
+    b = r.standard_normal((2, cfg.conv_kernel, cfg.hidden), dtype=np.float32) * np.float32(cfg.weight_std)
+    b[:, 0, :] += np.float32(1)
+    return np.ascontiguousarray(b)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -32,7 +32,8 @@ def build(src: str = SRC, out: str = LIB, opt: str = "-O3") -> str:
 class og_geometry(C.Structure):
     _fields_ = [("rope_theta", C.c_double), ("eps", C.c_double)] + [
         (n, C.c_int32) for n in ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab",
-                                 "block", "n_taps", "body_fmt", "fc_fmt", "head_fmt", "max_seqs", "max_ctx")]
+                                 "block", "n_taps", "body_fmt", "fc_fmt", "head_fmt", "max_seqs", "max_ctx",
+                                 "conv_group", "conv_kernel", "conv_fmt")]
 
 
 class og_matrix(C.Structure):
@@ -41,7 +42,8 @@ class og_matrix(C.Structure):
 
 class og_layer(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("in_norm", "post_norm", "q_norm", "k_norm")] + [
-        (n, og_matrix) for n in ("q", "k", "v", "o", "gate", "up", "down")]
+        (n, og_matrix) for n in ("q", "k", "v", "o", "gate", "up", "down", "attn_kp", "mlp_kp")] + [
+        ("attn_base", C.c_void_p), ("mlp_base", C.c_void_p)]
 
 
 class og_weights(C.Structure):
@@ -80,6 +82,7 @@ def lib(path: str | None = None):
             "og_matmul_f32": (None, [vp, i32, i32, vp, i32, vp]),
             "og_attend": (None, [vp, i32, vp, vp, i32, i32, f32, vp, vp]),
             "og_silu_mul": (None, [vp, vp, i32, vp]),
+            "og_row_conv": (None, [vp, i32, i32, i32, i32, i32, vp, vp, vp]),
             "og_create": (vp, [C.POINTER(og_geometry), C.POINTER(og_weights)]),
             "og_destroy": (None, [vp]),
             "og_ctx_append": (i32, [vp, i32, i64, vp, i32]),
@@ -223,6 +226,18 @@ def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return a
 
 
+def row_conv(x: np.ndarray, gs: int, kn: int, stage: int, base: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """One stage of the grouped causal row convolution over the rows x [rows][hidden]: base
+    [2][kn][hidden], d [rows][2*kn*hidden/gs] (dflash.rs Drafter::conv)."""
+    x, base, d = _c(x, np.float32), _c(base, np.float32), _c(d, np.float32)
+    rows, hidden = x.shape
+    if base.shape != (2, kn, hidden) or d.shape != (rows, 2 * kn * (hidden // gs)) or hidden % gs:
+        raise ValueError("row_conv: shapes")
+    y = np.empty_like(x)
+    lib().og_row_conv(_p(x), rows, hidden, gs, kn, stage, _p(base), _p(d), _p(y))
+    return y
+
+
 def top_k(x: np.ndarray, k: int):
     """dflash.rs top_k: the k largest of x with their indices, largest first (earlier index first
     among equal values)."""
@@ -269,6 +284,7 @@ class Model:
         for n in ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab", "block", "n_taps",
                   "body_fmt", "fc_fmt", "head_fmt"):
             setattr(g, n, getattr(cfg, n))
+        g.conv_group, g.conv_kernel, g.conv_fmt = cfg.conv_group, cfg.conv_kernel, cfg.fc_fmt
         g.max_seqs = max_seqs if max_seqs is not None else cfg.n_seqs
         g.max_ctx = max_ctx if max_ctx is not None else cfg.ctx + 64 * max(1, cfg.append_per_block)
         self.geometry = g
@@ -279,6 +295,10 @@ class Model:
                 setattr(L, n, lw[n].ctypes.data)
             for n in ("q", "k", "v", "o", "gate", "up", "down"):
                 setattr(L, n, _mat(lw[n]))
+            if cfg.conv_kernel:
+                for n in ("attn_kp", "mlp_kp"):
+                    setattr(L, n, _mat(lw[n]))
+                L.attn_base, L.mlp_base = lw["attn_base"].ctypes.data, lw["mlp_base"].ctypes.data
         self._layers = layers
         W = og_weights()
         W.fc, W.head = _mat(weights["fc"]), _mat(weights["head"])

@@ -203,6 +203,24 @@ void og_silu_mul(const float* g, const float* u, int n, float* a) {
   }
 }
 
+/* dflash.rs, Drafter::conv: row r of the output mixes rows r, r-1, ..., r-kn+1 of the block
+ * (fewer near its start), column by column, with the static kernel of that offset plus the
+ * row's dynamic kernel of the column's group; the sum is taken in f64 and rounded once. */
+void og_row_conv(const float* x, int rows, int hidden, int gs, int kn, int stage, const float* base,
+                 const float* d, float* y) {
+  const int groups = hidden / gs, pr = 2 * kn * groups;
+  for (int r = 0; r < rows; r++)
+    for (int i = 0; i < hidden; i++) {
+      double acc = 0.0;
+      for (int o = 0; o < kn && o <= r; o++) {
+        const int so = stage * kn + o;
+        const double k = (double)base[(size_t)so * hidden + i] + (double)d[(size_t)r * pr + (size_t)so * groups + i / gs];
+        acc += k * (double)x[(size_t)(r - o) * hidden + i];
+      }
+      y[(size_t)r * hidden + i] = (float)acc;
+    }
+}
+
 /* ------------------------------------------------------------------------------------------ */
 
 typedef struct {
@@ -228,7 +246,8 @@ static size_t seq_floats(const og_geometry* g) {
 
 og_model* og_create(const og_geometry* g, const og_weights* w) {
   if (!g || !w || g->layers <= 0 || g->block < 1 || g->kv_heads <= 0 || g->heads % g->kv_heads ||
-      g->head_dim % 2 || g->max_seqs <= 0 || g->max_ctx < 0)
+      g->head_dim % 2 || g->max_seqs <= 0 || g->max_ctx < 0 || g->conv_kernel < 0 ||
+      (g->conv_kernel > 0 && (g->conv_group <= 0 || g->hidden % g->conv_group)))
     return NULL;
   og_model* m = (og_model*)calloc(1, sizeof(og_model));
   m->g = *g;
@@ -403,7 +422,8 @@ int og_read_kv(const og_model* m, int layer, int seq, int row0, int n, float* k,
 
 /* dflash.rs, Drafter::block, for one sequence: rows [anchor, MASK...] at positions a, a+1, ...
  * pass every layer; returns the rows after the last norm.  Per layer its window and rotary
- * option; no row convolutions (the plain Qwen3 layer). */
+ * option, and, when the geometry declares them, the row convolutions around attention and
+ * the MLP (Drafter::conv_in before the sub-layer, the second stage on its output). */
 static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, float* out) {
   const og_geometry* g = &m->g;
   const int B = g->block, H = g->hidden, nh = g->heads, kvh = g->kv_heads, hd = g->head_dim;
@@ -424,6 +444,11 @@ static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, f
   float* up = (float*)malloc(sizeof(float) * (size_t)B * I);
   float* a = (float*)malloc(sizeof(float) * (size_t)B * I);
   float* tmp = (float*)malloc(sizeof(float) * (size_t)hd);
+  /* row convolutions: the kernels of both stages per row ([B][pr]) and a staging row block */
+  const int kn = g->conv_kernel, pr = kn ? 2 * kn * (H / g->conv_group) : 0;
+  float* da = (float*)malloc(sizeof(float) * (size_t)B * (pr ? pr : 1));
+  float* dm = (float*)malloc(sizeof(float) * (size_t)B * (pr ? pr : 1));
+  float* xc = (float*)malloc(sizeof(float) * (size_t)B * H);
 
   for (int l = 0; l < g->layers; l++) {
     const og_layer* L = &m->layers[l];
@@ -442,6 +467,12 @@ static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, f
     const int nctx = (int)(hi - lo);
     const int nk = nctx + B;
     for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, L->in_norm, H, eps, x + (size_t)r * H);
+    /* Drafter::conv_in: the second stage's kernels from the normed rows, the first stage on them */
+    if (kn) {
+      mm(g->conv_fmt, L->attn_kp, pr, H, x, B, da);
+      og_row_conv(x, B, H, g->conv_group, kn, 0, L->attn_base, da, xc);
+      memcpy(x, xc, sizeof(float) * (size_t)B * H);
+    }
     mm(g->body_fmt, L->q, qd, H, x, B, q);
     mm(g->body_fmt, L->k, kvd, H, x, B, k);
     mm(g->body_fmt, L->v, kvd, H, x, B, v);
@@ -496,15 +527,31 @@ static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, f
       free(kk);
     }
     mm(g->body_fmt, L->o, H, qd, y, B, o);
+    if (kn) { /* the second stage on the sub-layer's output, before the residual */
+      og_row_conv(o, B, H, g->conv_group, kn, 1, L->attn_base, da, xc);
+      memcpy(o, xc, sizeof(float) * (size_t)B * H);
+    }
     for (size_t i = 0; i < (size_t)B * H; i++) h[i] = h[i] + o[i];
     for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, L->post_norm, H, eps, x + (size_t)r * H);
+    if (kn) {
+      mm(g->conv_fmt, L->mlp_kp, pr, H, x, B, dm);
+      og_row_conv(x, B, H, g->conv_group, kn, 0, L->mlp_base, dm, xc);
+      memcpy(x, xc, sizeof(float) * (size_t)B * H);
+    }
     mm(g->body_fmt, L->gate, I, H, x, B, gt);
     mm(g->body_fmt, L->up, I, H, x, B, up);
     og_silu_mul(gt, up, B * I, a);
     mm(g->body_fmt, L->down, H, I, a, B, o);
+    if (kn) {
+      og_row_conv(o, B, H, g->conv_group, kn, 1, L->mlp_base, dm, xc);
+      memcpy(o, xc, sizeof(float) * (size_t)B * H);
+    }
     for (size_t i = 0; i < (size_t)B * H; i++) h[i] = h[i] + o[i];
   }
   for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, m->w.norm, H, eps, out + (size_t)r * H);
+  free(xc);
+  free(dm);
+  free(da);
   free(tmp);
   free(a);
   free(up);

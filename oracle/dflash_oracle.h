@@ -26,6 +26,9 @@ typedef struct {
   int32_t layers, hidden, heads, kv_heads, head_dim, intermediate, vocab, block, n_taps;
   int32_t body_fmt, fc_fmt, head_fmt;
   int32_t max_seqs, max_ctx;
+  /* row convolutions (dflash.rs Geometry conv_group / conv_kernel; 0: none): the kernel
+   * projections are in conv_fmt */
+  int32_t conv_group, conv_kernel, conv_fmt;
 } og_geometry;
 
 /* canonical matrix: F32 float [rows][cols]; Q4_32 uint8 [rows][cols/2] (low nibble = even
@@ -38,6 +41,10 @@ typedef struct {
 typedef struct {
   const float *in_norm, *post_norm, *q_norm, *k_norm;
   og_matrix q, k, v, o, gate, up, down;
+  /* with row convolutions: kernel projections [2*conv_kernel*hidden/conv_group][hidden] and
+   * static kernels [2][conv_kernel][hidden] of the attention's and the MLP's convolution */
+  og_matrix attn_kp, mlp_kp;
+  const float *attn_base, *mlp_base;
 } og_layer;
 
 typedef struct {
@@ -69,6 +76,11 @@ void og_matmul_f32(const float* w, int rows, int cols, const float* x, int m, fl
 void og_attend(const float* q, int nq, const float* k, const float* v, int nk, int head_dim, float scale,
                float* y, double* p);
 void og_silu_mul(const float* g, const float* u, int n, float* a);
+/* one stage of a grouped causal row convolution over the rows of one block (dflash.rs,
+ * Drafter::conv): y[r][i] = sum over o < min(kn, r+1) of (base[stage][o][i] +
+ * d[r][stage][o][i/gs]) * x[r-o][i]; d is [rows][2*kn*(hidden/gs)]; f64 inside, f32 out */
+void og_row_conv(const float* x, int rows, int hidden, int gs, int kn, int stage, const float* base,
+                 const float* d, float* y);
 
 /* ---- the drafter ---- */
 og_model* og_create(const og_geometry* g, const og_weights* w);

@@ -46,6 +46,46 @@ def _w(mat: dict) -> torch.Tensor:
     return torch.from_numpy(di.dequantize_rows(mat["codes"], mat["scales"], mat["fmt"], mat["cols"]))
 
 
+def _row_conv_torch(x: torch.Tensor, base: torch.Tensor, d: torch.Tensor, stage: int, gs: int) -> torch.Tensor:
+    """One stage of the drafter's row convolution on x [B][H] (float64), written with torch ops:
+    for every offset o, the rows shifted down by o (zeros shifted in), times the static kernel
+    plus the rows' dynamic kernels expanded over their column groups."""
+    B, H = x.shape
+    kn = base.shape[1]
+    dk = d.view(B, 2, kn, H // gs)[:, stage].repeat_interleave(gs, dim=-1)  # [B][kn][H]
+    y = torch.zeros_like(x)
+    for o in range(kn):
+        shifted = F.pad(x, (0, 0, o, 0))[:B]
+        y = y + (base[stage, o][None, :] + dk[:, o]) * shifted
+    return y
+
+
+class _ConvIn(torch.nn.Module):
+    """A layer norm followed by the first convolution stage; keeps the kernels for the second."""
+
+    def __init__(self, norm, kp, base, gs, lin):
+        super().__init__()
+        self.norm, self.kp, self.base, self.gs, self.lin = norm, kp, base, gs, lin
+        self.d = None
+
+    def forward(self, h):
+        x = self.norm(h)[0]
+        self.d = self.lin(x, self.kp)
+        return _row_conv_torch(x, self.base, self.d, 0, self.gs)[None]
+
+
+class _ConvOut(torch.nn.Module):
+    """A projection followed by the second convolution stage with the kernels _ConvIn kept."""
+
+    def __init__(self, proj, conv_in):
+        super().__init__()
+        self.proj, self.conv_in = proj, conv_in
+
+    def forward(self, x):
+        y = self.proj(x)[0]
+        return _row_conv_torch(y, self.conv_in.base, self.conv_in.d, 1, self.conv_in.gs)[None]
+
+
 class HFDrafter:
     def __init__(self, cfg: di.Config, weights: dict):
         from transformers.models.qwen3.modeling_qwen3 import Qwen3Config, Qwen3DecoderLayer, Qwen3RMSNorm
@@ -76,6 +116,16 @@ class HFDrafter:
                 for mod in L.modules():
                     if isinstance(mod, torch.nn.Linear):
                         mod.register_forward_pre_hook(lambda m, args: (_a8_fake(args[0]),))
+            if cfg.conv_kernel:  # the row convolutions around attention and the MLP
+                lin = lambda x, w: self._lin(x, w, cfg.fc_fmt)
+                ci = _ConvIn(L.input_layernorm, _w(lw["attn_kp"]), torch.from_numpy(lw["attn_base"]).double(),
+                             cfg.conv_group, lin)
+                L.input_layernorm = ci
+                L.self_attn.o_proj = _ConvOut(L.self_attn.o_proj, ci)
+                cm = _ConvIn(L.post_attention_layernorm, _w(lw["mlp_kp"]), torch.from_numpy(lw["mlp_base"]).double(),
+                             cfg.conv_group, lin)
+                L.post_attention_layernorm = cm
+                L.mlp.down_proj = _ConvOut(L.mlp.down_proj, cm)
             self.layers.append(L)
         self.hidden_norm = Qwen3RMSNorm(cfg.hidden, eps=cfg.eps).double()
         self.norm = Qwen3RMSNorm(cfg.hidden, eps=cfg.eps).double()

@@ -12,6 +12,7 @@ import pytest
 
 import dflash_inputs as di
 import oracle
+import test_oracle_conv as TC
 import test_oracle_model as TM
 import test_oracle_select as TS
 import test_oracle_units as TU
@@ -46,12 +47,21 @@ MUTANTS = [
      "og_rope_head(tmp, hd, p, m->inv_freq);"),
     ("a no-rope layer's queries rotated", "og_rmsnorm_row(qh, L->q_norm, hd, eps, tmp);\n        if (m->rotary[l]) og_rope_head",
      "og_rmsnorm_row(qh, L->q_norm, hd, eps, tmp);\n        if (1) og_rope_head"),
+    ("a convolution one offset short", "for (int o = 0; o < kn && o <= r; o++) {", "for (int o = 0; o < kn - 1 && o <= r; o++) {"),
+    ("a convolution skips the block's first row", "for (int o = 0; o < kn && o <= r; o++) {",
+     "for (int o = 0; o < kn && o < r; o++) {"),
+    ("the dynamic kernel of another group", "+ (size_t)so * groups + i / gs];", "+ (size_t)so * groups + i % groups];"),
+    ("the second stage takes the first stage's kernels", "const int so = stage * kn + o;", "const int so = o;"),
+    ("dynamic kernels dropped", "const double k = (double)base[(size_t)so * hidden + i] + (double)d[",
+     "const double k = (double)base[(size_t)so * hidden + i] + 0.0 * (double)d["),
+    ("the MLP's kernels projected with the attention's matrix", "mm(g->conv_fmt, L->mlp_kp, pr, H, x, B, dm);",
+     "mm(g->conv_fmt, L->attn_kp, pr, H, x, B, dm);"),
     ("the shortlist takes the whole head", "mm(g->head_fmt, m->w.head, head_rows, g->hidden,",
      "mm(g->head_fmt, m->w.head, head_rows > 16 ? head_rows - 16 : head_rows, g->hidden,"),
     ("silu sign", "a[i] = (float)(gv / (1.0 + exp(-gv)) * (double)u[i]);", "a[i] = (float)(gv / (1.0 + exp(gv)) * (double)u[i]);"),
     ("gate and up swapped", "og_silu_mul(gt, up, B * I, a);", "og_silu_mul(up, gt, B * I, a);"),
-    ("attention residual dropped", "mm(g->body_fmt, L->o, H, qd, y, B, o);\n    for (size_t i = 0; i < (size_t)B * H; i++) h[i] = h[i] + o[i];",
-     "mm(g->body_fmt, L->o, H, qd, y, B, o);\n    for (size_t i = 0; i < (size_t)B * H; i++) h[i] = o[i];"),
+    ("attention residual dropped", "h[i] = h[i] + o[i];\n    for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, L->post_norm",
+     "h[i] = o[i];\n    for (int r = 0; r < B; r++) og_rmsnorm_row(h + (size_t)r * H, L->post_norm"),
     ("post-norm weight is the in-norm's", "og_rmsnorm_row(h + (size_t)r * H, L->post_norm, H, eps,",
      "og_rmsnorm_row(h + (size_t)r * H, L->in_norm, H, eps,"),
     ("k-norm on the context is the q-norm", "og_rmsnorm_row(kh, L->k_norm, hd, (float)g->eps, tmp);",
@@ -97,6 +107,10 @@ CHECKS = [
     (TW.test_window_drop_bookkeeping, ()),
     (TW.test_no_rope_everywhere_is_position_free, ()),
     (TW.test_shortlist_head_is_a_prefix, ()),
+    (TC.test_row_conv_against_torch_conv1d, ()),
+    (TC.test_row_conv_reach, ()),
+    (TC.test_identity_convolutions_give_the_plain_layer, ()),
+    (TC.test_convolutions_match_transformers, ()),
 ]
 
 
