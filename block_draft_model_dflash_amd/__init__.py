@@ -31,7 +31,8 @@ EXPORTS = [
 class dflash_geometry(C.Structure):
     _fields_ = [("rope_theta", C.c_double), ("eps", C.c_double)] + [
         (n, C.c_int32) for n in ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab",
-                                 "block", "n_taps", "body_fmt", "fc_fmt", "head_fmt", "max_seqs", "max_ctx")]
+                                 "block", "n_taps", "body_fmt", "fc_fmt", "head_fmt", "max_seqs", "max_ctx",
+                                 "conv_group", "conv_kernel", "conv_fmt")]
 
 
 class dflash_matrix(C.Structure):
@@ -40,7 +41,8 @@ class dflash_matrix(C.Structure):
 
 class dflash_layer_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("in_norm", "post_norm", "q_norm", "k_norm")] + [
-        (n, dflash_matrix) for n in ("q", "k", "v", "o", "gate", "up", "down")]
+        (n, dflash_matrix) for n in ("q", "k", "v", "o", "gate", "up", "down", "attn_kp", "mlp_kp")] + [
+        ("attn_base", C.c_void_p), ("mlp_base", C.c_void_p)]
 
 
 class dflash_weights(C.Structure):

@@ -114,12 +114,14 @@ hipError_t launch_norm_act(const double* part, const float* x, int S, int part_m
 // RMSNorm + A8_32 (or f32) of rows whose sum of squares arrives in pieces: one workgroup per
 // (256 columns, row).  The pieces are added lane-strided then across the wave, the same order on
 // every run; s = 1/sqrt(f32(sum/N) + eps) and (h*s)*w in f32.  Rows >= M are written as zeros.
+// xc (optional) receives the f32 rows too (a row convolution's input).
 constexpr int RMS_COLS = 256;
 template <bool QUANT>
 __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ h, const double* __restrict__ ssq,
                                                       int nparts, const float* __restrict__ w, float eps, int M,
                                                       int Mpad, int N, int8_t* __restrict__ xq,
-                                                      float* __restrict__ dxT, float* __restrict__ xf) {
+                                                      float* __restrict__ dxT, float* __restrict__ xf,
+                                                      float* __restrict__ xc) {
   const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int i = blockIdx.x * RMS_COLS + tid;
   if (m >= M) {
@@ -130,6 +132,7 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
       } else {
         xf[(size_t)m * N + i] = 0.f;
       }
+      if (xc) xc[(size_t)m * N + i] = 0.f;
     }
     return;
   }
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
   if (i >= N) return;  // N is a multiple of 32: whole A8 groups leave together
   const float sc = 1.0f / sqrtf((float)(t / (double)N) + eps);
   const float y = (hv * sc) * wv;
+  if (xc) xc[(size_t)m * N + i] = y;
   if (QUANT)
     emit_a8(y, (size_t)m * N + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
   else
@@ -158,13 +162,83 @@ __global__ __launch_bounds__(RMS_COLS) void k_rms_act(const float* __restrict__ 
 }
 
 hipError_t launch_rms_act(const float* h, const double* ssq, int nparts, const float* w, float eps, int M, int Mpad,
-                          int N, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st) {
+                          int N, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st, float* xc) {
   if (N % 32 || M > Mpad || nparts < 1) return hipErrorInvalidValue;
   dim3 g((unsigned)((N + RMS_COLS - 1) / RMS_COLS), (unsigned)Mpad);
   if (quant)
-    hipLaunchKernelGGL(k_rms_act<true>, g, dim3(RMS_COLS), 0, st, h, ssq, nparts, w, eps, M, Mpad, N, xq, dxT, xf);
+    hipLaunchKernelGGL(k_rms_act<true>, g, dim3(RMS_COLS), 0, st, h, ssq, nparts, w, eps, M, Mpad, N, xq, dxT, xf,
+                       xc);
   else
-    hipLaunchKernelGGL(k_rms_act<false>, g, dim3(RMS_COLS), 0, st, h, ssq, nparts, w, eps, M, Mpad, N, xq, dxT, xf);
+    hipLaunchKernelGGL(k_rms_act<false>, g, dim3(RMS_COLS), 0, st, h, ssq, nparts, w, eps, M, Mpad, N, xq, dxT, xf,
+                       xc);
+  return hipGetLastError();
+}
+
+// Row convolutions (cortiq-engine dflash.rs, Drafter::conv_in / Drafter::conv, and the device
+// block's dflash_conv): y[r][i] = sum over o < min(kn, r + 1) of (base[stage][o][i] +
+// d[r][stage][o][i / gs]) * x[r - o][i], r the row's index in its sequence's block (rows of
+// different sequences never mix).  Evaluated in f64 (every product of two f32 sums is exact
+// there) and rounded once.  One thread per (column, row), 256 columns a workgroup.
+constexpr int CONV_COLS = 256;
+__device__ __forceinline__ float row_conv_at(const float* __restrict__ x, const float* __restrict__ d,
+                                             const float* __restrict__ base, int m, int i, int r, int N, int gs,
+                                             int kn, int stage) {
+  const int groups = N / gs, pr = 2 * kn * groups, g = i / gs;
+  double acc = 0.0;
+  for (int o = 0; o < kn && o <= r; o++) {
+    const int so = stage * kn + o;
+    const double k = (double)base[(size_t)so * N + i] + (double)d[(size_t)m * pr + (size_t)so * groups + g];
+    acc += k * (double)x[(size_t)(m - o) * N + i];
+  }
+  return (float)acc;
+}
+
+// Stage 0 on the normed rows x, then A8_32 into xq/dxT (or f32 into xf); rows M..Mpad zero.
+template <bool QUANT>
+__global__ __launch_bounds__(CONV_COLS) void k_conv_in(const float* __restrict__ x, const float* __restrict__ d,
+                                                       const float* __restrict__ base, int M, int Mpad, int B, int N,
+                                                       int gs, int kn, int8_t* __restrict__ xq,
+                                                       float* __restrict__ dxT, float* __restrict__ xf) {
+  const int m = blockIdx.y, i = blockIdx.x * CONV_COLS + threadIdx.x, lane = threadIdx.x & 63;
+  if (i >= N) return;  // N is a multiple of 32: whole A8 groups leave together
+  const float y = m < M ? row_conv_at(x, d, base, m, i, m % B, N, gs, kn, 0) : 0.f;
+  if (QUANT)
+    emit_a8(y, (size_t)m * N + i, xq, dxT, (size_t)(i >> 5) * Mpad + m, lane);
+  else
+    xf[(size_t)m * N + i] = y;
+}
+
+// Stage 1 on the sub-layer's output o, added to the residual rows h (h = f32(h + f32(conv))),
+// with the rows' sums of squares in 16-column pieces ssq[m*(N/16) + i/16], as the residual
+// GEMM epilogue writes them.
+__global__ __launch_bounds__(CONV_COLS) void k_conv_out(const float* __restrict__ o, const float* __restrict__ d,
+                                                        const float* __restrict__ base, int B, int N, int gs, int kn,
+                                                        float* __restrict__ h, double* __restrict__ ssq) {
+  const int m = blockIdx.y, i = blockIdx.x * CONV_COLS + threadIdx.x, lane = threadIdx.x & 63;
+  if (i >= N) return;  // N is a multiple of 32: whole 16-column pieces leave together
+  const float y = row_conv_at(o, d, base, m, i, m % B, N, gs, kn, 1);
+  const float hv = h[(size_t)m * N + i] + y;
+  h[(size_t)m * N + i] = hv;
+  const double sq = row16_sum_f64((double)hv * (double)hv);
+  if ((lane & 15) == 0) ssq[(size_t)m * (N / 16) + (i >> 4)] = sq;
+}
+
+hipError_t launch_conv_in(const float* x, const float* d, const float* base, int M, int Mpad, int B, int N, int gs,
+                          int kn, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st) {
+  if (N % 32 || M > Mpad || gs < 1 || N % gs || kn < 1 || B < 1) return hipErrorInvalidValue;
+  dim3 g((unsigned)((N + CONV_COLS - 1) / CONV_COLS), (unsigned)Mpad);
+  if (quant)
+    hipLaunchKernelGGL(k_conv_in<true>, g, dim3(CONV_COLS), 0, st, x, d, base, M, Mpad, B, N, gs, kn, xq, dxT, xf);
+  else
+    hipLaunchKernelGGL(k_conv_in<false>, g, dim3(CONV_COLS), 0, st, x, d, base, M, Mpad, B, N, gs, kn, xq, dxT, xf);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_out(const float* o, const float* d, const float* base, int M, int B, int N, int gs, int kn,
+                           float* h, double* ssq, hipStream_t st) {
+  if (N % 32 || gs < 1 || N % gs || kn < 1 || B < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_conv_out, dim3((unsigned)((N + CONV_COLS - 1) / CONV_COLS), (unsigned)M), dim3(CONV_COLS), 0,
+                     st, o, d, base, B, N, gs, kn, h, ssq);
   return hipGetLastError();
 }
 

@@ -45,6 +45,9 @@ struct Layout {
   size_t h, xq, dxT, xq2, dxT2, xf, q, kb, vb, part, ssq, apart, aml;
   size_t act_begin, total;
   size_t part_floats;
+  // row convolutions: packed kernel projections per layer, static kernels, and activations
+  std::vector<size_t> kpa, kpm;
+  size_t base_a = 0, base_m = 0, da = 0, dm = 0, xn = 0, ob = 0;
 };
 
 bool is_fmt(int f) { return f == DFLASH_F32 || f == DFLASH_Q4_32 || f == DFLASH_Q8_32; }
@@ -82,7 +85,21 @@ int check_geometry(const dflash_geometry* g, std::string* err) {
     return fail(DFLASH_ENOTSUP, "body shapes outside the kernels' tiles");
   if (H % 32 || I % 32 || qd % 32 || T % 32) return fail(DFLASH_ENOTSUP, "activation widths must be multiples of 32");
   if (H * 4 > 96 * 1024) return fail(DFLASH_ENOTSUP, "hidden too wide for one workgroup's row");
+  if (g->conv_kernel < 0) return fail(DFLASH_EINVAL, "negative conv_kernel");
+  if (g->conv_kernel > 0) {
+    if (g->conv_group < 1 || H % g->conv_group) return fail(DFLASH_EINVAL, "conv_group must divide hidden");
+    if (!is_fmt(g->conv_fmt)) return fail(DFLASH_EINVAL, "unknown conv format");
+    if ((g->conv_fmt == DFLASH_F32) != (g->body_fmt == DFLASH_F32))
+      return fail(DFLASH_ENOTSUP, "conv_fmt must be f32 with an f32 body and quantized with a quantized one");
+    if (!mat_ok(g->conv_fmt, 2L * g->conv_kernel * (H / g->conv_group), H))
+      return fail(DFLASH_ENOTSUP, "kernel projection shape outside the kernels' tiles");
+  }
   return DFLASH_OK;
+}
+
+// Rows of a kernel projection: both stages' kernels of every offset and column group.
+long conv_rows(const dflash_geometry* g) {
+  return g->conv_kernel > 0 ? 2L * g->conv_kernel * (g->hidden / g->conv_group) : 0;
 }
 
 void plan(const dflash_geometry* g, Layout* L) {
@@ -107,6 +124,17 @@ void plan(const dflash_geometry* g, Layout* L) {
     L->o[l] = take(packed_bytes(g->body_fmt, H, qd));
     L->gu[l] = take(packed_bytes(g->body_fmt, 2 * I, H));
     L->down[l] = take(packed_bytes(g->body_fmt, H, I));
+  }
+  const long PR = conv_rows(g);
+  if (PR) {
+    L->kpa.resize(NL);
+    L->kpm.resize(NL);
+    for (long l = 0; l < NL; l++) {
+      L->kpa[l] = take(packed_bytes(g->conv_fmt, PR, H));
+      L->kpm[l] = take(packed_bytes(g->conv_fmt, PR, H));
+    }
+    L->base_a = take(NL * 2 * g->conv_kernel * H * 4);
+    L->base_m = take(NL * 2 * g->conv_kernel * H * 4);
   }
   L->hidden_norm = take(H * 4);
   L->norm = take(H * 4);
@@ -145,6 +173,12 @@ void plan(const dflash_geometry* g, Layout* L) {
   const size_t arows = (size_t)g->max_seqs * kvh * MAXCH * rep * 16;
   L->apart = take(arows * hd * 8);
   L->aml = take(arows * 2 * 8);
+  if (PR) {  // the kernels of a call's rows (kept from stage 0 to stage 1), x, the sub-layer's output
+    L->da = take((size_t)MROWS * PR * 4);
+    L->dm = take((size_t)MROWS * PR * 4);
+    L->xn = take((size_t)MROWS * H * 4);
+    L->ob = take((size_t)MROWS * H * 4);
+  }
   L->total = off;
 }
 
@@ -268,6 +302,9 @@ int check_weights(const dflash_geometry* g, const dflash_weights* w, std::string
     if (!L.in_norm || !L.post_norm || !L.q_norm || !L.k_norm || !mat(L.q, f) || !mat(L.k, f) || !mat(L.v, f) ||
         !mat(L.o, f) || !mat(L.gate, f) || !mat(L.up, f) || !mat(L.down, f))
       return bad("a layer matrix or norm is null");
+    if (g->conv_kernel > 0 &&
+        (!mat(L.attn_kp, g->conv_fmt) || !mat(L.mlp_kp, g->conv_fmt) || !L.attn_base || !L.mlp_base))
+      return bad("a layer's convolution weights are null");
   }
   return DFLASH_OK;
 }
@@ -354,14 +391,42 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   const int fmt = g.body_fmt;
   const int copy_parts = (H + 255) / 256, tile_parts = H / 16;
 
+  // row convolutions (dflash.rs, Drafter::conv_in / conv): with them the normed rows are also
+  // kept in f32 (xn), a sub-layer's input is stage 0 of them with kernels projected from them
+  // (da / dm, kept for stage 1), and its output o goes through stage 1 before the residual
+  const int kn = g.conv_kernel, gs = g.conv_group, PR = (int)conv_rows(&g);
+  float* xn = kn ? c->at<float>(L.xn) : nullptr;
+  float* ob = kn ? c->at<float>(L.ob) : nullptr;
+  const size_t nbase = (size_t)2 * kn * H;
+  // d = KP . x (KP over A8(x), or f32 x), then x <- stage 0 of x, as the next matrix's input
+  auto conv_in = [&](size_t kp, float* d, const float* base) -> int {
+    int rc;
+    if (bq) {
+      GemmOut o = gemm_out(EPI_F32, M, Mpad);
+      o.y = d;
+      o.ld = PR;
+      o.m_store = M;
+      rc = run_gemm_q(c, g.conv_fmt, kp, PR, H, xq, dxT, o, "kernel projection");
+    } else {
+      rc = run_gemm_f32(c, kp, PR, H, Mpad, M, d, true, PR, M);
+    }
+    if (rc) return rc;
+    return c->hip(launch_conv_in(xn, d, base, M, Mpad, B, H, gs, kn, bq, xq, dxT, xf, c->st), "conv in");
+  };
+
   // h = the block rows; x = A8(RMSNorm(h, in_norm_0))
   TRY_HIP(c, launch_copy_ssq(h, hbuf, M, H, ssq, c->st), "copy block rows");
   TRY_HIP(c,
-          launch_rms_act(hbuf, ssq, copy_parts, c->at<float>(L.in_norm), eps, M, Mpad, H, bq, xq, dxT, xf, c->st),
+          launch_rms_act(hbuf, ssq, copy_parts, c->at<float>(L.in_norm), eps, M, Mpad, H, bq, xq, dxT, xf, c->st, xn),
           "in-norm");
   const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd;
   for (int l = 0; l < NL; l++) {
     int rc;
+    float* da = kn ? c->at<float>(L.da) : nullptr;
+    float* dm = kn ? c->at<float>(L.dm) : nullptr;
+    const float* base_a = kn ? c->at<float>(L.base_a) + (size_t)l * nbase : nullptr;
+    const float* base_m = kn ? c->at<float>(L.base_m) + (size_t)l * nbase : nullptr;
+    if (kn && (rc = conv_in(L.kpa[l], da, base_a))) return rc;
     {
       StageTimer t(c, DFLASH_STAGE_QKV);
       if (bq) {
@@ -399,7 +464,57 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
     const bool last = l + 1 == NL;
     const float* nw = last ? c->at<float>(L.norm) : c->at<float>(L.in_norm) + (size_t)(l + 1) * H;
     const bool nq = last ? (!hidden_only && g.head_fmt != DFLASH_F32) : bq;
-    if (bq) {
+    if (kn) {
+      // o = Wo y; h += stage 1 of o; x = RMSNorm(h, post_norm); x <- stage 0 of x (MLP kernels);
+      // a = silu(gate x) * up x; o = down a; h += stage 1 of o; the next norm
+      {
+        StageTimer t(c, DFLASH_STAGE_O);
+        if (bq) {
+          GemmOut o = gemm_out(EPI_F32, M, Mpad);
+          o.y = ob;
+          o.ld = H;
+          o.m_store = M;
+          rc = run_gemm_q(c, fmt, L.o[l], H, qd, xq, dxT, o, "o");
+        } else {
+          rc = run_gemm_f32(c, L.o[l], H, qd, Mpad, M, ob, true, H, M);
+        }
+        if (rc) return rc;
+      }
+      TRY_HIP(c, launch_conv_out(ob, da, base_a, M, B, H, gs, kn, hbuf, ssq, c->st), "conv out");
+      TRY_HIP(c,
+              launch_rms_act(hbuf, ssq, tile_parts, c->at<float>(L.post_norm) + (size_t)l * H, eps, M, Mpad, H, bq, xq,
+                             dxT, xf, c->st, xn),
+              "post-norm");
+      if ((rc = conv_in(L.kpm[l], dm, base_m))) return rc;
+      {
+        StageTimer t(c, DFLASH_STAGE_GATE_UP);
+        if (bq) {
+          GemmOut o = gemm_out(EPI_SWIGLU, M, Mpad);
+          o.xq = xq2;
+          o.dxT = dxT2;
+          rc = run_gemm_q(c, fmt, L.gu[l], 2 * I, H, xq, dxT, o, "gate|up + swiglu");
+        } else {
+          rc = run_gemm_f32(c, L.gu[l], 2 * I, H, Mpad, M, part, false, 0, 0);
+          if (!rc) rc = c->hip(launch_swiglu_act(part, 1, M, Mpad, I, false, xq, dxT, xf, c->st), "swiglu");
+        }
+        if (rc) return rc;
+      }
+      {
+        StageTimer t(c, DFLASH_STAGE_DOWN);
+        if (bq) {
+          GemmOut o = gemm_out(EPI_F32, M, Mpad);
+          o.y = ob;
+          o.ld = H;
+          o.m_store = M;
+          rc = run_gemm_q(c, fmt, L.down[l], H, I, xq2, dxT2, o, "down");
+        } else {
+          rc = run_gemm_f32(c, L.down[l], H, I, Mpad, M, ob, true, H, M);
+        }
+        if (rc) return rc;
+      }
+      TRY_HIP(c, launch_conv_out(ob, dm, base_m, M, B, H, gs, kn, hbuf, ssq, c->st), "conv out");
+      TRY_HIP(c, launch_rms_act(hbuf, ssq, tile_parts, nw, eps, M, Mpad, H, nq, xq, dxT, xf, c->st, xn), "next norm");
+    } else if (bq) {
       // h += Wo y; x = A8(RMSNorm(h, post_norm)); a = A8(silu(gate x) * up x); h += down a
       {
         StageTimer t(c, DFLASH_STAGE_O);
@@ -558,6 +673,13 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* works
     if ((e = cp(L.post_norm + (size_t)l * H * 4, W.post_norm, H))) return fin(e);
     if ((e = cp(L.q_norm + (size_t)l * hd * 4, W.q_norm, hd))) return fin(e);
     if ((e = cp(L.k_norm + (size_t)l * hd * 4, W.k_norm, hd))) return fin(e);
+    if (g->conv_kernel > 0) {
+      const long PR = conv_rows(g), nb = 2L * g->conv_kernel * H;
+      if ((e = pack(g->conv_fmt, W.attn_kp, PR, H, L.kpa[l], 0, 1))) return fin(e);
+      if ((e = pack(g->conv_fmt, W.mlp_kp, PR, H, L.kpm[l], 0, 1))) return fin(e);
+      if ((e = cp(L.base_a + (size_t)l * nb * 4, W.attn_base, nb))) return fin(e);
+      if ((e = cp(L.base_m + (size_t)l * nb * 4, W.mlp_base, nb))) return fin(e);
+    }
   }
   if ((e = c->hip(hipMemcpyAsync(c->ws + L.hidden_norm, w->hidden_norm, H * 4, hipMemcpyDeviceToDevice, c->st),
                   "copy norm")))

@@ -97,7 +97,15 @@ hipError_t launch_norm_act(const double* part, const float* x, int S, int part_m
 // RMSNorm + activation output of rows h [M][N] whose sums of squares arrive in nparts f64
 // pieces ssq[m*nparts + i]; many workgroups per row.
 hipError_t launch_rms_act(const float* h, const double* ssq, int nparts, const float* w, float eps, int M, int Mpad,
-                          int N, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st);
+                          int N, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st, float* xc = nullptr);
+// Row convolutions over each sequence's B block rows (rows of one call: M = sequences * B).
+// d [M][2*kn*N/gs] the rows' dynamic kernels, base [2][kn][N] the static ones.  conv_in: stage
+// 0 of x [M][N] f32, then A8_32 into xq/dxT (quant) or f32 into xf, rows M..Mpad zero.
+// conv_out: stage 1 of o [M][N] added to h, with the sums of squares of h in 16-column pieces.
+hipError_t launch_conv_in(const float* x, const float* d, const float* base, int M, int Mpad, int B, int N, int gs,
+                          int kn, bool quant, int8_t* xq, float* dxT, float* xf, hipStream_t st);
+hipError_t launch_conv_out(const float* o, const float* d, const float* base, int M, int B, int N, int gs, int kn,
+                           float* h, double* ssq, hipStream_t st);
 // h = x (M rows of N) and the rows' sums of squares in N/256 pieces ssq[m*(N/256) + i].
 hipError_t launch_copy_ssq(const float* x, float* h, int M, int N, double* ssq, hipStream_t st);
 // a = silu(gate) * up from the interleaved gate|up partials [S][Mpad][2I].

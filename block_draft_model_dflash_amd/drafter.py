@@ -24,6 +24,10 @@ def geometry(spec, max_ctx: int, max_seqs: int) -> dflash_geometry:
         setattr(g, n, int(getattr(spec, n)))
     g.max_ctx = int(max_ctx)
     g.max_seqs = int(max_seqs)
+    # row convolutions (absent: none); their kernel projections are coded like the FC
+    g.conv_group = int(getattr(spec, "conv_group", 0))
+    g.conv_kernel = int(getattr(spec, "conv_kernel", 0))
+    g.conv_fmt = int(getattr(spec, "conv_fmt", spec.fc_fmt))
     return g
 
 
@@ -61,6 +65,9 @@ class Drafter:
                 setattr(L, n, dev(lw[n]))
             for n in ("q", "k", "v", "o", "gate", "up", "down"):
                 setattr(L, n, mat(lw[n]))
+            if self.g.conv_kernel:
+                L.attn_kp, L.mlp_kp = mat(lw["attn_kp"]), mat(lw["mlp_kp"])
+                L.attn_base, L.mlp_base = dev(lw["attn_base"]), dev(lw["mlp_base"])
         W = dflash_weights()
         W.fc, W.head = mat(weights["fc"]), mat(weights["head"])
         W.hidden_norm, W.norm = dev(weights["hidden_norm"]), dev(weights["norm"])

@@ -68,6 +68,12 @@ typedef struct {
   int32_t head_fmt; /* head [vocab][hidden] */
   int32_t max_seqs; /* independent sequences (separate contexts, shared weights) */
   int32_t max_ctx;  /* context rows a sequence can hold */
+  /* Row convolutions around the attention and the MLP (dflash.rs, Geometry conv_group /
+   * conv_kernel; Drafter::conv_in and Drafter::conv).  conv_kernel 0: none (the plain Qwen3
+   * layer; the conv fields of the weights are then ignored).  Else conv_group divides hidden,
+   * the kernel projections have 2*conv_kernel*hidden/conv_group rows (a multiple of 16) and
+   * conv_fmt is DFLASH_F32 with an f32 body, DFLASH_Q4_32 / DFLASH_Q8_32 with a quantized one. */
+  int32_t conv_group, conv_kernel, conv_fmt;
 } dflash_geometry;
 
 /* A matrix in the canonical layout above (device pointers; scales NULL for DFLASH_F32). */
@@ -84,6 +90,11 @@ typedef struct {
   dflash_matrix o;                  /* [hidden][heads*head_dim] */
   dflash_matrix gate, up;           /* [intermediate][hidden] */
   dflash_matrix down;               /* [hidden][intermediate] */
+  /* with row convolutions: the kernel projections [2*conv_kernel*(hidden/conv_group)][hidden]
+   * (conv_fmt) of the attention's and the MLP's convolution, and their static kernels
+   * [2][conv_kernel][hidden] (stage 0 before the sub-layer, stage 1 after) */
+  dflash_matrix attn_kp, mlp_kp;
+  const float *attn_base, *mlp_base;
 } dflash_layer_weights;
 
 typedef struct {

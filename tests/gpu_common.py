@@ -15,7 +15,7 @@ def say(*a):
 
 
 _GEOM = ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "n_taps", "vocab", "body_fmt", "fc_fmt",
-         "head_fmt", "weight_std", "norm_mean", "norm_std")
+         "head_fmt", "weight_std", "norm_mean", "norm_std", "conv_group", "conv_kernel", "conv_std")
 
 
 def drafter_key(cfg: di.Config):

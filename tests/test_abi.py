@@ -53,14 +53,29 @@ def test_workspace_sizes_of_the_workloads(key):
     ({"hidden": 4000}, D.DFLASH_ENOTSUP),
     ({"layers": 0}, D.DFLASH_EINVAL),
     ({"body_fmt": 7}, D.DFLASH_EINVAL),
+    ({"conv_kernel": -1}, D.DFLASH_EINVAL),
+    ({"conv_kernel": 4, "conv_group": 24}, D.DFLASH_EINVAL),  # 24 does not divide 2048
+    ({"conv_kernel": 4, "conv_group": 16, "g.conv_fmt": D.DFLASH_F32}, D.DFLASH_ENOTSUP),  # f32 beside a q4 body
+    ({"conv_kernel": 1, "conv_group": 512}, D.DFLASH_ENOTSUP),  # 8 kernel rows: not a whole n-tile
 ])
 def test_geometry_checks(change, code):
-    c = di.CONFIGS["small_q"].replace(**change)
+    c = di.CONFIGS["small_q"].replace(**{k: v for k, v in change.items() if not k.startswith("g.")})
     g = geometry(c, 600, 1)
+    for k, v in change.items():  # fields of the C geometry alone
+        if k.startswith("g."):
+            setattr(g, k[2:], v)
     with pytest.raises(D.DFlashError) as e:
         D.dflash_workspace_bytes(g)
     assert e.value.code == code
     assert "geometry" in D.dflash_last_error(None)
+
+
+def test_convolution_workspace():
+    c = di.CONFIGS["qwen3_8b"]
+    plain = D.dflash_workspace_bytes(geometry(c, c.ctx + 64, 1))
+    conv = D.dflash_workspace_bytes(geometry(c.replace(conv_group=16, conv_kernel=4), c.ctx + 64, 1))
+    # two Q8_32 kernel projections of 2048 x 4096 per layer, at least
+    assert conv - plain >= c.layers * 2 * (2048 // 16) * (4096 // 128) * 2176
 
 
 def test_too_many_rows_refused():
