@@ -131,6 +131,9 @@ def main() -> int:
     ap.add_argument("--stages", type=int, default=1, help="also time each stage in its own untimed pass")
     ap.add_argument("--selection", type=int, default=1,
                     help="also time the candidate selection of one block's draft rows (top 16, rank 128)")
+    ap.add_argument("--variants", type=int, default=1,
+                    help="also time the block with the drafter's optional parts: a head shortlist, sliding "
+                         "windows, row convolutions (single-sequence workloads)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed region, run one plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -278,6 +281,42 @@ def main() -> int:
         torch.cuda.synchronize()
         sel_ms = e0.elapsed_time(e1) / K
 
+    # the block with the optional parts of the drafter the workloads do not declare (untimed for
+    # `value`): the head over its first 65536 rows; a 1024-position window on layers 0, 2, 4;
+    # row convolutions of 16 columns a group and 4 offsets (a drafter with the same weights plus
+    # the convolutions')
+    variants = {}
+    if args.variants and cfg.n_seqs == 1 and app is None:
+        def timed(fn):
+            for i in range(W):
+                fn(i)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for i in range(K):
+                fn(W + i)
+            torch.cuda.synchronize()
+            return round((time.perf_counter() - t) * 1e3 / K, 5)
+
+        def prefill(d):
+            for p0 in range(0, cfg.ctx, 4096):
+                d.append(0, p0, torch.from_numpy(di.make_taps(cfg, 0, p0, min(4096, cfg.ctx - p0))).cuda())
+            torch.cuda.synchronize()
+
+        if cfg.vocab > 65536:
+            short = torch.empty((1, cfg.block, 65536), dtype=torch.float32, device="cuda")
+            variants["head_shortlist_65536"] = timed(
+                lambda i: gm.block_forward(seqs, [cfg.ctx], hs[i], out=short, head_rows=65536))
+        gm.reset(0)
+        gm.set_layer_options([1024 if li % 2 == 0 else 0 for li in range(cfg.layers)], None)
+        prefill(gm)
+        variants["windows_1024_even_layers"] = timed(lambda i: gm.block_forward(seqs, [cfg.ctx], hs[i], out=logits))
+        ccfg = cfg.replace(conv_group=16, conv_kernel=4)
+        cm = Drafter(ccfg, di.add_conv_weights(ccfg, weights), max_ctx=cfg.ctx + 64, max_seqs=1)
+        prefill(cm)
+        variants["row_conv_group16_kernel4"] = timed(lambda i: cm.block_forward(seqs, [cfg.ctx], hs[i], out=logits))
+        cm.close()
+        log("variants ms/block:", variants)
+
     if args.copy_probe_mib:
         # a plain streaming kernel of known size (read n bytes, write n bytes): the reference
         # against which the HBM byte counters of the other kernels are scaled
@@ -341,6 +380,7 @@ def main() -> int:
         "ms_per_step_with_kernel_events": round(ms_events, 5),
         "stages_ms_per_step": stages,
         "selection_ms_per_block": None if sel_ms is None else round(sel_ms, 5),
+        "variants_ms_per_block": variants,
     }
     if args.cpu_baseline and cfg.n_seqs == 1 and cfg.ctx <= 8192:
         out["cpu_baseline"] = cpu_baseline(cfg, weights)

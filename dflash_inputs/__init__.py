@@ -213,9 +213,6 @@ def make_weights(cfg: Config, threads: int | None = None) -> dict:
         for mi, name in enumerate(MATRIX_NAMES):
             rows, cols = shapes[name]
             jobs[(li, name)] = (10 + li * 16 + mi, rows, cols, cfg.body_fmt)
-        if cfg.conv_kernel:  # kernel projections: the FC's format (Q8_32, or f32 unquantized)
-            for ci, name in enumerate(CONV_NAMES):
-                jobs[(li, name)] = (10 + li * 16 + 8 + ci, cfg.conv_rows, H, cfg.fc_fmt, 8192, cfg.conv_std)
     threads = threads or min(8, os.cpu_count() or 1)
     with _cf.ThreadPoolExecutor(max_workers=threads) as ex:
         futs = {k: ex.submit(_draw_matrix, cfg, *v) for k, v in jobs.items()}
@@ -228,10 +225,28 @@ def make_weights(cfg: Config, threads: int | None = None) -> dict:
         layer["post_norm"] = _norm_vec(cfg, 10 + li * 8 + 1, H)
         layer["q_norm"] = _norm_vec(cfg, 10 + li * 8 + 2, hd)
         layer["k_norm"] = _norm_vec(cfg, 10 + li * 8 + 3, hd)
-        if cfg.conv_kernel:
-            for ci, name in enumerate(CONV_NAMES):
-                layer[name] = mats[(li, name)]
-                layer[name.replace("_kp", "_base")] = _conv_base(cfg, li * 2 + ci)
+        out["layers"].append(layer)
+    return add_conv_weights(cfg, out, threads) if cfg.conv_kernel else out
+
+
+def add_conv_weights(cfg: Config, weights: dict, threads: int | None = None) -> dict:
+    """The drafter's weights with its row convolutions' drawn in (a copy of the layer dicts; the
+    other arrays are shared): per layer the kernel projections ``attn_kp`` / ``mlp_kp``, coded
+    like the FC (Q8_32, or f32 unquantized), and the static kernels ``attn_base`` / ``mlp_base``."""
+    H = cfg.hidden
+    jobs = {(li, name): (10 + li * 16 + 8 + ci, cfg.conv_rows, H, cfg.fc_fmt, 8192, cfg.conv_std)
+            for li in range(cfg.layers) for ci, name in enumerate(CONV_NAMES)}
+    threads = threads or min(8, os.cpu_count() or 1)
+    with _cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        futs = {k: ex.submit(_draw_matrix, cfg, *v) for k, v in jobs.items()}
+        mats = {k: f.result() for k, f in futs.items()}
+    out = dict(weights)
+    out["layers"] = []
+    for li, lw in enumerate(weights["layers"]):
+        layer = dict(lw)
+        for ci, name in enumerate(CONV_NAMES):
+            layer[name] = mats[(li, name)]
+            layer[name.replace("_kp", "_base")] = _conv_base(cfg, li * 2 + ci)
         out["layers"].append(layer)
     return out
 
