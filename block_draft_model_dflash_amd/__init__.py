@@ -77,7 +77,7 @@ def lib():
             "dflash_ctx_reset": (i32, [vp, i32]),
             "dflash_ctx_span": (i32, [vp, i32, C.POINTER(i64), C.POINTER(i64)]),
             "dflash_block_forward": (i32, [vp, i32, vp, vp, vp, vp]),
-            "dflash_block_forward_rows": (i32, [vp, i32, vp, vp, vp, i32, vp]),
+            "dflash_block_forward_rows": (i32, [vp, i32, vp, vp, vp, i32, i32, vp]),
             "dflash_set_layer_options": (i32, [vp, vp, vp]),
             "dflash_ctx_dropped": (i32, [vp, i32, i32, C.POINTER(i64)]),
             "dflash_block_hidden": (i32, [vp, i32, vp, vp, vp, vp]),
@@ -161,10 +161,10 @@ def dflash_block_forward(ctx, seqs, anchors, h: int, logits: int) -> int:
     return _check(lib().dflash_block_forward(ctx, n, C.cast(s, C.c_void_p), C.cast(a, C.c_void_p), h, logits), ctx)
 
 
-def dflash_block_forward_rows(ctx, seqs, anchors, h: int, head_rows: int, logits: int) -> int:
+def dflash_block_forward_rows(ctx, seqs, anchors, h: int, block_rows: int, head_rows: int, logits: int) -> int:
     n, s, a = _host_arrays(seqs, anchors)
     return _check(lib().dflash_block_forward_rows(ctx, n, C.cast(s, C.c_void_p), C.cast(a, C.c_void_p), h,
-                                                  int(head_rows), logits), ctx)
+                                                  int(block_rows), int(head_rows), logits), ctx)
 
 
 def dflash_set_layer_options(ctx, windows=None, rotary=None) -> int:

@@ -337,7 +337,7 @@ void layer_ranges(const dflash_ctx* c, int l, const int32_t* seqs, const int64_t
 }
 
 int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
-                 float* out, bool hidden_only, int head_rows) {
+                 float* out, bool hidden_only, int head_rows, int block_rows) {
   const dflash_geometry& g = c->g;
   if (n_seqs < 1 || n_seqs > g.max_seqs) return c->fail(DFLASH_EINVAL, "n_seqs %d outside [1, %d]", n_seqs, g.max_seqs);
   if (!seqs || !anchors || !h || !out) return c->fail(DFLASH_EINVAL, "null pointer");
@@ -352,7 +352,8 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
     si.slot[i] = seqs[i];
     si.pos0[i] = anchors[i];
   }
-  const int B = g.block, H = g.hidden, nh = g.heads, kvh = g.kv_heads, hd = g.head_dim, NL = g.layers;
+  // the block's rows: all of them, or the first block_rows (the anchor and the rows after it)
+  const int B = block_rows, H = g.hidden, nh = g.heads, kvh = g.kv_heads, hd = g.head_dim, NL = g.layers;
   const int qd = nh * hd, kvd = kvh * hd, I = g.intermediate, V = g.vocab;
   const int M = n_seqs * B, Mpad = round16(M);
   const float eps = (float)g.eps;
@@ -826,17 +827,19 @@ int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, con
                          float* logits) {
   if (!c) return DFLASH_EINVAL;
   StageTimer t(c, DFLASH_STAGE_BLOCK);
-  return block_common(c, n_seqs, seqs, anchors, h, logits, false, c->g.vocab);
+  return block_common(c, n_seqs, seqs, anchors, h, logits, false, c->g.vocab, c->g.block);
 }
 
 int dflash_block_forward_rows(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors,
-                              const float* h, int32_t head_rows, float* logits) {
+                              const float* h, int32_t block_rows, int32_t head_rows, float* logits) {
   if (!c) return DFLASH_EINVAL;
+  if (block_rows < 1 || block_rows > c->g.block)
+    return c->fail(DFLASH_EINVAL, "block_rows %d outside [1, %d]", block_rows, c->g.block);
   if (head_rows != c->g.vocab && (head_rows < 16 || head_rows > c->g.vocab || head_rows % 16))
     return c->fail(DFLASH_EINVAL, "head_rows %d: a multiple of 16 in [16, %d], or %d", head_rows, c->g.vocab,
                    c->g.vocab);
   StageTimer t(c, DFLASH_STAGE_BLOCK);
-  return block_common(c, n_seqs, seqs, anchors, h, logits, false, head_rows);
+  return block_common(c, n_seqs, seqs, anchors, h, logits, false, head_rows, block_rows);
 }
 
 int dflash_time_stage(dflash_ctx* c, int32_t stage) {
@@ -883,7 +886,7 @@ int dflash_read_timing(dflash_ctx* c, int32_t stage, double* total_ms, int64_t* 
 int dflash_block_hidden(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                         float* hidden) {
   if (!c) return DFLASH_EINVAL;
-  return block_common(c, n_seqs, seqs, anchors, h, hidden, true, c->g.vocab);
+  return block_common(c, n_seqs, seqs, anchors, h, hidden, true, c->g.vocab, c->g.block);
 }
 
 const char* dflash_last_error(const dflash_ctx* c) { return c ? c->err.c_str() : g_create_err.c_str(); }

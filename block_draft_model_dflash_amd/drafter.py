@@ -112,17 +112,19 @@ class Drafter:
 
     # -- blocks ----------------------------------------------------------------------------
     def block_forward(self, seqs, anchors, h, out=None, head_rows=None):
-        """Logits of every block row, over the head's first head_rows rows when given."""
+        """Logits of every block row, over the head's first head_rows rows when given.  h is
+        [seqs][rows][hidden]: fewer rows than the block's cut the block to those rows."""
         torch = self.torch
         t = self._f32(h)
+        rows = t.shape[1]
         n = self.g.vocab if head_rows is None else int(head_rows)
         if out is None:
-            out = torch.empty((len(seqs), self.g.block, n), dtype=torch.float32, device=self.device)
+            out = torch.empty((len(seqs), rows, n), dtype=torch.float32, device=self.device)
         self._sync_stream()
-        if head_rows is None:
+        if head_rows is None and rows == self.g.block:
             dflash_block_forward(self.ctx, seqs, anchors, t.data_ptr(), out.data_ptr())
         else:
-            dflash_block_forward_rows(self.ctx, seqs, anchors, t.data_ptr(), n, out.data_ptr())
+            dflash_block_forward_rows(self.ctx, seqs, anchors, t.data_ptr(), rows, n, out.data_ptr())
         self._last_inputs = t
         return out
 

@@ -165,12 +165,15 @@ int dflash_ctx_span(const dflash_ctx* c, int32_t seq, int64_t* first, int64_t* e
 int dflash_block_forward(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors,
                          const float* h, float* logits);
 
-/* The same block with the head over its first head_rows rows only, a shortlist of the
- * vocabulary (dflash.rs, Drafter::block_dev: the drafts' head over the table's first rows):
- * logits receives device [n_seqs][block][head_rows] f32.  head_rows is a multiple of 16 in
- * [16, vocab] (or vocab itself), else DFLASH_EINVAL. */
+/* The same block cut to its first block_rows rows, with the head over its first head_rows rows
+ * only.  The cut block (gpu_wgpu/dflash_dev.rs, Dev::block: the anchor and the rows after it,
+ * eight there) is a whole block of block_rows rows, the attention among block rows included;
+ * the shortlist (dflash.rs, Drafter::block_dev: the drafts' head over the table's first rows)
+ * is a prefix of the vocabulary.  h is device [n_seqs][block_rows][hidden] f32, logits
+ * receives device [n_seqs][block_rows][head_rows] f32.  block_rows in [1, block]; head_rows a
+ * multiple of 16 in [16, vocab], or vocab itself; else DFLASH_EINVAL. */
 int dflash_block_forward_rows(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors,
-                              const float* h, int32_t head_rows, float* logits);
+                              const float* h, int32_t block_rows, int32_t head_rows, float* logits);
 
 /* The same block, stopping after the final RMSNorm: hidden receives device
  * [n_seqs][block][hidden] f32 (the rows the head reads; a diagnostic of the block body). */

@@ -91,7 +91,7 @@ def lib(path: str | None = None):
             "og_ctx_span": (i32, [vp, i32, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
             "og_read_kv": (i32, [vp, i32, i32, i32, i32, vp, vp]),
             "og_block_forward": (i32, [vp, i32, vp, vp, vp, vp]),
-            "og_block_forward_rows": (i32, [vp, i32, vp, vp, vp, i32, vp]),
+            "og_block_forward_rows": (i32, [vp, i32, vp, vp, vp, i32, i32, vp]),
             "og_set_layer_options": (i32, [vp, vp, vp]),
             "og_dropped": (i64, [vp, i32, i32]),
             "og_block_hidden": (i32, [vp, i32, vp, vp, vp, vp]),
@@ -360,13 +360,15 @@ class Model:
         return int(lib().og_dropped(self.h, seq, layer))
 
     def block_forward(self, seqs, anchors, h: np.ndarray, head_rows: int | None = None) -> np.ndarray:
-        """Logits of every block row; with head_rows, over the head's first head_rows rows only."""
+        """Logits of every block row; with head_rows, over the head's first head_rows rows only.
+        h [seqs][rows][hidden]: fewer rows than the block's cut it to those rows."""
         seqs = np.asarray(seqs, np.int32)
         anchors = np.asarray(anchors, np.int64)
         h = _c(h, np.float32)
+        rows = h.shape[1]
         n = self.cfg.vocab if head_rows is None else int(head_rows)
-        out = np.empty((len(seqs), self.cfg.block, n), np.float32)
-        rc = lib().og_block_forward_rows(self.h, len(seqs), _p(seqs), _p(anchors), _p(h), n, _p(out))
+        out = np.empty((len(seqs), rows, n), np.float32)
+        rc = lib().og_block_forward_rows(self.h, len(seqs), _p(seqs), _p(anchors), _p(h), rows, n, _p(out))
         if rc:
             raise ValueError(rc)
         return out

@@ -424,9 +424,9 @@ int og_read_kv(const og_model* m, int layer, int seq, int row0, int n, float* k,
  * pass every layer; returns the rows after the last norm.  Per layer its window and rotary
  * option, and, when the geometry declares them, the row convolutions around attention and
  * the MLP (Drafter::conv_in before the sub-layer, the second stage on its output). */
-static void block_one(og_model* m, int seq, int64_t anchor, const float* h_in, float* out) {
+static void block_one(og_model* m, int seq, int64_t anchor, int B, const float* h_in, float* out) {
   const og_geometry* g = &m->g;
-  const int B = g->block, H = g->hidden, nh = g->heads, kvh = g->kv_heads, hd = g->head_dim;
+  const int H = g->hidden, nh = g->heads, kvh = g->kv_heads, hd = g->head_dim;
   const int qd = nh * hd, kvd = kvh * hd, I = g->intermediate, rep = nh / kvh;
   const float eps = (float)g->eps;
   const float scale = powf((float)hd, -0.5f); /* Drafter::block: (hd as f32).powf(-0.5) */
@@ -579,28 +579,33 @@ int og_block_hidden(og_model* m, int n_seqs, const int32_t* seqs, const int64_t*
                     float* hidden) {
   if (check_block_args(m, n_seqs, seqs, anchors)) return -1;
   size_t per = (size_t)m->g.block * m->g.hidden;
-  for (int i = 0; i < n_seqs; i++) block_one(m, seqs[i], anchors[i], h + per * i, hidden + per * i);
+  for (int i = 0; i < n_seqs; i++) block_one(m, seqs[i], anchors[i], m->g.block, h + per * i, hidden + per * i);
   return 0;
 }
 
 /* dflash.rs, module header: logits = head . norm(h); every block row gets its logits.  The
- * device block (Drafter::block_dev) may take the head's first rows only, a shortlist of the
- * vocabulary: the same product over those rows. */
+ * device block (gpu_wgpu/dflash_dev.rs, Dev::block) may cut the block to its first block_rows
+ * rows (the anchor and the next rows, up to eight there), which then are the whole block of the
+ * forward, the attention among block rows included; Drafter::block_dev may take the head's
+ * first rows only, a shortlist of the vocabulary: the same product over those rows.  h and
+ * logits hold block_rows rows per sequence. */
 int og_block_forward_rows(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
-                          int head_rows, float* logits) {
-  if (check_block_args(m, n_seqs, seqs, anchors) || head_rows < 1 || head_rows > m->g.vocab) return -1;
+                          int block_rows, int head_rows, float* logits) {
+  if (check_block_args(m, n_seqs, seqs, anchors) || head_rows < 1 || head_rows > m->g.vocab || block_rows < 1 ||
+      block_rows > m->g.block)
+    return -1;
   const og_geometry* g = &m->g;
-  size_t per = (size_t)g->block * g->hidden;
+  size_t per = (size_t)block_rows * g->hidden;
   float* x = (float*)malloc(sizeof(float) * per * (size_t)(n_seqs > 0 ? n_seqs : 1));
-  for (int i = 0; i < n_seqs; i++) block_one(m, seqs[i], anchors[i], h + per * i, x + per * i);
-  if (n_seqs > 0) mm(g->head_fmt, m->w.head, head_rows, g->hidden, x, n_seqs * g->block, logits);
+  for (int i = 0; i < n_seqs; i++) block_one(m, seqs[i], anchors[i], block_rows, h + per * i, x + per * i);
+  if (n_seqs > 0) mm(g->head_fmt, m->w.head, head_rows, g->hidden, x, n_seqs * block_rows, logits);
   free(x);
   return 0;
 }
 
 int og_block_forward(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                      float* logits) {
-  return og_block_forward_rows(m, n_seqs, seqs, anchors, h, m->g.vocab, logits);
+  return og_block_forward_rows(m, n_seqs, seqs, anchors, h, m->g.block, m->g.vocab, logits);
 }
 
 /* ---- candidate selection ---- */

@@ -102,9 +102,10 @@ int64_t og_dropped(const og_model* m, int seq, int layer);
 /* logits[s][block][vocab] of the block rows h[s][block][hidden] anchored at anchors[s] */
 int og_block_forward(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                      float* logits);
-/* the same over the head's first head_rows rows (a shortlist): logits[s][block][head_rows] */
+/* the same with the block cut to its first block_rows rows (h [s][block_rows][hidden]) and the
+ * head over its first head_rows rows (a shortlist): logits[s][block_rows][head_rows] */
 int og_block_forward_rows(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
-                          int head_rows, float* logits);
+                          int block_rows, int head_rows, float* logits);
 /* the same, stopping after the final norm: hidden[s][block][hidden] */
 int og_block_hidden(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                     float* hidden);

@@ -131,3 +131,42 @@ def test_shortlist_and_option_errors():
     with pytest.raises(DFlashError):
         gm.set_layer_options([4, -1], None)
     assert [gm.dropped(0, li) for li in range(cfg.layers)] == [0, 0]
+
+
+def _cut_block(cfg, om, gm, seqs, anchors, index, rows, tol, head_rows=None):
+    h = np.ascontiguousarray(np.stack([di.make_block_input(cfg, s, index) for s in seqs])[:, :rows])
+    say(f"{cfg.key}: block cut to {rows} rows, seqs={list(seqs)} head_rows={head_rows}")
+    got = gm.block_forward(list(seqs), list(anchors), h, head_rows=head_rows)
+    torch.cuda.synchronize()
+    ref = om.block_forward(list(seqs), list(anchors), h, head_rows=head_rows)
+    assert got.shape == ref.shape
+    rel, top1 = logits_parity(got.cpu().numpy(), ref)
+    say(f"{cfg.key}: rel {rel:.3e} top1 {top1:.4f}")
+    assert rel <= tol and top1 >= 0.999
+
+
+def test_block_cut_to_its_first_rows():
+    """The device block's cut (gpu_wgpu/dflash_dev.rs, Dev::block): the anchor and the next
+    rows only, several sequences in one call and with windows on."""
+    from block_draft_model_dflash_amd import DFlashError
+
+    cfg = QTINY.replace(n_seqs=3)
+    om, gm = _pair(cfg, [12, 0], None, 200, n_seqs=3)
+    _append(cfg, om, gm, 0, 0, 37)
+    _append(cfg, om, gm, 1, 500, 21)
+    _append(cfg, om, gm, 2, 0, 70)
+    for rows in (1, 5, 8):
+        _cut_block(cfg, om, gm, (0, 1, 2), (37, 521, 70), rows, rows, 2e-3)
+    _cut_block(cfg, om, gm, (2,), (70,), 3, 4, 2e-3, head_rows=32)
+    h = np.zeros((1, 9, cfg.hidden), np.float32)  # more rows than the block holds
+    with pytest.raises(DFlashError):
+        gm.block_forward([0], [37], h)
+
+
+@pytest.mark.timeout(600)
+def test_block_cut_qwen3_8b_shaped():
+    cfg = Q8B
+    om, gm = _pair(cfg, None, None, cfg.ctx + 64)
+    _append(cfg, om, gm, 0, 0, cfg.ctx)
+    _cut_block(cfg, om, gm, (0,), (cfg.ctx,), 0, 8, 2e-3)
+    _cut_block(cfg, om, gm, (0,), (cfg.ctx,), 1, 8, 2e-3, head_rows=65536)

@@ -56,6 +56,8 @@ MUTANTS = [
      "const double k = (double)base[(size_t)so * hidden + i] + 0.0 * (double)d["),
     ("the MLP's kernels projected with the attention's matrix", "mm(g->conv_fmt, L->mlp_kp, pr, H, x, B, dm);",
      "mm(g->conv_fmt, L->attn_kp, pr, H, x, B, dm);"),
+    ("a cut block reads the rows of the whole block", "block_one(m, seqs[i], anchors[i], block_rows, h + per * i, x + per * i);",
+     "block_one(m, seqs[i], anchors[i], block_rows, h + (size_t)m->g.block * m->g.hidden * i, x + per * i);"),
     ("the shortlist takes the whole head", "mm(g->head_fmt, m->w.head, head_rows, g->hidden,",
      "mm(g->head_fmt, m->w.head, head_rows > 16 ? head_rows - 16 : head_rows, g->hidden,"),
     ("silu sign", "a[i] = (float)(gv / (1.0 + exp(-gv)) * (double)u[i]);", "a[i] = (float)(gv / (1.0 + exp(gv)) * (double)u[i]);"),
@@ -107,6 +109,7 @@ CHECKS = [
     (TW.test_window_drop_bookkeeping, ()),
     (TW.test_no_rope_everywhere_is_position_free, ()),
     (TW.test_shortlist_head_is_a_prefix, ()),
+    (TW.test_block_cut_to_its_first_rows_matches_transformers, ()),
     (TC.test_row_conv_against_torch_conv1d, ()),
     (TC.test_row_conv_reach, ()),
     (TC.test_identity_convolutions_give_the_plain_layer, ()),

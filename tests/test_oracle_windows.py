@@ -170,3 +170,28 @@ def test_shortlist_head_is_a_prefix():
         full = m.block_forward([0], [cfg.ctx], h[None])
         for n in (16, cfg.vocab // 4, cfg.vocab):
             np.testing.assert_array_equal(m.block_forward([0], [cfg.ctx], h[None], head_rows=n), full[..., :n])
+
+
+def test_block_cut_to_its_first_rows_matches_transformers():
+    """The device block may run only the anchor and the next rows (gpu_wgpu/dflash_dev.rs,
+    Dev::block): those rows are then the whole block, attention among them included."""
+    cfg = SHARP2
+    first = 40
+    w = di.make_weights(cfg)
+    m = oracle.Model(cfg, w, max_ctx=cfg.ctx + 64, max_seqs=2)
+    taps = di.make_taps(cfg, 0, first, cfg.ctx)
+    for s in (0, 1):  # two sequences of one call, the same context
+        assert m.append(s, first, taps) == 0
+    hf = HFDrafter(cfg, w)
+    kv = hf.context_kv(taps, first)
+    h = np.stack([di.make_block_input(cfg, 0, 3), di.make_block_input(cfg, 0, 4)])
+    full = m.block_forward([0, 1], [first + cfg.ctx] * 2, h)
+    for b in (2, 5, cfg.block):
+        got = m.block_forward([0, 1], [first + cfg.ctx] * 2, np.ascontiguousarray(h[:, :b]))
+        assert got.shape == (2, b, cfg.vocab)
+        for s in (0, 1):
+            _check(cfg, got[s], hf.block_logits(kv, first + cfg.ctx, h[s, :b]))
+        if b < cfg.block:  # the later mask rows shape the earlier ones: cutting them changes those
+            assert _rel(got, full[:, :b]) > 1e-3
+        else:
+            np.testing.assert_array_equal(got, full)
