@@ -282,7 +282,8 @@ def main() -> int:
         sel_ms = e0.elapsed_time(e1) / K
 
     # the block with the optional parts of the drafter the workloads do not declare (untimed for
-    # `value`): the head over its first 65536 rows; a 1024-position window on layers 0, 2, 4;
+    # `value`): the head over its first 65536 rows; the block cut to 8 rows; a 1024-position
+    # window on layers 0, 2, 4;
     # row convolutions of 16 columns a group and 4 offsets (a drafter with the same weights plus
     # the convolutions')
     variants = {}
@@ -306,6 +307,10 @@ def main() -> int:
             short = torch.empty((1, cfg.block, 65536), dtype=torch.float32, device="cuda")
             variants["head_shortlist_65536"] = timed(
                 lambda i: gm.block_forward(seqs, [cfg.ctx], hs[i], out=short, head_rows=65536))
+        if cfg.block > 8:  # the device block's cut: the anchor and the next seven rows
+            hs8 = hs[:, :, :8].contiguous()
+            out8 = torch.empty((1, 8, cfg.vocab), dtype=torch.float32, device="cuda")
+            variants["block_cut_8_rows"] = timed(lambda i: gm.block_forward(seqs, [cfg.ctx], hs8[i], out=out8))
         gm.reset(0)
         gm.set_layer_options([1024 if li % 2 == 0 else 0 for li in range(cfg.layers)], None)
         prefill(gm)
