@@ -75,6 +75,7 @@ class Config:
     conv_group: int = 0
     conv_kernel: int = 0
     conv_std: float = 0.0025
+    kv_f16: bool = False  # the K/V cache holds f16 elements instead of f32
 
     @property
     def tap_width(self) -> int:

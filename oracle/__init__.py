@@ -33,7 +33,7 @@ class og_geometry(C.Structure):
     _fields_ = [("rope_theta", C.c_double), ("eps", C.c_double)] + [
         (n, C.c_int32) for n in ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab",
                                  "block", "n_taps", "body_fmt", "fc_fmt", "head_fmt", "max_seqs", "max_ctx",
-                                 "conv_group", "conv_kernel", "conv_fmt")]
+                                 "conv_group", "conv_kernel", "conv_fmt", "kv_f16")]
 
 
 class og_matrix(C.Structure):
@@ -73,6 +73,7 @@ def lib(path: str | None = None):
         sig = {
             "og_set_threads": (None, [i32]), "og_get_threads": (i32, []),
             "og_f16_to_f64": (f64, [C.c_uint16]),
+            "og_round_f16": (f64, [f32]),
             "og_inv_freq": (None, [f64, i32, vp]),
             "og_rmsnorm_row": (None, [vp, vp, i32, f32, vp]),
             "og_rope_head": (None, [vp, i32, i64, vp]),
@@ -129,6 +130,13 @@ def _c(a, dtype):
 
 def f16_to_f64(bits: int) -> float:
     return lib().og_f16_to_f64(int(bits))
+
+
+def round_f16(x) -> np.ndarray:
+    """Each f32 value rounded to binary16 (ties to even), returned as f64."""
+    x = np.asarray(x, np.float32).ravel()
+    L = lib()
+    return np.array([L.og_round_f16(float(v)) for v in x], np.float64)
 
 
 def inv_freq(theta: float, head_dim: int) -> np.ndarray:
@@ -285,6 +293,7 @@ class Model:
                   "body_fmt", "fc_fmt", "head_fmt"):
             setattr(g, n, getattr(cfg, n))
         g.conv_group, g.conv_kernel, g.conv_fmt = cfg.conv_group, cfg.conv_kernel, cfg.fc_fmt
+        g.kv_f16 = int(cfg.kv_f16)
         g.max_seqs = max_seqs if max_seqs is not None else cfg.n_seqs
         g.max_ctx = max_ctx if max_ctx is not None else cfg.ctx + 64 * max(1, cfg.append_per_block)
         self.geometry = g

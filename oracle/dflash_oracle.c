@@ -44,6 +44,22 @@ double og_f16_to_f64(uint16_t h) {
 }
 
 /* dflash.rs, Drafter::new: inv_freq[i] = theta^(-2i/hd) evaluated in f64, stored f32. */
+/* IEEE 754 binary16, round to nearest with ties to even: the value's binade [2^(e-1), 2^e)
+ * holds 1024 steps of 2^(e-11), never finer than the subnormal step 2^-24; x / step is exact
+ * in f64, so rounding it to an integer (nearbyint under the default mode: ties to even) and
+ * scaling back gives the rounded value.  Past the largest finite half, 65504, values from 65520
+ * (the tie with 65536, whose even neighbour is out of range) overflow to infinity. */
+double og_round_f16(float xf) {
+  const double x = xf, a = fabs(x);
+  if (isnan(x)) return x;
+  if (a >= 65520.0) return copysign(INFINITY, x);
+  if (a == 0.0) return x;
+  int e;
+  (void)frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+  const double step = ldexp(1.0, e - 11 > -24 ? e - 11 : -24);
+  return copysign(nearbyint(a / step) * step, x);
+}
+
 void og_inv_freq(double theta, int head_dim, float* out) {
   for (int i = 0; i < head_dim / 2; i++) out[i] = (float)pow(theta, -(2.0 * i) / (double)head_dim);
 }
@@ -365,6 +381,11 @@ int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
         size_t off = (((size_t)l * g->max_ctx + row) * kvh + h) * hd;
         memcpy(s->k + off, tmp, sizeof(float) * hd);
         memcpy(s->v + off, v + (size_t)i * kvd + (size_t)h * hd, sizeof(float) * hd);
+        if (g->kv_f16) /* an f16 cache keeps each f32 element rounded to binary16 */
+          for (int d = 0; d < hd; d++) {
+            s->k[off + d] = (float)og_round_f16(s->k[off + d]);
+            s->v[off + d] = (float)og_round_f16(s->v[off + d]);
+          }
       }
     }
   }

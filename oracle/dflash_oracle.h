@@ -29,6 +29,8 @@ typedef struct {
   /* row convolutions (dflash.rs Geometry conv_group / conv_kernel; 0: none): the kernel
    * projections are in conv_fmt */
   int32_t conv_group, conv_kernel, conv_fmt;
+  /* the K/V cache keeps every element as f16 (1) instead of f32 (0) */
+  int32_t kv_f16;
 } og_geometry;
 
 /* canonical matrix: F32 float [rows][cols]; Q4_32 uint8 [rows][cols/2] (low nibble = even
@@ -60,6 +62,8 @@ int og_get_threads(void);
 
 /* ---- unit steps (each is what the model functions below call) ---- */
 double og_f16_to_f64(uint16_t h);
+/* x rounded to the nearest IEEE binary16 value, ties to even (overflow to +-inf), as a double */
+double og_round_f16(float x);
 void og_inv_freq(double theta, int head_dim, float* out /* [head_dim/2] */);
 void og_rmsnorm_row(const float* x, const float* w, int n, float eps, float* y);
 void og_rope_head(float* x, int head_dim, int64_t pos, const float* inv_freq);

@@ -13,6 +13,7 @@ import pytest
 import dflash_inputs as di
 import oracle
 import test_oracle_conv as TC
+import test_oracle_f16 as TF
 import test_oracle_model as TM
 import test_oracle_select as TS
 import test_oracle_units as TU
@@ -58,6 +59,10 @@ MUTANTS = [
      "mm(g->conv_fmt, L->attn_kp, pr, H, x, B, dm);"),
     ("a cut block reads the rows of the whole block", "block_one(m, seqs[i], anchors[i], block_rows, h + per * i, x + per * i);",
      "block_one(m, seqs[i], anchors[i], block_rows, h + (size_t)m->g.block * m->g.hidden * i, x + per * i);"),
+    ("f16 rounding truncates", "return copysign(nearbyint(a / step) * step, x);", "return copysign(trunc(a / step) * step, x);"),
+    ("f16 steps one bit too coarse", "ldexp(1.0, e - 11 > -24 ? e - 11 : -24)", "ldexp(1.0, e - 10 > -24 ? e - 10 : -24)"),
+    ("f16 subnormal steps too fine", "ldexp(1.0, e - 11 > -24 ? e - 11 : -24)", "ldexp(1.0, e - 11 > -26 ? e - 11 : -26)"),
+    ("the f16 cache keeps keys in f32", "s->k[off + d] = (float)og_round_f16(s->k[off + d]);", "(void)0;"),
     ("the shortlist takes the whole head", "mm(g->head_fmt, m->w.head, head_rows, g->hidden,",
      "mm(g->head_fmt, m->w.head, head_rows > 16 ? head_rows - 16 : head_rows, g->hidden,"),
     ("silu sign", "a[i] = (float)(gv / (1.0 + exp(-gv)) * (double)u[i]);", "a[i] = (float)(gv / (1.0 + exp(gv)) * (double)u[i]);"),
@@ -110,6 +115,9 @@ CHECKS = [
     (TW.test_no_rope_everywhere_is_position_free, ()),
     (TW.test_shortlist_head_is_a_prefix, ()),
     (TW.test_block_cut_to_its_first_rows_matches_transformers, ()),
+    (TF.test_round_f16_against_numpy, ()),
+    (TF.test_f16_cache_holds_the_rounded_rows, ()),
+    (TF.test_f16_cache_block_matches_transformers, ()),
     (TC.test_row_conv_against_torch_conv1d, ()),
     (TC.test_row_conv_reach, ()),
     (TC.test_identity_convolutions_give_the_plain_layer, ()),
