@@ -32,7 +32,7 @@ class dflash_geometry(C.Structure):
     _fields_ = [("rope_theta", C.c_double), ("eps", C.c_double)] + [
         (n, C.c_int32) for n in ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab",
                                  "block", "n_taps", "body_fmt", "fc_fmt", "head_fmt", "max_seqs", "max_ctx",
-                                 "conv_group", "conv_kernel", "conv_fmt")]
+                                 "conv_group", "conv_kernel", "conv_fmt", "kv_f16")]
 
 
 class dflash_matrix(C.Structure):

@@ -369,20 +369,22 @@ hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B
 }
 
 // Context append: grid (layers * 2 * kvh, n), one wave each.  Columns of the all-layer K|V
-// projection: layer l's k heads then its v heads.  Cache layout [L][max_seqs][kvh][max_ctx][hd].
+// projection: layer l's k heads then its v heads.  Cache layout [L][max_seqs][kvh][max_ctx][hd],
+// elements f32 or (an f16 cache) the f32 values rounded to f16, to nearest even.
+template <typename CT>
 __global__ __launch_bounds__(64) void k_kv_append(const double* __restrict__ part, int S, int Mpad, int layers,
                                                  int kvh, int hd, const float* __restrict__ k_norms,
                                                  const float* __restrict__ inv_freq, float eps,
                                                  unsigned long long rot_mask, long long pos0, int row0, int slot,
-                                                 int max_seqs, int max_ctx, float* __restrict__ kc,
-                                                 float* __restrict__ vc) {
+                                                 int max_seqs, int max_ctx, CT* __restrict__ kc,
+                                                 CT* __restrict__ vc) {
   const int unit = blockIdx.x, i = blockIdx.y, lane = threadIdx.x, half = hd >> 1;
   const int l = unit / (2 * kvh), rem = unit % (2 * kvh), kind = rem / kvh, h = rem % kvh;
   const size_t kvd = (size_t)kvh * hd, N = (size_t)layers * 2 * kvd;
   const size_t col0 = ((size_t)l * 2 + kind) * kvd + (size_t)h * hd;
   const size_t dst = ((((size_t)l * max_seqs + slot) * kvh + h) * max_ctx + (size_t)(row0 + i)) * hd;
   if (kind == 1) {
-    for (int d = lane; d < hd; d += 64) vc[dst + d] = reduce_parts(part, S, Mpad, i, N, col0 + d);
+    for (int d = lane; d < hd; d += 64) vc[dst + d] = (CT)reduce_parts(part, S, Mpad, i, N, col0 + d);
     return;
   }
   const bool on = lane < half;
@@ -392,17 +394,44 @@ __global__ __launch_bounds__(64) void k_kv_append(const double* __restrict__ par
   const bool rope = l >= 64 || ((rot_mask >> l) & 1ull);
   head_norm_rope(x0, x1, lane, hd, k_norms + (size_t)l * hd, eps, inv_freq, pos0 + i, rope, o0, o1);
   if (!on) return;
-  kc[dst + lane] = o0;
-  kc[dst + lane + half] = o1;
+  kc[dst + lane] = (CT)o0;
+  kc[dst + lane + half] = (CT)o1;
 }
 
 hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
                             const float* k_norms, const float* inv_freq, float eps, unsigned long long rot_mask,
-                            long long pos0, int row0, int slot, int max_seqs, int max_ctx, float* kc, float* vc,
-                            hipStream_t st) {
+                            long long pos0, int row0, int slot, int max_seqs, int max_ctx, bool f16, void* kc,
+                            void* vc, hipStream_t st) {
   if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_kv_append, dim3(layers * 2 * kvh, n), dim3(64), 0, st, part, S, Mpad, layers, kvh, hd,
-                     k_norms, inv_freq, eps, rot_mask, pos0, row0, slot, max_seqs, max_ctx, kc, vc);
+  if (f16)
+    hipLaunchKernelGGL(k_kv_append<_Float16>, dim3(layers * 2 * kvh, n), dim3(64), 0, st, part, S, Mpad, layers, kvh,
+                       hd, k_norms, inv_freq, eps, rot_mask, pos0, row0, slot, max_seqs, max_ctx, (_Float16*)kc,
+                       (_Float16*)vc);
+  else
+    hipLaunchKernelGGL(k_kv_append<float>, dim3(layers * 2 * kvh, n), dim3(64), 0, st, part, S, Mpad, layers, kvh, hd,
+                       k_norms, inv_freq, eps, rot_mask, pos0, row0, slot, max_seqs, max_ctx, (float*)kc, (float*)vc);
+  return hipGetLastError();
+}
+
+// Cache rows back to f32 (a read-back for checks): out[r][h][d] = cache[layer][seq][h][row0+r][d].
+template <typename CT>
+__global__ __launch_bounds__(128) void k_read_cache(const CT* __restrict__ cache, size_t layer_elems, int layer,
+                                                    int seq, int row0, int kvh, int hd, int max_ctx,
+                                                    float* __restrict__ out) {
+  const int r = blockIdx.x, h = blockIdx.y;
+  const CT* src = cache + (size_t)layer * layer_elems + (((size_t)seq * kvh + h) * max_ctx + row0 + r) * hd;
+  for (int d = threadIdx.x; d < hd; d += blockDim.x) out[((size_t)r * kvh + h) * hd + d] = (float)src[d];
+}
+
+hipError_t launch_read_cache(const void* cache, bool f16, size_t layer_elems, int layer, int seq, int row0, int n,
+                             int kvh, int hd, int max_ctx, float* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (f16)
+    hipLaunchKernelGGL(k_read_cache<_Float16>, dim3(n, kvh), dim3(128), 0, st, (const _Float16*)cache, layer_elems,
+                       layer, seq, row0, kvh, hd, max_ctx, out);
+  else
+    hipLaunchKernelGGL(k_read_cache<float>, dim3(n, kvh), dim3(128), 0, st, (const float*)cache, layer_elems, layer,
+                       seq, row0, kvh, hd, max_ctx, out);
   return hipGetLastError();
 }
 

@@ -85,6 +85,7 @@ int check_geometry(const dflash_geometry* g, std::string* err) {
     return fail(DFLASH_ENOTSUP, "body shapes outside the kernels' tiles");
   if (H % 32 || I % 32 || qd % 32 || T % 32) return fail(DFLASH_ENOTSUP, "activation widths must be multiples of 32");
   if (H * 4 > 96 * 1024) return fail(DFLASH_ENOTSUP, "hidden too wide for one workgroup's row");
+  if (g->kv_f16 != 0 && g->kv_f16 != 1) return fail(DFLASH_EINVAL, "kv_f16 must be 0 or 1");
   if (g->conv_kernel < 0) return fail(DFLASH_EINVAL, "negative conv_kernel");
   if (g->conv_kernel > 0) {
     if (g->conv_group < 1 || H % g->conv_group) return fail(DFLASH_EINVAL, "conv_group must divide hidden");
@@ -143,7 +144,7 @@ void plan(const dflash_geometry* g, Layout* L) {
   L->q_norm = take(NL * hd * 4);
   L->k_norm = take(NL * hd * 4);
   L->inv_freq = take(hd / 2 * 4);
-  const size_t cache = (size_t)NL * g->max_seqs * kvh * (size_t)g->max_ctx * hd * 4;
+  const size_t cache = (size_t)NL * g->max_seqs * kvh * (size_t)g->max_ctx * hd * (g->kv_f16 ? 2 : 4);
   L->kc = take(cache);
   L->vc = take(cache);
   L->act_begin = off;
@@ -374,6 +375,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   as.max_seqs = g.max_seqs;
   as.maxch = MAXCH;
   as.scale = powf((float)hd, -0.5f);  // dflash.rs, Drafter::block: (hd as f32).powf(-0.5)
+  as.kv_f16 = g.kv_f16;
   // about one workgroup per CU: n_seqs * q heads * chunks ~ 256 (a workgroup serves one q head
   // of one chunk), chunks a multiple of 32 keys; per layer, as its windows give it keys
   int nch_target = (256 + n_seqs * nh - 1) / (n_seqs * nh);
@@ -420,7 +422,8 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   TRY_HIP(c,
           launch_rms_act(hbuf, ssq, copy_parts, c->at<float>(L.in_norm), eps, M, Mpad, H, bq, xq, dxT, xf, c->st, xn),
           "in-norm");
-  const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd;
+  // bytes of one layer's cache
+  const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd * (g.kv_f16 ? 2 : 4);
   for (int l = 0; l < NL; l++) {
     int rc;
     float* da = kn ? c->at<float>(L.da) : nullptr;
@@ -452,8 +455,8 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
       {
         StageTimer tc(c, DFLASH_STAGE_ATTN_CHUNKS);
         TRY_HIP(c,
-                launch_attention_chunks(as, si, c->at<float>(L.q), c->at<float>(L.kc) + (size_t)l * layer_cache,
-                                        c->at<float>(L.vc) + (size_t)l * layer_cache, c->at<double>(L.apart),
+                launch_attention_chunks(as, si, c->at<float>(L.q), c->ws + L.kc + (size_t)l * layer_cache,
+                                        c->ws + L.vc + (size_t)l * layer_cache, c->at<double>(L.apart),
                                         c->at<double>(L.aml), c->st),
                 "attention chunks");
       }
@@ -757,7 +760,7 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
     TRY_HIP(c,
             launch_kv_append(part, 1, Mpad, nn, NL, g.kv_heads, g.head_dim, c->at<float>(L.k_norm),
                              c->at<float>(L.inv_freq), eps, c->rot_mask, pos + c0, (int)(pos - first) + c0, seq,
-                             g.max_seqs, g.max_ctx, c->at<float>(L.kc), c->at<float>(L.vc), c->st),
+                             g.max_seqs, g.max_ctx, g.kv_f16 != 0, c->ws + L.kc, c->ws + L.vc, c->st),
             "k/v into the cache");
   }
   c->len[seq] = len + n;
@@ -900,17 +903,13 @@ int dflash_read_kv(const dflash_ctx* c, int32_t layer, int32_t seq, int32_t row0
     return DFLASH_EINVAL;
   if (n == 0) return DFLASH_OK;
   const size_t hd = g.head_dim, kvh = g.kv_heads;
-  const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd;
-  for (size_t h = 0; h < kvh; h++) {
-    const size_t src = (size_t)layer * layer_cache + (((size_t)seq * kvh + h) * g.max_ctx + row0) * hd;
-    hipError_t e = hipMemcpy2DAsync(k + h * hd, kvh * hd * 4, c->at<float>(c->lay.kc) + src, hd * 4, hd * 4, n,
-                                    hipMemcpyDeviceToDevice, c->st);
-    if (e == hipSuccess)
-      e = hipMemcpy2DAsync(v + h * hd, kvh * hd * 4, c->at<float>(c->lay.vc) + src, hd * 4, hd * 4, n,
-                           hipMemcpyDeviceToDevice, c->st);
-    if (e != hipSuccess) return DFLASH_EHIP;
-  }
-  return DFLASH_OK;
+  const size_t layer_elems = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd;
+  hipError_t e = launch_read_cache(c->ws + c->lay.kc, g.kv_f16 != 0, layer_elems, layer, seq, row0, n, (int)kvh,
+                                   (int)hd, g.max_ctx, k, c->st);
+  if (e == hipSuccess)
+    e = launch_read_cache(c->ws + c->lay.vc, g.kv_f16 != 0, layer_elems, layer, seq, row0, n, (int)kvh, (int)hd,
+                          g.max_ctx, v, c->st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
 }
 
 int dflash_quant_act(const float* x, int32_t rows, int32_t cols, int8_t* q, float* d, void* stream) {

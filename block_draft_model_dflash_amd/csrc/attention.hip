@@ -21,6 +21,8 @@
 //   Y^T[d][q]  += V^T . P^T (A = 16-dim slices of V, B = the probabilities, already in the
 //                            accumulator layout of S^T)
 // so the probabilities never leave registers.  Context K/V is f32 [slot][kvh][max_ctx][hd].
+// Context K/V is f32 or, with an f16 cache, f16 [slot][kvh][max_ctx][hd]; either converts to f64
+// exactly.
 // Lane layout of the f64 16x16x4 MFMA: lane l gives A[l%16][l/16] and B[l/16][l%16] and holds
 // D[l/16 + 4r][l%16] in accumulator slot r (rows interleaved, unlike the f32 16x16 forms).
 //
@@ -55,11 +57,29 @@ constexpr size_t attn_lds_bytes() {
 
 // Grid: ceil(tasks / 8) * 8 * rep workgroups for tasks (sequence, kv head, chunk) numbered
 // t = (s * kvh + g) * maxn + c; id = (t / 8) * 8 * rep + h * 8 + t % 8 serves q head g*rep + h.
-template <int HD>
+// Four cache elements of a row as loaded: f32 (16 bytes) or f16 (8 bytes, an f16 cache).
+template <typename CT>
+struct CacheVec;
+template <>
+struct CacheVec<float> {
+  typedef float v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ v4 load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(v4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+};
+template <>
+struct CacheVec<_Float16> {
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ v4 load(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(v4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  }
+};
+
+template <int HD, typename CT>
 __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqInfo si, int maxn,
                                                                const float* __restrict__ q,
-                                                               const float* __restrict__ kc,
-                                                               const float* __restrict__ vc,
+                                                               const CT* __restrict__ kc,
+                                                               const CT* __restrict__ vc,
                                                                double* __restrict__ part, double* __restrict__ ml) {
   constexpr int NI = HD / 16;  // 16-dim slices: k-steps of the scores, output tiles of the values
   constexpr int ND = HD / 64;  // 64-dim groups of a value row
@@ -76,8 +96,8 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
   const int j = g * rep + h;
   const int k0 = c * a.ck, kend = min(nctx, k0 + a.ck);
   const int nt = (kend - k0 + 15) / 16;  // >= 1: every launched chunk holds context rows
-  const float* Kctx = kc + (((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s]) * HD;
-  const float* Vctx = vc + (((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s]) * HD;
+  const CT* Kctx = kc + (((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s]) * HD;
+  const CT* Vctx = vc + (((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s]) * HD;
   // under a window, query row col does not see the keys before index mask0 + col: their scores
   // become -1e300, so exp() gives them exactly 0 beside any visible key; a chunk in which a row
   // sees no key keeps the finite maximum -1e300, and the merge weights it by exp(-1e300 - m) = 0
@@ -107,22 +127,22 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
   //               64*d4 + 4*col + e of output tile dt = 4*d4 + e)
   // (buffer loads: a plain load of read-only memory may be re-issued next to its use when
   // registers run short, which would take the next tile out of flight)
-  v4f kr[NI], vr[4][ND];
-  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)Kctx, (short)0, kend * HD * 4, 0x00020000);
-  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)Vctx, (short)0, kend * HD * 4, 0x00020000);
+  typedef typename CacheVec<CT>::v4 v4c;
+  constexpr int ES = (int)sizeof(CT);
+  v4c kr[NI], vr[4][ND];
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)Kctx, (short)0, kend * HD * ES, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)Vctx, (short)0, kend * HD * ES, 0x00020000);
   auto load_k = [&](int i) {
     const int key = min(k0 + 16 * i + col, kend - 1);
 #pragma unroll
-    for (int i4 = 0; i4 < NI; i4++)
-      kr[i4] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(kres, (key * HD + 16 * i4 + 4 * quarter) * 4, 0, 0));
+    for (int i4 = 0; i4 < NI; i4++) kr[i4] = CacheVec<CT>::load(kres, (key * HD + 16 * i4 + 4 * quarter) * ES);
   };
   auto load_v = [&](int i) {
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       const int key = min(k0 + 16 * i + 4 * k + quarter, kend - 1);
 #pragma unroll
-      for (int d4 = 0; d4 < ND; d4++)
-        vr[k][d4] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(vres, (key * HD + 64 * d4 + 4 * col) * 4, 0, 0));
+      for (int d4 = 0; d4 < ND; d4++) vr[k][d4] = CacheVec<CT>::load(vres, (key * HD + 64 * d4 + 4 * col) * ES);
     }
   };
   const int last = nt - 1;
@@ -340,9 +360,9 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqIn
     xf[(size_t)m * qd + colx] = val;
 }
 
-template <int HD>
-static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const float* q, const float* kc,
-                                  const float* vc, double* part, double* ml, hipStream_t st) {
+template <int HD, typename CT>
+static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const float* q, const CT* kc,
+                                  const CT* vc, double* part, double* ml, hipStream_t st) {
   int maxn = 0;
   for (int i = 0; i < si.n; i++) {
     const int nch = si.nctx[i] > 0 ? (si.nctx[i] + a.ck - 1) / a.ck : 0;
@@ -351,11 +371,12 @@ static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const f
   if (maxn > a.maxch) return hipErrorInvalidValue;
   if (maxn == 0) return hipSuccess;  // no sequence has context rows: the merge does it all
   const size_t lds = attn_lds_bytes<HD>();
-  hipError_t e = allow_lds((const void*)k_attn_partial<HD>, lds);
+  hipError_t e = allow_lds((const void*)k_attn_partial<HD, CT>, lds);
   if (e != hipSuccess) return e;
   const int tasks = si.n * a.kvh * maxn, rep = a.nh / a.kvh;
   const int grid = (tasks + 7) / 8 * 8 * rep;
-  hipLaunchKernelGGL(k_attn_partial<HD>, dim3(grid), dim3(ATTN_THREADS), lds, st, a, si, maxn, q, kc, vc, part, ml);
+  hipLaunchKernelGGL((k_attn_partial<HD, CT>), dim3(grid), dim3(ATTN_THREADS), lds, st, a, si, maxn, q, kc, vc, part,
+                     ml);
   return hipGetLastError();
 }
 
@@ -395,11 +416,15 @@ static bool attn_shape_ok(const AttnShape& a) {
          (a.hd == 64 || a.hd == 128);
 }
 
-hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const float* kc,
-                                   const float* vc, double* part, double* ml, hipStream_t st) {
+hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const void* kc,
+                                   const void* vc, double* part, double* ml, hipStream_t st) {
   if (!attn_shape_ok(a)) return hipErrorInvalidValue;
-  if (a.hd == 64) return attn_partial_hd<64>(a, si, q, kc, vc, part, ml, st);
-  return attn_partial_hd<128>(a, si, q, kc, vc, part, ml, st);
+  if (a.kv_f16) {
+    const _Float16 *k = (const _Float16*)kc, *v = (const _Float16*)vc;
+    return a.hd == 64 ? attn_partial_hd<64>(a, si, q, k, v, part, ml, st) : attn_partial_hd<128>(a, si, q, k, v, part, ml, st);
+  }
+  const float *k = (const float*)kc, *v = (const float*)vc;
+  return a.hd == 64 ? attn_partial_hd<64>(a, si, q, k, v, part, ml, st) : attn_partial_hd<128>(a, si, q, k, v, part, ml, st);
 }
 
 hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,

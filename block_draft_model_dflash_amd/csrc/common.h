@@ -120,20 +120,24 @@ hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B
 // keys are rotated when bit l of rot_mask is set (layers >= 64 always are).
 hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
                             const float* k_norms, const float* inv_freq, float eps, unsigned long long rot_mask,
-                            long long pos0, int row0, int slot, int max_seqs, int max_ctx, float* kc, float* vc,
-                            hipStream_t st);
+                            long long pos0, int row0, int slot, int max_seqs, int max_ctx, bool f16, void* kc,
+                            void* vc, hipStream_t st);
+// n rows of one (layer, sequence) of the cache, every kv head, into out [n][kvh][hd] f32.
+hipError_t launch_read_cache(const void* cache, bool f16, size_t layer_elems, int layer, int seq, int row0, int n,
+                             int kvh, int hd, int max_ctx, float* out, hipStream_t st);
 
 // Attention of the block rows over context + block keys, split over context chunks.
 struct AttnShape {
   int nh, kvh, hd, B, max_ctx, max_seqs, ck, maxch;
   float scale;
+  int kv_f16;  // the cache holds f16 elements
 };
 // The chunk kernel writes per-chunk (max, sum, acc) of the context keys in f64 to part/ml; the
 // merge scores the block's own keys, combines them with a sequence's chunks per (q head, row)
 // and writes the f32 result (A8 into xq/dxT, or f32 xf).
 constexpr int ATTN_MAXCH = 64;  // context chunks per (sequence, kv head) at most
-hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const float* kc,
-                                   const float* vc, double* part, double* ml, hipStream_t st);
+hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const void* kc,
+                                   const void* vc, double* part, double* ml, hipStream_t st);
 hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
                                   const float* vb, const double* part, const double* ml, int Mpad, bool quant,
                                   int8_t* xq, float* dxT, float* xf, hipStream_t st);

@@ -28,6 +28,7 @@ def geometry(spec, max_ctx: int, max_seqs: int) -> dflash_geometry:
     g.conv_group = int(getattr(spec, "conv_group", 0))
     g.conv_kernel = int(getattr(spec, "conv_kernel", 0))
     g.conv_fmt = int(getattr(spec, "conv_fmt", spec.fc_fmt))
+    g.kv_f16 = int(bool(getattr(spec, "kv_f16", False)))
     return g
 
 

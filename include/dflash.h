@@ -74,6 +74,9 @@ typedef struct {
    * the kernel projections have 2*conv_kernel*hidden/conv_group rows (a multiple of 16) and
    * conv_fmt is DFLASH_F32 with an f32 body, DFLASH_Q4_32 / DFLASH_Q8_32 with a quantized one. */
   int32_t conv_group, conv_kernel, conv_fmt;
+  /* 1: the K/V cache keeps each element as f16 (the f32 value rounded to nearest even; half
+   * the bytes), 0: f32 */
+  int32_t kv_f16;
 } dflash_geometry;
 
 /* A matrix in the canonical layout above (device pointers; scales NULL for DFLASH_F32). */
@@ -264,7 +267,8 @@ int dflash_select(const float* logits, int32_t rows, int32_t width, int32_t ld, 
                   int32_t* chosen, int32_t* plain, void* scratch, void* stream);
 
 /* Copy K and V of context rows row0..row0+n-1 (index = position - first) of one layer and
- * sequence into device k, v [n][kv_heads][head_dim] f32 (a read-back of the cache). */
+ * sequence into device k, v [n][kv_heads][head_dim] f32 (a read-back of the cache; an f16
+ * cache's elements converted exactly). */
 int dflash_read_kv(const dflash_ctx* c, int32_t layer, int32_t seq, int32_t row0, int32_t n, float* k, float* v);
 
 #ifdef __cplusplus
