@@ -76,6 +76,7 @@ class Config:
     conv_kernel: int = 0
     conv_std: float = 0.0025
     kv_f16: bool = False  # the K/V cache holds f16 elements instead of f32
+    pending_rows: int = 0  # context rows that may wait unsettled (0: every row settles at once)
 
     @property
     def tap_width(self) -> int:

@@ -33,7 +33,7 @@ class og_geometry(C.Structure):
     _fields_ = [("rope_theta", C.c_double), ("eps", C.c_double)] + [
         (n, C.c_int32) for n in ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab",
                                  "block", "n_taps", "body_fmt", "fc_fmt", "head_fmt", "max_seqs", "max_ctx",
-                                 "conv_group", "conv_kernel", "conv_fmt", "kv_f16")]
+                                 "conv_group", "conv_kernel", "conv_fmt", "kv_f16", "pending_rows")]
 
 
 class og_matrix(C.Structure):
@@ -88,6 +88,9 @@ def lib(path: str | None = None):
             "og_destroy": (None, [vp]),
             "og_ctx_append": (i32, [vp, i32, i64, vp, i32]),
             "og_ctx_truncate": (i32, [vp, i32, i64]),
+            "og_ctx_queue": (i32, [vp, i32, i64, vp, i32]),
+            "og_ctx_settle": (i32, [vp, i32]),
+            "og_pending": (i64, [vp, i32]),
             "og_ctx_reset": (i32, [vp, i32]),
             "og_ctx_span": (i32, [vp, i32, C.POINTER(C.c_int64), C.POINTER(C.c_int64)]),
             "og_read_kv": (i32, [vp, i32, i32, i32, i32, vp, vp]),
@@ -294,6 +297,7 @@ class Model:
             setattr(g, n, getattr(cfg, n))
         g.conv_group, g.conv_kernel, g.conv_fmt = cfg.conv_group, cfg.conv_kernel, cfg.fc_fmt
         g.kv_f16 = int(cfg.kv_f16)
+        g.pending_rows = int(cfg.pending_rows)
         g.max_seqs = max_seqs if max_seqs is not None else cfg.n_seqs
         g.max_ctx = max_ctx if max_ctx is not None else cfg.ctx + 64 * max(1, cfg.append_per_block)
         self.geometry = g
@@ -333,6 +337,17 @@ class Model:
         taps = _c(taps, np.float32)
         n = taps.shape[0] if taps.ndim == 2 else 0
         return lib().og_ctx_append(self.h, seq, pos, _p(taps) if n else None, n)
+
+    def queue(self, seq: int, pos: int, taps: np.ndarray) -> int:
+        taps = _c(taps, np.float32)
+        n = taps.shape[0] if taps.ndim == 2 else 0
+        return lib().og_ctx_queue(self.h, seq, pos, _p(taps) if n else None, n)
+
+    def settle(self, seq: int) -> int:
+        return lib().og_ctx_settle(self.h, seq)
+
+    def pending(self, seq: int) -> int:
+        return int(lib().og_pending(self.h, seq))
 
     def truncate(self, seq: int, pos: int) -> int:
         return lib().og_ctx_truncate(self.h, seq, pos)

@@ -241,6 +241,8 @@ void og_row_conv(const float* x, int rows, int hidden, int gs, int kn, int stage
 
 typedef struct {
   int64_t first, len;
+  int64_t npend;    /* rows waiting to be settled, at positions first+len, ... */
+  float* pend;      /* their taps [npend][n_taps*hidden] */
   int64_t* dropped; /* [layers]: context rows a layer no longer holds (the oldest) */
   float* k;         /* [layers][max_ctx][kv_heads][head_dim] */
   float* v;
@@ -289,6 +291,7 @@ void og_destroy(og_model* m) {
   if (!m) return;
   for (int s = 0; s < m->g.max_seqs; s++) {
     free(m->seqs[s].dropped);
+    free(m->seqs[s].pend);
     free(m->seqs[s].k);
     free(m->seqs[s].v);
   }
@@ -340,25 +343,12 @@ static void mm(int fmt, og_matrix w, int rows, int cols, const float* x, int n, 
   free(xq);
 }
 
-/* dflash.rs, Drafter::queue_context and Drafter::truncate: a position inside the held span
- * replaces it and what follows; a gap, or a position before the first, starts over there. */
-int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
+/* dflash.rs, Drafter::settle_rows: the rows of positions first+len, ... become context: t =
+ * rms(FC . taps, hidden_norm); every layer's k, v of t; k = rotate(rms(k, k_norm), position);
+ * then a layer holding more than twice its window keeps only the last window's worth. */
+static void settle_rows(og_model* m, og_seq* s, const float* taps, int n) {
   const og_geometry* g = &m->g;
-  if (seq < 0 || seq >= g->max_seqs || pos < 0 || n < 0 || (n > 0 && !taps)) return -1;
-  og_seq* s = &m->seqs[seq];
-  int64_t first = s->first, len = s->len;
-  if (pos > first + len || pos < first) {
-    first = pos;
-    len = 0;
-  } else {
-    len = pos - first;
-  }
-  if (len + n > g->max_ctx) return -2;
-  keep_rows(m, s, first == s->first ? len : 0); /* truncate(pos), or truncate(0) on a restart */
-  s->first = first;
-  if (n == 0) return 0;
-  /* dflash.rs, Drafter::settle_rows: t = rms(FC . taps, hidden_norm); every layer's k, v of t;
-   * k = rotate(rms(k, k_norm), position); then the rows are kept. */
+  const int64_t pos = s->first + s->len;
   const int H = g->hidden, T = g->n_taps * g->hidden, kvh = g->kv_heads, hd = g->head_dim, kvd = kvh * hd;
   float* t = (float*)malloc(sizeof(float) * (size_t)n * H);
   float* tn = (float*)malloc(sizeof(float) * (size_t)n * H);
@@ -389,9 +379,7 @@ int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
       }
     }
   }
-  s->len = len + n;
-  /* Drafter::settle_rows, at the end: a layer holding more than twice its window keeps only the
-   * last window's worth */
+  s->len += n;
   for (int l = 0; l < g->layers; l++) {
     const int64_t w = m->window[l], held = s->len - s->dropped[l];
     if (w > 0 && held > 2 * w) s->dropped[l] += held - w;
@@ -401,24 +389,84 @@ int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
   free(k);
   free(tn);
   free(t);
+}
+
+/* dflash.rs, Drafter::truncate: forget positions >= pos, the waiting rows among them too (the
+ * first stays); a layer's dropped rows are clipped to what is kept */
+static void truncate_to(og_model* m, og_seq* s, int64_t pos) {
+  const int64_t held = s->first + s->len;
+  const int64_t wait = pos > held ? pos - held : 0;
+  if (s->npend > wait) s->npend = wait;
+  int64_t keep = pos - s->first;
+  if (keep < 0) keep = 0;
+  if (keep > s->len) keep = s->len;
+  keep_rows(m, s, keep);
+}
+
+/* dflash.rs, Drafter::queue_context: a position inside the span (waiting rows included)
+ * replaces it and what follows; a gap, or a position before the first, starts over there.  The
+ * rows wait; past pending_rows waiting rows the oldest are settled, a whole number of 64-row
+ * chunks (CONTEXT_CHUNK) at a time. */
+int og_ctx_queue(og_model* m, int seq, int64_t pos, const float* taps, int n) {
+  const og_geometry* g = &m->g;
+  if (seq < 0 || seq >= g->max_seqs || pos < 0 || n < 0 || (n > 0 && !taps)) return -1;
+  og_seq* s = &m->seqs[seq];
+  const int64_t next = s->first + s->len + s->npend;
+  const int restart = pos > next || pos < s->first;
+  if (pos + n - (restart ? pos : s->first) > g->max_ctx) return -2;
+  if (restart) {
+    truncate_to(m, s, 0);
+    s->first = pos;
+  } else {
+    truncate_to(m, s, pos);
+  }
+  const size_t T = (size_t)g->n_taps * g->hidden;
+  if (n > 0) {
+    s->pend = (float*)realloc(s->pend, sizeof(float) * T * (size_t)(s->npend + n));
+    memcpy(s->pend + (size_t)s->npend * T, taps, sizeof(float) * T * (size_t)n);
+    s->npend += n;
+  }
+  if (s->npend > g->pending_rows) {
+    int64_t over = (s->npend - g->pending_rows + 63) / 64 * 64;
+    if (over > s->npend) over = s->npend;
+    settle_rows(m, s, s->pend, (int)over);
+    memmove(s->pend, s->pend + (size_t)over * T, sizeof(float) * T * (size_t)(s->npend - over));
+    s->npend -= over;
+  }
   return 0;
+}
+
+/* dflash.rs, Drafter::settle: every waiting row becomes context */
+int og_ctx_settle(og_model* m, int seq) {
+  if (seq < 0 || seq >= m->g.max_seqs) return -1;
+  og_seq* s = &m->seqs[seq];
+  if (s->npend > 0) settle_rows(m, s, s->pend, (int)s->npend);
+  s->npend = 0;
+  return 0;
+}
+
+/* dflash.rs, Drafter::push_context: queue_context, then settle */
+int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps, int n) {
+  const int rc = og_ctx_queue(m, seq, pos, taps, n);
+  return rc ? rc : og_ctx_settle(m, seq);
+}
+
+int64_t og_pending(const og_model* m, int seq) {
+  if (seq < 0 || seq >= m->g.max_seqs) return -1;
+  return m->seqs[seq].npend;
 }
 
 /* dflash.rs, Drafter::truncate: keep positions before pos (the first stays). */
 int og_ctx_truncate(og_model* m, int seq, int64_t pos) {
   if (seq < 0 || seq >= m->g.max_seqs || pos < 0) return -1;
-  og_seq* s = &m->seqs[seq];
-  int64_t keep = pos - s->first;
-  if (keep < 0) keep = 0;
-  if (keep > s->len) keep = s->len;
-  keep_rows(m, s, keep);
+  truncate_to(m, &m->seqs[seq], pos);
   return 0;
 }
 
 /* dflash.rs, Drafter::reset */
 int og_ctx_reset(og_model* m, int seq) {
   if (seq < 0 || seq >= m->g.max_seqs) return -1;
-  keep_rows(m, &m->seqs[seq], 0);
+  truncate_to(m, &m->seqs[seq], 0);
   m->seqs[seq].first = 0;
   return 0;
 }
@@ -426,7 +474,7 @@ int og_ctx_reset(og_model* m, int seq) {
 int og_ctx_span(const og_model* m, int seq, int64_t* first, int64_t* end) {
   if (seq < 0 || seq >= m->g.max_seqs) return -1;
   *first = m->seqs[seq].first;
-  *end = m->seqs[seq].first + m->seqs[seq].len;
+  *end = m->seqs[seq].first + m->seqs[seq].len + m->seqs[seq].npend; /* Drafter::next_position */
   return 0;
 }
 
@@ -599,6 +647,7 @@ static int check_block_args(const og_model* m, int n_seqs, const int32_t* seqs, 
 int og_block_hidden(og_model* m, int n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                     float* hidden) {
   if (check_block_args(m, n_seqs, seqs, anchors)) return -1;
+  for (int i = 0; i < n_seqs; i++) og_ctx_settle(m, seqs[i]); /* a block reads settled rows */
   size_t per = (size_t)m->g.block * m->g.hidden;
   for (int i = 0; i < n_seqs; i++) block_one(m, seqs[i], anchors[i], m->g.block, h + per * i, hidden + per * i);
   return 0;
@@ -615,6 +664,7 @@ int og_block_forward_rows(og_model* m, int n_seqs, const int32_t* seqs, const in
   if (check_block_args(m, n_seqs, seqs, anchors) || head_rows < 1 || head_rows > m->g.vocab || block_rows < 1 ||
       block_rows > m->g.block)
     return -1;
+  for (int i = 0; i < n_seqs; i++) og_ctx_settle(m, seqs[i]); /* a block reads settled rows */
   const og_geometry* g = &m->g;
   size_t per = (size_t)block_rows * g->hidden;
   float* x = (float*)malloc(sizeof(float) * per * (size_t)(n_seqs > 0 ? n_seqs : 1));

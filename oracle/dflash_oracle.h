@@ -31,6 +31,8 @@ typedef struct {
   int32_t conv_group, conv_kernel, conv_fmt;
   /* the K/V cache keeps every element as f16 (1) instead of f32 (0) */
   int32_t kv_f16;
+  /* context rows that may wait unsettled (dflash.rs PENDING_ROWS; 0: none wait) */
+  int32_t pending_rows;
 } og_geometry;
 
 /* canonical matrix: F32 float [rows][cols]; Q4_32 uint8 [rows][cols/2] (low nibble = even
@@ -90,6 +92,12 @@ void og_row_conv(const float* x, int rows, int hidden, int gs, int kn, int stage
 og_model* og_create(const og_geometry* g, const og_weights* w);
 void og_destroy(og_model* m);
 int og_ctx_append(og_model* m, int seq, int64_t pos, const float* taps /* [n][n_taps*hidden] */, int n);
+/* the same rows queued (Drafter::queue_context: they wait, the oldest settled past pending_rows),
+ * and every waiting row settled (Drafter::settle); og_pending: rows waiting.  A block settles the
+ * waiting rows of its sequences first. */
+int og_ctx_queue(og_model* m, int seq, int64_t pos, const float* taps, int n);
+int og_ctx_settle(og_model* m, int seq);
+int64_t og_pending(const og_model* m, int seq);
 int og_ctx_truncate(og_model* m, int seq, int64_t pos);
 int og_ctx_reset(og_model* m, int seq);
 int og_ctx_span(const og_model* m, int seq, int64_t* first, int64_t* end);

@@ -14,6 +14,7 @@ import dflash_inputs as di
 import oracle
 import test_oracle_conv as TC
 import test_oracle_f16 as TF
+import test_oracle_queue as TQ
 import test_oracle_model as TM
 import test_oracle_select as TS
 import test_oracle_units as TU
@@ -63,6 +64,13 @@ MUTANTS = [
     ("f16 steps one bit too coarse", "ldexp(1.0, e - 11 > -24 ? e - 11 : -24)", "ldexp(1.0, e - 10 > -24 ? e - 10 : -24)"),
     ("f16 subnormal steps too fine", "ldexp(1.0, e - 11 > -24 ? e - 11 : -24)", "ldexp(1.0, e - 11 > -26 ? e - 11 : -26)"),
     ("the f16 cache keeps keys in f32", "s->k[off + d] = (float)og_round_f16(s->k[off + d]);", "(void)0;"),
+    ("waiting rows settled without rounding to chunks", "int64_t over = (s->npend - g->pending_rows + 63) / 64 * 64;",
+     "int64_t over = s->npend - g->pending_rows;"),
+    ("a truncation keeps the waiting rows", "if (s->npend > wait) s->npend = wait;", "(void)wait;"),
+    ("the span leaves out the waiting rows", "m->seqs[seq].len + m->seqs[seq].npend; /* Drafter::next_position */",
+     "m->seqs[seq].len; /* Drafter::next_position */"),
+    ("the block reads before settling", "  for (int i = 0; i < n_seqs; i++) og_ctx_settle(m, seqs[i]); /* a block reads settled rows */\n  const og_geometry* g = &m->g;",
+     "  const og_geometry* g = &m->g;"),
     ("the shortlist takes the whole head", "mm(g->head_fmt, m->w.head, head_rows, g->hidden,",
      "mm(g->head_fmt, m->w.head, head_rows > 16 ? head_rows - 16 : head_rows, g->hidden,"),
     ("silu sign", "a[i] = (float)(gv / (1.0 + exp(-gv)) * (double)u[i]);", "a[i] = (float)(gv / (1.0 + exp(gv)) * (double)u[i]);"),
@@ -77,8 +85,7 @@ MUTANTS = [
      "og_rope_head(tmp, hd, (int64_t)row, m->inv_freq);"),
     ("hidden norm skipped", "og_rmsnorm_row(t + (size_t)i * H, m->w.hidden_norm, H, (float)g->eps, tn + (size_t)i * H);",
      "memcpy(tn + (size_t)i * H, t + (size_t)i * H, sizeof(float) * H);"),
-    ("a gap keeps the old first", "  if (pos > first + len || pos < first) {\n    first = pos;",
-     "  if (pos > first + len || pos < first) {\n    first = first;"),
+    ("a gap keeps the old first", "    truncate_to(m, s, 0);\n    s->first = pos;", "    truncate_to(m, s, 0);\n    s->first = s->first;"),
     ("softmax max not subtracted consistently", "s[j] = exp(s[j] - top);", "s[j] = exp(s[j] - top) * (j == 0 ? 2.0 : 1.0);"),
     ("top-k keeps the later of equal values", "while (at < len && vals[at] >= v) at++;",
      "while (at < len && vals[at] > v) at++;"),
@@ -115,6 +122,9 @@ CHECKS = [
     (TW.test_no_rope_everywhere_is_position_free, ()),
     (TW.test_shortlist_head_is_a_prefix, ()),
     (TW.test_block_cut_to_its_first_rows_matches_transformers, ()),
+    (TQ.test_queue_counts_by_hand, ()),
+    (TQ.test_deferral_leaves_the_cache_and_the_block_unchanged, ()),
+    (TQ.test_window_drops_follow_the_settles, ()),
     (TF.test_round_f16_against_numpy, ()),
     (TF.test_f16_cache_holds_the_rounded_rows, ()),
     (TF.test_f16_cache_block_matches_transformers, ()),
