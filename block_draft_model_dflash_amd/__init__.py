@@ -22,7 +22,8 @@ EXPORTS = [
     "dflash_destroy", "dflash_quant_act", "dflash_packed_bytes", "dflash_pack", "dflash_gemm_scratch_bytes",
     "dflash_gemm", "dflash_group_sums", "dflash_read_kv", "dflash_time_stage", "dflash_read_timing",
     "dflash_top_k_scratch_bytes", "dflash_top_k", "dflash_select_scratch_bytes", "dflash_select",
-    "dflash_set_layer_options", "dflash_ctx_dropped", "dflash_block_forward_rows",
+    "dflash_set_layer_options", "dflash_ctx_dropped", "dflash_block_forward_rows", "dflash_ctx_queue",
+    "dflash_ctx_settle", "dflash_ctx_pending",
 ]
 (DFLASH_STAGE_HEAD, DFLASH_STAGE_QKV, DFLASH_STAGE_ATTENTION, DFLASH_STAGE_O, DFLASH_STAGE_GATE_UP, DFLASH_STAGE_DOWN,
  DFLASH_STAGE_BLOCK, DFLASH_STAGE_APPEND, DFLASH_STAGE_ATTN_CHUNKS) = range(9)
@@ -32,7 +33,7 @@ class dflash_geometry(C.Structure):
     _fields_ = [("rope_theta", C.c_double), ("eps", C.c_double)] + [
         (n, C.c_int32) for n in ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab",
                                  "block", "n_taps", "body_fmt", "fc_fmt", "head_fmt", "max_seqs", "max_ctx",
-                                 "conv_group", "conv_kernel", "conv_fmt", "kv_f16")]
+                                 "conv_group", "conv_kernel", "conv_fmt", "kv_f16", "pending_rows")]
 
 
 class dflash_matrix(C.Structure):
@@ -74,6 +75,9 @@ def lib():
             "dflash_set_stream": (i32, [vp, vp]),
             "dflash_ctx_append": (i32, [vp, i32, i64, vp, i32]),
             "dflash_ctx_truncate": (i32, [vp, i32, i64]),
+            "dflash_ctx_queue": (i32, [vp, i32, i64, vp, i32]),
+            "dflash_ctx_settle": (i32, [vp, i32]),
+            "dflash_ctx_pending": (i32, [vp, i32, C.POINTER(i64)]),
             "dflash_ctx_reset": (i32, [vp, i32]),
             "dflash_ctx_span": (i32, [vp, i32, C.POINTER(i64), C.POINTER(i64)]),
             "dflash_block_forward": (i32, [vp, i32, vp, vp, vp, vp]),
@@ -133,6 +137,20 @@ def dflash_set_stream(ctx, stream: int) -> int:
 
 def dflash_ctx_append(ctx, seq: int, pos: int, taps: int, n: int) -> int:
     return _check(lib().dflash_ctx_append(ctx, seq, pos, taps, n), ctx)
+
+
+def dflash_ctx_queue(ctx, seq: int, pos: int, taps: int, n: int) -> int:
+    return _check(lib().dflash_ctx_queue(ctx, seq, pos, taps, n), ctx)
+
+
+def dflash_ctx_settle(ctx, seq: int) -> int:
+    return _check(lib().dflash_ctx_settle(ctx, seq), ctx)
+
+
+def dflash_ctx_pending(ctx, seq: int) -> int:
+    n = C.c_int64()
+    _check(lib().dflash_ctx_pending(ctx, seq, C.byref(n)), ctx)
+    return n.value
 
 
 def dflash_ctx_truncate(ctx, seq: int, pos: int) -> int:

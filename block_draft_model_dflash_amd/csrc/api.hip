@@ -48,6 +48,7 @@ struct Layout {
   // row convolutions: packed kernel projections per layer, static kernels, and activations
   std::vector<size_t> kpa, kpm;
   size_t base_a = 0, base_m = 0, da = 0, dm = 0, xn = 0, ob = 0;
+  size_t pend = 0;  // waiting context rows: [max_seqs][pending_rows][n_taps*hidden] f32
 };
 
 bool is_fmt(int f) { return f == DFLASH_F32 || f == DFLASH_Q4_32 || f == DFLASH_Q8_32; }
@@ -86,6 +87,7 @@ int check_geometry(const dflash_geometry* g, std::string* err) {
   if (H % 32 || I % 32 || qd % 32 || T % 32) return fail(DFLASH_ENOTSUP, "activation widths must be multiples of 32");
   if (H * 4 > 96 * 1024) return fail(DFLASH_ENOTSUP, "hidden too wide for one workgroup's row");
   if (g->kv_f16 != 0 && g->kv_f16 != 1) return fail(DFLASH_EINVAL, "kv_f16 must be 0 or 1");
+  if (g->pending_rows < 0) return fail(DFLASH_EINVAL, "negative pending_rows");
   if (g->conv_kernel < 0) return fail(DFLASH_EINVAL, "negative conv_kernel");
   if (g->conv_kernel > 0) {
     if (g->conv_group < 1 || H % g->conv_group) return fail(DFLASH_EINVAL, "conv_group must divide hidden");
@@ -147,6 +149,7 @@ void plan(const dflash_geometry* g, Layout* L) {
   const size_t cache = (size_t)NL * g->max_seqs * kvh * (size_t)g->max_ctx * hd * (g->kv_f16 ? 2 : 4);
   L->kc = take(cache);
   L->vc = take(cache);
+  if (g->pending_rows > 0) L->pend = take((size_t)g->max_seqs * g->pending_rows * T * 4);
   L->act_begin = off;
   long Kmax = H;
   if (qd > Kmax) Kmax = qd;
@@ -192,6 +195,7 @@ struct dflash_ctx {
   Layout lay;
   uint8_t* ws = nullptr;
   std::vector<int64_t> first, len;
+  std::vector<int64_t> npend, pstart;  // waiting rows of each sequence and the ring's oldest slot
   // per-layer options (0 = every position; 1 = rotary) and, per (sequence, layer), the oldest
   // context rows the layer dropped
   std::vector<int32_t> window, rotary;
@@ -337,6 +341,8 @@ void layer_ranges(const dflash_ctx* c, int l, const int32_t* seqs, const int64_t
   }
 }
 
+int settle_seq(dflash_ctx* c, int seq);
+
 int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64_t* anchors, const float* h,
                  float* out, bool hidden_only, int head_rows, int block_rows) {
   const dflash_geometry& g = c->g;
@@ -352,6 +358,10 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
     if (anchors[i] < 0) return c->fail(DFLASH_EINVAL, "negative anchor");
     si.slot[i] = seqs[i];
     si.pos0[i] = anchors[i];
+  }
+  for (int i = 0; i < n_seqs; i++) {  // a block reads settled rows (Drafter::settle first)
+    const int rc = settle_seq(c, seqs[i]);
+    if (rc) return rc;
   }
   // the block's rows: all of them, or the first block_rows (the anchor and the rows after it)
   const int B = block_rows, H = g.hidden, nh = g.heads, kvh = g.kv_heads, hd = g.head_dim, NL = g.layers;
@@ -634,6 +644,8 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* works
   c->st = (hipStream_t)stream;
   c->first.assign(g->max_seqs, 0);
   c->len.assign(g->max_seqs, 0);
+  c->npend.assign(g->max_seqs, 0);
+  c->pstart.assign(g->max_seqs, 0);
   c->window.assign(g->layers, 0);
   c->rotary.assign(g->layers, 1);
   c->dropped.assign((size_t)g->max_seqs * g->layers, 0);
@@ -702,24 +714,15 @@ int dflash_set_stream(dflash_ctx* c, void* stream) {
   return DFLASH_OK;
 }
 
-int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps, int32_t n) {
-  if (!c) return DFLASH_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// Drafter::settle_rows: n rows of taps (device) become the context rows at positions first+len,
+// ...; then a layer holding more than twice its window keeps only the last window's worth (the
+// rows stay in the cache; they are never read again).
+int settle_rows(dflash_ctx* c, int seq, const float* taps, int n) {
   const dflash_geometry& g = c->g;
-  if (seq < 0 || seq >= g.max_seqs) return c->fail(DFLASH_EINVAL, "sequence %d out of range", seq);
-  if (pos < 0 || n < 0 || (n > 0 && !taps)) return c->fail(DFLASH_EINVAL, "bad position, count or taps");
-  int64_t first = c->first[seq], len = c->len[seq];
-  if (pos > first + len || pos < first) {
-    first = pos;
-    len = 0;
-  } else {
-    len = pos - first;
-  }
-  if (len + n > g.max_ctx)
-    return c->fail(DFLASH_ECAPACITY, "sequence %d: %lld + %d rows exceed max_ctx %d", seq, (long long)len, n,
-                   g.max_ctx);
-  c->keep_rows(seq, first == c->first[seq] ? len : 0);  // truncate(pos), or truncate(0) on a restart
-  c->first[seq] = first;
-  StageTimer timer(c, DFLASH_STAGE_APPEND);
   const int H = g.hidden, T = g.n_taps * g.hidden, kvd = g.kv_heads * g.head_dim, NL = g.layers;
   const float eps = (float)g.eps;
   const Layout& L = c->lay;
@@ -727,6 +730,8 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
   int8_t* xq = c->at<int8_t>(L.xq);
   float* dxT = c->at<float>(L.dxT);
   float* xf = c->at<float>(L.xf);
+  const int64_t pos = c->first[seq] + c->len[seq];
+  const int row = (int)c->len[seq];
   for (int c0 = 0; c0 < n; c0 += APPEND_CHUNK) {
     const int nn = n - c0 < APPEND_CHUNK ? n - c0 : APPEND_CHUNK;
     const int Mpad = round16(nn);
@@ -759,34 +764,147 @@ int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps
     if (rc) return rc;
     TRY_HIP(c,
             launch_kv_append(part, 1, Mpad, nn, NL, g.kv_heads, g.head_dim, c->at<float>(L.k_norm),
-                             c->at<float>(L.inv_freq), eps, c->rot_mask, pos + c0, (int)(pos - first) + c0, seq,
-                             g.max_seqs, g.max_ctx, g.kv_f16 != 0, c->ws + L.kc, c->ws + L.vc, c->st),
+                             c->at<float>(L.inv_freq), eps, c->rot_mask, pos + c0, row + c0, seq, g.max_seqs,
+                             g.max_ctx, g.kv_f16 != 0, c->ws + L.kc, c->ws + L.vc, c->st),
             "k/v into the cache");
   }
-  c->len[seq] = len + n;
-  // Drafter::settle_rows, at the end: a layer holding more than twice its window keeps only the
-  // last window's worth (the rows stay in the cache; they are never read again)
-  for (int l = 0; l < NL; l++) {
+  c->len[seq] += n;
+  return DFLASH_OK;
+}
+
+void drop_rows(dflash_ctx* c, int seq) {
+  for (int l = 0; l < c->g.layers; l++) {
     const int64_t w = c->window[l], held = c->len[seq] - c->drop(seq, l);
     if (w > 0 && held > 2 * w) c->drop(seq, l) += held - w;
   }
+}
+
+// The waiting rows of a sequence sit in a ring of pending_rows taps rows in the workspace:
+// the oldest at index pstart.  ring_row(seq, i) is the i-th waiting row's slot.
+float* ring_row(dflash_ctx* c, int seq, int64_t i) {
+  const int64_t cap = c->g.pending_rows;
+  const size_t T = (size_t)c->g.n_taps * c->g.hidden;
+  return c->at<float>(c->lay.pend) + ((size_t)seq * cap + (size_t)((c->pstart[seq] + i) % cap)) * T;
+}
+// the ring's first k waiting rows settled, in at most two contiguous pieces
+int settle_ring(dflash_ctx* c, int seq, int64_t k) {
+  const int64_t cap = c->g.pending_rows;
+  while (k > 0) {
+    const int64_t run = std::min(k, cap - c->pstart[seq]);
+    const int rc = settle_rows(c, seq, ring_row(c, seq, 0), (int)run);
+    if (rc) return rc;
+    c->pstart[seq] = (c->pstart[seq] + run) % cap;
+    c->npend[seq] -= run;
+    k -= run;
+  }
   return DFLASH_OK;
+}
+
+// Drafter::truncate: positions >= pos are forgotten, waiting rows among them too
+void truncate_seq(dflash_ctx* c, int seq, int64_t pos) {
+  const int64_t held = c->first[seq] + c->len[seq];
+  const int64_t wait = pos > held ? pos - held : 0;
+  if (c->npend[seq] > wait) c->npend[seq] = wait;
+  int64_t keep = pos - c->first[seq];
+  if (keep < 0) keep = 0;
+  if (keep > c->len[seq]) keep = c->len[seq];
+  c->keep_rows(seq, keep);
+}
+
+int settle_seq(dflash_ctx* c, int seq) {
+  if (c->npend[seq] == 0) return DFLASH_OK;
+  StageTimer timer(c, DFLASH_STAGE_APPEND);
+  const int rc = settle_ring(c, seq, c->npend[seq]);
+  if (rc) return rc;
+  drop_rows(c, seq);
+  c->pstart[seq] = 0;
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Drafter::queue_context: a position inside the span (waiting rows included) replaces it and
+// what follows; a gap, or a position before the first, starts over there.  The rows wait; past
+// pending_rows waiting rows the oldest settle, a whole number of 64-row chunks at a time (the
+// rows that stay waiting never exceed pending_rows, so new rows settled at once never pass
+// through the ring).
+int dflash_ctx_queue(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps, int32_t n) {
+  if (!c) return DFLASH_EINVAL;
+  const dflash_geometry& g = c->g;
+  if (seq < 0 || seq >= g.max_seqs) return c->fail(DFLASH_EINVAL, "sequence %d out of range", seq);
+  if (pos < 0 || n < 0 || (n > 0 && !taps)) return c->fail(DFLASH_EINVAL, "bad position, count or taps");
+  const int64_t next = c->first[seq] + c->len[seq] + c->npend[seq];
+  const bool restart = pos > next || pos < c->first[seq];
+  const int64_t first = restart ? pos : c->first[seq];
+  if (pos + n - first > g.max_ctx)
+    return c->fail(DFLASH_ECAPACITY, "sequence %d: positions %lld..%lld exceed max_ctx %d from %lld", seq,
+                   (long long)pos, (long long)(pos + n), g.max_ctx, (long long)first);
+  if (restart) {
+    truncate_seq(c, seq, 0);
+    c->first[seq] = pos;
+  } else {
+    truncate_seq(c, seq, pos);
+  }
+  const int64_t cap = g.pending_rows, held = c->npend[seq] + n;
+  int64_t over = 0;
+  if (held > cap) {
+    over = (held - cap + 63) / 64 * 64;
+    if (over > held) over = held;
+  }
+  const int64_t from_ring = std::min(over, c->npend[seq]), from_taps = over - from_ring;
+  if (over > 0) {
+    StageTimer timer(c, DFLASH_STAGE_APPEND);
+    int rc = settle_ring(c, seq, from_ring);
+    if (!rc && from_taps > 0) rc = settle_rows(c, seq, taps, (int)from_taps);
+    if (rc) return rc;
+    drop_rows(c, seq);
+  }
+  if (c->npend[seq] == 0) c->pstart[seq] = 0;
+  const size_t T = (size_t)g.n_taps * g.hidden;
+  for (int64_t r = from_taps; r < n;) {  // the rest waits: copied into the ring, in order
+    const int64_t slot = (c->pstart[seq] + c->npend[seq]) % cap;
+    const int64_t run = std::min(n - r, cap - slot);
+    TRY_HIP(c,
+            hipMemcpyAsync(ring_row(c, seq, c->npend[seq]), taps + (size_t)r * T, (size_t)run * T * 4,
+                           hipMemcpyDeviceToDevice, c->st),
+            "queue rows");
+    c->npend[seq] += run;
+    r += run;
+  }
+  return DFLASH_OK;
+}
+
+int dflash_ctx_settle(dflash_ctx* c, int32_t seq) {
+  if (!c) return DFLASH_EINVAL;
+  if (seq < 0 || seq >= c->g.max_seqs) return c->fail(DFLASH_EINVAL, "sequence %d out of range", seq);
+  return settle_seq(c, seq);
+}
+
+int dflash_ctx_pending(const dflash_ctx* c, int32_t seq, int64_t* n) {
+  if (!c || !n || seq < 0 || seq >= c->g.max_seqs) return DFLASH_EINVAL;
+  *n = c->npend[seq];
+  return DFLASH_OK;
+}
+
+// Drafter::push_context: queue_context, then settle.
+int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps, int32_t n) {
+  const int rc = dflash_ctx_queue(c, seq, pos, taps, n);
+  return rc ? rc : settle_seq(c, seq);
 }
 
 int dflash_ctx_truncate(dflash_ctx* c, int32_t seq, int64_t pos) {
   if (!c) return DFLASH_EINVAL;
   if (seq < 0 || seq >= c->g.max_seqs || pos < 0) return c->fail(DFLASH_EINVAL, "bad sequence or position");
-  int64_t keep = pos - c->first[seq];
-  if (keep < 0) keep = 0;
-  if (keep > c->len[seq]) keep = c->len[seq];
-  c->keep_rows(seq, keep);
+  truncate_seq(c, seq, pos);
   return DFLASH_OK;
 }
 
 int dflash_ctx_reset(dflash_ctx* c, int32_t seq) {
   if (!c) return DFLASH_EINVAL;
   if (seq < 0 || seq >= c->g.max_seqs) return c->fail(DFLASH_EINVAL, "bad sequence");
-  c->keep_rows(seq, 0);
+  truncate_seq(c, seq, 0);
   c->first[seq] = 0;
   return DFLASH_OK;
 }
@@ -822,7 +940,7 @@ int dflash_ctx_dropped(const dflash_ctx* c, int32_t seq, int32_t layer, int64_t*
 int dflash_ctx_span(const dflash_ctx* c, int32_t seq, int64_t* first, int64_t* end) {
   if (!c || !first || !end || seq < 0 || seq >= c->g.max_seqs) return DFLASH_EINVAL;
   *first = c->first[seq];
-  *end = c->first[seq] + c->len[seq];
+  *end = c->first[seq] + c->len[seq] + c->npend[seq];  // Drafter::next_position
   return DFLASH_OK;
 }
 

@@ -7,7 +7,8 @@ import ctypes as C
 import numpy as np
 
 from . import (DFLASH_F32, dflash_block_forward, dflash_block_forward_rows, dflash_block_hidden, dflash_create,
-               dflash_ctx_append, dflash_ctx_dropped, dflash_ctx_reset, dflash_ctx_span, dflash_ctx_truncate,
+               dflash_ctx_append, dflash_ctx_dropped, dflash_ctx_pending, dflash_ctx_queue, dflash_ctx_reset,
+               dflash_ctx_settle, dflash_ctx_span, dflash_ctx_truncate,
                dflash_destroy, dflash_geometry, dflash_layer_weights, dflash_matrix, dflash_read_kv,
                dflash_set_layer_options, dflash_set_stream, dflash_weights, dflash_workspace_bytes)
 
@@ -29,6 +30,7 @@ def geometry(spec, max_ctx: int, max_seqs: int) -> dflash_geometry:
     g.conv_kernel = int(getattr(spec, "conv_kernel", 0))
     g.conv_fmt = int(getattr(spec, "conv_fmt", spec.fc_fmt))
     g.kv_f16 = int(bool(getattr(spec, "kv_f16", False)))
+    g.pending_rows = int(getattr(spec, "pending_rows", 0))
     return g
 
 
@@ -93,6 +95,21 @@ class Drafter:
 
     def dropped(self, seq: int, layer: int) -> int:
         return dflash_ctx_dropped(self.ctx, seq, layer)
+
+    def queue(self, seq: int, pos: int, taps) -> None:
+        """Context rows that wait until a block reads them or more than pending_rows wait."""
+        t = self._f32(taps)
+        n = t.shape[0] if t.dim() == 2 else 0
+        self._sync_stream()
+        dflash_ctx_queue(self.ctx, seq, pos, t.data_ptr() if n else None, n)
+        self._last_inputs = t
+
+    def settle(self, seq: int) -> None:
+        self._sync_stream()
+        dflash_ctx_settle(self.ctx, seq)
+
+    def pending(self, seq: int) -> int:
+        return dflash_ctx_pending(self.ctx, seq)
 
     def truncate(self, seq: int, pos: int) -> None:
         dflash_ctx_truncate(self.ctx, seq, pos)

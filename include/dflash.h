@@ -77,6 +77,10 @@ typedef struct {
   /* 1: the K/V cache keeps each element as f16 (the f32 value rounded to nearest even; half
    * the bytes), 0: f32 */
   int32_t kv_f16;
+  /* context rows a sequence may keep waiting, unsettled (dflash.rs PENDING_ROWS, 512 there;
+   * dflash_ctx_queue); 0: every row settles at once.  Each sequence gets a device ring of
+   * pending_rows * n_taps * hidden f32 in the workspace. */
+  int32_t pending_rows;
 } dflash_geometry;
 
 /* A matrix in the canonical layout above (device pointers; scales NULL for DFLASH_F32). */
@@ -132,6 +136,20 @@ int dflash_set_stream(dflash_ctx* c, void* stream);
  * position - first.  n == 0 only applies that bookkeeping.  DFLASH_ECAPACITY if the sequence
  * would pass max_ctx rows (nothing changes then). */
 int dflash_ctx_append(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps, int32_t n);
+
+/* The deferred form of append (dflash.rs, Drafter::queue_context and Drafter::settle).
+ * dflash_ctx_queue takes the same arguments and bookkeeping as dflash_ctx_append, with the
+ * waiting rows counted in the span, but the rows wait (their taps are copied into the
+ * sequence's ring on the ctx stream); once more than pending_rows wait, the oldest are settled,
+ * a whole number of 64-row chunks (CONTEXT_CHUNK) at a time.  dflash_ctx_settle settles every
+ * waiting row of a sequence; dflash_ctx_append is queue then settle (Drafter::push_context).
+ * Every settle applies the window drop once at its end, so the rows a window drops follow the
+ * settles.  A block first settles the waiting rows of the sequences it is given.  A truncation
+ * forgets waiting rows at positions >= pos too.  dflash_ctx_pending: host *n receives the
+ * number of waiting rows. */
+int dflash_ctx_queue(dflash_ctx* c, int32_t seq, int64_t pos, const float* taps, int32_t n);
+int dflash_ctx_settle(dflash_ctx* c, int32_t seq);
+int dflash_ctx_pending(const dflash_ctx* c, int32_t seq, int64_t* n);
 
 /* Per-layer attention options (dflash.rs, Geometry window / windows / no_rope with window_of
  * and rotary): windows host [layers], positions a block row of that layer sees back (0: all of
