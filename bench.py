@@ -185,21 +185,23 @@ def main() -> int:
     # truncates it back to the prefill, and the next step appends right after it again
     grown = [0]
 
-    def step(i):
+    def step(i, d=None):
+        d = d or gm
         if app is not None:
             p = cfg.ctx + grown[0] * cfg.append_per_block
-            gm.append(0, p, app[grown[0]])
+            d.append(0, p, app[grown[0]])
             grown[0] += 1
             anchors = [p + cfg.append_per_block]
         else:
             anchors = [cfg.ctx] * cfg.n_seqs
-        gm.block_forward(seqs, anchors, hs[i], out=logits)
+        d.block_forward(seqs, anchors, hs[i], out=logits)
 
-    def rewind():
+    def rewind(d=None):
+        d = d or gm
         if app is not None:
-            gm.truncate(0, cfg.ctx)
+            d.truncate(0, cfg.ctx)
             grown[0] = 0
-            assert gm.span(0) == (0, cfg.ctx)
+            assert d.span(0) == (0, cfg.ctx)
 
     for i in range(W):
         step(i)
@@ -281,12 +283,31 @@ def main() -> int:
         torch.cuda.synchronize()
         sel_ms = e0.elapsed_time(e1) / K
 
+    # the same step with an f16 K/V cache (half the cache's bytes; a drafter with the same
+    # weights), every workload
+    variants = {}
+    if args.variants:
+        d16 = Drafter(cfg.replace(kv_f16=True), weights, max_ctx=max_ctx, max_seqs=cfg.n_seqs)
+        for sq in range(cfg.n_seqs):
+            for p0 in range(0, cfg.ctx, 4096):
+                d16.append(sq, p0, torch.from_numpy(di.make_taps(cfg, sq, p0, min(4096, cfg.ctx - p0))).cuda())
+        for i in range(W):
+            step(i, d16)
+        rewind(d16)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(K):
+            step(W + i, d16)
+        torch.cuda.synchronize()
+        variants["kv_cache_f16"] = round((time.perf_counter() - t) * 1e3 / K, 5)
+        d16.close()
+        del d16
+
     # the block with the optional parts of the drafter the workloads do not declare (untimed for
     # `value`): the head over its first 65536 rows; the block cut to 8 rows; a 1024-position
     # window on layers 0, 2, 4;
     # row convolutions of 16 columns a group and 4 offsets (a drafter with the same weights plus
     # the convolutions')
-    variants = {}
     if args.variants and cfg.n_seqs == 1 and app is None:
         def timed(fn):
             for i in range(W):
