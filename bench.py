@@ -291,6 +291,7 @@ def main() -> int:
         for sq in range(cfg.n_seqs):
             for p0 in range(0, cfg.ctx, 4096):
                 d16.append(sq, p0, torch.from_numpy(di.make_taps(cfg, sq, p0, min(4096, cfg.ctx - p0))).cuda())
+        rewind(d16)  # the step counter starts over (the context is already the prefill)
         for i in range(W):
             step(i, d16)
         rewind(d16)
