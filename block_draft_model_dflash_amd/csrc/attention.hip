@@ -75,7 +75,7 @@ struct CacheVec<_Float16> {
   }
 };
 
-template <int HD, typename CT>
+template <int HD, typename CT, bool WIN>
 __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqInfo si, int maxn,
                                                                const float* __restrict__ q,
                                                                const CT* __restrict__ kc,
@@ -98,9 +98,10 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
   const int nt = (kend - k0 + 15) / 16;  // >= 1: every launched chunk holds context rows
   const CT* Kctx = kc + (((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s]) * HD;
   const CT* Vctx = vc + (((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s]) * HD;
-  // under a window, query row col does not see the keys before index mask0 + col: their scores
-  // become -1e300, so exp() gives them exactly 0 beside any visible key; a chunk in which a row
-  // sees no key keeps the finite maximum -1e300, and the merge weights it by exp(-1e300 - m) = 0
+  // under a window (WIN: some row of the call masks keys), query row col does not see the keys
+  // before index mask0 + col: their scores become -1e300, so exp() gives them exactly 0 beside
+  // any visible key; a chunk in which a row sees no key keeps the finite maximum -1e300, and the
+  // merge weights it by exp(-1e300 - m) = 0
   const int kmin = si.mask0[s] + col;
 
   // the head's queries in LDS as f64 (converted once here, not once per tile; rows HD + 2
@@ -167,7 +168,8 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int key = quarter + 4 * r;  // accumulator slot r holds key row quarter + 4r
-      p[r] = key < nvalid ? (k0 + 16 * i + key >= kmin ? (st0[r] + st1[r]) * (double)a.scale : -1e300) : -INFINITY;
+      const double sc = (st0[r] + st1[r]) * (double)a.scale;
+      p[r] = key < nvalid ? (!WIN || k0 + 16 * i + key >= kmin ? sc : -1e300) : -INFINITY;
       mx = fmax(mx, p[r]);
     }
     mx = cross4_max_f64(mx);  // the same query's slots in the other three lane rows
@@ -360,6 +362,19 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_attn_merge(AttnShape a, SeqIn
     xf[(size_t)m * qd + colx] = val;
 }
 
+template <int HD, typename CT, bool WIN>
+static hipError_t attn_partial_inst(const AttnShape& a, const SeqInfo& si, int maxn, const float* q, const CT* kc,
+                                    const CT* vc, double* part, double* ml, hipStream_t st) {
+  const size_t lds = attn_lds_bytes<HD>();
+  hipError_t e = allow_lds((const void*)k_attn_partial<HD, CT, WIN>, lds);
+  if (e != hipSuccess) return e;
+  const int tasks = si.n * a.kvh * maxn, rep = a.nh / a.kvh;
+  const int grid = (tasks + 7) / 8 * 8 * rep;
+  hipLaunchKernelGGL((k_attn_partial<HD, CT, WIN>), dim3(grid), dim3(ATTN_THREADS), lds, st, a, si, maxn, q, kc, vc,
+                     part, ml);
+  return hipGetLastError();
+}
+
 template <int HD, typename CT>
 static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const float* q, const CT* kc,
                                   const CT* vc, double* part, double* ml, hipStream_t st) {
@@ -370,14 +385,12 @@ static hipError_t attn_partial_hd(const AttnShape& a, const SeqInfo& si, const f
   }
   if (maxn > a.maxch) return hipErrorInvalidValue;
   if (maxn == 0) return hipSuccess;  // no sequence has context rows: the merge does it all
-  const size_t lds = attn_lds_bytes<HD>();
-  hipError_t e = allow_lds((const void*)k_attn_partial<HD, CT>, lds);
-  if (e != hipSuccess) return e;
-  const int tasks = si.n * a.kvh * maxn, rep = a.nh / a.kvh;
-  const int grid = (tasks + 7) / 8 * 8 * rep;
-  hipLaunchKernelGGL((k_attn_partial<HD, CT>), dim3(grid), dim3(ATTN_THREADS), lds, st, a, si, maxn, q, kc, vc, part,
-                     ml);
-  return hipGetLastError();
+  // the masked instance only where some row of some sequence has keys before its window
+  bool win = false;
+  for (int i = 0; i < si.n; i++)
+    if (si.nctx[i] > 0 && si.mask0[i] + a.B - 1 > 0) win = true;
+  return win ? attn_partial_inst<HD, CT, true>(a, si, maxn, q, kc, vc, part, ml, st)
+             : attn_partial_inst<HD, CT, false>(a, si, maxn, q, kc, vc, part, ml, st);
 }
 
 template <int HD, int MAXC>
