@@ -5,9 +5,9 @@
 //
 // Top-k order: larger value first, the earlier index first among equal values -- the order in
 // which the pages' insertion list keeps its entries.  A row is cut into chunks of 4096; a
-// workgroup finds a chunk's top T by T rounds of a workgroup-wide arg-max (each thread owns 16
-// elements and a mask of those already taken), and a second kernel merges the chunks' lists the
-// same way.  The re-scoring repeats the pages' f32 arithmetic term by term, in their order and
+// workgroup finds a chunk's top T (each wave its own through a threshold and a sort across the
+// lanes, then wave 0 over the waves' lists), and a second kernel merges the chunks' lists the
+// same way.  Elements compare as 64-bit keys, so every step is exact.  The re-scoring repeats the pages' f32 arithmetic term by term, in their order and
 // without contraction, so its decisions are those of the reference evaluation.
 #include "common.h"
 #include "lanes.h"
@@ -48,17 +48,83 @@ __device__ __forceinline__ void wave_top(unsigned long long (&key)[PER], int T, 
   }
 }
 
-// The top T of the keys of the whole workgroup: each wave finds its own top T (no barrier
-// between rounds), then wave 0 finds the top T of those 4T keys.  Written by the first T lanes
-// of wave 0 to out_v, out_i (index -1 where there are fewer than T elements).
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const int lo = __shfl_xor((int)(unsigned)v, m), hi = __shfl_xor((int)(unsigned)(v >> 32), m);
+  return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+}
+
+// The wave's 64 keys (one a lane) sorted largest first across the lanes by a bitonic network:
+// blocks of k lanes alternate direction, so each merge step sees a bitonic sequence; in the
+// last (k = 64) every lower partner keeps the larger key.
+__device__ __forceinline__ unsigned long long wave_sort_desc(unsigned long long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const unsigned long long o = shfl_xor_u64(v, j);
+      const bool keep_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
+    }
+  return v;
+}
+
+// The wave's top T (T <= 64) through a threshold: the T-th largest of the lanes' maxima is at
+// most the T-th largest key (those T maxima are T distinct keys), so the wave's top T are among
+// the keys at least that large -- usually a few dozen.  Those are gathered (cand, 64 keys of
+// LDS), sorted across the lanes, and the first T written to out[0..T).  More than 64 of them
+// (many of the top keys in a few lanes), or T > 64: the rounds of wave_top instead.
+template <int PER>
+__device__ __forceinline__ void wave_top_fast(unsigned long long (&key)[PER], int T, unsigned long long* out,
+                                              unsigned long long* cand) {
+  const int lane = threadIdx.x & 63;
+  if (T > 64) {
+    wave_top<PER>(key, T, out);
+    return;
+  }
+  unsigned long long m = 0;
+#pragma unroll
+  for (int e = 0; e < PER; e++) m = key[e] > m ? key[e] : m;
+  const unsigned long long sm = wave_sort_desc(m);
+  const unsigned th_lo = __builtin_amdgcn_readlane((unsigned)sm, T - 1);
+  const unsigned th_hi = __builtin_amdgcn_readlane((unsigned)(sm >> 32), T - 1);
+  const unsigned long long th = ((unsigned long long)th_hi << 32) | th_lo;
+  int base = 0;
+#pragma unroll
+  for (int e = 0; e < PER; e++) {  // every nonempty key >= th gets a slot, in lane order
+    const bool take = key[e] != 0ull && key[e] >= th;
+    const unsigned long long bal = __builtin_amdgcn_ballot_w64(take);
+    const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0));
+    if (take && slot < 64) cand[slot] = key[e];
+    base += __builtin_popcountll(bal);
+  }
+  if (base > 64) {  // uniform: base is the same in every lane
+    wave_top<PER>(key, T, out);
+    return;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the lanes' stores before their loads
+  const unsigned long long v = wave_sort_desc(lane < base ? cand[lane] : 0ull);
+  if (lane < T) out[lane] = v;
+}
+
+// The top T of the keys of the whole workgroup: each wave finds its own top T, then wave 0
+// finds the top T of those 4T keys (one sort when 4T <= 64).  Written by the first T lanes of
+// wave 0 to out_v, out_i (index -1 where there are fewer than T elements).
 __device__ void block_top(unsigned long long (&key)[TK_PER], int T, float* out_v, int* out_i) {
   constexpr int NW = TK_THREADS / 64;
   __shared__ unsigned long long lk[NW][64];
+  __shared__ unsigned long long cand[NW][64];
   __shared__ unsigned long long ok[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  wave_top<TK_PER>(key, T, lk[wave]);
+  wave_top_fast<TK_PER>(key, T, lk[wave], cand[wave]);
   __syncthreads();
   if (wave != 0) return;
+  if (NW * T <= 64) {
+    const int w = min(lane / T, NW - 1), t = lane % T;
+    const unsigned long long v = wave_sort_desc(lane < NW * T ? lk[w][t] : 0ull);
+    if (lane < T) topk_decode(v, out_v[lane], out_i[lane]);
+    return;
+  }
   unsigned long long ck[NW];
 #pragma unroll
   for (int k = 0; k < NW; k++) {

@@ -41,6 +41,12 @@ def test_top_k_matches_the_oracle(width, k, ld):
     x = rng.standard_normal((rows, width)).astype(np.float32)
     x[1] = rng.integers(-3, 4, width).astype(np.float32)  # a row of many equal values
     x[2, :] = 1.0  # every value equal: the first k indices
+    # the largest values crowded into few threads of one workgroup (the first 16 of every 256
+    # indices of the first chunk): more candidates than one sort holds
+    i = np.arange(min(width, 4096))
+    x[3, i[(i % 256) < 16]] += 10.0
+    x[4, ::7] = -0.0  # -0 ties with +0 (and with the other zeros)
+    x[4, 3::7] = 0.0
     vals, idx = _gpu_top_k(x, k, ld)
     for r in range(rows):
         ov, oi = oracle.top_k(x[r], k)
