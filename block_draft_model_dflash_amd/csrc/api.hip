@@ -481,9 +481,24 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
     if (kn) {
       // o = Wo y; h += stage 1 of o; x = RMSNorm(h, post_norm); x <- stage 0 of x (MLP kernels);
       // a = silu(gate x) * up x; o = down a; h += stage 1 of o; the next norm
+      // stage 1 in the product's epilogue where a block's rows stay inside a 16-row group
+      const bool fused = bq && 16 % B == 0;
+      auto conv_epi = [&](const float* d, const float* base) {
+        GemmOut o = gemm_out(EPI_CONV, M, Mpad);
+        o.h = hbuf;
+        o.ssq = ssq;
+        o.cd = d;
+        o.cbase = base;
+        o.cB = B;
+        o.cgs = gs;
+        o.ckn = kn;
+        return o;
+      };
       {
         StageTimer t(c, DFLASH_STAGE_O);
-        if (bq) {
+        if (fused) {
+          rc = run_gemm_q(c, fmt, L.o[l], H, qd, xq, dxT, conv_epi(da, base_a), "o + conv + residual");
+        } else if (bq) {
           GemmOut o = gemm_out(EPI_F32, M, Mpad);
           o.y = ob;
           o.ld = H;
@@ -494,7 +509,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
         }
         if (rc) return rc;
       }
-      TRY_HIP(c, launch_conv_out(ob, da, base_a, M, B, H, gs, kn, hbuf, ssq, c->st), "conv out");
+      if (!fused) TRY_HIP(c, launch_conv_out(ob, da, base_a, M, B, H, gs, kn, hbuf, ssq, c->st), "conv out");
       TRY_HIP(c,
               launch_rms_act(hbuf, ssq, tile_parts, c->at<float>(L.post_norm) + (size_t)l * H, eps, M, Mpad, H, bq, xq,
                              dxT, xf, c->st, xn),
@@ -515,7 +530,9 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
       }
       {
         StageTimer t(c, DFLASH_STAGE_DOWN);
-        if (bq) {
+        if (fused) {
+          rc = run_gemm_q(c, fmt, L.down[l], H, I, xq2, dxT2, conv_epi(dm, base_m), "down + conv + residual");
+        } else if (bq) {
           GemmOut o = gemm_out(EPI_F32, M, Mpad);
           o.y = ob;
           o.ld = H;
@@ -526,7 +543,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
         }
         if (rc) return rc;
       }
-      TRY_HIP(c, launch_conv_out(ob, dm, base_m, M, B, H, gs, kn, hbuf, ssq, c->st), "conv out");
+      if (!fused) TRY_HIP(c, launch_conv_out(ob, dm, base_m, M, B, H, gs, kn, hbuf, ssq, c->st), "conv out");
       TRY_HIP(c, launch_rms_act(hbuf, ssq, tile_parts, nw, eps, M, Mpad, H, nq, xq, dxT, xf, c->st, xn), "next norm");
     } else if (bq) {
       // h += Wo y; x = A8(RMSNorm(h, post_norm)); a = A8(silu(gate x) * up x); h += down a

@@ -57,9 +57,12 @@ enum GemmEpi {
   EPI_F32 = 1,    // float y[m*ld + n] for m < m_store
   EPI_RESID = 2,  // h[m*N + n] += f32(y) for m < M; ssq[m*(N/16) + n/16] = sum of h^2 over the
                   // 16 columns of n's tile (f64; 0 for rows >= M), m < Mpad
-  EPI_SWIGLU = 3  // N = 2I with gate|up interleaved by 16-column tiles: a = silu(gate) * up
-                  // (f64 from the f32 products, one rounding) -> A8_32 into xq [Mpad][I] and
-                  // dxT [I/32][Mpad], or f32 into xf [Mpad][I] when xq is null
+  EPI_SWIGLU = 3,  // N = 2I with gate|up interleaved by 16-column tiles: a = silu(gate) * up
+                   // (f64 from the f32 products, one rounding) -> A8_32 into xq [Mpad][I] and
+                   // dxT [I/32][Mpad], or f32 into xf [Mpad][I] when xq is null
+  EPI_CONV = 4     // as EPI_RESID, with the row convolution's stage 1 on f32(y) before the add:
+                   // h[m] += conv(f32(y))[m] (kernels cd [M][2*ckn*N/cgs], cbase [2][ckn][N]; rows
+                   // of one sequence's block, cB of them, lie in one workgroup's row group)
 };
 struct GemmOut {
   int epi;
@@ -71,6 +74,9 @@ struct GemmOut {
   int8_t* xq;
   float* dxT;
   float* xf;
+  const float* cd;
+  const float* cbase;
+  int cB, cgs, ckn;
 };
 // layout < 0: chosen from the shape (0: four n-tiles x two k-waves per workgroup; 1: K split
 // over the waves of one (two) n-tile(s); 2: four n-tiles, one wave each); SwiGLU always uses

@@ -18,6 +18,8 @@
 // evaluation gives.  Every product feeds an int8 quantizer downstream, and a value one ulp off
 // there flips codes that the following layers amplify to percent-level differences in the
 // logits; correctly rounded outputs keep two implementations on the same codes.
+#include <type_traits>
+
 #include "common.h"
 #include "lanes.h"
 
@@ -142,7 +144,7 @@ __device__ __forceinline__ void superblock_mfma(const Super<FMT>& r, const int8_
 // partials in LDS and k-wave s % KW adds slot s's in wave order (the same order on every run)
 // and finishes it.  Output slot s = 4*mt + q of the accumulators is rows m0 + 16*mt + 4*quarter +
 // q, column row16 of n-tile ntile.
-template <int FMT, int MT, int NTW, int KW>
+template <int FMT, int MT, int NTW, int KW, bool CONV>
 __device__ __forceinline__ void gemm_finish(double (&acc)[MT][4], const float (&hres)[MT][4], uint8_t* smem,
                                             const GemmOut& o, int N, int m0, int nb, int ntile, bool active,
                                             int nt, int kw) {
@@ -201,6 +203,44 @@ __device__ __forceinline__ void gemm_finish(double (&acc)[MT][4], const float (&
     }
     return;
   }
+  if (CONV) {  // EPI_CONV (its own instances, so the other epilogues carry none of this)
+    // the row convolution's stage 1 needs the rows before each row, which sit in other lanes
+    // and waves: the workgroup's f32 tile goes through LDS first (rows of a block never cross
+    // the row group, checked at launch), then one thread per (row, column) adds its convolved
+    // value to h; 16 consecutive threads hold one n-tile's 16 columns of a row for the sums of
+    // squares
+    constexpr int WC = NTW * 16;
+    __syncthreads();
+    float* Y = (float*)smem;  // [MR][WC]
+    if (active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+          if (mine(4 * mt + q)) Y[(mt * 16 + 4 * quarter + q) * WC + nt * 16 + row16] = (float)(acc[mt][q] * post);
+    __syncthreads();
+    const int groups = N / o.cgs, pr = 2 * o.ckn * groups;
+    for (int i = tid; i < MR * WC; i += NT) {
+      const int ml = i / WC, cc = i % WC, m = m0 + ml, nn = nb * WC + cc;
+      if (m >= Mpad) break;  // rows in order: the rest are past Mpad too (whole 16-lane groups)
+      double sq = 0.0;
+      if (m < o.M && nn < N) {
+        const int r = m % o.cB, g = nn / o.cgs;
+        double c = 0.0;
+        for (int k = 0; k < o.ckn && k <= r; k++) {
+          const int so = o.ckn + k;  // stage 1
+          const double kk = (double)o.cbase[(size_t)so * N + nn] + (double)o.cd[(size_t)m * pr + (size_t)so * groups + g];
+          c += kk * (double)Y[(ml - k) * WC + cc];
+        }
+        const float hv = o.h[(size_t)m * N + nn] + (float)c;
+        o.h[(size_t)m * N + nn] = hv;
+        sq = (double)hv * (double)hv;
+      }
+      sq = row16_sum_f64(sq);
+      if ((lane & 15) == 0 && nn < N) o.ssq[(size_t)m * (N >> 4) + (nn >> 4)] = sq;
+    }
+    return;
+  }
   if (!active) return;
 #pragma unroll
   for (int mt = 0; mt < MT; mt++) {
@@ -237,7 +277,7 @@ __device__ __forceinline__ void gemm_finish(double (&acc)[MT][4], const float (&
 // where the slots read zeros), so the ring is straight-line code and the compiler counts the
 // loads in flight exactly; TURNS = 0 is the same with a runtime loop (shapes smaller than one
 // full chunk).
-template <int FMT, int MT, int NTW, int KW, int TURNS>
+template <int FMT, int MT, int NTW, int KW, int TURNS, bool CONV>
 __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restrict__ W, int N, int K,
                                                          const int8_t* __restrict__ xq,
                                                          const float* __restrict__ dxT, int kcb, int RG,
@@ -382,7 +422,7 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
     if (active) chunk(c0, c1);
   }
 
-  gemm_finish<FMT, MT, NTW, KW>(acc, hres, smem, o, N, m0, nb, ntile, active, nt, kw);
+  gemm_finish<FMT, MT, NTW, KW, CONV>(acc, hres, smem, o, N, m0, nb, ntile, active, nt, kw);
 }
 
 // The integer accumulators of the same tiles: sums[m][n][g] for every group (Q4 shifted back).
@@ -458,18 +498,24 @@ static hipError_t gemm_inst(const void* W, int N, int K, const int8_t* xq, const
   if (lds > max_dynamic_lds()) return hipErrorInvalidValue;
   // whole chunks of whole ring turns take the unrolled kernel
   const bool unrolled = kcb == KCB && KCB % STEP == 0;
-  const void* kern = unrolled ? (const void*)k_gemm_q<FMT, MT, NTW, KW, KCB / STEP>
-                              : (const void*)k_gemm_q<FMT, MT, NTW, KW, 0>;
-  hipError_t e = allow_lds(kern, lds);
-  if (e != hipSuccess) return e;
   const int RG = ceil_div(o.Mpad, MR);
   dim3 grid((unsigned)(ceil_div(N / 16, NTW) * RG));
-  if (unrolled)
-    hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW, KCB / STEP>), grid, dim3(64 * NTW * KW), lds, st,
-                       (const uint8_t*)W, N, K, xq, dxT, kcb, RG, o);
-  else
-    hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW, 0>), grid, dim3(64 * NTW * KW), lds, st, (const uint8_t*)W, N, K,
-                       xq, dxT, kcb, RG, o);
+  auto go = [&](auto conv) -> hipError_t {
+    constexpr bool CV = decltype(conv)::value;
+    const void* kern = unrolled ? (const void*)k_gemm_q<FMT, MT, NTW, KW, KCB / STEP, CV>
+                                : (const void*)k_gemm_q<FMT, MT, NTW, KW, 0, CV>;
+    hipError_t e = allow_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    if (unrolled)
+      hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW, KCB / STEP, CV>), grid, dim3(64 * NTW * KW), lds, st,
+                         (const uint8_t*)W, N, K, xq, dxT, kcb, RG, o);
+    else
+      hipLaunchKernelGGL((k_gemm_q<FMT, MT, NTW, KW, 0, CV>), grid, dim3(64 * NTW * KW), lds, st, (const uint8_t*)W,
+                         N, K, xq, dxT, kcb, RG, o);
+    return hipSuccess;
+  };
+  const hipError_t e = o.epi == EPI_CONV ? go(std::true_type()) : go(std::false_type());
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
@@ -497,7 +543,9 @@ hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq,
   if (N % 16 || K % 128 || o.Mpad % 16 || o.Mpad < 16 || o.Mpad > 128 || o.M > o.Mpad) return hipErrorInvalidValue;
   if (o.epi == EPI_SWIGLU && (N % 64 || (!o.xq && !o.xf) || (o.xq && !o.dxT))) return hipErrorInvalidValue;
   if ((o.epi == EPI_F64 || o.epi == EPI_F32) && !o.y) return hipErrorInvalidValue;
-  if (o.epi == EPI_RESID && (!o.h || !o.ssq)) return hipErrorInvalidValue;
+  if ((o.epi == EPI_RESID || o.epi == EPI_CONV) && (!o.h || !o.ssq)) return hipErrorInvalidValue;
+  if (o.epi == EPI_CONV && (!o.cd || !o.cbase || o.cB < 1 || 16 % o.cB || o.cgs < 1 || N % o.cgs || o.ckn < 1))
+    return hipErrorInvalidValue;  // a block's rows within every 16-row group
   if (layout < 0) layout = gemm_layout(N, o.Mpad, o.epi);
   if (o.epi == EPI_SWIGLU && layout != 0 && layout != 3) layout = 0;  // whole groups of four n-tiles
   if (o.epi == EPI_SWIGLU && layout == 3 && N % 128) layout = 0;
