@@ -53,6 +53,16 @@ def head_bytes(cfg) -> int:
     return w + x + rows * cfg.vocab * 4
 
 
+def prefill_bytes(cfg) -> int:
+    """Bytes the prefill of every sequence's context must move: the FC and all layers' Wk|Wv in
+    their stored formats once, the tapped rows read (f32), the K/V rows written (f32)."""
+    def mbytes(rows, cols, fmt):
+        return rows * cols * 4 if fmt == 0 else rows * (cols // 32) * (18 if fmt == 1 else 34)
+    rows = cfg.n_seqs * cfg.ctx
+    return (mbytes(cfg.hidden, cfg.tap_width, cfg.fc_fmt) + cfg.layers * mbytes(2 * cfg.kv_dim, cfg.hidden, cfg.body_fmt)
+            + rows * cfg.tap_width * 4 + rows * cfg.layers * 2 * cfg.kv_dim * 4)
+
+
 def attention_flops(cfg, nctx: int) -> int:
     """Flops of one layer's attention of every sequence's block: per q head and block row, the
     scores against nctx context keys + the block's own keys and the weighted sum of as many
@@ -401,6 +411,9 @@ def main() -> int:
         "achieved_GBps_step": round(block_gbs, 1),
         "frac_of_hbm_peak_step": round(block_gbs / HBM_PEAK_GBS, 4),
         "gpu_prefill_rows_per_s": round(cfg.n_seqs * cfg.ctx / (prefill_ms * 1e-3), 1),
+        # the prefill's algorithmic bytes: FC and every layer's Wk|Wv once, the taps read, the K/V
+        # rows written; it runs 128-row products, so it is bound by their arithmetic, not by HBM
+        "gpu_prefill_GBps": round(prefill_bytes(cfg) / (prefill_ms * 1e-3) / 1e9, 1),
         "int8_mfma_util_step": round(int8_macs(cfg) * 2 / (ms * 1e-3) / I8_MFMA_PEAK_OPS, 5),
         "roofline": dominant,
         "roofline_next": other,
