@@ -28,7 +28,9 @@
  *  - All GPU work of a ctx is enqueued on its stream (dflash_create / dflash_set_stream) and
  *    nothing synchronizes except dflash_create; a call returns once its work is enqueued.
  *  - Every call checks its arguments on the host before enqueueing anything and, on error,
- *    returns a negative status with the ctx state unchanged (dflash_last_error says why).
+ *    returns a negative status with the ctx state unchanged (dflash_last_error says why).  A
+ *    launch the runtime refuses after that (DFLASH_EHIP) leaves the context's rows undefined:
+ *    reset the sequences involved (or destroy the ctx) before using them again.
  *  - The library never allocates device memory: the caller hands dflash_create one workspace
  *    buffer (packed weights, K/V cache, activations) and owns it, the taps, block inputs and
  *    logits.  Borrowed buffers must stay valid until the work enqueued on them has run.
