@@ -79,8 +79,8 @@ struct GemmOut {
   int cB, cgs, ckn;
 };
 // layout < 0: chosen from the shape (0: four n-tiles x two k-waves per workgroup; 1: K split
-// over the waves of one (two) n-tile(s); 2: four n-tiles, one wave each); SwiGLU always uses
-// layout 0.
+// over the waves of one (two) n-tile(s); 2: four n-tiles, one wave each; 3: eight n-tiles, one
+// wave each); SwiGLU takes whole groups of four n-tiles (layouts 0, 2, 3).
 hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq, const float* dxT, int layout,
                          const GemmOut& o, hipStream_t st);
 int gemm_layout(int N, int Mpad, int epi);

@@ -10,8 +10,9 @@
 // per-group rescale is applied to its integer result right away.  The int8 activation block and
 // its scales are staged in LDS and shared by the workgroup's waves.  A product with few n-tiles
 // splits K over the waves of one workgroup, which add their sums in LDS; the epilogue (the
-// residual add with the row's sum of squares, or SwiGLU with its A8 quantizer) runs in the same
-// kernel, so no partial sums travel through memory.
+// residual add with the row's sum of squares, with or without a row convolution's second stage,
+// or SwiGLU with its A8 quantizer) runs in the same kernel, so no partial sums travel through
+// memory.
 //
 // The rescale accumulates in f64: d_w*d_x is exact in f64 and so is its product with a Q4 group
 // sum, so each output is the f32 rounding of (nearly) the exact sum, the same value a plain f64
