@@ -141,6 +141,8 @@ def main() -> int:
     ap.add_argument("--stages", type=int, default=1, help="also time each stage in its own untimed pass")
     ap.add_argument("--selection", type=int, default=1,
                     help="also time the candidate selection of one block's draft rows (top 16, rank 128)")
+    ap.add_argument("--flush", type=int, default=1,
+                    help="also time single steps after overwriting 1 GiB (cold caches), median and spread")
     ap.add_argument("--variants", type=int, default=1,
                     help="also time the block with the drafter's optional parts: a head shortlist, sliding "
                          "windows, row convolutions (single-sequence workloads)")
@@ -228,6 +230,26 @@ def main() -> int:
     if app is not None:  # every step extended the same context
         assert gm.span(0) == (0, cfg.ctx + K * cfg.append_per_block), gm.span(0)
     ms = (t1 - t0) * 1e3 / K
+
+    # each step on its own after an untimed overwrite of 1 GiB (L2 and the 256 MB MALL then hold
+    # none of the step's data), timed with events on the step's stream: the median and spread of
+    # single cold steps, beside `value` (K steps back to back)
+    flushed = None
+    if args.flush:
+        rewind()
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            scrub.fill_(float(i))
+            ev[i][0].record()
+            step(W + i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t_ms = np.sort([a.elapsed_time(b) for a, b in ev])
+        flushed = {"median": round(float(np.median(t_ms)), 5), "p10": round(float(np.percentile(t_ms, 10)), 5),
+                   "p90": round(float(np.percentile(t_ms, 90)), 5), "steps": K}
+        del scrub
+        log("cold steps (after a 1 GiB overwrite):", flushed)
 
     # the same K steps again with HIP events (on the library's stream) around the head's product
     # and around every layer's attention chunk kernel, the two largest kernels of the step; the
@@ -418,6 +440,7 @@ def main() -> int:
         "roofline": dominant,
         "roofline_next": other,
         "ms_per_step_with_kernel_events": round(ms_events, 5),
+        "cold_ms_per_step": flushed,
         "stages_ms_per_step": stages,
         "selection_ms_per_block": None if sel_ms is None else round(sel_ms, 5),
         "variants_ms_per_block": variants,
