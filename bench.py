@@ -231,26 +231,6 @@ def main() -> int:
         assert gm.span(0) == (0, cfg.ctx + K * cfg.append_per_block), gm.span(0)
     ms = (t1 - t0) * 1e3 / K
 
-    # each step on its own after an untimed overwrite of 1 GiB (L2 and the 256 MB MALL then hold
-    # none of the step's data), timed with events on the step's stream: the median and spread of
-    # single cold steps, beside `value` (K steps back to back)
-    flushed = None
-    if args.flush:
-        rewind()
-        scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-        for i in range(K):
-            scrub.fill_(float(i))
-            ev[i][0].record()
-            step(W + i)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        t_ms = np.sort([a.elapsed_time(b) for a, b in ev])
-        flushed = {"median": round(float(np.median(t_ms)), 5), "p10": round(float(np.percentile(t_ms, 10)), 5),
-                   "p90": round(float(np.percentile(t_ms, 90)), 5), "steps": K}
-        del scrub
-        log("cold steps (after a 1 GiB overwrite):", flushed)
-
     # the same K steps again with HIP events (on the library's stream) around the head's product
     # and around every layer's attention chunk kernel, the two largest kernels of the step; the
     # event pairs cost a few microseconds per step, so this repetition is not the one in `value`
@@ -287,6 +267,26 @@ def main() -> int:
             D.dflash_time_stage(gm.ctx, -1)
             stages[name] = round(tot / K, 5)  # ms per step, summed over the stage's launches
         log("stages ms/step:", stages)
+
+    # each step on its own after an untimed overwrite of 1 GiB (L2 and the 256 MB MALL then hold
+    # none of the step's data), timed with events on the step's stream: the median and spread of
+    # single cold steps, beside `value` (K steps back to back)
+    flushed = None
+    if args.flush:
+        rewind()
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for i in range(K):
+            scrub.fill_(float(i))
+            ev[i][0].record()
+            step(W + i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t_ms = np.sort([a.elapsed_time(b) for a, b in ev])
+        flushed = {"median": round(float(np.median(t_ms)), 5), "p10": round(float(np.percentile(t_ms, 10)), 5),
+                   "p90": round(float(np.percentile(t_ms, 90)), 5), "steps": K}
+        del scrub
+        log("cold steps (after a 1 GiB overwrite):", flushed)
 
     # the candidate selection the pages run after the block (not part of the step): top 16 of the
     # draft rows' logits and the greedy re-scoring with a rank-128 selector, timed on its own
