@@ -365,7 +365,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   }
   // the block's rows: all of them, or the first block_rows (the anchor and the rows after it)
   const int B = block_rows, H = g.hidden, nh = g.heads, kvh = g.kv_heads, hd = g.head_dim, NL = g.layers;
-  const int qd = nh * hd, kvd = kvh * hd, I = g.intermediate, V = g.vocab;
+  const int qd = nh * hd, kvd = kvh * hd, I = g.intermediate;
   const int M = n_seqs * B, Mpad = round16(M);
   const float eps = (float)g.eps;
   const Layout& L = c->lay;
