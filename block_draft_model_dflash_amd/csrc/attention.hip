@@ -192,10 +192,12 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
       l_run = l_run + ps;
     }
     m_run = m_new;
+    // step k pairs the probabilities of slot k with those keys' values; the NI output tiles are
+    // independent, so consecutive MFMAs never wait on each other's result
 #pragma unroll
-    for (int dt = 0; dt < NI; dt++) {
+    for (int k = 0; k < 4; k++) {
 #pragma unroll
-      for (int k = 0; k < 4; k++)  // step k pairs the probabilities of slot k with those keys' values
+      for (int dt = 0; dt < NI; dt++)
         acc[dt] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)vr[k][dt >> 2][dt & 3], p[k], acc[dt], 0, 0, 0);
     }
     load_v(min(i + ATTN_WAVES, last));
