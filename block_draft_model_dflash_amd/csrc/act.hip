@@ -31,8 +31,8 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 
 constexpr int ROW_THREADS = 1024;  // one workgroup per row, 16 waves
 
-// v = resid + o; optional write-back; optional RMSNorm; then A8_32 or f32.  The dx element of
-// (row m, group g) sits at g*dxg + m*dxm.
+// v = resid + o; optional write-back; RMSNorm (NORM; without it k_act_cols below runs instead);
+// then A8_32 or f32.  The dx element of (row m, group g) sits at g*dxg + m*dxm.
 template <bool NORM, bool QUANT>
 __global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restrict__ part,
                                                          const float* __restrict__ x, int S, int part_mstride,
@@ -55,17 +55,30 @@ __global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restri
     return;
   }
   double ss = 0.0;
-  for (int i = tid; i < N; i += ROW_THREADS) {
-    const float o = part ? reduce_parts(part, S, part_mstride, m, N, i) : x[(size_t)m * N + i];
-    const float v = resid ? resid[(size_t)m * N + i] + o : o;
-    if (h_out) h_out[(size_t)m * N + i] = v;
-    if (NORM) {
-      row[i] = v;
-      ss += (double)v * (double)v;
-    } else if (QUANT) {
-      emit_a8(v, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
-    } else {
-      xf[(size_t)m * N + i] = v;
+  // four elements a thread at a time, their loads issued together (a row of 4096 in one sweep)
+  constexpr int U = 4;
+  for (int i0 = tid; i0 < N; i0 += U * ROW_THREADS) {
+    float o[U], r[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int i = i0 + u * ROW_THREADS;
+      o[u] = i < N ? (part ? reduce_parts(part, S, part_mstride, m, N, i) : x[(size_t)m * N + i]) : 0.f;
+      r[u] = i < N && resid ? resid[(size_t)m * N + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int i = i0 + u * ROW_THREADS;
+      if (i >= N) break;
+      const float v = resid ? r[u] + o[u] : o[u];
+      if (h_out) h_out[(size_t)m * N + i] = v;
+      if (NORM) {
+        row[i] = v;
+        ss += (double)v * (double)v;
+      } else if (QUANT) {
+        emit_a8(v, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
+      } else {
+        xf[(size_t)m * N + i] = v;
+      }
     }
   }
   if (!NORM) return;
@@ -81,15 +94,56 @@ __global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restri
   }
 }
 
+// The same without a norm, where nothing crosses a row: one workgroup per (256 columns, row),
+// so a few wide rows (the taps of an append) spread over the whole chip.  N % 32 == 0 when
+// quantizing, so a 32-element group is all in or all out of range.
+constexpr int ACT_COLS = 256;
+template <bool QUANT>
+__global__ __launch_bounds__(ACT_COLS) void k_act_cols(const double* __restrict__ part, const float* __restrict__ x,
+                                                      int S, int part_mstride, const float* __restrict__ resid,
+                                                      float* __restrict__ h_out, int M, int N, int8_t* __restrict__ xq,
+                                                      float* __restrict__ dx, int dxg, int dxm,
+                                                      float* __restrict__ xf) {
+  const int m = blockIdx.y, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * ACT_COLS + threadIdx.x;
+  const bool in = i < N;
+  if (m >= M) {
+    if (!in) return;
+    if (QUANT) {
+      xq[(size_t)m * N + i] = 0;
+      if ((lane & 31) == 0) dx[(size_t)(i >> 5) * dxg + (size_t)m * dxm] = 0.f;
+    } else {
+      xf[(size_t)m * N + i] = 0.f;
+    }
+    return;
+  }
+  float v = 0.f;
+  if (in) {
+    const float o = part ? reduce_parts(part, S, part_mstride, m, N, i) : x[(size_t)m * N + i];
+    v = resid ? resid[(size_t)m * N + i] + o : o;
+    if (h_out) h_out[(size_t)m * N + i] = v;
+  }
+  if (QUANT) {
+    if (in) emit_a8(v, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
+  } else if (in) {
+    xf[(size_t)m * N + i] = v;
+  }
+}
+
 template <bool NORM, bool QUANT>
 static hipError_t norm_act_inst(const double* part, const float* x, int S, int part_mstride, const float* resid,
                                 float* h_out, const float* w, float eps, int M, int grid, int N, int8_t* xq,
                                 float* dx, int dxg, int dxm, float* xf, hipStream_t st) {
-  const size_t lds = NORM ? (size_t)N * 4 : 0;
-  hipError_t e = allow_lds((const void*)k_norm_act<NORM, QUANT>, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_norm_act<NORM, QUANT>), dim3(grid), dim3(ROW_THREADS), lds, st, part, x, S, part_mstride, resid,
-                     h_out, w, eps, M, N, xq, dx, dxg, dxm, xf);
+  if constexpr (!NORM) {
+    hipLaunchKernelGGL((k_act_cols<QUANT>), dim3((N + ACT_COLS - 1) / ACT_COLS, grid), dim3(ACT_COLS), 0, st, part, x,
+                       S, part_mstride, resid, h_out, M, N, xq, dx, dxg, dxm, xf);
+  } else {
+    const size_t lds = (size_t)N * 4;
+    hipError_t e = allow_lds((const void*)k_norm_act<NORM, QUANT>, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_norm_act<NORM, QUANT>), dim3(grid), dim3(ROW_THREADS), lds, st, part, x, S, part_mstride,
+                       resid, h_out, w, eps, M, N, xq, dx, dxg, dxm, xf);
+  }
   return hipGetLastError();
 }
 
