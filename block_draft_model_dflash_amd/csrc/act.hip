@@ -31,16 +31,19 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 
 constexpr int ROW_THREADS = 1024;  // one workgroup per row, 16 waves
 
-// v = resid + o; optional write-back; RMSNorm (NORM; without it k_act_cols below runs instead);
-// then A8_32 or f32.  The dx element of (row m, group g) sits at g*dxg + m*dxm.
-template <bool NORM, bool QUANT>
+// v = resid + o; optional write-back; RMSNorm; then A8_32 (QUANT) or f32.  The dx element of
+// (row m, group g) sits at g*dxg + m*dxm.  One workgroup per row (without a norm, k_act_cols
+// below runs instead).  Each sweep takes four elements a thread, their loads issued together;
+// the first sweep also loads its norm weights, so a row of up to 4096 waits on memory once
+// before the sum of squares and not again after it.
+template <bool QUANT>
 __global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restrict__ part,
                                                          const float* __restrict__ x, int S, int part_mstride,
                                                          const float* __restrict__ resid, float* __restrict__ h_out,
                                                          const float* __restrict__ w, float eps, int M, int N,
                                                          int8_t* __restrict__ xq, float* __restrict__ dx, int dxg,
                                                          int dxm, float* __restrict__ xf) {
-  extern __shared__ float row[];  // N floats when NORM
+  extern __shared__ float row[];  // N floats
   __shared__ double red[ROW_THREADS / 64];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   if (m >= M) {
@@ -54,16 +57,17 @@ __global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restri
     }
     return;
   }
+  constexpr int U = 4, SWEEP = U * ROW_THREADS;
   double ss = 0.0;
-  // four elements a thread at a time, their loads issued together (a row of 4096 in one sweep)
-  constexpr int U = 4;
-  for (int i0 = tid; i0 < N; i0 += U * ROW_THREADS) {
+  float w0[U];  // the first sweep's weights
+  for (int i0 = tid; i0 < N; i0 += SWEEP) {
     float o[U], r[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int i = i0 + u * ROW_THREADS;
       o[u] = i < N ? (part ? reduce_parts(part, S, part_mstride, m, N, i) : x[(size_t)m * N + i]) : 0.f;
       r[u] = i < N && resid ? resid[(size_t)m * N + i] : 0.f;
+      if (i0 == tid) w0[u] = i < N ? w[i] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -71,26 +75,24 @@ __global__ __launch_bounds__(ROW_THREADS) void k_norm_act(const double* __restri
       if (i >= N) break;
       const float v = resid ? r[u] + o[u] : o[u];
       if (h_out) h_out[(size_t)m * N + i] = v;
-      if (NORM) {
-        row[i] = v;
-        ss += (double)v * (double)v;
-      } else if (QUANT) {
-        emit_a8(v, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
-      } else {
-        xf[(size_t)m * N + i] = v;
-      }
+      row[i] = v;
+      ss += (double)v * (double)v;
     }
   }
-  if (!NORM) return;
   ss = block_sum_f64(ss, red);
   const float sc = 1.0f / sqrtf((float)(ss / (double)N) + eps);
-  for (int i = tid; i < N; i += ROW_THREADS) {
-    const float t = row[i] * sc;
-    const float y = t * w[i];
-    if (QUANT)
-      emit_a8(y, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
-    else
-      xf[(size_t)m * N + i] = y;
+  for (int i0 = tid; i0 < N; i0 += SWEEP) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int i = i0 + u * ROW_THREADS;
+      if (i >= N) break;
+      const float t = row[i] * sc;
+      const float y = t * (i0 == tid ? w0[u] : w[i]);
+      if (QUANT)
+        emit_a8(y, (size_t)m * N + i, xq, dx, (size_t)(i >> 5) * dxg + (size_t)m * dxm, lane);
+      else
+        xf[(size_t)m * N + i] = y;
+    }
   }
 }
 
@@ -139,10 +141,10 @@ static hipError_t norm_act_inst(const double* part, const float* x, int S, int p
                        S, part_mstride, resid, h_out, M, N, xq, dx, dxg, dxm, xf);
   } else {
     const size_t lds = (size_t)N * 4;
-    hipError_t e = allow_lds((const void*)k_norm_act<NORM, QUANT>, lds);
+    hipError_t e = allow_lds((const void*)k_norm_act<QUANT>, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_norm_act<NORM, QUANT>), dim3(grid), dim3(ROW_THREADS), lds, st, part, x, S, part_mstride,
-                       resid, h_out, w, eps, M, N, xq, dx, dxg, dxm, xf);
+    hipLaunchKernelGGL((k_norm_act<QUANT>), dim3(grid), dim3(ROW_THREADS), lds, st, part, x, S, part_mstride, resid,
+                       h_out, w, eps, M, N, xq, dx, dxg, dxm, xf);
   }
   return hipGetLastError();
 }
