@@ -150,8 +150,8 @@ def main() -> int:
                     help="after the timed region, run one plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU; the path's multi-GPU sharding is a design "
-              "(see the design notes) and no figure at several GPUs is produced", file=sys.stderr)
+        print("bench.py: measures one GPU only; sharding the path over several GPUs is designed but "
+              "not built, so no figure at several GPUs is produced", file=sys.stderr)
         return 2
 
     import numpy as np
