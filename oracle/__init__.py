@@ -106,7 +106,8 @@ def lib(path: str | None = None):
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        # at most 16 threads: the CPU share of a one-GPU machine, whatever the host reports
+        # at most 16 threads, whatever the host reports: on a machine whose cores are shared
+        # among several GPUs, one GPU's process gets about that many
         L.og_set_threads(int(os.environ.get("DFLASH_ORACLE_THREADS", min(16, os.cpu_count() or 1))))
         _lib = L
     return _lib
