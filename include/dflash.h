@@ -263,7 +263,9 @@ int dflash_read_timing(dflash_ctx* c, int32_t stage, double* total_ms, int64_t* 
  * dflash_top_k: the k largest entries of each of `rows` rows of x (device f32, row r at
  * x + r*ld, `width` entries, ld >= width) with their indices, largest first and, among equal
  * values, the earlier index first (the order the pages' top_k list keeps).  vals device
- * [rows][k] f32, idx device [rows][k] int32.  1 <= k <= min(width, 64); values must be finite.
+ * [rows][k] f32, idx device [rows][k] int32; vals[r][i] compares equal to the entry at
+ * idx[r][i] (a -0 entry ties with +0 and comes back as +0).  1 <= k <= min(width, 64); values
+ * must be finite.
  * `scratch`: device memory of dflash_top_k_scratch_bytes() bytes.
  *
  * dflash_select: the draft tokens of `rows` rows from their logits (device, as for top_k; row j

@@ -148,3 +148,44 @@ def test_selection_chain_of_the_8b_drafter():
     say(f"chosen {chosen.cpu().numpy().tolist()} plain {plain.cpu().numpy().tolist()}")
     assert np.array_equal(plain.cpu().numpy(), op)
     assert np.array_equal(chosen.cpu().numpy(), oc)
+
+
+# random widths, k, strides and value mixes; DFLASH_TOPK_CASES asks for a longer sweep
+TOPK_CASES = int(__import__("os").environ.get("DFLASH_TOPK_CASES", "60"))
+
+
+@pytest.mark.parametrize("seed", range(TOPK_CASES))
+def test_top_k_random_shapes(seed):
+    """Seeded random shapes: width 1..160000, k 1..min(64, width), a row stride past the width,
+    and rows drawn from five mixes (normal, a few integer values with many ties, one constant,
+    maxima crowded into one corner of a chunk, signed zeros among small values).  Indices must
+    equal the oracle's, ties included, and values compare equal to it and to the entries they
+    index (a -0 entry ties with +0 and comes back as +0, which compares equal)."""
+    r = np.random.default_rng(50_000 + seed)
+    width = int(r.choice([int(r.integers(1, 300)), int(r.integers(300, 20000)), int(r.integers(20000, 160000))]))
+    k = int(r.integers(1, min(64, width) + 1))
+    ld = width + int(r.choice([0, 0, 1, 7, 64]))
+    rows = int(r.integers(1, 6))
+    x = np.empty((rows, width), np.float32)
+    for row in range(rows):
+        mix = int(r.integers(5))
+        if mix == 0:
+            x[row] = r.standard_normal(width)
+        elif mix == 1:
+            x[row] = r.integers(-2, 3, width)
+        elif mix == 2:
+            x[row] = np.float32(r.standard_normal())
+        elif mix == 3:
+            x[row] = r.standard_normal(width)
+            lo = int(r.integers(0, width))
+            x[row, lo:lo + int(r.integers(1, 300))] += 50.0
+        else:
+            x[row] = np.round(r.standard_normal(width), 1) * (r.random(width) < 0.5)
+            x[row, r.random(width) < 0.3] = -0.0
+    say(f"top_k random seed={seed} rows={rows} width={width} k={k} ld={ld}")
+    vals, idx = _gpu_top_k(x, k, ld)
+    for row in range(rows):
+        ov, oi = oracle.top_k(x[row], k)
+        assert np.array_equal(idx[row], oi), (seed, row)
+        assert np.array_equal(vals[row], ov), (seed, row)
+        assert np.array_equal(vals[row], x[row, idx[row]]), (seed, row)
