@@ -60,10 +60,11 @@ def test_top_k_pages_example_on_gpu():
     assert list(idx[0]) == [4, 1, 3] and list(vals[0]) == [3.5, 2.0, 2.0]
 
 
-def _gpu_select(logits, hp, pred, succ, top, anchor, ld=None):
+def _gpu_select(logits, hp, pred, succ, top, anchor, ld=None, width=None):
+    """logits [rows][ld or its width]: each row's first `width` entries (all, by default) count."""
     import block_draft_model_dflash_amd as D
 
-    rows, width = logits.shape
+    rows, width = logits.shape[0], width or logits.shape[1]
     vocab, rank = pred.shape
     gl = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
     gh = torch.from_numpy(np.ascontiguousarray(hp, np.float32)).cuda()
@@ -189,3 +190,39 @@ def test_top_k_random_shapes(seed):
         assert np.array_equal(idx[row], oi), (seed, row)
         assert np.array_equal(vals[row], ov), (seed, row)
         assert np.array_equal(vals[row], x[row, idx[row]]), (seed, row)
+
+
+SELECT_CASES = int(__import__("os").environ.get("DFLASH_SELECT_CASES", "40"))
+
+
+@pytest.mark.parametrize("seed", range(SELECT_CASES))
+def test_select_random_shapes(seed):
+    """Seeded random selector problems: 1..16 rows, vocab 2..60000 (width up to the vocab, a row
+    stride past it), rank 1..512 (now and then 4096, the sequential kernel), top 1..min(64,
+    width), any anchor; logits sometimes with many ties, codebooks sometimes all zero (the
+    re-scoring then keeps each row's own top token).  Chosen and plain tokens must equal the
+    oracle's."""
+    r = np.random.default_rng(70_000 + seed)
+    rows = int(r.integers(1, 17))
+    vocab = int(r.choice([int(r.integers(2, 200)), int(r.integers(200, 5000)), int(r.integers(5000, 60000))]))
+    width = int(r.integers(1, vocab + 1)) if r.integers(4) == 0 else vocab
+    ld = width + int(r.choice([0, 0, 3]))
+    rank = 4096 if r.integers(12) == 0 else int(r.integers(1, 513))
+    top = int(r.integers(1, min(64, width) + 1))
+    anchor = int(r.integers(0, vocab))
+    logits = r.standard_normal((rows, width)).astype(np.float32)
+    if r.integers(3) == 0:
+        logits = np.round(logits * 2).astype(np.float32)  # many equal logits
+    hp = r.standard_normal((rows, rank)).astype(np.float32)
+    scale = 0.0 if r.integers(6) == 0 else float(r.choice([0.05, 0.3, 1.0]))
+    pred = (r.standard_normal((vocab, rank)) * scale).astype(np.float16)
+    succ = (r.standard_normal((vocab, rank)) * scale).astype(np.float16)
+    say(f"select random seed={seed} rows={rows} vocab={vocab} width={width} ld={ld} rank={rank} top={top}")
+    buf = np.zeros((rows, ld), np.float32)
+    buf[:, :width] = logits
+    chosen, plain = _gpu_select(buf, hp, pred, succ, top, anchor, ld=ld, width=width)
+    oc, op = oracle.select(logits, hp, pred, succ, top, anchor)
+    assert np.array_equal(plain, op), seed
+    assert np.array_equal(chosen, oc), seed
+    if scale == 0.0:
+        assert np.array_equal(chosen, plain), seed
