@@ -131,3 +131,22 @@ def _check_gemm(fmt, rows, cols, m, splits):
 @pytest.mark.parametrize("rows,cols,m", [(16400, 2048, 16), (16400, 4096, 3)])
 def test_gemm_many_tiles(fmt, rows, cols, m):
     _check_gemm(fmt, rows, cols, m, 0)
+
+
+GEMM_CASES = int(__import__("os").environ.get("DFLASH_GEMM_CASES", "100"))
+
+
+@pytest.mark.parametrize("seed", range(GEMM_CASES))
+def test_gemm_random_shapes(seed):
+    """Seeded random products: 16..4096 weight rows, 128..6144 columns, 1..128 activation rows,
+    either format, any of the layouts (splits 0 = chosen from the shape, 1, 2, 8); the bar of
+    the fixed shapes above (one ulp at most, 99.9% equal to the oracle's f32)."""
+    r = np.random.default_rng(90_000 + seed)
+    rows = 16 * int(r.integers(1, 257))
+    cols = 128 * int(r.integers(1, 49))
+    m = int(r.integers(1, 17)) if r.integers(2) else int(r.integers(17, 129))
+    while m > 1 and rows * cols * m > 400_000_000:  # keep the oracle's share to a few seconds
+        m //= 2
+    fmt = di.Q4_32 if r.integers(2) else di.Q8_32
+    splits = int(r.choice([0, 1, 2, 8]))
+    _check_gemm(fmt, rows, cols, m, splits)
