@@ -87,6 +87,10 @@ int check_geometry(const dflash_geometry* g, std::string* err) {
   if (H % 32 || I % 32 || qd % 32 || T % 32) return fail(DFLASH_ENOTSUP, "activation widths must be multiples of 32");
   if (H * 4 > 96 * 1024) return fail(DFLASH_ENOTSUP, "hidden too wide for one workgroup's row");
   if (g->kv_f16 != 0 && g->kv_f16 != 1) return fail(DFLASH_EINVAL, "kv_f16 must be 0 or 1");
+  // attention addresses one (sequence, kv head)'s cache rows through a buffer resource with
+  // 32-bit byte offsets
+  if ((size_t)g->max_ctx * g->head_dim * (g->kv_f16 ? 2 : 4) >= ((size_t)1 << 31))
+    return fail(DFLASH_ENOTSUP, "max_ctx * head_dim * element bytes must stay below 2^31");
   if (g->pending_rows < 0) return fail(DFLASH_EINVAL, "negative pending_rows");
   if (g->conv_kernel < 0) return fail(DFLASH_EINVAL, "negative conv_kernel");
   if (g->conv_kernel > 0) {
@@ -223,8 +227,10 @@ struct dflash_ctx {
     }
     return hipEventRecord(ev_pool[ev_used++], st);
   }
+  hipEvent_t switch_ev = nullptr;  // orders a stream switch after the old stream's work
   ~dflash_ctx() {
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    if (switch_ev) (void)hipEventDestroy(switch_ev);
   }
 
   template <class T>
@@ -725,9 +731,17 @@ int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* works
   return fin(DFLASH_OK);
 }
 
+// Work already enqueued on the old stream uses the same workspace (activations, partials, the
+// waiting rows), so the new stream first waits for it: an event recorded on the old stream and
+// a device-side wait on the new one (the host does not wait).
 int dflash_set_stream(dflash_ctx* c, void* stream) {
   if (!c) return DFLASH_EINVAL;
-  c->st = (hipStream_t)stream;
+  hipStream_t ns = (hipStream_t)stream;
+  if (ns == c->st) return DFLASH_OK;
+  if (!c->switch_ev) TRY_HIP(c, hipEventCreateWithFlags(&c->switch_ev, hipEventDisableTiming), "stream switch event");
+  TRY_HIP(c, hipEventRecord(c->switch_ev, c->st), "stream switch record");
+  TRY_HIP(c, hipStreamWaitEvent(ns, c->switch_ev, 0), "stream switch wait");
+  c->st = ns;
   return DFLASH_OK;
 }
 
@@ -954,6 +968,8 @@ int dflash_ctx_dropped(const dflash_ctx* c, int32_t seq, int32_t layer, int64_t*
   return DFLASH_OK;
 }
 
+// dflash.rs, Drafter::span and Drafter::next_position: the first position held and the next one
+// to append (waiting rows count as held).
 int dflash_ctx_span(const dflash_ctx* c, int32_t seq, int64_t* first, int64_t* end) {
   if (!c || !first || !end || seq < 0 || seq >= c->g.max_seqs) return DFLASH_EINVAL;
   *first = c->first[seq];
@@ -1130,6 +1146,7 @@ extern "C" {
 
 int dflash_top_k_scratch_bytes(int32_t rows, int32_t width, int32_t k, size_t* bytes) {
   if (!bytes || rows < 1 || width < 1 || k < 1 || k > 64 || k > width) return DFLASH_EINVAL;
+  if (!top_k_fits(width, k)) return DFLASH_EINVAL;  // the chunks' lists must fit one merge
   *bytes = top_k_scratch(rows, width, k);
   return DFLASH_OK;
 }

@@ -1,8 +1,8 @@
-// Block-vs-context attention (cortiq-engine "dflash.rs", Drafter::block: each q head j reads
-// kv head j / rep; its keys and values are the layer's context rows before the anchor, as far
-// back as its window reaches, followed by the block's own rows, with no causal mask; under a
-// window, block row r masks the context positions before anchor + r + 1 - w;
-// s = (q . k) * hd^-0.5, softmax, y = sum p v).
+// Block-vs-context attention (cortiq-engine "dflash.rs", Drafter::block).  Query head j uses
+// kv head j / rep.  Its key set is the layer's range [lo, hi) of context positions (the caller
+// computes it) plus all of the block's own rows, with no causal mask among the block rows.  A
+// windowed layer also hides, from block row r, the context positions below anchor + r + 1 - w.
+// Scores are (q . k) * hd^-0.5, then a softmax over the key set and y = sum of p * v.
 //
 // The pages' device kernel (gpu_wgpu/dflash_dev.rs, dflash_attn) writes every score to a global
 // scratch and re-reads it; here the context is split into chunks, each wave keeps a running

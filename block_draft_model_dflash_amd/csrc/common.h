@@ -158,6 +158,8 @@ hipError_t allow_lds(const void* kernel, size_t bytes);
 hipError_t launch_top_k(const float* x, int rows, int width, int ld, int T, float* part_v, int* part_i, float* vals,
                         int* idx, hipStream_t st);
 size_t top_k_scratch(int rows, int width, int T);
+// The chunk lists of a row (ceil(width/4096) * T entries) must fit the merge's 4096 slots.
+bool top_k_fits(int width, int T);
 hipError_t launch_select(const float* cv, const int* ci, int rows, int T, const float* hp, int rank,
                          const uint16_t* pred, const uint16_t* succ, int anchor, int* chosen, int* plain,
                          float* scores, hipStream_t st);

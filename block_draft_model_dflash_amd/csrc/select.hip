@@ -178,6 +178,8 @@ hipError_t launch_top_k(const float* x, int rows, int width, int ld, int T, floa
   return hipGetLastError();
 }
 
+bool top_k_fits(int width, int T) { return (long)((width + TK_CHUNK - 1) / TK_CHUNK) * T <= TK_CHUNK; }
+
 size_t top_k_scratch(int rows, int width, int T) {
   const size_t nch = (width + TK_CHUNK - 1) / TK_CHUNK;
   return 2 * ((rows * nch * T * 4 + 255) & ~(size_t)255);

@@ -60,7 +60,8 @@ enum dflash_format { DFLASH_F32 = 0, DFLASH_Q4_32 = 1, DFLASH_Q8_32 = 2 };
  * convolutions, the selector, windows and target binding) plus the cache's capacity.
  * Limits: layers >= 1; 2 <= block <= 16; heads % kv_heads == 0 and heads/kv_heads <= 16;
  * head_dim 64 or 128; hidden, heads*head_dim, intermediate and n_taps*hidden multiples of 128
- * (of 4 for f32 matrices); vocab a multiple of 16; max_seqs*block <= 128; max_ctx >= 0. */
+ * (of 4 for f32 matrices); vocab a multiple of 16; max_seqs*block <= 128; max_ctx >= 0 and
+ * max_ctx * head_dim * (2 for an f16 cache, else 4) < 2^31 (DFLASH_ENOTSUP past that). */
 typedef struct {
   double rope_theta; /* RoPE base (inv_freq[i] = theta^(-2i/head_dim)) */
   double eps;        /* RMSNorm epsilon, applied in f32 */
@@ -127,7 +128,9 @@ int dflash_workspace_bytes(const dflash_geometry* g, size_t* bytes);
 int dflash_create(const dflash_geometry* g, const dflash_weights* w, void* workspace, size_t bytes, void* stream,
                   dflash_ctx** out);
 
-/* Later calls enqueue on `stream` (hipStream_t; NULL = default stream). */
+/* Later calls enqueue on `stream` (hipStream_t; NULL = default stream).  A different stream first
+ * waits (on the device, through an event) for the work already enqueued on the old one, since
+ * both use the same workspace; the host does not wait. */
 int dflash_set_stream(dflash_ctx* c, void* stream);
 
 /* Add context rows (cortiq-engine dflash.rs, Drafter::push_context / queue_context /
@@ -174,7 +177,9 @@ int dflash_ctx_truncate(dflash_ctx* c, int32_t seq, int64_t pos);
 /* Empty a sequence and set its first position to 0 (dflash.rs, Drafter::reset). */
 int dflash_ctx_reset(dflash_ctx* c, int32_t seq);
 
-/* host *first, *end receive the positions a sequence holds: [first, end). */
+/* host *first, *end receive the positions a sequence holds, [first, end) (dflash.rs,
+ * Drafter::span and Drafter::next_position: end is the next position to append, waiting rows
+ * included). */
 int dflash_ctx_span(const dflash_ctx* c, int32_t seq, int64_t* first, int64_t* end);
 
 /* One block for each of n_seqs distinct sequences (dflash.rs, Drafter::block, and the head of
@@ -264,8 +269,9 @@ int dflash_read_timing(dflash_ctx* c, int32_t stage, double* total_ms, int64_t* 
  * x + r*ld, `width` entries, ld >= width) with their indices, largest first and, among equal
  * values, the earlier index first (the order the pages' top_k list keeps).  vals device
  * [rows][k] f32, idx device [rows][k] int32; vals[r][i] compares equal to the entry at
- * idx[r][i] (a -0 entry ties with +0 and comes back as +0).  1 <= k <= min(width, 64); values
- * must be finite.
+ * idx[r][i] (a -0 entry ties with +0 and comes back as +0).  1 <= k <= min(width, 64) and
+ * ceil(width / 4096) * k <= 4096 (the chunks' lists of a row fit one merge; with k = 64 width is
+ * at most 262144); values must be finite.
  * `scratch`: device memory of dflash_top_k_scratch_bytes() bytes.
  *
  * dflash_select: the draft tokens of `rows` rows from their logits (device, as for top_k; row j

@@ -521,9 +521,9 @@ static void block_one(og_model* m, int seq, int64_t anchor, int B, const float* 
 
   for (int l = 0; l < g->layers; l++) {
     const og_layer* L = &m->layers[l];
-    /* Drafter::block: the layer's context rows before the anchor, as far back as its first row
-     * sees: base = first + dropped, hi = max(min(anchor, first + len), base), lo = base, or with
-     * a window w: clamp(anchor + 1 - w, base, hi) */
+    /* the key range of this layer (cortiq-engine dflash.rs, Drafter::block): every kept row is
+     * readable from base = first + dropped; the range ends at hi = max(min(anchor, first + len),
+     * base) and starts at lo = base, or under a window w at clamp(anchor + 1 - w, base, hi) */
     const int64_t w = m->window[l], base = s->first + s->dropped[l];
     int64_t hi = anchor < s->first + s->len ? anchor : s->first + s->len;
     if (hi < base) hi = base;

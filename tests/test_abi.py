@@ -85,6 +85,19 @@ def test_too_many_rows_refused():
     assert e.value.code == D.DFLASH_ENOTSUP
 
 
+@pytest.mark.parametrize("f16", [0, 1])
+def test_cache_rows_within_32_bit_offsets(f16):
+    """Attention addresses a (sequence, kv head)'s cache rows with 32-bit byte offsets: a
+    max_ctx whose rows reach 2^31 bytes is refused, one row less is accepted."""
+    c = di.CONFIGS["small_q"].replace(kv_f16=bool(f16))
+    limit = (1 << 31) // (c.head_dim * (2 if f16 else 4))
+    g = geometry(c, limit - 1, 1)
+    assert D.dflash_workspace_bytes(g) > 0
+    with pytest.raises(D.DFlashError) as e:
+        D.dflash_workspace_bytes(geometry(c, limit, 1))
+    assert e.value.code == D.DFLASH_ENOTSUP
+
+
 def test_null_arguments_refused_before_any_gpu_work():
     L = D.lib()
     g = geometry(di.CONFIGS["tiny_f32"], 128, 1)
@@ -107,6 +120,10 @@ def test_selection_arguments_refused_before_any_gpu_work():
     assert L.dflash_top_k_scratch_bytes(2, 100, 65, C.byref(n)) == D.DFLASH_EINVAL
     assert L.dflash_top_k_scratch_bytes(2, 10, 11, C.byref(n)) == D.DFLASH_EINVAL
     assert L.dflash_top_k_scratch_bytes(2, 151936, 16, C.byref(n)) == D.DFLASH_OK and n.value > 0
+    # the chunks' lists of a row (ceil(width / 4096) * k entries) must fit one merge of 4096
+    assert L.dflash_top_k_scratch_bytes(2, 262144, 64, C.byref(n)) == D.DFLASH_OK
+    assert L.dflash_top_k_scratch_bytes(2, 262145, 64, C.byref(n)) == D.DFLASH_EINVAL
+    assert L.dflash_select_scratch_bytes(2, 262145, 64, C.byref(n)) == D.DFLASH_EINVAL
     assert L.dflash_top_k(None, 2, 100, 100, 4, None, None, None, None) == D.DFLASH_EINVAL
     assert L.dflash_select_scratch_bytes(15, 151936, 16, C.byref(n)) == D.DFLASH_OK
     # width beyond the codebooks' vocabulary, anchor outside it, rank 0: refused
