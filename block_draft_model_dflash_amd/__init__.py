@@ -23,7 +23,7 @@ EXPORTS = [
     "dflash_gemm", "dflash_group_sums", "dflash_read_kv", "dflash_time_stage", "dflash_read_timing",
     "dflash_top_k_scratch_bytes", "dflash_top_k", "dflash_select_scratch_bytes", "dflash_select",
     "dflash_set_layer_options", "dflash_ctx_dropped", "dflash_block_forward_rows", "dflash_ctx_queue",
-    "dflash_ctx_settle", "dflash_ctx_pending",
+    "dflash_ctx_settle", "dflash_ctx_pending", "dflash_top_k_noalloc",
 ]
 (DFLASH_STAGE_HEAD, DFLASH_STAGE_QKV, DFLASH_STAGE_ATTENTION, DFLASH_STAGE_O, DFLASH_STAGE_GATE_UP, DFLASH_STAGE_DOWN,
  DFLASH_STAGE_BLOCK, DFLASH_STAGE_APPEND, DFLASH_STAGE_ATTN_CHUNKS) = range(9)
@@ -98,6 +98,7 @@ def lib():
             "dflash_read_timing": (i32, [vp, i32, C.POINTER(C.c_double), C.POINTER(i64)]),
             "dflash_top_k_scratch_bytes": (i32, [i32, i32, i32, C.POINTER(sz)]),
             "dflash_top_k": (i32, [vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "dflash_top_k_noalloc": (i32, [vp, i32, i32, i32, i32, vp, vp, vp]),
             "dflash_select_scratch_bytes": (i32, [i32, i32, i32, C.POINTER(sz)]),
             "dflash_select": (i32, [vp, i32, i32, i32, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp]),
         }
@@ -264,6 +265,10 @@ def dflash_top_k_scratch_bytes(rows: int, width: int, k: int) -> int:
 
 def dflash_top_k(x: int, rows: int, width: int, ld: int, k: int, vals: int, idx: int, scratch: int, stream) -> int:
     return _check(lib().dflash_top_k(x, rows, width, ld, k, vals, idx, scratch, stream))
+
+
+def dflash_top_k_noalloc(x: int, rows: int, width: int, ld: int, k: int, vals: int, idx: int, stream) -> int:
+    return _check(lib().dflash_top_k_noalloc(x, rows, width, ld, k, vals, idx, stream))
 
 
 def dflash_select_scratch_bytes(rows: int, width: int, top: int) -> int:

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libdflash.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["pack.hip", "gemm.hip", "act.hip", "attention.hip", "select.hip", "api.hip"]
+SOURCES = ["pack.hip", "gemm.hip", "act.hip", "attention.hip", "select.hip", "api.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

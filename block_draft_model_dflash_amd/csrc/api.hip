@@ -34,6 +34,12 @@ int unit_fail(int code, const char* what, hipError_t e = hipSuccess) {
   return code;
 }
 
+}  // namespace
+
+int dfl::unit_error(int code, const char* what, hipError_t e) { return unit_fail(code, what, e); }
+
+namespace {
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int round16(int x) { return (x + 15) & ~15; }
 

@@ -166,6 +166,10 @@ hipError_t launch_select(const float* cv, const int* ci, int rows, int T, const 
 size_t select_scratch(int rows, int T);
 
 hipError_t launch_inv_freq(double theta, int hd, float* out, hipStream_t st);
+
+// Records the error of a call without a ctx (dflash_last_error(NULL) returns it) and gives back
+// `code`.
+int unit_error(int code, const char* what, hipError_t e = hipSuccess);
 hipError_t launch_quant_rows(const float* x, int rows, int cols, int8_t* q, float* d, hipStream_t st);
 hipError_t launch_transpose_scales(const float* d, int rows, int groups, int Mpad, float* dT, hipStream_t st);
 

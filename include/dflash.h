@@ -289,6 +289,15 @@ int dflash_read_timing(dflash_ctx* c, int32_t stage, double* total_ms, int64_t* 
 int dflash_top_k_scratch_bytes(int32_t rows, int32_t width, int32_t k, size_t* bytes);
 int dflash_top_k(const float* x, int32_t rows, int32_t width, int32_t ld, int32_t k, float* vals, int32_t* idx,
                  void* scratch, void* stream);
+/* dflash_top_k without caller scratch, for callers that cannot allocate device memory (code
+ * under graph capture, serving loops that forbid allocation): the same arguments, kernels and
+ * results as dflash_top_k, with the chunk lists kept in a fixed 1 MiB device array of the library
+ * (each GPU holds its own copy until the process ends; nothing is allocated per call).  Sizes
+ * with rows * ceil(width / 4096) * k > 131072 return DFLASH_EINVAL with nothing enqueued.  Every
+ * call on one GPU uses that GPU's one array: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be ordered by the caller. */
+int dflash_top_k_noalloc(const float* x, int32_t rows, int32_t width, int32_t ld, int32_t k, float* vals,
+                         int32_t* idx, void* stream);
 int dflash_select_scratch_bytes(int32_t rows, int32_t width, int32_t top, size_t* bytes);
 int dflash_select(const float* logits, int32_t rows, int32_t width, int32_t ld, const float* hp, int32_t rank,
                   const uint16_t* pred, const uint16_t* succ, int32_t vocab, int32_t top, int32_t anchor,

@@ -125,6 +125,11 @@ def test_selection_arguments_refused_before_any_gpu_work():
     assert L.dflash_top_k_scratch_bytes(2, 262145, 64, C.byref(n)) == D.DFLASH_EINVAL
     assert L.dflash_select_scratch_bytes(2, 262145, 64, C.byref(n)) == D.DFLASH_EINVAL
     assert L.dflash_top_k(None, 2, 100, 100, 4, None, None, None, None) == D.DFLASH_EINVAL
+    # the allocation-free top-k refuses sizes past its fixed array before touching the GPU
+    fake = 256  # never dereferenced
+    assert L.dflash_top_k_noalloc(fake, 128, 151936, 151936, 64, fake, fake, None) == D.DFLASH_EINVAL
+    assert "131072" in D.dflash_last_error(None)
+    assert L.dflash_top_k_noalloc(None, 2, 100, 100, 4, fake, fake, None) == D.DFLASH_EINVAL
     assert L.dflash_select_scratch_bytes(15, 151936, 16, C.byref(n)) == D.DFLASH_OK
     # width beyond the codebooks' vocabulary, anchor outside it, rank 0: refused
     fake = 256  # never dereferenced: the checks come first
