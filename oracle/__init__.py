@@ -106,11 +106,23 @@ def lib(path: str | None = None):
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
-        # at most 16 threads, whatever the host reports: on a machine whose cores are shared
-        # among several GPUs, one GPU's process gets about that many
-        L.og_set_threads(int(os.environ.get("DFLASH_ORACLE_THREADS", min(16, os.cpu_count() or 1))))
+        L.og_set_threads(default_threads())
         _lib = L
     return _lib
+
+
+def default_threads() -> int:
+    """Threads the oracle runs on: DFLASH_ORACLE_THREADS if set, else the host's CPU share for
+    this process -- OMP_NUM_THREADS where the host sets it (a machine whose cores are shared among
+    several GPUs gives one GPU's process that many), else the cores this process may run on."""
+    for var in ("DFLASH_ORACLE_THREADS", "OMP_NUM_THREADS"):
+        v = os.environ.get(var, "").strip()
+        if v.isdigit() and int(v) > 0:
+            return int(v)
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
 
 
 def set_threads(n: int) -> None:

@@ -560,12 +560,15 @@ static void block_one(og_model* m, int seq, int64_t anchor, int B, const float* 
       }
     }
     /* per kv head gi: its keys and values are the context rows then the block's rows (not
-     * causal); q head j reads kv head j / rep */
-#pragma omp parallel for schedule(dynamic) num_threads(g_threads)
+     * causal); q head j reads kv head j / rep.  The keys and values are gathered per kv head
+     * first; then every (q head, row) is one independent og_attend call (threads share them out,
+     * each call's arithmetic is unchanged) */
+    float** kks = (float**)malloc(sizeof(float*) * (size_t)kvh);
+    float** vvs = (float**)malloc(sizeof(float*) * (size_t)kvh);
+#pragma omp parallel for schedule(static) num_threads(g_threads)
     for (int gi = 0; gi < kvh; gi++) {
       float* kk = (float*)malloc(sizeof(float) * (size_t)nk * hd);
       float* vv = (float*)malloc(sizeof(float) * (size_t)nk * hd);
-      float* qq = (float*)malloc(sizeof(float) * (size_t)hd);
       for (int c = 0; c < nctx; c++) {
         size_t off = (((size_t)l * g->max_ctx + (size_t)(lo - s->first + c)) * kvh + gi) * hd;
         memcpy(kk + (size_t)c * hd, s->k + off, sizeof(float) * hd);
@@ -575,26 +578,31 @@ static void block_one(og_model* m, int seq, int64_t anchor, int B, const float* 
         memcpy(kk + (size_t)(nctx + r) * hd, k + (size_t)r * kvd + (size_t)gi * hd, sizeof(float) * hd);
         memcpy(vv + (size_t)(nctx + r) * hd, v + (size_t)r * kvd + (size_t)gi * hd, sizeof(float) * hd);
       }
-      for (int j = gi * rep; j < (gi + 1) * rep; j++)
-        for (int r = 0; r < B; r++) {
-          /* under a window, row r sees context positions from anchor + r + 1 - w on (the
-           * earlier ones are masked out); the block's own rows are all seen */
-          int64_t c0 = 0;
-          if (w > 0) {
-            int64_t from = anchor + r + 1 - w;
-            if (from < 0) from = 0;
-            c0 = from - lo;
-            if (c0 < 0) c0 = 0;
-            if (c0 > nctx) c0 = nctx;
-          }
-          memcpy(qq, q + (size_t)r * qd + (size_t)j * hd, sizeof(float) * hd);
-          og_attend(qq, 1, kk + (size_t)c0 * hd, vv + (size_t)c0 * hd, nk - (int)c0, hd, scale,
-                    y + (size_t)r * qd + (size_t)j * hd, NULL);
-        }
-      free(qq);
-      free(vv);
-      free(kk);
+      kks[gi] = kk;
+      vvs[gi] = vv;
     }
+#pragma omp parallel for schedule(dynamic) num_threads(g_threads)
+    for (int jr = 0; jr < nh * B; jr++) {
+      const int j = jr / B, r = jr % B, gi = j / rep;
+      /* under a window, row r sees context positions from anchor + r + 1 - w on (the
+       * earlier ones are masked out); the block's own rows are all seen */
+      int64_t c0 = 0;
+      if (w > 0) {
+        int64_t from = anchor + r + 1 - w;
+        if (from < 0) from = 0;
+        c0 = from - lo;
+        if (c0 < 0) c0 = 0;
+        if (c0 > nctx) c0 = nctx;
+      }
+      og_attend(q + (size_t)r * qd + (size_t)j * hd, 1, kks[gi] + (size_t)c0 * hd, vvs[gi] + (size_t)c0 * hd, nk - (int)c0, hd, scale,
+                y + (size_t)r * qd + (size_t)j * hd, NULL);
+    }
+    for (int gi = 0; gi < kvh; gi++) {
+      free(kks[gi]);
+      free(vvs[gi]);
+    }
+    free(vvs);
+    free(kks);
     mm(g->body_fmt, L->o, H, qd, y, B, o);
     if (kn) { /* the second stage on the sub-layer's output, before the residual */
       og_row_conv(o, B, H, g->conv_group, kn, 1, L->attn_base, da, xc);

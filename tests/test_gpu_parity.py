@@ -51,6 +51,33 @@ def _kv_check(cfg, om, gm, seq, rows, tol):
             assert ek <= tol and ev <= tol, (li, r0, ek, ev)
 
 
+class Pooled:
+    """Parity over every row of every block evaluated on a workload: max |dlogit| over all of
+    them against max |logit| over all of them, and the share of rows whose top-1 agrees (lowest
+    index on ties on both sides); blocks bit-identical to the oracle are counted too."""
+
+    def __init__(self, key):
+        self.key, self.diff, self.ref, self.agree, self.rows, self.blocks, self.equal = key, 0.0, 0.0, 0, 0, 0, 0
+
+    def add(self, got, ref):
+        got = np.asarray(got, np.float32).reshape(-1, got.shape[-1])
+        ref = np.asarray(ref, np.float32).reshape(-1, ref.shape[-1])
+        self.diff = max(self.diff, float(np.abs(got.astype(np.float64) - ref).max()))
+        self.ref = max(self.ref, float(np.abs(ref).max()))
+        self.agree += int((got.argmax(axis=1) == ref.argmax(axis=1)).sum())
+        self.rows += got.shape[0]
+        self.blocks += 1
+        self.equal += int(np.array_equal(got, ref))
+
+    def check(self, tol, top1_min, rows_min):
+        rel, top1 = self.diff / self.ref, self.agree / self.rows
+        say(f"{self.key}: {self.blocks} blocks, {self.rows} rows: max|d| / max|logit| {rel:.3e}, top-1 "
+            f"{self.agree}/{self.rows}, {self.equal} blocks bit-identical")
+        assert self.rows >= rows_min, (self.key, self.rows)
+        assert rel <= tol, (self.key, rel)
+        assert top1 >= top1_min, (self.key, top1)
+
+
 def _blocks(cfg, om, gm, cases, tol, top1_min):
     rels, agree = [], []
     for seqs, anchors, index in cases:
@@ -116,46 +143,87 @@ def test_append_chunking_truncate_and_empty_on_gpu():
     assert b.span(0) == (0, 300)
 
 
+def _scale_blocks(cfg, om, gm, pooled, seqs, anchors, index):
+    h = np.stack([di.make_block_input(cfg, s, index) for s in seqs])
+    got = gm.block_forward(list(seqs), list(anchors), h)
+    torch.cuda.synchronize()
+    ref = om.block_forward(list(seqs), list(anchors), h)
+    pooled.add(got.cpu().numpy(), ref)
+
+
+@pytest.mark.timeout(300)
+def test_tiny_f32_drafter_128_blocks():
+    """The tiny f32 workload as its measurement states it: context positions 0..63, 128 blocks
+    anchored at 64, each with its own anchor row.  No quantizer: held to 1e-5."""
+    cfg = TINY
+    _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64)
+    pooled = Pooled(cfg.key)
+    for i in range(128):
+        _scale_blocks(cfg, om, gm, pooled, (0,), (cfg.ctx,), i)
+    pooled.check(1e-5, 1.0, 1024)
+
+
+@pytest.mark.timeout(300)
 def test_small_quantized_drafter():
+    """The small quantized workload: 512 context rows, 64 blocks of 16 rows (1024 rows)."""
     cfg = SMALL
     _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64)
     _kv_check(cfg, om, gm, 0, [(0, 64), (448, 64)], 2e-3)
-    _blocks(cfg, om, gm, [((0,), (cfg.ctx,), i) for i in range(3)], 2e-3, 0.999)
+    pooled = Pooled(cfg.key)
+    for i in range(64):
+        _scale_blocks(cfg, om, gm, pooled, (0,), (cfg.ctx,), i)
+    pooled.check(2e-3, 0.999, 1024)
 
 
 @pytest.mark.timeout(600)
 def test_qwen3_8b_shaped_drafter():
-    """The 8B-shaped drafter at its full size: 4096 context rows, 16-row blocks, 151936 vocab."""
+    """The 8B-shaped drafter at its full size: 4096 context rows, 64 blocks of 16 rows (1024
+    rows), 151936 logits each."""
     cfg = Q8B
     _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64)
     _kv_check(cfg, om, gm, 0, [(0, 32), (2000, 16), (4064, 32)], 2e-3)
-    _blocks(cfg, om, gm, [((0,), (cfg.ctx,), i) for i in range(2)], 2e-3, 0.999)
+    pooled = Pooled(cfg.key)
+    for i in range(64):
+        _scale_blocks(cfg, om, gm, pooled, (0,), (cfg.ctx,), i)
+        if i % 16 == 15:
+            say(f"{cfg.key}: {i + 1} blocks")
+    pooled.check(2e-3, 0.999, 1024)
 
 
 @pytest.mark.timeout(900)
 def test_long_context_append_then_block():
-    """The long-context workload at its full size: a 32768-row context, then per step 16 new
+    """The long-context workload at its full size: a 32768-row context, then 64 steps of 16 new
     context rows appended and a block anchored after them (the step the benchmark times)."""
     cfg = LONG
-    _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64)
+    steps = 64
+    _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + steps * cfg.append_per_block + 64)
     _kv_check(cfg, om, gm, 0, [(0, 16), (20000, 16), (32752, 16)], 2e-3)
-    for step in range(2):
+    pooled = Pooled(cfg.key)
+    for step in range(steps):
         p = cfg.ctx + step * cfg.append_per_block
         taps = di.make_taps(cfg, 0, p, cfg.append_per_block)
         assert om.append(0, p, taps) == 0
         gm.append(0, p, taps)
-        _kv_check(cfg, om, gm, 0, [(p, cfg.append_per_block)], 2e-3)
-        _blocks(cfg, om, gm, [((0,), (p + cfg.append_per_block,), step)], 2e-3, 0.999)
+        if step % 16 == 0:
+            _kv_check(cfg, om, gm, 0, [(p, cfg.append_per_block)], 2e-3)
+        _scale_blocks(cfg, om, gm, pooled, (0,), (p + cfg.append_per_block,), step)
+        if step % 16 == 15:
+            say(f"{cfg.key}: {step + 1} steps")
+    pooled.check(2e-3, 0.999, 1024)
 
 
 @pytest.mark.timeout(900)
 def test_eight_sequences_batched():
-    """The batched workload at its full size: 8 sequences of 8192 context rows, one block of
-    16 rows each in one call (128 rows through every matrix)."""
+    """The batched workload at its full size: 8 sequences of 8192 context rows, 8 forwards of
+    one 16-row block each in one call (128 rows through every matrix; 1024 rows in all), then a
+    subset of the sequences, out of order and with other anchors."""
     cfg = BATCH
     _, om, gm = _pair(cfg, cfg.ctx, cfg.ctx + 64, n_seqs=cfg.n_seqs)
     _kv_check(cfg, om, gm, 7, [(0, 16), (8176, 16)], 2e-3)
     seqs = tuple(range(cfg.n_seqs))
-    _blocks(cfg, om, gm, [(seqs, (cfg.ctx,) * cfg.n_seqs, 0)], 2e-3, 0.999)
-    # a subset of the sequences, out of order and with different anchors
-    _blocks(cfg, om, gm, [((5, 2, 7), (cfg.ctx, cfg.ctx - 100, 4000), 1)], 2e-3, 0.999)
+    pooled = Pooled(cfg.key)
+    for i in range(8):
+        _scale_blocks(cfg, om, gm, pooled, seqs, (cfg.ctx,) * cfg.n_seqs, i)
+        say(f"{cfg.key}: {i + 1} forwards")
+    pooled.check(2e-3, 0.999, 1024)
+    _blocks(cfg, om, gm, [((5, 2, 7), (cfg.ctx, cfg.ctx - 100, 4000), 8)], 2e-3, 0.999)

@@ -37,7 +37,8 @@ MUTANTS = [
     ("attention scale dropped", "s[j] = dot * (double)scale;", "s[j] = dot;"),
     ("wrong kv head for the context", "(((size_t)l * g->max_ctx + (size_t)(lo - s->first + c)) * kvh + gi) * hd;",
      "(((size_t)l * g->max_ctx + (size_t)(lo - s->first + c)) * kvh + (kvh - 1 - gi)) * hd;"),
-    ("causal block rows", "vv + (size_t)c0 * hd, nk - (int)c0, hd, scale,", "vv + (size_t)c0 * hd, nctx - (int)c0 + r + 1, hd, scale,"),
+    ("causal block rows", "vvs[gi] + (size_t)c0 * hd, nk - (int)c0, hd, scale,",
+     "vvs[gi] + (size_t)c0 * hd, nctx - (int)c0 + r + 1, hd, scale,"),
     ("context past the anchor read", "int64_t hi = anchor < s->first + s->len ? anchor : s->first + s->len;",
      "int64_t hi = s->first + s->len;"),
     ("a row's window counted from the anchor row", "int64_t from = anchor + r + 1 - w;", "int64_t from = anchor + 1 - w;"),
