@@ -454,6 +454,297 @@ __global__ __launch_bounds__(256) void k_group_sums(const uint8_t* __restrict__ 
   }
 }
 
+// ---- products of more than 16 rows (a batch of sequences, the context append) ----
+//
+// The weights are the MFMA's A operand and the activations its B operand, so lane l of a wave
+// accumulates D[n][m] for the four n-rows 4*quarter .. +3 of its n-tile and the single
+// activation row m = l % 16 of each m-tile.  The rescale of a group then needs one activation
+// scale per lane and m-tile (the same for the lane's four n-rows) and four weight scales per
+// lane (the same for every m-tile), converted once per superblock: each term costs one int->f64
+// conversion, one product d_w * d_x and one fused multiply-add.  A workgroup serves MT m-tiles
+// (all the rows of its row group), NTW n-tiles and KW k-waves; every weight superblock is read
+// once per row group and used for all of its rows.  The activations come in chunks of KW
+// k-blocks (one for each k-wave) through two LDS buffers: while the waves multiply chunk c, the
+// loads of chunk c + 1 are in flight to registers, and they are stored to the other buffer
+// before the barrier that closes the step; the activation scales are kept in LDS as f64.
+
+// A superblock for this orientation: the lane's codes as in Super<FMT>, and the f16 scales of
+// the lane's four n-rows (rows 4*quarter .. +3 of the tile, four groups each: 32 bytes).
+template <int FMT>
+struct SuperR;
+template <>
+struct SuperR<Q4> {
+  uint4 c;
+  uint4 s0, s1;
+};
+template <>
+struct SuperR<Q8> {
+  uint4 c0, c1;
+  uint4 s0, s1;
+};
+
+__device__ __forceinline__ void super_load_r(__amdgpu_buffer_rsrc_t rs, int off, int lane, SuperR<Q4>& r) {
+  r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, off, 0));
+  const int so = SB_SCALES_Q4 + 32 * (lane >> 4);
+  r.s0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, so, off, 0));
+  r.s1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, so + 16, off, 0));
+}
+__device__ __forceinline__ void super_load_r(__amdgpu_buffer_rsrc_t rs, int off, int lane, SuperR<Q8>& r) {
+  r.c0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, off, 0));
+  r.c1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 1024 + 16 * lane, off, 0));
+  const int so = SB_SCALES_Q8 + 32 * (lane >> 4);
+  r.s0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, so, off, 0));
+  r.s1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, so + 16, off, 0));
+}
+__device__ __forceinline__ long a_operand(const SuperR<Q4>& r, int j) {
+  const uint32_t w = pick(r.c, j);
+  const uint32_t lo = (w << 4) & 0xF0F0F0F0u, hi = w & 0xF0F0F0F0u;
+  return (long)(((unsigned long)hi << 32) | lo);
+}
+__device__ __forceinline__ long a_operand(const SuperR<Q8>& r, int j) {
+  const uint4 v = j < 2 ? r.c0 : r.c1;
+  const uint32_t lo = (j & 1) ? v.z : v.x, hi = (j & 1) ? v.w : v.y;
+  return (long)(((unsigned long)hi << 32) | lo);
+}
+// the scale of n-row 4*quarter + rr, group j, as f64 (f16 scales [row][group] in s0 | s1)
+template <int FMT>
+__device__ __forceinline__ double w_scale_r(const SuperR<FMT>& r, int rr, int j) {
+  const int i = rr * 4 + j;  // 0..15
+  const uint4 v = i < 8 ? r.s0 : r.s1;
+  const uint32_t w = pick(v, (i & 7) >> 1);
+  return (double)f16_to_f32(w >> (16 * (i & 1)));
+}
+
+constexpr int ROWS_XSTR = 144;  // LDS bytes per staged row of a k-block (128 + 16: rows 36 banks apart)
+
+template <int MT, int KW>
+struct RowsChunk {
+  static constexpr int MR = MT * 16;
+  static constexpr int XBYTES = KW * MR * ROWS_XSTR;               // codes [KW][MR][144]
+  static constexpr int BYTES = XBYTES + KW * 4 * MR * 8;           // + scales [KW][4][MR] f64
+  static constexpr int PIECES = (KW * MR * 8 + 511) / 512;          // 16-byte code pieces per thread
+  static constexpr int SCALES = (KW * 4 * MR + 511) / 512;          // scales per thread
+};
+
+template <int FMT, int MT, int NTW, int KW>
+__global__ __launch_bounds__(512) void k_gemm_rows(const uint8_t* __restrict__ W, int N, int K,
+                                                  const int8_t* __restrict__ xq, const float* __restrict__ dxT,
+                                                  int RG, GemmOut o) {
+  static_assert(NTW * KW == 8, "eight waves");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  using CH = RowsChunk<MT, KW>;
+  constexpr int MR = CH::MR, NT = 512, RD = 3;  // RD: chunks of weights in flight per wave
+  constexpr int SBB = FMT == Q4 ? SB_Q4 : SB_Q8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nt = wave % NTW, kw = wave / NTW;
+  const int rg = blockIdx.x % RG, nb = blockIdx.x / RG, m0 = rg * MR;
+  const int ntile = nb * NTW + nt;
+  const bool active = ntile < (N >> 4);
+  const int KB = K >> 7, NC = (KB + KW - 1) / KW, Mpad = o.Mpad;
+  const int quarter = lane >> 4, col = lane & 15;
+
+  // activations: rows past Mpad read as zeros through the resource; a k-block past K is clamped
+  // to the last one (its weights read as zeros, so it adds exactly 0)
+  const __amdgpu_buffer_rsrc_t xr = wave_rsrc((const uint8_t*)xq, Mpad * K);
+  uint4 av[CH::PIECES];
+  float dv[CH::SCALES];
+  auto stage_load = [&](int c) {
+#pragma unroll
+    for (int b = 0; b < CH::PIECES; b++) {
+      const int i = tid + b * NT, w = i / (MR * 8), rem = i % (MR * 8), row = rem >> 3, pc = rem & 7;
+      const int kb = min(c * KW + min(w, KW - 1), KB - 1);
+      av[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, (m0 + row) * K + kb * 128 + pc * 16, 0, 0));
+    }
+#pragma unroll
+    for (int b = 0; b < CH::SCALES; b++) {
+      const int i = min(tid + b * NT, KW * 4 * MR - 1), w = i / (4 * MR), rem = i % (4 * MR), g = rem / MR, row = rem % MR;
+      const int kb = min(c * KW + w, KB - 1);
+      dv[b] = m0 + row < Mpad ? dxT[(size_t)(kb * 4 + g) * Mpad + m0 + row] : 0.f;
+    }
+  };
+  auto stage_store = [&](int buf) {
+    uint8_t* X = smem + buf * CH::BYTES;
+    double* DX = (double*)(X + CH::XBYTES);
+#pragma unroll
+    for (int b = 0; b < CH::PIECES; b++) {
+      const int i = tid + b * NT, w = i / (MR * 8), rem = i % (MR * 8), row = rem >> 3, pc = rem & 7;
+      if (i < KW * MR * 8) *(uint4*)(X + (w * MR + row) * ROWS_XSTR + pc * 16) = av[b];
+    }
+#pragma unroll
+    for (int b = 0; b < CH::SCALES; b++) {
+      const int i = tid + b * NT;
+      if (i < KW * 4 * MR) DX[i] = (double)dv[b];
+    }
+  };
+
+  // this wave's weights: one superblock per chunk (k-block c*KW + kw); past the tile: zeros
+  const uint8_t* wt = W + (size_t)(active ? ntile : 0) * KB * SBB;
+  const __amdgpu_buffer_rsrc_t rs = wave_rsrc(wt, active ? KB * SBB : 0);
+  SuperR<FMT> ring[RD];
+
+  double acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+    for (int rr = 0; rr < 4; rr++) acc[mt][rr] = 0.0;
+
+  auto compute = [&](int buf, const SuperR<FMT>& r) {
+    const uint8_t* X = smem + buf * CH::BYTES + kw * MR * ROWS_XSTR;
+    const double* DX = (const double*)(smem + buf * CH::BYTES + CH::XBYTES) + kw * 4 * MR;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const long a = a_operand(r, j);
+      double dw[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) dw[rr] = w_scale_r<FMT>(r, rr, j);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        const long b = *(const long*)(X + (mt * 16 + col) * ROWS_XSTR + 32 * j + 8 * quarter);
+        const v4i sm = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (v4i){0, 0, 0, 0}, 0, 0, 0);
+        const double dx = DX[j * MR + mt * 16 + col];
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) acc[mt][rr] = __builtin_fma((double)sm[rr], dw[rr] * dx, acc[mt][rr]);
+      }
+    }
+  };
+
+  // chunk 0's activations first (loads return in order: the store then waits for them alone),
+  // then the weights of the first RD chunks, then chunk 1's activations
+  stage_load(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int p = 0; p < RD; p++) super_load_r(rs, (p * KW + kw) * SBB, lane, ring[p]);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store(0);
+  if (NC > 1) stage_load(1);
+  __syncthreads();
+  for (int c0 = 0; c0 < NC; c0 += RD) {
+#pragma unroll
+    for (int p = 0; p < RD; p++) {
+      const int c = c0 + p;
+      if (c >= NC) break;  // uniform
+      if (active) compute(c & 1, ring[p]);
+      if (c + 1 < NC) stage_store((c + 1) & 1);
+      if (c + 2 < NC) stage_load(c + 2);
+      super_load_r(rs, ((c + RD) * KW + kw) * SBB, lane, ring[p]);
+      __syncthreads();
+    }
+  }
+
+  // the k-waves' sums through LDS, added in wave order by k-wave 0, which finishes the n-tile
+  // (slot (mt, rr): row m0 + 16*mt + col, column 16*ntile + 4*quarter + rr)
+  const bool fin = kw == 0;
+  if (KW > 1) {
+    double* red = (double*)smem;
+    if (active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) red[(((kw * NTW + nt) * MT + mt) * 4 + rr) * 64 + lane] = acc[mt][rr];
+    __syncthreads();
+    if (fin && active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+          double v = red[((nt * MT + mt) * 4 + rr) * 64 + lane];
+          for (int k = 1; k < KW; k++) v += red[(((k * NTW + nt) * MT + mt) * 4 + rr) * 64 + lane];
+          acc[mt][rr] = v;
+        }
+  }
+  const double post = FMT == Q4 ? 0.0625 : 1.0;  // Q4 codes entered the MFMA as 16*q
+  const int n0 = ntile * 16 + 4 * quarter;       // the lane's first column
+
+  if (o.epi == EPI_SWIGLU) {
+    // NTW = 4g: each group of four n-tiles gate(2b), up(2b), gate(2b+1), up(2b+1) gives the 32
+    // columns 32b.. of a = silu(gate) * up, one A8 group per row
+    constexpr int WC = NTW * 16, AC = NTW * 8;
+    __syncthreads();
+    float* G = (float*)smem;  // [MR][WC]
+    if (fin && active)
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) G[(mt * 16 + col) * WC + nt * 16 + 4 * quarter + rr] = (float)(acc[mt][rr] * post);
+    __syncthreads();
+    const int I = N >> 1;
+    for (int i = tid; i < MR * AC; i += NT) {
+      const int ml = i / AC, j = i % AC, m = m0 + ml;
+      if (m >= Mpad) break;  // whole 32-lane groups leave together (AC is a multiple of 32)
+      const int jj = j & 31;
+      const int gc = (j >> 5) * 64 + (jj >> 4) * 32 + (jj & 15);
+      const double g = G[ml * WC + gc], u = G[ml * WC + gc + 16];
+      const float av2 = (float)(g / (1.0 + exp(-g)) * u);
+      const int c = nb * AC + j;
+      if (o.xq)
+        emit_a8(av2, (size_t)m * I + c, o.xq, o.dxT, (size_t)(c >> 5) * Mpad + m, lane);
+      else
+        o.xf[(size_t)m * I + c] = av2;
+    }
+    return;
+  }
+  if (!fin || !active) return;
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) {
+    const int m = m0 + mt * 16 + col;
+    if (o.epi == EPI_F64) {
+      if (m < Mpad)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) ((double*)o.y)[(size_t)m * N + n0 + rr] = acc[mt][rr] * post;
+    } else if (o.epi == EPI_F32) {
+      if (m < o.m_store)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) ((float*)o.y)[(size_t)m * o.ld + n0 + rr] = (float)(acc[mt][rr] * post);
+    } else {  // EPI_RESID: h += f32(v), and the n-tile's share of each row's sum of squares
+      double sq = 0.0;
+      if (m < o.M) {
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+          const float hv = o.h[(size_t)m * N + n0 + rr] + (float)(acc[mt][rr] * post);
+          o.h[(size_t)m * N + n0 + rr] = hv;
+          sq += (double)hv * (double)hv;
+        }
+      }
+      sq = cross4_sum_f64(sq);  // the four quarters hold the n-tile's other columns of row m
+      if (quarter == 0 && m < Mpad) o.ssq[(size_t)m * (N >> 4) + ntile] = sq;
+    }
+  }
+}
+
+template <int FMT, int MT, int NTW, int KW>
+static hipError_t gemm_rows_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
+                                 hipStream_t st) {
+  using CH = RowsChunk<MT, KW>;
+  size_t lds = 2 * (size_t)CH::BYTES;
+  const size_t red = KW > 1 ? (size_t)KW * NTW * MT * 4 * 64 * 8 : 0;
+  const size_t swg = (size_t)CH::MR * NTW * 16 * 4;
+  if (red > lds) lds = red;
+  if (swg > lds) lds = swg;
+  if (lds > max_dynamic_lds()) return hipErrorInvalidValue;
+  const void* kern = (const void*)k_gemm_rows<FMT, MT, NTW, KW>;
+  hipError_t e = allow_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  const int RG = (o.Mpad + CH::MR - 1) / CH::MR;
+  dim3 grid((unsigned)(((N / 16 + NTW - 1) / NTW) * RG));
+  hipLaunchKernelGGL((k_gemm_rows<FMT, MT, NTW, KW>), grid, dim3(512), lds, st, (const uint8_t*)W, N, K, xq, dxT, RG,
+                     o);
+  return hipGetLastError();
+}
+
+// Shape of a product of more than 16 rows: 64 rows per workgroup (32 for up to 32 rows); four
+// n-tiles x two k-waves where there are many n-tiles (and for SwiGLU, which needs whole groups of
+// four), else two n-tiles x four k-waves so a product with few n-tiles still fills the chip.
+template <int FMT>
+static hipError_t gemm_rows_fmt(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
+                                hipStream_t st) {
+  const bool wide = o.epi == EPI_SWIGLU || N / 16 >= 2048;
+  if (o.Mpad <= 16)
+    return wide ? gemm_rows_inst<FMT, 1, 8, 1>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 1, 1, 8>(W, N, K, xq, dxT, o, st);
+  if (o.Mpad <= 32)
+    return wide ? gemm_rows_inst<FMT, 2, 4, 2>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 2, 2, 4>(W, N, K, xq, dxT, o, st);
+  return wide ? gemm_rows_inst<FMT, 4, 4, 2>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 4, 2, 4>(W, N, K, xq, dxT, o, st);
+}
+
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // rows one workgroup takes: 16 for up to 16 rows; more rows are split into groups of 16 (or 32
@@ -547,6 +838,13 @@ hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq,
   if ((o.epi == EPI_RESID || o.epi == EPI_CONV) && (!o.h || !o.ssq)) return hipErrorInvalidValue;
   if (o.epi == EPI_CONV && (!o.cd || !o.cbase || o.cB < 1 || 16 % o.cB || o.cgs < 1 || N % o.cgs || o.ckn < 1))
     return hipErrorInvalidValue;  // a block's rows within every 16-row group
+  // more than 16 rows: the row kernel (every weight superblock read once per 64 rows), unless a
+  // specific layout is asked for or the epilogue is a row convolution's
+  if ((layout < 0 && o.Mpad > 16 && o.epi != EPI_CONV) || layout == 8) {
+    if (fmt == Q4) return gemm_rows_fmt<Q4>(W, N, K, xq, dxT, o, st);
+    if (fmt == Q8) return gemm_rows_fmt<Q8>(W, N, K, xq, dxT, o, st);
+    return hipErrorInvalidValue;
+  }
   if (layout < 0) layout = gemm_layout(N, o.Mpad, o.epi);
   if (o.epi == EPI_SWIGLU && layout != 0 && layout != 3) layout = 0;  // whole groups of four n-tiles
   if (o.epi == EPI_SWIGLU && layout == 3 && N % 128) layout = 0;
