@@ -299,7 +299,8 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = wave % NTW, kw = wave / NTW;
   // blockIdx.x = n-block * RG + row group: the row groups of one n-block are neighbours in the
-  // grid, so they ask for the same weights at about the same time (one HBM read, cache hits)
+  // grid, so they ask for the same weights at about the same time (this layout runs more than
+  // one row group only for a row convolution's epilogue over more than 16 rows)
   const int rg = blockIdx.x % RG, nb = blockIdx.x / RG, m0 = rg * MR;
   const int ntile = nb * NTW + nt;
   const bool active = ntile < (N >> 4);
@@ -537,7 +538,10 @@ __global__ __launch_bounds__(512) void k_gemm_rows(const uint8_t* __restrict__ W
   constexpr int SBB = FMT == Q4 ? SB_Q4 : SB_Q8;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = wave % NTW, kw = wave / NTW;
-  const int rg = blockIdx.x % RG, nb = blockIdx.x / RG, m0 = rg * MR;
+  // workgroups go round-robin over the eight XCDs (each with its own L2): the RG row groups of
+  // an n-block get ids eight apart, so they run on one XCD and read its weights through one L2
+  const int nb = (blockIdx.x / (8 * RG)) * 8 + blockIdx.x % 8, rg = (blockIdx.x / 8) % RG, m0 = rg * MR;
+  if (nb * NTW >= (N >> 4)) return;  // the whole workgroup: padding of the last group of eight
   const int ntile = nb * NTW + nt;
   const bool active = ntile < (N >> 4);
   const int KB = K >> 7, NC = (KB + KW - 1) / KW, Mpad = o.Mpad;
@@ -725,7 +729,8 @@ static hipError_t gemm_rows_inst(const void* W, int N, int K, const int8_t* xq, 
   hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   const int RG = (o.Mpad + CH::MR - 1) / CH::MR;
-  dim3 grid((unsigned)(((N / 16 + NTW - 1) / NTW) * RG));
+  const int nblocks = (N / 16 + NTW - 1) / NTW;
+  dim3 grid((unsigned)((nblocks + 7) / 8 * 8 * RG));
   hipLaunchKernelGGL((k_gemm_rows<FMT, MT, NTW, KW>), grid, dim3(512), lds, st, (const uint8_t*)W, N, K, xq, dxT, RG,
                      o);
   return hipGetLastError();
