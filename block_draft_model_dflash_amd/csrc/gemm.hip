@@ -427,6 +427,100 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
   gemm_finish<FMT, MT, NTW, KW, CONV>(acc, hres, smem, o, N, m0, nb, ntile, active, nt, kw);
 }
 
+// 16 rows, K split over the eight waves of a workgroup (the products with few n-tiles), with
+// every wave staging only its own activations.  Wave kw uses k-blocks kw, kw + 8, ... and
+// nothing else, so the workgroup never copies all 16 x K codes into LDS behind a barrier: each
+// ring slot carries a superblock's weights together with its k-block's 16 activation rows
+// (32 bytes per lane, four lanes a row, coalesced) and their 64 scales, and the wave passes the
+// activations through its own LDS buffer into the MFMA's operand layout right before use (a
+// wave's LDS accesses take effect in order, so it needs no barrier).  The arithmetic and its
+// order are k_gemm_q's with one m-tile, one n-tile and eight k-waves: both give the same bits.
+template <int FMT>
+struct KsSlot {
+  Super<FMT> w;
+  uint4 a0, a1;  // row lane / 4, bytes 32 * (lane % 4) .. +32 of the k-block
+  float d;       // scale of group lane / 16, row lane % 16
+};
+constexpr int KS_WAVES = 8, KS_RD = 4, KS_XSTR = 144;  // deeper rings measured slower
+constexpr int KS_BUF = 16 * KS_XSTR + 64 * 4;  // a wave's LDS: 16 rows of codes, 64 scales
+template <int FMT>
+__global__ __launch_bounds__(64 * KS_WAVES) void k_gemm_ks(const uint8_t* __restrict__ W, int N, int K,
+                                                          const int8_t* __restrict__ xq,
+                                                          const float* __restrict__ dxT, GemmOut o) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int SBB = FMT == Q4 ? SB_Q4 : SB_Q8;
+  const int tid = threadIdx.x, lane = tid & 63, kw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int quarter = lane >> 4, row16 = lane & 15;
+  const int ntile = blockIdx.x;  // the grid has exactly N/16 workgroups, and Mpad is 16
+  const int KB = K >> 7;
+  uint8_t* X = smem + kw * KS_BUF;
+  float* DX = (float*)(X + 16 * KS_XSTR);
+  // superblocks past the tile read as zeros (weights and scales: every product is 0); the
+  // activations of such a slot come from the tile's last k-block, finite values
+  const __amdgpu_buffer_rsrc_t rs = wave_rsrc(W + (size_t)ntile * KB * SBB, KB * SBB);
+  const __amdgpu_buffer_rsrc_t xr = wave_rsrc((const uint8_t*)xq, 16 * K);
+  const __amdgpu_buffer_rsrc_t dr = wave_rsrc((const uint8_t*)dxT, (K >> 5) * 16 * 4);
+  const int arow = lane >> 2, apart = lane & 3;
+  auto load = [&](int kb, KsSlot<FMT>& s) {
+    const int kc = min(kb, KB - 1);
+    s.a0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, arow * K + kc * 128 + 32 * apart, 0, 0));
+    s.a1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, arow * K + kc * 128 + 32 * apart + 16, 0, 0));
+    s.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(dr, (kc * 64 + lane) * 4, 0, 0));
+    super_load(rs, kb * SBB, lane, s.w);
+  };
+  KsSlot<FMT> r[KS_RD];
+#pragma unroll
+  for (int p = 0; p < KS_RD; p++) load(kw + p * KS_WAVES, r[p]);
+  // the residual rows the epilogue adds to (needed only at the end)
+  const __amdgpu_buffer_rsrc_t hr = wave_rsrc((const uint8_t*)o.h, o.epi == EPI_RESID ? o.M * N * 4 : 0);
+  float hres[1][4];
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    hres[0][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(hr, ((4 * quarter + q) * N + ntile * 16 + row16) * 4, 0, 0));
+
+  double acc[1][4] = {{0.0, 0.0, 0.0, 0.0}};
+  constexpr int STEP = KS_RD * KS_WAVES;
+  const int turns = (KB - kw + STEP - 1) / STEP;
+  for (int t = 0; t < turns; t++) {
+#pragma unroll
+    for (int p = 0; p < KS_RD; p++) {
+      KsSlot<FMT>& s = r[p];
+      *(uint4*)(X + arow * KS_XSTR + 32 * apart) = s.a0;
+      *(uint4*)(X + arow * KS_XSTR + 32 * apart + 16) = s.a1;
+      DX[lane] = s.d;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const long b = b_operand(s.w, j);
+        const double dw = (double)w_scale<FMT>(s.w, j);
+        const long a = *(const long*)(X + row16 * KS_XSTR + 32 * j + 8 * quarter);
+        const v4i sm = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, b, (v4i){0, 0, 0, 0}, 0, 0, 0);
+        const v4f dx = *(const v4f*)(DX + 16 * j + 4 * quarter);
+        acc[0][0] = __builtin_fma((double)sm[0], dw * (double)dx[0], acc[0][0]);
+        acc[0][1] = __builtin_fma((double)sm[1], dw * (double)dx[1], acc[0][1]);
+        acc[0][2] = __builtin_fma((double)sm[2], dw * (double)dx[2], acc[0][2]);
+        acc[0][3] = __builtin_fma((double)sm[3], dw * (double)dx[3], acc[0][3]);
+      }
+      // refill the slot one ring turn ahead (past the tile: zeros, no traffic)
+      load(kw + (t + 1) * STEP + p * KS_WAVES, s);
+    }
+  }
+  gemm_finish<FMT, 1, 1, KS_WAVES, false>(acc, hres, smem, o, N, 0, ntile, ntile, true, 0, kw);
+}
+
+template <int FMT>
+static hipError_t gemm_ks_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
+                               hipStream_t st) {
+  size_t lds = (size_t)KS_WAVES * KS_BUF;
+  const size_t red = (size_t)KS_WAVES * 4 * 64 * 8;  // every k-wave's partials (after the loop)
+  if (red > lds) lds = red;
+  const void* kern = (const void*)k_gemm_ks<FMT>;
+  hipError_t e = allow_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gemm_ks<FMT>, dim3((unsigned)(N / 16)), dim3(64 * KS_WAVES), lds, st, (const uint8_t*)W, N, K,
+                     xq, dxT, o);
+  return hipGetLastError();
+}
+
 // The integer accumulators of the same tiles: sums[m][n][g] for every group (Q4 shifted back).
 template <int FMT>
 __global__ __launch_bounds__(256) void k_group_sums(const uint8_t* __restrict__ W, int N, int K,
@@ -840,6 +934,8 @@ static hipError_t gemm_mt_inst(int layout, const void* W, int N, int K, const in
   if (layout == 0) return gemm_inst<FMT, MT, 4, 2>(W, N, K, xq, dxT, o, st);
   if (layout == 2) return gemm_inst<FMT, MT, 4, 1>(W, N, K, xq, dxT, o, st);
   if (layout == 3) return gemm_inst<FMT, MT, 8, 1>(W, N, K, xq, dxT, o, st);
+  if constexpr (MT == 1)
+    if (o.Mpad == 16 && o.epi != EPI_CONV) return gemm_ks_inst<FMT>(W, N, K, xq, dxT, o, st);
   if constexpr (MT <= 2)
     return gemm_inst<FMT, MT, 1, 8>(W, N, K, xq, dxT, o, st);
   else
