@@ -441,7 +441,7 @@ struct KsSlot {
   uint4 a0, a1;  // row lane / 4, bytes 32 * (lane % 4) .. +32 of the k-block
   float d;       // scale of group lane / 16, row lane % 16
 };
-constexpr int KS_WAVES = 8, KS_RD = 4, KS_XSTR = 144;  // deeper rings measured slower
+constexpr int KS_WAVES = 8, KS_RD = 4, KS_XSTR = 144;  // 16 waves or deeper rings measured slower
 constexpr int KS_BUF = 16 * KS_XSTR + 64 * 4;  // a wave's LDS: 16 rows of codes, 64 scales
 template <int FMT>
 __global__ __launch_bounds__(64 * KS_WAVES) void k_gemm_ks(const uint8_t* __restrict__ W, int N, int K,
