@@ -280,6 +280,19 @@ class Leg:
         D.dflash_time_stage(ctx, -1)
         return head, attn
 
+    def event_pair_ms(self, n=50):
+        """Median of n empty event pairs on the step's stream: what a pair adds to the kernel it
+        brackets (the dispatch of the kernel and the two markers), beside a trace's durations."""
+        import numpy as np
+
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        return round(float(np.median([a.elapsed_time(b) for a, b in ev])), 5)
+
     def stages(self):
         import block_draft_model_dflash_amd as D
 
@@ -330,6 +343,7 @@ class Leg:
         """The head's product (HBM) and the attention chunk kernel (its f32 K/V bytes; the f64
         matrix rate beside) per launch, from the event pairs."""
         cfg, K = self.cfg, self.K
+        pair = self.event_pair_ms()
         (head_ms, head_n), (attn_ms, attn_n) = head, attn
         hb = head_bytes(cfg)
         head_avg = head_ms / max(head_n, 1)
@@ -338,7 +352,8 @@ class Leg:
                      "frac": round(head_gbs / HBM_PEAK_GBS, 4),
                      "traffic": profile_value(f"head_gemm_{cfg.key}_pmc", "traffic_bytes_per_launch", ["gemm.hip"]),
                      "kernel": "k_gemm_q (head logits, Q8_32 x A8_32)", "bytes_per_launch": hb,
-                     "avg_launch_ms": round(head_avg, 5), "launches": head_n, "ms_per_step": round(head_ms / K, 5)}
+                     "avg_launch_ms": round(head_avg, 5), "empty_event_pair_ms": pair, "launches": head_n,
+                     "ms_per_step": round(head_ms / K, 5)}
         ctxs = [self.ctx_rows(i) for i in range(K)]
         kv = sum(attention_kv_bytes(cfg, n) for n in ctxs) * cfg.layers
         flops = sum(attention_flops(cfg, n) for n in ctxs) * cfg.layers
@@ -351,7 +366,7 @@ class Leg:
                                               ["attention.hip"]),
                      "kernel": "k_attn_partial (context keys: f64 scores, online softmax, f64 values)",
                      "bytes_per_launch": round(kv / max(attn_n, 1)), "avg_launch_ms": round(attn_avg, 5),
-                     "launches": attn_n, "ms_per_step": round(attn_ms / K, 5),
+                     "empty_event_pair_ms": pair, "launches": attn_n, "ms_per_step": round(attn_ms / K, 5),
                      "f64_mfma": {"achieved_TFLOPs": round(attn_tf, 2), "peak_TFLOPs": F64_MFMA_PEAK_TFS,
                                   "frac": round(attn_tf / F64_MFMA_PEAK_TFS, 4),
                                   "flops_per_launch": round(flops / max(attn_n, 1))}}
