@@ -64,6 +64,20 @@ def attention_kv_bytes(cfg, nctx: int) -> int:
     return cfg.n_seqs * nctx * 2 * cfg.kv_dim * 4
 
 
+def attention_digit_bytes(cfg, nctx: int) -> int:
+    """Bytes one layer's digit-scored attention launch reads: per context row and kv head the
+    key's seven int8 digit planes (7 x head_dim), its exponent (4) and the value row (f32, or
+    f16 for an f16 cache)."""
+    v = cfg.head_dim * (2 if cfg.kv_f16 else 4)
+    return cfg.n_seqs * nctx * cfg.kv_heads * (7 * cfg.head_dim + 4 + v)
+
+
+def attention_digit_ops(cfg, nctx: int) -> int:
+    """int8 operations of one layer's digit-scored launch: per q head, block row and context
+    key the 28 digit pairs whose weights reach 128^-6, each a head_dim-long product."""
+    return 2 * 28 * cfg.n_seqs * cfg.block * cfg.heads * nctx * cfg.head_dim
+
+
 def prefill_bytes(cfg) -> int:
     """Bytes the prefill of every sequence's context must move: the FC and all layers' Wk|Wv in
     their stored formats once, the tapped rows read (f32), the K/V rows written (f32)."""
@@ -340,8 +354,11 @@ class Leg:
         }
 
     def kernel_lines(self, head, attn):
-        """The head's product (HBM) and the attention chunk kernel (its f32 K/V bytes; the f64
-        matrix rate beside) per launch, from the event pairs."""
+        """The head's product (HBM) and the attention chunk kernel per launch, from the event
+        pairs: for f64 scores its f32 K/V bytes with the f64 matrix rate beside; for digit scores
+        the key digits and values it reads with the int8 and f64 matrix rates beside."""
+        import block_draft_model_dflash_amd as D
+
         cfg, K = self.cfg, self.K
         pair = self.event_pair_ms()
         (head_ms, head_n), (attn_ms, attn_n) = head, attn
@@ -355,21 +372,35 @@ class Leg:
                      "avg_launch_ms": round(head_avg, 5), "empty_event_pair_ms": pair, "launches": head_n,
                      "ms_per_step": round(head_ms / K, 5)}
         ctxs = [self.ctx_rows(i) for i in range(K)]
-        kv = sum(attention_kv_bytes(cfg, n) for n in ctxs) * cfg.layers
-        flops = sum(attention_flops(cfg, n) for n in ctxs) * cfg.layers
-        attn_avg = attn_ms / max(attn_n, 1)
-        attn_gbs = kv / max(attn_n, 1) / (attn_avg * 1e-3) / 1e9
-        attn_tf = flops / max(attn_n, 1) / (attn_avg * 1e-3) / 1e12
+        digits = self.gm.last_scores() == D.DFLASH_SCORES_DIGITS
+        n = max(attn_n, 1)
+        attn_avg = attn_ms / n
+        if digits:  # the kernel reads key digits and values; int8 scores, f64 value products
+            kv = sum(attention_digit_bytes(cfg, c) for c in ctxs) * cfg.layers
+            ops = sum(attention_digit_ops(cfg, c) for c in ctxs) * cfg.layers
+            pv = sum(2 * cfg.n_seqs * cfg.block * cfg.heads * c * cfg.head_dim for c in ctxs) * cfg.layers
+            i8_tops = ops / n / (attn_avg * 1e-3) / 1e12
+            pv_tf = pv / n / (attn_avg * 1e-3) / 1e12
+            name = "k_attn_gqa_dig (context keys: int8 digit-split scores, online softmax, f64 values)"
+            extra = {"i8_mfma": {"achieved_TOPs": round(i8_tops, 1), "peak_TOPs": I8_MFMA_PEAK_OPS / 1e12,
+                                 "frac": round(i8_tops * 1e12 / I8_MFMA_PEAK_OPS, 4), "ops_per_launch": round(ops / n)},
+                     "f64_mfma": {"achieved_TFLOPs": round(pv_tf, 2), "peak_TFLOPs": F64_MFMA_PEAK_TFS,
+                                  "frac": round(pv_tf / F64_MFMA_PEAK_TFS, 4), "flops_per_launch": round(pv / n)}}
+        else:
+            kv = sum(attention_kv_bytes(cfg, c) for c in ctxs) * cfg.layers
+            flops = sum(attention_flops(cfg, c) for c in ctxs) * cfg.layers
+            attn_tf = flops / n / (attn_avg * 1e-3) / 1e12
+            name = "k_attn_partial (context keys: f64 scores, online softmax, f64 values)"
+            extra = {"f64_mfma": {"achieved_TFLOPs": round(attn_tf, 2), "peak_TFLOPs": F64_MFMA_PEAK_TFS,
+                                  "frac": round(attn_tf / F64_MFMA_PEAK_TFS, 4), "flops_per_launch": round(flops / n)}}
+        attn_gbs = kv / n / (attn_avg * 1e-3) / 1e9
         attn_line = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": profile_value(f"attn_chunks_{cfg.key}_pmc", "traffic_bytes_per_launch",
                                               ["attention.hip"]),
-                     "kernel": "k_attn_partial (context keys: f64 scores, online softmax, f64 values)",
-                     "bytes_per_launch": round(kv / max(attn_n, 1)), "avg_launch_ms": round(attn_avg, 5),
+                     "kernel": name, "bytes_per_launch": round(kv / n), "avg_launch_ms": round(attn_avg, 5),
                      "empty_event_pair_ms": pair, "launches": attn_n, "ms_per_step": round(attn_ms / K, 5),
-                     "f64_mfma": {"achieved_TFLOPs": round(attn_tf, 2), "peak_TFLOPs": F64_MFMA_PEAK_TFS,
-                                  "frac": round(attn_tf / F64_MFMA_PEAK_TFS, 4),
-                                  "flops_per_launch": round(flops / max(attn_n, 1))}}
+                     **extra}
         return (attn_line, head_line) if attn_ms > head_ms else (head_line, attn_line)
 
     def close(self):

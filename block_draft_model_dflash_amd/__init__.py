@@ -23,8 +23,10 @@ EXPORTS = [
     "dflash_gemm", "dflash_group_sums", "dflash_read_kv", "dflash_time_stage", "dflash_read_timing",
     "dflash_top_k_scratch_bytes", "dflash_top_k", "dflash_select_scratch_bytes", "dflash_select",
     "dflash_set_layer_options", "dflash_ctx_dropped", "dflash_block_forward_rows", "dflash_ctx_queue",
-    "dflash_ctx_settle", "dflash_ctx_pending", "dflash_top_k_noalloc",
+    "dflash_ctx_settle", "dflash_ctx_pending", "dflash_top_k_noalloc", "dflash_set_score_mode",
+    "dflash_last_scores",
 ]
+DFLASH_SCORES_AUTO, DFLASH_SCORES_F64, DFLASH_SCORES_DIGITS = 0, 1, 2
 (DFLASH_STAGE_HEAD, DFLASH_STAGE_QKV, DFLASH_STAGE_ATTENTION, DFLASH_STAGE_O, DFLASH_STAGE_GATE_UP, DFLASH_STAGE_DOWN,
  DFLASH_STAGE_BLOCK, DFLASH_STAGE_APPEND, DFLASH_STAGE_ATTN_CHUNKS) = range(9)
 
@@ -83,6 +85,8 @@ def lib():
             "dflash_block_forward": (i32, [vp, i32, vp, vp, vp, vp]),
             "dflash_block_forward_rows": (i32, [vp, i32, vp, vp, vp, i32, i32, vp]),
             "dflash_set_layer_options": (i32, [vp, vp, vp]),
+            "dflash_set_score_mode": (i32, [vp, i32]),
+            "dflash_last_scores": (i32, [vp, C.POINTER(C.c_int32)]),
             "dflash_ctx_dropped": (i32, [vp, i32, i32, C.POINTER(i64)]),
             "dflash_block_hidden": (i32, [vp, i32, vp, vp, vp, vp]),
             "dflash_last_error": (C.c_char_p, [vp]),
@@ -192,6 +196,18 @@ def dflash_set_layer_options(ctx, windows=None, rotary=None) -> int:
     r = None if rotary is None else (C.c_int32 * len(rotary))(*[int(x) for x in rotary])
     return _check(lib().dflash_set_layer_options(ctx, None if w is None else C.cast(w, C.c_void_p),
                                                  None if r is None else C.cast(r, C.c_void_p)), ctx)
+
+
+def dflash_set_score_mode(ctx, mode: int) -> int:
+    """DFLASH_SCORES_AUTO, DFLASH_SCORES_F64 or DFLASH_SCORES_DIGITS (include/dflash.h)."""
+    return _check(lib().dflash_set_score_mode(ctx, int(mode)), ctx)
+
+
+def dflash_last_scores(ctx) -> int:
+    """What the last block call scored with: DFLASH_SCORES_F64 or _DIGITS (_AUTO before one)."""
+    m = C.c_int32()
+    _check(lib().dflash_last_scores(ctx, C.byref(m)), ctx)
+    return m.value
 
 
 def dflash_ctx_dropped(ctx, seq: int, layer: int) -> int:

@@ -13,6 +13,7 @@
 // rounded f32 of its step; the f32 steps the pages fix (the RMSNorm scale and products, the
 // RoPE angle, the quantizer) are done in f32 exactly as written.
 #include "common.h"
+#include "digits.h"
 #include "lanes.h"
 #include "head.h"
 
@@ -393,7 +394,8 @@ __global__ __launch_bounds__(64) void k_qkv_epilogue(const double* __restrict__ 
                                                     const float* __restrict__ k_norm,
                                                     const float* __restrict__ inv_freq, float eps, int rope,
                                                     float* __restrict__ q, float* __restrict__ k,
-                                                    float* __restrict__ v) {
+                                                    float* __restrict__ v, int8_t* __restrict__ qd,
+                                                    int* __restrict__ qe) {
   const int head = blockIdx.x, m = blockIdx.y, lane = threadIdx.x, half = hd >> 1;
   const size_t N = (size_t)(nh + 2 * kvh) * hd;
   const size_t col = (size_t)head * hd + lane;
@@ -409,6 +411,20 @@ __global__ __launch_bounds__(64) void k_qkv_epilogue(const double* __restrict__ 
   const bool isq = head < nh;
   float o0 = 0.f, o1 = 0.f;
   head_norm_rope(x0, x1, lane, hd, isq ? q_norm : k_norm, eps, inv_freq, pos, rope != 0, o0, o1);
+  if (qd && isq) {  // head_dim 128: lane l holds dims l and l + 64
+    const int E = dig_exponent(wave_max_f32(fmaxf(fabsf(o0), fabsf(o1))));
+    int d0[DIG_T], d1[DIG_T];
+    dig_split(o0, E, d0);
+    dig_split(o1, E, d1);
+    const size_t r = (size_t)m * nh + head;
+    int8_t* row = qd + r * DIG_ROW;
+#pragma unroll
+    for (int t = 0; t < DIG_T; t++) {
+      row[t * 128 + lane] = (int8_t)d0[t];
+      row[t * 128 + 64 + lane] = (int8_t)d1[t];
+    }
+    if (lane == 0) qe[r] = E;
+  }
   if (!on) return;
   float* dst = isq ? q + ((size_t)m * nh + head) * hd : k + ((size_t)m * kvh + (head - nh)) * hd;
   dst[lane] = o0;
@@ -417,10 +433,10 @@ __global__ __launch_bounds__(64) void k_qkv_epilogue(const double* __restrict__ 
 
 hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
                                int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
-                               bool rope, float* q, float* k, float* v, hipStream_t st) {
-  if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
+                               bool rope, float* q, float* k, float* v, int8_t* qd, int* qe, hipStream_t st) {
+  if (hd > 128 || hd % 2 || S > MAX_SLICES || (qd && (hd != 128 || !qe))) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_qkv_epilogue, dim3(nh + 2 * kvh, M), dim3(64), 0, st, part, S, Mpad, B, si, nh, kvh, hd,
-                     q_norm, k_norm, inv_freq, eps, (int)rope, q, k, v);
+                     q_norm, k_norm, inv_freq, eps, (int)rope, q, k, v, qd, qe);
   return hipGetLastError();
 }
 
@@ -433,7 +449,8 @@ __global__ __launch_bounds__(64) void k_kv_append(const double* __restrict__ par
                                                  const float* __restrict__ inv_freq, float eps,
                                                  unsigned long long rot_mask, long long pos0, int row0, int slot,
                                                  int max_seqs, int max_ctx, CT* __restrict__ kc,
-                                                 CT* __restrict__ vc) {
+                                                 CT* __restrict__ vc, int8_t* __restrict__ kd,
+                                                 int* __restrict__ ke) {
   const int unit = blockIdx.x, i = blockIdx.y, lane = threadIdx.x, half = hd >> 1;
   const int l = unit / (2 * kvh), rem = unit % (2 * kvh), kind = rem / kvh, h = rem % kvh;
   const size_t kvd = (size_t)kvh * hd, N = (size_t)layers * 2 * kvd;
@@ -449,6 +466,21 @@ __global__ __launch_bounds__(64) void k_kv_append(const double* __restrict__ par
   float o0 = 0.f, o1 = 0.f;
   const bool rope = l >= 64 || ((rot_mask >> l) & 1ull);
   head_norm_rope(x0, x1, lane, hd, k_norms + (size_t)l * hd, eps, inv_freq, pos0 + i, rope, o0, o1);
+  if (kd) {  // head_dim 128: lane l holds dims l and l + 64; the digits of the values stored
+    const float v0 = (float)(CT)o0, v1 = (float)(CT)o1;
+    const int E = dig_exponent(wave_max_f32(fmaxf(fabsf(v0), fabsf(v1))));
+    int d0[DIG_T], d1[DIG_T];
+    dig_split(v0, E, d0);
+    dig_split(v1, E, d1);
+    const size_t r = (((size_t)l * max_seqs + slot) * kvh + h) * max_ctx + (size_t)(row0 + i);
+    int8_t* row = kd + r * DIG_ROW;
+#pragma unroll
+    for (int t = 0; t < DIG_T; t++) {
+      row[t * 128 + lane] = (int8_t)d0[t];
+      row[t * 128 + 64 + lane] = (int8_t)d1[t];
+    }
+    if (lane == 0) ke[r] = E;
+  }
   if (!on) return;
   kc[dst + lane] = (CT)o0;
   kc[dst + lane + half] = (CT)o1;
@@ -457,15 +489,16 @@ __global__ __launch_bounds__(64) void k_kv_append(const double* __restrict__ par
 hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
                             const float* k_norms, const float* inv_freq, float eps, unsigned long long rot_mask,
                             long long pos0, int row0, int slot, int max_seqs, int max_ctx, bool f16, void* kc,
-                            void* vc, hipStream_t st) {
-  if (hd > 128 || hd % 2 || S > MAX_SLICES) return hipErrorInvalidValue;
+                            void* vc, int8_t* kd, int* ke, hipStream_t st) {
+  if (hd > 128 || hd % 2 || S > MAX_SLICES || (kd && (hd != 128 || !ke))) return hipErrorInvalidValue;
   if (f16)
     hipLaunchKernelGGL(k_kv_append<_Float16>, dim3(layers * 2 * kvh, n), dim3(64), 0, st, part, S, Mpad, layers, kvh,
                        hd, k_norms, inv_freq, eps, rot_mask, pos0, row0, slot, max_seqs, max_ctx, (_Float16*)kc,
-                       (_Float16*)vc);
+                       (_Float16*)vc, kd, ke);
   else
     hipLaunchKernelGGL(k_kv_append<float>, dim3(layers * 2 * kvh, n), dim3(64), 0, st, part, S, Mpad, layers, kvh, hd,
-                       k_norms, inv_freq, eps, rot_mask, pos0, row0, slot, max_seqs, max_ctx, (float*)kc, (float*)vc);
+                       k_norms, inv_freq, eps, rot_mask, pos0, row0, slot, max_seqs, max_ctx, (float*)kc, (float*)vc,
+                       kd, ke);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@
 
 #include "../../include/dflash.h"
 #include "common.h"
+#include "digits.h"
 
 using namespace dfl;
 
@@ -48,6 +49,9 @@ struct Layout {
   std::vector<size_t> qkv, o, gu, down;
   size_t hidden_norm, norm, in_norm, post_norm, q_norm, k_norm, inv_freq;
   size_t kc, vc;
+  // integer scores (head_dim 128, four q heads per kv head): the keys' int8 digits and row
+  // exponents beside the cache, the block queries' beside q (digits.h)
+  size_t kd = 0, ke = 0, qd = 0, qe = 0;
   size_t h, xq, dxT, xq2, dxT2, xf, q, kb, vb, part, ssq, apart, aml;
   size_t act_begin, total;
   size_t part_floats;
@@ -97,6 +101,8 @@ int check_geometry(const dflash_geometry* g, std::string* err) {
   // 32-bit byte offsets
   if ((size_t)g->max_ctx * g->head_dim * (g->kv_f16 ? 2 : 4) >= ((size_t)1 << 31))
     return fail(DFLASH_ENOTSUP, "max_ctx * head_dim * element bytes must stay below 2^31");
+  if (attn_digit_scores(g->heads, g->kv_heads, g->head_dim) && (size_t)g->max_ctx * DIG_ROW >= ((size_t)1 << 31))
+    return fail(DFLASH_ENOTSUP, "max_ctx * 896 digit bytes must stay below 2^31");  // the keys' digit rows
   if (g->pending_rows < 0) return fail(DFLASH_EINVAL, "negative pending_rows");
   if (g->conv_kernel < 0) return fail(DFLASH_EINVAL, "negative conv_kernel");
   if (g->conv_kernel > 0) {
@@ -159,6 +165,12 @@ void plan(const dflash_geometry* g, Layout* L) {
   const size_t cache = (size_t)NL * g->max_seqs * kvh * (size_t)g->max_ctx * hd * (g->kv_f16 ? 2 : 4);
   L->kc = take(cache);
   L->vc = take(cache);
+  const bool digits = attn_digit_scores((int)g->heads, (int)kvh, (int)hd);
+  if (digits) {
+    const size_t rows = (size_t)NL * g->max_seqs * kvh * (size_t)g->max_ctx;
+    L->kd = take(rows * DIG_ROW);
+    L->ke = take(rows * 4);
+  }
   if (g->pending_rows > 0) L->pend = take((size_t)g->max_seqs * g->pending_rows * T * 4);
   L->act_begin = off;
   long Kmax = H;
@@ -170,6 +182,10 @@ void plan(const dflash_geometry* g, Layout* L) {
   L->dxT = take((size_t)(Kmax / 32) * MROWS * 4);
   L->xf = take((size_t)MROWS * Kmax * 4);
   L->q = take((size_t)MROWS * qd * 4);
+  if (digits) {
+    L->qd = take((size_t)MROWS * g->heads * DIG_ROW);
+    L->qe = take((size_t)MROWS * g->heads * 4);
+  }
   L->kb = take((size_t)MROWS * kvd * 4);
   L->vb = take((size_t)MROWS * kvd * 4);
   // the second activation buffer: SwiGLU's output, read by down while gate|up's input stays put
@@ -211,6 +227,8 @@ struct dflash_ctx {
   std::vector<int32_t> window, rotary;
   std::vector<int64_t> dropped;  // [max_seqs][layers]
   unsigned long long rot_mask = ~0ull;  // bit l: layer l rotates (layers >= 64 always do)
+  int score_mode = DFLASH_SCORES_AUTO;
+  int last_scores = DFLASH_SCORES_AUTO;  // what the last block call scored with
   int64_t& drop(int seq, int l) { return dropped[(size_t)seq * g.layers + l]; }
   // Drafter::truncate: a layer's dropped rows are clipped to what a sequence keeps
   void keep_rows(int seq, int64_t keep) {
@@ -399,8 +417,18 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
   as.scale = powf((float)hd, -0.5f);  // dflash.rs, Drafter::block: (hd as f32).powf(-0.5)
   as.kv_f16 = g.kv_f16;
   // about one workgroup per CU: n_seqs * q heads * chunks ~ 256 (a workgroup serves one q head
-  // of one chunk), chunks a multiple of 32 keys; per layer, as its windows give it keys
-  int nch_target = (256 + n_seqs * nh - 1) / (n_seqs * nh);
+  // of one chunk), chunks a multiple of 32 keys; per layer, as its windows give it keys.  The
+  // integer-score kernel serves a kv head's four q heads with four waves: two workgroups a CU,
+  // n_seqs * kv heads * chunks ~ 512
+  long call_rows = 0;  // context rows of the call, over its sequences (windows aside)
+  for (int i = 0; i < n_seqs; i++) {
+    const int64_t f = c->first[seqs[i]], hi = std::min<int64_t>(anchors[i], f + c->len[seqs[i]]);
+    call_rows += (long)std::max<int64_t>(0, hi - f);
+  }
+  const bool dig = L.kd != 0 && (c->score_mode == DFLASH_SCORES_DIGITS ||
+                                 (c->score_mode == DFLASH_SCORES_AUTO && call_rows >= DIG_AUTO_ROWS));
+  c->last_scores = dig ? DFLASH_SCORES_DIGITS : DFLASH_SCORES_F64;
+  int nch_target = dig ? (512 + n_seqs * kvh - 1) / (n_seqs * kvh) : (256 + n_seqs * nh - 1) / (n_seqs * nh);
   if (nch_target > MAXCH) nch_target = MAXCH;
   auto chunk_keys = [&]() {
     int nmax = 0;
@@ -446,6 +474,7 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
           "in-norm");
   // bytes of one layer's cache
   const size_t layer_cache = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx * hd * (g.kv_f16 ? 2 : 4);
+  const size_t layer_rows = (size_t)g.max_seqs * kvh * (size_t)g.max_ctx;  // key rows of a layer's digits
   for (int l = 0; l < NL; l++) {
     int rc;
     float* da = kn ? c->at<float>(L.da) : nullptr;
@@ -468,18 +497,22 @@ int block_common(dflash_ctx* c, int32_t n_seqs, const int32_t* seqs, const int64
             launch_qkv_epilogue(part, 1, Mpad, M, B, si, nh, kvh, hd, c->at<float>(L.q_norm) + (size_t)l * hd,
                                 c->at<float>(L.k_norm) + (size_t)l * hd, c->at<float>(L.inv_freq), eps,
                                 c->rotary[l] != 0, c->at<float>(L.q), c->at<float>(L.kb), c->at<float>(L.vb),
-                                c->st),
+                                dig ? c->at<int8_t>(L.qd) : nullptr, dig ? c->at<int>(L.qe) : nullptr, c->st),
             "q/k norm + rope");
     layer_ranges(c, l, seqs, anchors, si);
     as.ck = chunk_keys();
+    DigitRows digs{};
+    if (dig)
+      digs = DigitRows{c->at<int8_t>(L.qd), c->at<int>(L.qe), c->at<int8_t>(L.kd) + (size_t)l * layer_rows * DIG_ROW,
+                       c->at<int>(L.ke) + (size_t)l * layer_rows};
     {
       StageTimer t(c, DFLASH_STAGE_ATTENTION);
       {
         StageTimer tc(c, DFLASH_STAGE_ATTN_CHUNKS);
         TRY_HIP(c,
                 launch_attention_chunks(as, si, c->at<float>(L.q), c->ws + L.kc + (size_t)l * layer_cache,
-                                        c->ws + L.vc + (size_t)l * layer_cache, c->at<double>(L.apart),
-                                        c->at<double>(L.aml), c->st),
+                                        c->ws + L.vc + (size_t)l * layer_cache, dig ? &digs : nullptr,
+                                        c->at<double>(L.apart), c->at<double>(L.aml), c->st),
                 "attention chunks");
       }
       TRY_HIP(c,
@@ -802,7 +835,8 @@ int settle_rows(dflash_ctx* c, int seq, const float* taps, int n) {
     TRY_HIP(c,
             launch_kv_append(part, 1, Mpad, nn, NL, g.kv_heads, g.head_dim, c->at<float>(L.k_norm),
                              c->at<float>(L.inv_freq), eps, c->rot_mask, pos + c0, row + c0, seq, g.max_seqs,
-                             g.max_ctx, g.kv_f16 != 0, c->ws + L.kc, c->ws + L.vc, c->st),
+                             g.max_ctx, g.kv_f16 != 0, c->ws + L.kc, c->ws + L.vc,
+                             L.kd ? c->at<int8_t>(L.kd) : nullptr, L.ke ? c->at<int>(L.ke) : nullptr, c->st),
             "k/v into the cache");
   }
   c->len[seq] += n;
@@ -965,6 +999,22 @@ int dflash_set_layer_options(dflash_ctx* c, const int32_t* windows, const int32_
   }
   c->rot_mask = mask;
   std::fill(c->dropped.begin(), c->dropped.end(), 0);
+  return DFLASH_OK;
+}
+
+int dflash_set_score_mode(dflash_ctx* c, int32_t mode) {
+  if (!c) return DFLASH_EINVAL;
+  if (mode != DFLASH_SCORES_AUTO && mode != DFLASH_SCORES_F64 && mode != DFLASH_SCORES_DIGITS)
+    return c->fail(DFLASH_EINVAL, "score mode %d", mode);
+  if (mode == DFLASH_SCORES_DIGITS && !c->lay.kd)
+    return c->fail(DFLASH_EINVAL, "digit scores need head_dim 128 and four q heads per kv head");
+  c->score_mode = mode;
+  return DFLASH_OK;
+}
+
+int dflash_last_scores(const dflash_ctx* c, int32_t* mode) {
+  if (!c || !mode) return DFLASH_EINVAL;
+  *mode = c->last_scores;
   return DFLASH_OK;
 }
 

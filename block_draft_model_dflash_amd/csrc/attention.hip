@@ -31,6 +31,7 @@
 // ulp off flips codes that the following layers amplify, so it has to be the correctly rounded
 // result that any exact evaluation gives.
 #include "common.h"
+#include "digits.h"
 #include "lanes.h"
 
 namespace dfl {
@@ -246,6 +247,213 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
   }
 }
 
+// ---- the chunk partials with integer scores (head_dim 128, four q heads per kv head) ----
+//
+// The scores come from exact int8 digit splits (digits.h) of the queries (written by the q/k
+// epilogue) and of the keys (written beside the cache by the append): q . k is 2^(Eq+Ek) *
+// 128^-2 * sum_d 128^-d S_d over the diagonals d <= 6, each S_d an exact int32 sum of the digit
+// pairs t + u = d, two v_mfma_i32_16x16x64_i8 per pair; the seven diagonals are combined in f64
+// and scaled by hd^-0.5.  The softmax and the values stay f64, as in k_attn_partial, and the
+// partials and their layout are the same, so the merge reads either.
+//
+// A workgroup serves one (sequence, kv head, chunk) with one wave per q head of the kv head, so
+// each 16-key tile is read once for four heads: the key digits go from memory straight into LDS
+// (buffer loads to LDS; 14 blocks of 1 KB, block 2u + hh holding plane u, dims 64hh + 16*quarter
+// .. +16 of key col at lane position 16*quarter + col, the A operand's layout), the values are
+// converted to f64 into LDS once, and the key exponents are kept there too.  The tiles are
+// double-buffered: tile i + 1 lands while tile i is computed, and tile i + 2 is requested after
+// the barrier that ends tile i.  A wave keeps its head's query digits in registers (the B
+// operand) and runs every tile of the chunk, so its (max, sum, acc) is the chunk's partial.
+constexpr int GQ_REP = 4, GQ_THREADS = 64 * GQ_REP;
+constexpr int GQ_KD = 2 * DIG_T * 1024;           // one tile's key digits
+constexpr int GQ_VS = 128 + 4;                    // LDS row of a value row, in doubles
+constexpr int GQ_VB = 16 * GQ_VS * 8;             // one tile's values, bytes
+constexpr int GQ_TILES = 2 * (GQ_KD + GQ_VB + 64);  // two buffers of digits, values, exponents
+constexpr int GQ_STAGE = GQ_REP * 16 * 129 * 8;   // the partials' staging after the loop
+constexpr size_t GQ_LDS = GQ_TILES > GQ_STAGE ? GQ_TILES : GQ_STAGE;
+
+template <typename CT, bool WIN>
+__global__ __launch_bounds__(GQ_THREADS, 2) void k_attn_gqa_dig(AttnShape a, SeqInfo si, int maxn,
+                                                                const int8_t* __restrict__ qd,
+                                                                const int* __restrict__ qe,
+                                                                const CT* __restrict__ vc,
+                                                                const int8_t* __restrict__ kd,
+                                                                const int* __restrict__ ke,
+                                                                double* __restrict__ part, double* __restrict__ ml) {
+  constexpr int HD = 128, NI = HD / 16, ND = HD / 64;
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int task = blockIdx.x;
+  if (task >= si.n * a.kvh * maxn) return;
+  const int s = task / (a.kvh * maxn), g = (task / maxn) % a.kvh, c = task % maxn;
+  const int nctx = si.nctx[s];
+  if (c >= attn_chunks(nctx, a.ck)) return;  // the whole workgroup: this sequence has fewer chunks
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int quarter = lane >> 4, col = lane & 15;
+  const int j = g * GQ_REP + w;
+  const int k0 = c * a.ck, kend = min(nctx, k0 + a.ck);
+  const int nt = (kend - k0 + 15) / 16;  // >= 1: every launched chunk holds context rows
+  const size_t row0 = ((size_t)si.slot[s] * a.kvh + g) * a.max_ctx + si.ctx0[s];
+  const CT* Vctx = vc + row0 * HD;
+  const int kmin = si.mask0[s] + col;  // a window: query row col sees keys from here on
+
+  // this head's query digits (rows past B: a copy of the last, whose results are not kept)
+  v4i qdr[DIG_T][2];
+  int eq;
+  {
+    const int rr = min(col, a.B - 1);
+    const size_t qrow = (size_t)(s * a.B + rr) * a.nh + j;
+    const int8_t* qp = qd + qrow * DIG_ROW + 16 * quarter;
+#pragma unroll
+    for (int t = 0; t < DIG_T; t++)
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) qdr[t][hh] = *(const v4i*)(qp + t * 128 + 64 * hh);
+    eq = qe[qrow];
+  }
+
+  // tile buffers: [2][digits GQ_KD | values GQ_VB | exponents 16 ints]
+  auto kbuf = [&](int b) { return lds + b * (GQ_KD + GQ_VB + 64); };
+  typedef typename CacheVec<CT>::v4 v4c;
+  constexpr int ES = (int)sizeof(CT);
+  const __amdgpu_buffer_rsrc_t kdres = __builtin_amdgcn_make_buffer_rsrc((void*)(kd + row0 * DIG_ROW), (short)0, kend * DIG_ROW, 0x00020000);
+  const __amdgpu_buffer_rsrc_t keres = __builtin_amdgcn_make_buffer_rsrc((void*)(ke + row0), (short)0, kend * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)Vctx, (short)0, kend * HD * ES, 0x00020000);
+  v4c vl[2];
+  int kel = 0;
+  // tile i's loads: the digit blocks b = w, w + 4, .. (buffer loads to LDS), two 4-element
+  // pieces of values per thread (registers), one exponent per thread of the first 16; keys past
+  // the chunk clamped to its last key (masked below)
+  auto gload = [&](int i) {
+    uint8_t* B = kbuf(i & 1);
+    const int keyk = min(k0 + 16 * i + col, kend - 1);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int blk = w + 4 * b;
+      if (blk < 2 * DIG_T)  // uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kdres, (__attribute__((address_space(3))) void*)(B + blk * 1024), 16,
+                                                 keyk * DIG_ROW + (blk >> 1) * 128 + 64 * (blk & 1) + 16 * quarter, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int p = tid + u * GQ_THREADS, row = p >> 5, c4 = p & 31;
+      const int key = min(k0 + 16 * i + row, kend - 1);
+      vl[u] = CacheVec<CT>::load(vres, (key * HD + 4 * c4) * ES);
+    }
+    if (tid < 16) kel = (int)__builtin_amdgcn_raw_buffer_load_b32(keres, min(k0 + 16 * i + tid, kend - 1) * 4, 0, 0);
+  };
+  auto lstore = [&](int i) {
+    uint8_t* B = kbuf(i & 1);
+    double* V = (double*)(B + GQ_KD);
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int p = tid + u * GQ_THREADS, row = p >> 5, c4 = p & 31;
+      *(v4d*)(V + row * GQ_VS + 4 * c4) = (v4d){(double)vl[u][0], (double)vl[u][1], (double)vl[u][2], (double)vl[u][3]};
+    }
+    if (tid < 16) ((int*)(B + GQ_KD + GQ_VB))[tid] = kel;
+  };
+  // the loads to LDS are counted by vmcnt but not waited for by the compiler: every wave waits
+  // for all of its loads before the barrier that publishes a tile (the memory clobber keeps the
+  // LDS reads below it)
+  auto publish = [&]() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+  gload(0);
+  lstore(0);
+  if (nt > 1) gload(1);
+  publish();
+
+  double m_run = -INFINITY, l_run = 0.0;
+  v4d acc[NI];
+#pragma unroll
+  for (int dt = 0; dt < NI; dt++) acc[dt] = (v4d){0.0, 0.0, 0.0, 0.0};
+  for (int i = 0; i < nt; i++) {
+    const uint8_t* B = kbuf(i & 1);
+    const double* V = (const double*)(B + GQ_KD);
+    const int* KE = (const int*)(B + GQ_KD + GQ_VB);
+    const int nvalid = min(16, kend - (k0 + 16 * i));
+    // the 28 digit pairs t + u <= 6, the pairs of one diagonal into one exact int32 sum
+    v4i dacc[DIG_T];
+#pragma unroll
+    for (int d = 0; d < DIG_T; d++) dacc[d] = (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+      for (int u = 0; u < DIG_T; u++) {
+        const v4i kdv = *(const v4i*)(B + (2 * u + hh) * 1024 + lane * 16);
+#pragma unroll
+        for (int t = 0; t + u < DIG_T; t++)
+          dacc[t + u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kdv, qdr[t][hh], dacc[t + u], 0, 0, 0);
+      }
+    // accumulator slot r: key 4*quarter + r, query col (int32 16x16 rows are contiguous)
+    double p[4], mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int key = 4 * quarter + r;
+      double S = (double)dacc[DIG_T - 1][r];
+#pragma unroll
+      for (int d = DIG_T - 2; d >= 0; d--) S = __builtin_fma(S, 0.0078125, (double)dacc[d][r]);
+      const double sc = ldexp(S, eq + KE[key] - 14) * (double)a.scale;
+      p[r] = key < nvalid ? (!WIN || k0 + 16 * i + key >= kmin ? sc : -1e300) : -INFINITY;
+      mx = fmax(mx, p[r]);
+    }
+    mx = cross4_max_f64(mx);  // the same query's slots in the other three lane rows
+    const double m_new = fmax(m_run, mx);
+    double ps = 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      p[r] = exp(p[r] - m_new);
+      ps += p[r];
+    }
+    ps = cross4_sum_f64(ps);
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+      const double corr = exp(m_run - m_new);
+      l_run = l_run * corr + ps;
+#pragma unroll
+      for (int dt = 0; dt < NI; dt++) acc[dt] *= corr;
+    } else {
+      l_run = l_run + ps;
+    }
+    m_run = m_new;
+    // Y^T[d][q] += V^T . P^T: step k pairs slot k (key 4*quarter + k) with that key's values,
+    // A = V[key][64*d4 + 4*col + e] for output tile 4*d4 + e
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+#pragma unroll
+      for (int d4 = 0; d4 < ND; d4++) {
+        const v4d vv = *(const v4d*)(V + (4 * quarter + k) * GQ_VS + 64 * d4 + 4 * col);
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          acc[4 * d4 + e] = __builtin_amdgcn_mfma_f64_16x16x4f64(vv[e], p[k], acc[4 * d4 + e], 0, 0, 0);
+      }
+    }
+    // tile i + 1's values into its buffer (its digits landed during tile i), then the barrier
+    // that ends tile i, then tile i + 2 into the buffer tile i leaves
+    if (i + 1 < nt) lstore(i + 1);
+    publish();
+    if (i + 2 < nt) gload(i + 2);
+  }
+
+  // the partial through LDS (the buffers are free after the loop's last barrier, with no load
+  // in flight), so the stores are whole rows: wave w's acc at [w][query][HD + 1]
+  double* A = (double*)lds + (size_t)w * 16 * (HD + 1);
+#pragma unroll
+  for (int dt = 0; dt < NI; dt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++)  // slot r of tile dt: dim 64*(dt/4) + 16r + 4*quarter + dt%4
+      A[col * (HD + 1) + 64 * (dt >> 2) + 16 * r + 4 * quarter + (dt & 3)] = acc[dt][r];
+  const size_t prow0 = ((((size_t)s * a.kvh + g) * a.maxch + c) * GQ_REP + w) * 16;
+  if (quarter == 0 && col < a.B) {
+    ml[(prow0 + col) * 2] = m_run;
+    ml[(prow0 + col) * 2 + 1] = l_run;
+  }
+  for (int o = lane; o < 16 * HD; o += 64) {  // a wave's LDS accesses take effect in order
+    const int qq = o / HD, d = o % HD;
+    if (qq >= a.B) break;  // rows in order: the rest are past B too
+    part[(prow0 + qq) * HD + d] = A[qq * (HD + 1) + d];
+  }
+}
+
 // One workgroup per (q head, block row, sequence) finishes the row: it scores the block's own
 // keys (f64 dot products of the f32 query and keys, then the same scale), takes the common
 // maximum of those scores and of the chunks' maxima, and adds the block's values and the
@@ -431,9 +639,45 @@ static bool attn_shape_ok(const AttnShape& a) {
          (a.hd == 64 || a.hd == 128);
 }
 
+template <typename CT, bool WIN>
+static hipError_t attn_gqa_dig_inst(const AttnShape& a, const SeqInfo& si, int maxn, const int8_t* qd, const int* qe,
+                                    const CT* vc, const int8_t* kd, const int* ke, double* part, double* ml,
+                                    hipStream_t st) {
+  hipError_t e = allow_lds((const void*)k_attn_gqa_dig<CT, WIN>, GQ_LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_attn_gqa_dig<CT, WIN>), dim3(si.n * a.kvh * maxn), dim3(GQ_THREADS), GQ_LDS, st, a, si, maxn, qd,
+                     qe, vc, kd, ke, part, ml);
+  return hipGetLastError();
+}
+
+template <typename CT>
+static hipError_t attn_gqa_dig(const AttnShape& a, const SeqInfo& si, const int8_t* qd, const int* qe, const CT* vc,
+                               const int8_t* kd, const int* ke, double* part, double* ml, hipStream_t st) {
+  int maxn = 0;
+  bool win = false;
+  for (int i = 0; i < si.n; i++) {
+    const int nch = si.nctx[i] > 0 ? (si.nctx[i] + a.ck - 1) / a.ck : 0;
+    if (nch > maxn) maxn = nch;
+    if (si.nctx[i] > 0 && si.mask0[i] + a.B - 1 > 0) win = true;
+  }
+  if (maxn > a.maxch) return hipErrorInvalidValue;
+  if (maxn == 0) return hipSuccess;  // no sequence has context rows: the merge does it all
+  return win ? attn_gqa_dig_inst<CT, true>(a, si, maxn, qd, qe, vc, kd, ke, part, ml, st)
+             : attn_gqa_dig_inst<CT, false>(a, si, maxn, qd, qe, vc, kd, ke, part, ml, st);
+}
+
+bool attn_digit_scores(int nh, int kvh, int hd) { return hd == 128 && nh == GQ_REP * kvh; }
+
 hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const void* kc,
-                                   const void* vc, double* part, double* ml, hipStream_t st) {
+                                   const void* vc, const DigitRows* dig, double* part, double* ml, hipStream_t st) {
   if (!attn_shape_ok(a)) return hipErrorInvalidValue;
+  if (dig) {
+    if (!attn_digit_scores(a.nh, a.kvh, a.hd) || !dig->qd || !dig->qe || !dig->kd || !dig->ke)
+      return hipErrorInvalidValue;
+    if (a.kv_f16)
+      return attn_gqa_dig(a, si, dig->qd, dig->qe, (const _Float16*)vc, dig->kd, dig->ke, part, ml, st);
+    return attn_gqa_dig(a, si, dig->qd, dig->qe, (const float*)vc, dig->kd, dig->ke, part, ml, st);
+  }
   if (a.kv_f16) {
     const _Float16 *k = (const _Float16*)kc, *v = (const _Float16*)vc;
     return a.hd == 64 ? attn_partial_hd<64>(a, si, q, k, v, part, ml, st) : attn_partial_hd<128>(a, si, q, k, v, part, ml, st);

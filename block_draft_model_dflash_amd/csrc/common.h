@@ -118,16 +118,19 @@ hipError_t launch_copy_ssq(const float* x, float* h, int M, int N, double* ssq, 
 hipError_t launch_swiglu_act(const double* part, int S, int M, int Mpad, int I, bool quant, int8_t* xq, float* dxT,
                              float* xf, hipStream_t st);
 // q/k/v of the block rows from the fused projection partials [S][Mpad][qd + 2 kvd]:
-// q-norm / k-norm, then (rope) RoPE at si.pos0[m / B] + m % B.
+// q-norm / k-norm, then (rope) RoPE at si.pos0[m / B] + m % B; with qd / qe (head_dim 128) also
+// each query row's int8 digits [M][nh][7*128] and exponent [M][nh] (digits.h).
 hipError_t launch_qkv_epilogue(const double* part, int S, int Mpad, int M, int B, const SeqInfo& si, int nh, int kvh,
                                int hd, const float* q_norm, const float* k_norm, const float* inv_freq, float eps,
-                               bool rope, float* q, float* k, float* v, hipStream_t st);
+                               bool rope, float* q, float* k, float* v, int8_t* qd, int* qe, hipStream_t st);
 // Context rows into the cache from the all-layer K|V partials [S][Mpad][L * 2 kvd]; layer l's
-// keys are rotated when bit l of rot_mask is set (layers >= 64 always are).
+// keys are rotated when bit l of rot_mask is set (layers >= 64 always are).  kd / ke (head_dim
+// 128, else null): each key row's int8 digits [L][max_seqs][kvh][max_ctx][7][128] and exponent
+// [L][max_seqs][kvh][max_ctx] (digits.h), of the value the cache holds.
 hipError_t launch_kv_append(const double* part, int S, int Mpad, int n, int layers, int kvh, int hd,
                             const float* k_norms, const float* inv_freq, float eps, unsigned long long rot_mask,
                             long long pos0, int row0, int slot, int max_seqs, int max_ctx, bool f16, void* kc,
-                            void* vc, hipStream_t st);
+                            void* vc, int8_t* kd, int* ke, hipStream_t st);
 // n rows of one (layer, sequence) of the cache, every kv head, into out [n][kvh][hd] f32.
 hipError_t launch_read_cache(const void* cache, bool f16, size_t layer_elems, int layer, int seq, int row0, int n,
                              int kvh, int hd, int max_ctx, float* out, hipStream_t st);
@@ -142,8 +145,20 @@ struct AttnShape {
 // merge scores the block's own keys, combines them with a sequence's chunks per (q head, row)
 // and writes the f32 result (A8 into xq/dxT, or f32 xf).
 constexpr int ATTN_MAXCH = 64;  // context chunks per (sequence, kv head) at most
+// The digit rows of integer scores (digits.h): the block's queries qd [M][nh][7*128] with
+// exponents qe [M][nh], the layer's keys kd [slot][kvh][max_ctx][7*128] with ke [slot][kvh][max_ctx].
+struct DigitRows {
+  const int8_t* qd;
+  const int* qe;
+  const int8_t* kd;
+  const int* ke;
+};
+// whether a geometry scores with digits (the grouped-query kernel: head_dim 128, four q heads per
+// kv head); then the q/k epilogue and the append write the digit rows and dig is given here, else
+// dig is null and the scores are f64 from kc
+bool attn_digit_scores(int nh, int kvh, int hd);
 hipError_t launch_attention_chunks(const AttnShape& a, const SeqInfo& si, const float* q, const void* kc,
-                                   const void* vc, double* part, double* ml, hipStream_t st);
+                                   const void* vc, const DigitRows* dig, double* part, double* ml, hipStream_t st);
 hipError_t launch_attention_merge(const AttnShape& a, const SeqInfo& si, const float* q, const float* kb,
                                   const float* vb, const double* part, const double* ml, int Mpad, bool quant,
                                   int8_t* xq, float* dxT, float* xf, hipStream_t st);

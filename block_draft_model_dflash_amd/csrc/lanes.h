@@ -55,6 +55,14 @@ __device__ __forceinline__ float half32_max_f32(float x) {
   return fmaxf(__uint_as_float(lo), __uint_as_float(hi));
 }
 
+// maximum over the whole wave
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = half32_max_f32(x);
+  unsigned lo, hi;
+  swap32_u32(__float_as_uint(x), lo, hi);
+  return fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+}
+
 __device__ __forceinline__ double row16_sum_f64(double x) {
   x += dpp_f64<DPP_XOR1>(x);
   x += dpp_f64<DPP_XOR2>(x);

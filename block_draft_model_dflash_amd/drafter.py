@@ -9,8 +9,10 @@ import numpy as np
 from . import (DFLASH_F32, dflash_block_forward, dflash_block_forward_rows, dflash_block_hidden, dflash_create,
                dflash_ctx_append, dflash_ctx_dropped, dflash_ctx_pending, dflash_ctx_queue, dflash_ctx_reset,
                dflash_ctx_settle, dflash_ctx_span, dflash_ctx_truncate,
-               dflash_destroy, dflash_geometry, dflash_layer_weights, dflash_matrix, dflash_read_kv,
-               dflash_set_layer_options, dflash_set_stream, dflash_weights, dflash_workspace_bytes)
+               dflash_destroy, dflash_geometry, dflash_last_scores, dflash_layer_weights, dflash_matrix,
+               dflash_read_kv,
+               dflash_set_layer_options, dflash_set_score_mode, dflash_set_stream, dflash_weights,
+               dflash_workspace_bytes)
 
 GEOMETRY_FIELDS = ("layers", "hidden", "heads", "kv_heads", "head_dim", "intermediate", "vocab", "block", "n_taps",
                    "body_fmt", "fc_fmt", "head_fmt")
@@ -92,6 +94,14 @@ class Drafter:
         L = self.g.layers
         as_list = lambda x: None if x is None else [int(v) for v in np.broadcast_to(np.asarray(x), (L,))]
         dflash_set_layer_options(self.ctx, as_list(windows), as_list(rotary))
+
+    def set_score_mode(self, mode: int) -> None:
+        """How attention scores context keys: DFLASH_SCORES_AUTO, _F64 or _DIGITS."""
+        dflash_set_score_mode(self.ctx, mode)
+
+    def last_scores(self) -> int:
+        """What the last block call scored with (DFLASH_SCORES_F64 or _DIGITS)."""
+        return dflash_last_scores(self.ctx)
 
     def dropped(self, seq: int, layer: int) -> int:
         return dflash_ctx_dropped(self.ctx, seq, layer)

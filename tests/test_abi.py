@@ -88,9 +88,14 @@ def test_too_many_rows_refused():
 @pytest.mark.parametrize("f16", [0, 1])
 def test_cache_rows_within_32_bit_offsets(f16):
     """Attention addresses a (sequence, kv head)'s cache rows with 32-bit byte offsets: a
-    max_ctx whose rows reach 2^31 bytes is refused, one row less is accepted."""
+    max_ctx whose rows reach 2^31 bytes is refused, one row less is accepted.  Where the scores
+    come from digits (head_dim 128, four q heads per kv head) the keys' digit rows (7 x 128 bytes
+    a row) count too."""
     c = di.CONFIGS["small_q"].replace(kv_f16=bool(f16))
-    limit = (1 << 31) // (c.head_dim * (2 if f16 else 4))
+    row_bytes = c.head_dim * (2 if f16 else 4)
+    if c.head_dim == 128 and c.heads == 4 * c.kv_heads:
+        row_bytes = max(row_bytes, 7 * 128)
+    limit = -(-(1 << 31) // row_bytes)  # the first max_ctx whose rows reach 2^31 bytes
     g = geometry(c, limit - 1, 1)
     assert D.dflash_workspace_bytes(g) > 0
     with pytest.raises(D.DFlashError) as e:

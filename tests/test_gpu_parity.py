@@ -23,6 +23,12 @@ LONG = di.CONFIGS["qwen3_8b_long"]
 BATCH = di.CONFIGS["qwen3_8b_batch8"]
 
 
+def _scores(name):
+    import block_draft_model_dflash_amd as D
+
+    return getattr(D, "DFLASH_SCORES_" + name)
+
+
 def _pair(cfg, ctx, max_ctx, n_seqs=1, first=0, chunk=4096):
     from block_draft_model_dflash_amd import Drafter
 
@@ -188,6 +194,7 @@ def test_qwen3_8b_shaped_drafter():
         if i % 16 == 15:
             say(f"{cfg.key}: {i + 1} blocks")
     pooled.check(2e-3, 0.999, 1024)
+    assert gm.last_scores() == _scores("F64")  # 4096 context rows: the default scores in f64
 
 
 @pytest.mark.timeout(900)
@@ -207,6 +214,7 @@ def test_long_context_append_then_block():
         if step % 16 == 0:
             _kv_check(cfg, om, gm, 0, [(p, cfg.append_per_block)], 2e-3)
         _scale_blocks(cfg, om, gm, pooled, (0,), (p + cfg.append_per_block,), step)
+        assert gm.last_scores() == _scores("DIGITS")  # over 16384 context rows: digit scores
         if step % 16 == 15:
             say(f"{cfg.key}: {step + 1} steps")
     pooled.check(2e-3, 0.999, 1024)
@@ -224,6 +232,7 @@ def test_eight_sequences_batched():
     pooled = Pooled(cfg.key)
     for i in range(8):
         _scale_blocks(cfg, om, gm, pooled, seqs, (cfg.ctx,) * cfg.n_seqs, i)
+        assert gm.last_scores() == _scores("DIGITS")  # 65536 context rows in the call
         say(f"{cfg.key}: {i + 1} forwards")
     pooled.check(2e-3, 0.999, 1024)
     _blocks(cfg, om, gm, [((5, 2, 7), (cfg.ctx, cfg.ctx - 100, 4000), 8)], 2e-3, 0.999)
