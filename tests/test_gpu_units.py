@@ -125,10 +125,41 @@ def _check_gemm(fmt, rows, cols, m, splits):
     assert np.mean(got == ref32) >= 0.999
 
 
+# The production loops' integer accumulators, bit for bit: with every weight scale and activation
+# scale 1.0 each rescale term d_w * d_x * s_g is the group sum s_g itself, every f64 partial sum is
+# an integer below 2^53, and the f32 output below 2^24 is exact, so the product must equal the sum
+# over groups of the oracle's integer group sums exactly.  One case per path the product takes:
+# the K-split kernel (16 rows, few n-tiles), one and two k-waves per n-tile, eight n-tiles a
+# workgroup (16 rows, more than 1024 n-tiles; the head's K) and the row kernel (more than 16 rows).
+UNIT_SHAPES = [(96, 4096, 16, 0), (96, 4096, 16, 8), (48, 2560, 16, 1), (64, 4608, 16, 2), (16400, 1024, 16, 0),
+               (65600, 4096, 16, 0), (96, 4096, 48, 0), (80, 1024, 128, 0), (2048, 512, 100, 0)]
+
+
+@pytest.mark.parametrize("fmt", [di.Q4_32, di.Q8_32], ids=["q4", "q8"])
+@pytest.mark.parametrize("rows,cols,m,splits", UNIT_SHAPES)
+def test_gemm_integer_accumulators_exact(fmt, rows, cols, m, splits):
+    say(f"gemm unit scales fmt={fmt} rows={rows} cols={cols} m={m} splits={splits}")
+    rng = np.random.default_rng(rows + 5 * cols + m + fmt + splits)
+    mat = _matrix(rng, fmt, rows, cols)
+    mat["scales"] = np.ones_like(mat["scales"])
+    xq = rng.integers(-127, 128, (m, cols), dtype=np.int16).astype(np.int8)
+    want = oracle.group_sums(mat, xq).astype(np.int64).sum(axis=2)
+    assert np.abs(want).max() < 2 ** 24  # exact in f32
+    p = _packed(mat)
+    scratch = torch.empty(D.dflash_gemm_scratch_bytes(rows, cols, m, splits), dtype=torch.uint8, device="cuda")
+    y = torch.empty((m, rows), dtype=torch.float32, device="cuda")
+    gx, gd = _dev(xq), _dev(np.ones((m, cols // 32), np.float32))
+    D.dflash_gemm(fmt, p.data_ptr(), rows, cols, gx.data_ptr(), gd.data_ptr(), m, y.data_ptr(), splits,
+                  scratch.data_ptr(), _st())
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.int64), want)
+
+
 # thousands of n-tiles with 16 activation rows: workgroups of eight n-tiles (ragged: 1025 tiles
 # are not a whole number of eight-tile blocks)
 @pytest.mark.parametrize("fmt", [di.Q4_32, di.Q8_32], ids=["q4", "q8"])
-@pytest.mark.parametrize("rows,cols,m", [(16400, 2048, 16), (16400, 4096, 3)])
+# (65600 rows: 4100 n-tiles, more than four rounds of the grid, the head's K)
+@pytest.mark.parametrize("rows,cols,m", [(16400, 2048, 16), (16400, 4096, 3), (65600, 4096, 16), (65600, 4096, 5)])
 def test_gemm_many_tiles(fmt, rows, cols, m):
     _check_gemm(fmt, rows, cols, m, 0)
 
