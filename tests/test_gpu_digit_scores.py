@@ -1,8 +1,8 @@
 """Attention scored from int8 digit splits of the queries and keys (dflash_set_score_mode,
 DFLASH_SCORES_DIGITS) against the oracle, which scores in f64, on the cases the default mode
 leaves to the f64 kernel (contexts under 16384 rows): small contexts with ragged tiles, several
-sequences of different ranges in one call, windows and unrotated layers, truncation, an f16
-cache, and the 8B-shaped drafter.  Both modes give the correctly rounded f32 of the exact
+sequences of different ranges in one call, windows and unrotated layers, truncation, blocks cut
+to fewer rows with a head shortlist, an f16 cache, and the 8B-shaped drafter.  Both modes give the correctly rounded f32 of the exact
 attention sums, so they are held to the same bar as every block: logits max |d| <= 2e-3 * max
 |logit| and top-1 agreement >= 99.9%."""
 import numpy as np
@@ -87,6 +87,25 @@ def test_digit_scores_sequences_windows_truncation():
     for m in (om, gm):
         m.truncate(2, 90)
     _block(cfg, om, gm, (2, 1), (90, 521), 6)
+
+
+def test_digit_scores_cut_blocks_and_shortlist():
+    """Blocks cut to their first rows (fewer query rows than the 16 of a tile) and a head
+    shortlist, two sequences."""
+    cfg = SMALL.replace(n_seqs=2)
+    om, gm = _pair(cfg, 300, n_seqs=2)
+    _append(cfg, om, gm, 0, 0, 120)
+    _append(cfg, om, gm, 1, 40, 61)
+    for rows, head_rows in ((1, None), (5, 512), (8, None), (15, 16)):
+        h = np.ascontiguousarray(np.stack([di.make_block_input(cfg, s, rows) for s in (0, 1)])[:, :rows])
+        say(f"{cfg.key}: digit-scored cut block rows={rows} head_rows={head_rows}")
+        got = gm.block_forward([0, 1], [120, 101], h, head_rows=head_rows)
+        torch.cuda.synchronize()
+        ref = om.block_forward([0, 1], [120, 101], h, head_rows=head_rows)
+        assert got.shape == ref.shape
+        rel, top1 = logits_parity(got.cpu().numpy(), ref)
+        say(f"{cfg.key}: rel {rel:.3e} top1 {top1:.4f}")
+        assert rel <= 2e-3 and top1 >= 0.999
 
 
 def test_digit_scores_f16_cache():

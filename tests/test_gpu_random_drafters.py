@@ -2,7 +2,8 @@
 the oracle: shapes (hidden, heads, head_dim, intermediate, taps, vocab, block rows, sequences),
 formats (f32 or Q4_32/Q8_32), row convolutions, the f16 cache, waiting rows, per-layer windows
 and unrotated layers drawn per case; then appends, queued rows, truncations, settles and blocks
-(cut or whole, with or without a shortlist) at random anchors.  Integer state (spans, waiting
+(cut or whole, with or without a shortlist) at random anchors; three in four drafters whose geometry
+allows it (head_dim 128, four q heads per kv head) score attention from int8 digits.  Integer state (spans, waiting
 and dropped rows) must be equal after every call, the cache read back equal but for isolated
 one-unit-in-the-last-place elements (gpu_common.cache_match), and logits within
 max |d| <= 2e-3 * max |logit| (1e-5 for f32 drafters) with top-1 >= 99.9% over a case."""
@@ -58,6 +59,11 @@ def test_random_drafter_and_calls(seed):
     gm = Drafter(cfg, w, max_ctx=max_ctx, max_seqs=cfg.n_seqs)
     assert om.set_layer_options(windows, rotary) == 0
     gm.set_layer_options(windows, rotary)
+    if cfg.head_dim == 128 and cfg.heads == 4 * cfg.kv_heads and seed % 4 != 0:
+        from block_draft_model_dflash_amd import DFLASH_SCORES_DIGITS
+
+        say(f"case {seed}: scores from int8 digits")
+        gm.set_score_mode(DFLASH_SCORES_DIGITS)  # three in four of the cases whose geometry can take them
     tol = 1e-5 if cfg.body_fmt == di.F32 else 2e-3
     agree = []
 
