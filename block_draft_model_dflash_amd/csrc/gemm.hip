@@ -649,9 +649,9 @@ __global__ __launch_bounds__(512) void k_gemm_rows(const uint8_t* __restrict__ W
   const __amdgpu_buffer_rsrc_t xr = wave_rsrc((const uint8_t*)xq, Mpad * K);
   // NSET register sets of staged activations: chunk c's loads are issued NSET chunk steps
   // before the step that stores them (set c % NSET), so their latency is hidden behind that many
-  // steps of work.  Measured with weights read cold (µs, 128 rows, one set / four): head 556 /
-  // 527, gate|up 100 / 93, down 51 / 49; at 32 rows the head with eight n-tiles a workgroup is
-  // fastest with one set (158 / 167 with two) and the other products with two.
+  // steps of work.  With 64-row workgroups, weights read cold (µs, 128 rows, one set / four):
+  // head 556 / 527, gate|up 100 / 93, down 51 / 49; with 32-row ones (two workgroups a CU) one
+  // set for four n-tiles and two for two measured the same as two sets for all.
   constexpr int NSET = MT >= 4 ? 4 : MT == 2 && NTW >= 4 ? 1 : 2;
   uint4 avs[NSET][CH::PIECES];
   float dvs[NSET][CH::SCALES];
@@ -848,18 +848,19 @@ static hipError_t gemm_rows_inst(const void* W, int N, int K, const int8_t* xq, 
   return hipGetLastError();
 }
 
-// Shape of a product of more than 16 rows: 64 rows per workgroup (32 for up to 32 rows); four
-// n-tiles x two k-waves where there are many n-tiles (and for SwiGLU, which needs whole groups of
-// four), else two n-tiles x four k-waves so a product with few n-tiles still fills the chip.
+// Shape of a product of more than 16 rows: 32 rows per workgroup; four n-tiles x two k-waves
+// where there are many n-tiles (and for SwiGLU, which needs whole groups of four), else two
+// n-tiles x four k-waves so a product with few n-tiles still fills the chip.  At 32 rows the
+// kernel stays within 128 registers, so two workgroups share a CU and one's start (its first
+// weights) overlaps the other's stream; 64-row workgroups (one a CU) measured 6% slower on the
+// batched forward, 16-row ones 8% slower.
 template <int FMT>
 static hipError_t gemm_rows_fmt(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
                                 hipStream_t st) {
   const bool wide = o.epi == EPI_SWIGLU || N / 16 >= 2048;
   if (o.Mpad <= 16)
     return wide ? gemm_rows_inst<FMT, 1, 8, 1>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 1, 1, 8>(W, N, K, xq, dxT, o, st);
-  if (o.Mpad <= 32)
-    return wide ? gemm_rows_inst<FMT, 2, 4, 2>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 2, 2, 4>(W, N, K, xq, dxT, o, st);
-  return wide ? gemm_rows_inst<FMT, 4, 4, 2>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 4, 2, 4>(W, N, K, xq, dxT, o, st);
+  return wide ? gemm_rows_inst<FMT, 2, 4, 2>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 2, 2, 4>(W, N, K, xq, dxT, o, st);
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -957,7 +958,7 @@ hipError_t launch_gemm_q(int fmt, const void* W, int N, int K, const int8_t* xq,
   if ((o.epi == EPI_RESID || o.epi == EPI_CONV) && (!o.h || !o.ssq)) return hipErrorInvalidValue;
   if (o.epi == EPI_CONV && (!o.cd || !o.cbase || o.cB < 1 || 16 % o.cB || o.cgs < 1 || N % o.cgs || o.ckn < 1))
     return hipErrorInvalidValue;  // a block's rows within every 16-row group
-  // more than 16 rows: the row kernel (every weight superblock read once per 64 rows), unless a
+  // more than 16 rows: the row kernel (every weight superblock read once per 32 rows), unless a
   // specific layout is asked for or the epilogue is a row convolution's
   if ((layout < 0 && o.Mpad > 16 && o.epi != EPI_CONV) || layout == 8) {
     if (fmt == Q4) return gemm_rows_fmt<Q4>(W, N, K, xq, dxT, o, st);
