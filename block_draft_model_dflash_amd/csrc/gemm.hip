@@ -624,8 +624,10 @@ struct RowsChunk {
   static constexpr int SCALES = (KW * 4 * MR + 511) / 512;          // scales per thread
 };
 
+// (at most 128 registers: two workgroups a CU; only the Q8 product with two n-tiles x four k-waves
+// needs the cap, and spills two registers outside its loop)
 template <int FMT, int MT, int NTW, int KW>
-__global__ __launch_bounds__(512) void k_gemm_rows(const uint8_t* __restrict__ W, int N, int K,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_rows(const uint8_t* __restrict__ W, int N, int K,
                                                   const int8_t* __restrict__ xq, const float* __restrict__ dxT,
                                                   int RG, GemmOut o) {
   static_assert(NTW * KW == 8, "eight waves");
