@@ -850,19 +850,21 @@ static hipError_t gemm_rows_inst(const void* W, int N, int K, const int8_t* xq, 
   return hipGetLastError();
 }
 
-// Shape of a product of more than 16 rows: 32 rows per workgroup; four n-tiles x two k-waves
+// Shape of a product of more than 16 rows: 32 rows per workgroup; eight n-tiles x one k-wave
 // where there are many n-tiles (and for SwiGLU, which needs whole groups of four), else two
 // n-tiles x four k-waves so a product with few n-tiles still fills the chip.  At 32 rows the
 // kernel stays within 128 registers, so two workgroups share a CU and one's start (its first
 // weights) overlaps the other's stream; 64-row workgroups (one a CU) measured 6% slower on the
-// batched forward, 16-row ones 8% slower.
+// batched forward, 16-row ones 8% slower.  Batched, per forward: eight n-tiles x one k-wave
+// for the head 418 µs against 448 with four x two (gate|up the same); four x two for the
+// others 159 / 122 / 276 µs (qkv, o, down) against 144 / 110 / 230 with two x four.
 template <int FMT>
 static hipError_t gemm_rows_fmt(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
                                 hipStream_t st) {
   const bool wide = o.epi == EPI_SWIGLU || N / 16 >= 2048;
   if (o.Mpad <= 16)
     return wide ? gemm_rows_inst<FMT, 1, 8, 1>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 1, 1, 8>(W, N, K, xq, dxT, o, st);
-  return wide ? gemm_rows_inst<FMT, 2, 4, 2>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 2, 2, 4>(W, N, K, xq, dxT, o, st);
+  return wide ? gemm_rows_inst<FMT, 2, 8, 1>(W, N, K, xq, dxT, o, st) : gemm_rows_inst<FMT, 2, 2, 4>(W, N, K, xq, dxT, o, st);
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
