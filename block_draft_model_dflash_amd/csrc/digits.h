@@ -22,7 +22,8 @@ namespace dfl {
 constexpr int DIG_T = 7;                       // digits per element
 constexpr int DIG_ROW = DIG_T * 128;           // bytes of one 128-dim row's digits: [plane][dim]
 // context rows in a call from which the default mode scores with digits (below them the f64
-// kernel, with a workgroup per q head, is faster: measured at 4096 and 32768 rows)
+// kernel, with a workgroup per q head, is faster: on the 8B-shaped block with one sequence the
+// two cross between 12288 and 16384 rows)
 constexpr long DIG_AUTO_ROWS = 16384;
 
 // the exponent E of a row from its largest magnitude
