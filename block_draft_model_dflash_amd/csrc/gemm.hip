@@ -151,6 +151,8 @@ __device__ __forceinline__ void gemm_finish(double (&acc)[MT][4], const float (&
                                             int nt, int kw) {
   constexpr int MR = MT * 16, NT = 64 * NTW * KW;
   const int tid = threadIdx.x, lane = tid & 63, quarter = lane >> 4, row16 = lane & 15, Mpad = o.Mpad;
+  // output slot s = 4*mt + q of the accumulators (rows m0 + 16*mt + 4*quarter + q, column
+  // row16 of the n-tile) is finished by k-wave s % KW
   auto mine = [&](int s) { return KW == 1 || s % KW == kw; };
   if (KW > 1) {
     __syncthreads();
@@ -363,10 +365,6 @@ __global__ __launch_bounds__(64 * NTW * KW) void k_gemm_q(const uint8_t* __restr
 #pragma unroll
   for (int p = 0; p < RD; p++) super_load(rs, (kw + p * KW) * SBB, lane, r[p]);
   __builtin_amdgcn_sched_barrier(0);
-
-  // output slot s = 4*mt + q of the accumulators (rows m0 + 16*mt + 4*quarter + q, column
-  // row16 of the n-tile) is finished by k-wave s % KW
-  auto mine = [&](int s) { return KW == 1 || s % KW == kw; };
 
   // the residual rows the epilogue adds to (needed only at the end), loaded without a branch
   // (a branch around them would make every later wait count them as possibly missing): rows
