@@ -6,7 +6,7 @@ import ctypes as C
 
 import numpy as np
 
-from . import (DFLASH_F32, dflash_block_forward, dflash_block_forward_rows, dflash_block_hidden, dflash_create,
+from . import (dflash_block_forward, dflash_block_forward_rows, dflash_block_hidden, dflash_create,
                dflash_ctx_append, dflash_ctx_dropped, dflash_ctx_pending, dflash_ctx_queue, dflash_ctx_reset,
                dflash_ctx_settle, dflash_ctx_span, dflash_ctx_truncate,
                dflash_destroy, dflash_geometry, dflash_last_scores, dflash_layer_weights, dflash_matrix,

@@ -1,7 +1,6 @@
 """One drafter driven from two streams in turn.  Appends and blocks share the drafter's workspace
 (activations, partial sums, the cache), so a call on a new stream must wait for the work still in
 flight on the old one; the logits then equal the oracle's on every block."""
-import numpy as np
 import pytest
 
 import dflash_inputs as di
