@@ -2,7 +2,8 @@
 DFLASH_SCORES_DIGITS) against the oracle, which scores in f64, on the cases the default mode
 leaves to the f64 kernel (contexts under 16384 rows): small contexts with ragged tiles, several
 sequences of different ranges in one call, windows and unrotated layers, truncation, blocks cut
-to fewer rows with a head shortlist, an f16 cache, and the 8B-shaped drafter.  Both modes give the correctly rounded f32 of the exact
+to fewer rows with a head shortlist, an f16 cache, and the 8B-shaped drafter; and the default
+mode's switch at 16384 context rows a call.  Both modes give the correctly rounded f32 of the exact
 attention sums, so they are held to the same bar as every block: logits max |d| <= 2e-3 * max
 |logit| and top-1 agreement >= 99.9%."""
 import numpy as np
@@ -139,6 +140,36 @@ def test_digit_and_f64_scores_8b_shaped():
         assert gm.last_scores() == DFLASH_SCORES_DIGITS
         same += int(torch.equal(a, b))
     say(f"{cfg.key}: {same} of 4 blocks bit-identical between the two score modes")
+
+
+@pytest.mark.timeout(300)
+def test_default_mode_switches_at_16384_call_rows():
+    """The default mode scores a call with digits from 16384 context rows, counted over the
+    call's sequences: one sequence at 16383 / 16384 rows, then two whose rows add up to 16383 /
+    16384.  Each block's logits equal those of the same block with that mode forced (the same
+    kernels on the same inputs, with no atomics: bit for bit), and `last_scores` reports it."""
+    from block_draft_model_dflash_amd import (DFLASH_SCORES_AUTO, DFLASH_SCORES_DIGITS, DFLASH_SCORES_F64,
+                                              Drafter)
+
+    cfg = SMALL.replace(n_seqs=2)
+    gm = Drafter(cfg, weights_for(cfg), max_ctx=16400, max_seqs=2)
+    for seq, n in ((0, 16384), (1, 8192)):
+        for p0 in range(0, n, 4096):
+            gm.append(seq, p0, di.make_taps(cfg, seq, p0, 4096))
+    cases = [((0,), (16383,), DFLASH_SCORES_F64), ((0,), (16384,), DFLASH_SCORES_DIGITS),
+             ((0, 1), (8192, 8191), DFLASH_SCORES_F64), ((0, 1), (8192, 8192), DFLASH_SCORES_DIGITS)]
+    for i, (seqs, anchors, want) in enumerate(cases):
+        h = np.stack([di.make_block_input(cfg, s, i) for s in seqs])
+        say(f"{cfg.key}: default score mode, seqs={list(seqs)} anchors={list(anchors)}")
+        gm.set_score_mode(DFLASH_SCORES_AUTO)
+        auto = gm.block_forward(list(seqs), list(anchors), h).clone()
+        assert gm.last_scores() == want
+        gm.set_score_mode(want)
+        forced = gm.block_forward(list(seqs), list(anchors), h)
+        torch.cuda.synchronize()
+        assert gm.last_scores() == want
+        assert torch.equal(auto, forced)
+    gm.close()
 
 
 def test_score_mode_refused_where_the_geometry_cannot_take_it():
