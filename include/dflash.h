@@ -169,8 +169,12 @@ int dflash_ctx_pending(const dflash_ctx* c, int32_t seq, int64_t* n);
 int dflash_set_layer_options(dflash_ctx* c, const int32_t* windows, const int32_t* rotary);
 
 /* How the block-vs-context attention scores its context keys (the attention step of dflash.rs,
- * Drafter::block; every mode gives the correctly rounded f32 of the exact softmax-weighted sum,
- * so the results agree).  DFLASH_SCORES_F64: f64 products of the f32 queries and keys.
+ * Drafter::block).  Both modes round the f64-evaluated softmax-weighted sum once to f32; the
+ * scores' dot products lie within f64 rounding of the exact ones (F64) or within
+ * 2^-41 * 2^(Eq+Ek) of them, where 2^Eq and 2^Ek are the powers of two just above twice the
+ * two rows' largest magnitudes (DIGITS).  The outputs agree except where an exact value lies
+ * within that difference of an f32 rounding boundary.
+ * DFLASH_SCORES_F64: f64 products of the f32 queries and keys.
  * DFLASH_SCORES_DIGITS: exact int8 digit splits of the queries and keys (seven base-128 digits a
  * value) multiplied on the int8 matrix unit, the digit sums combined in f64; available where
  * head_dim is 128 and every kv head has four q heads, the key digits then kept beside the cache.
@@ -180,7 +184,8 @@ enum { DFLASH_SCORES_AUTO = 0, DFLASH_SCORES_F64 = 1, DFLASH_SCORES_DIGITS = 2 }
 int dflash_set_score_mode(dflash_ctx* c, int32_t mode);
 
 /* host *mode receives what the last block call scored its context keys with:
- * DFLASH_SCORES_F64 or DFLASH_SCORES_DIGITS (DFLASH_SCORES_AUTO before the first call). */
+ * DFLASH_SCORES_F64 or DFLASH_SCORES_DIGITS (DFLASH_SCORES_AUTO before the first call).
+ * A null ctx or mode: DFLASH_EINVAL. */
 int dflash_last_scores(const dflash_ctx* c, int32_t* mode);
 
 /* host *dropped receives how many of a sequence's oldest context rows layer `layer` dropped. */
