@@ -142,6 +142,25 @@ def test_digit_and_f64_scores_8b_shaped():
     say(f"{cfg.key}: {same} of 4 blocks bit-identical between the two score modes")
 
 
+@pytest.mark.timeout(600)
+def test_ragged_sequences_8b_shaped_both_modes():
+    """The 8B-shaped drafter with four sequences of 8192, 3000, 100 and 0 context rows in one
+    call (the longest sets the chunk size and count; the others' chunks past their rows, and every
+    chunk of the empty one, do nothing), then three of them with anchors inside their contexts:
+    f64 and digit scores each against the oracle."""
+    from block_draft_model_dflash_amd import DFLASH_SCORES_DIGITS, DFLASH_SCORES_F64
+
+    cfg = Q8B.replace(n_seqs=4)
+    om, gm = _pair(cfg, 8192 + 64, n_seqs=4, mode=DFLASH_SCORES_F64)
+    for seq, n in ((0, 8192), (1, 3000), (2, 100)):
+        _append(cfg, om, gm, seq, 0, n)
+    for i, (seqs, anchors) in enumerate((((0, 1, 2, 3), (8192, 3000, 100, 0)), ((2, 0, 1), (64, 5000, 2999)))):
+        gm.set_score_mode(DFLASH_SCORES_F64)
+        _, ref = _block(cfg, om, gm, seqs, anchors, i)
+        gm.set_score_mode(DFLASH_SCORES_DIGITS)
+        _block(cfg, om, gm, seqs, anchors, i, ref=ref)
+
+
 @pytest.mark.timeout(300)
 def test_default_mode_switches_at_16384_call_rows():
     """The default mode scores a call with digits from 16384 context rows, counted over the
