@@ -45,10 +45,11 @@ constexpr int ATTN_THREADS = 64 * ATTN_WAVES;
 // Chunks a sequence with n context rows takes (the block's own rows are the merge's part).
 __device__ __forceinline__ int attn_chunks(int nctx, int ck) { return nctx > 0 ? (nctx + ck - 1) / ck : 0; }
 
-// LDS of the combine: every wave's (max, sum) per query and its acc, rows HD + 1 doubles apart
+// LDS of the combine: every wave's (max, sum, weight) per query and its acc, rows HD + 1 doubles
+// apart, and one more (max, sum, weight) row for the common maximum
 template <int HD>
 constexpr size_t attn_comb_bytes() {
-  return (size_t)ATTN_WAVES * 16 * (HD + 1) * 8 + (size_t)ATTN_WAVES * 16 * 3 * 8;
+  return (size_t)ATTN_WAVES * 16 * (HD + 1) * 8 + (size_t)(ATTN_WAVES + 1) * 16 * 3 * 8;
 }
 // all of a workgroup's LDS: the combine, then the queries (16 rows of HD + 2 doubles)
 template <int HD>
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
   // finite), e_w = exp(m_w - M) (0 for a wave without tiles), L = sum e_w l_w,
   // acc = sum e_w acc_w
   double* A = (double*)lds;                   // [wave][query][HDP]
-  double* MLs = A + ATTN_WAVES * 16 * HDP;    // [wave][query]: m, l, then e
+  double* MLs = A + ATTN_WAVES * 16 * HDP;    // [wave][query]: m, l, then e (then M)
 #pragma unroll
   for (int dt = 0; dt < NI; dt++)
 #pragma unroll
@@ -219,23 +220,26 @@ __global__ __launch_bounds__(ATTN_THREADS) void k_attn_partial(AttnShape a, SeqI
     MLs[(w * 16 + col) * 3 + 1] = l_run;
   }
   __syncthreads();
-  if (tid < 16) {  // one thread per query: the weights and the sum
+  // one thread per (wave, query) takes that wave's weight, so the exps run side by side rather
+  // than eight after another in one thread; M is kept in the row past the waves'
+  if (tid < ATTN_WAVES * 16) {
+    const int qr = tid & 15, v = tid >> 4;
     double M = -INFINITY;
-    for (int v = 0; v < ATTN_WAVES; v++) M = fmax(M, MLs[(v * 16 + tid) * 3]);
+    for (int u = 0; u < ATTN_WAVES; u++) M = fmax(M, MLs[(u * 16 + qr) * 3]);
+    const double mv = MLs[(v * 16 + qr) * 3];
+    MLs[(v * 16 + qr) * 3 + 2] = mv == -INFINITY ? 0.0 : exp(mv - M);
+    if (v == 0) MLs[(ATTN_WAVES * 16 + qr) * 3] = M;
+  }
+  __syncthreads();
+  if (tid < 16) {  // one thread per query: the sum, in wave order (the loop below reads only e)
     double L = 0.0;
-    for (int v = 0; v < ATTN_WAVES; v++) {
-      const double mv = MLs[(v * 16 + tid) * 3];
-      const double e = mv == -INFINITY ? 0.0 : exp(mv - M);
-      MLs[(v * 16 + tid) * 3 + 2] = e;
-      L += MLs[(v * 16 + tid) * 3 + 1] * e;
-    }
+    for (int v = 0; v < ATTN_WAVES; v++) L += MLs[(v * 16 + tid) * 3 + 1] * MLs[(v * 16 + tid) * 3 + 2];
     const size_t prow = ((((size_t)s * a.kvh + g) * a.maxch + c) * rep + h) * 16 + tid;
     if (tid < a.B) {
-      ml[prow * 2] = M;
+      ml[prow * 2] = MLs[(ATTN_WAVES * 16 + tid) * 3];
       ml[prow * 2 + 1] = L;
     }
   }
-  __syncthreads();
   for (int o = tid; o < 16 * HD; o += ATTN_THREADS) {
     const int qq = o / HD, d = o % HD;
     if (qq >= a.B) break;  // rows in order: the rest are past B too
