@@ -1,7 +1,8 @@
 """The algorithmic bytes the bench divides by its times (the roofline's numerator), against the
 per-part sizes of the 8B-shaped workloads worked out by hand from their geometry: a Q4_32 group
 of 32 weights is 16 bytes of codes and a 2-byte f16 scale (18), a Q8_32 group 32 + 2 (34); the
-context's K/V rows are read in f32; the logits are written in f32.  CPU only."""
+context's K/V rows are read in f32; the logits are written in f32.  Also bench.py's refusal of
+more than one GPU.  CPU only."""
 import pytest
 
 import dflash_inputs as di
@@ -47,3 +48,17 @@ def test_batched_forward_bytes():
     assert ab["kv"] == 2_684_354_560
     assert ab["logits"] == 77_791_232
     assert ab["total"] / MB == pytest.approx(3966.01, abs=0.01)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU is measured: `--gpus 2` exits with status 2 and says why, before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout + r.stderr
+    assert not r.stdout.strip().startswith("{")  # no bench line
