@@ -441,7 +441,11 @@ struct KsSlot {
 };
 constexpr int KS_WAVES = 8, KS_RD = 4, KS_XSTR = 144;  // 16 waves or deeper rings measured slower
 constexpr int KS_BUF = 16 * KS_XSTR + 64 * 4;  // a wave's LDS: 16 rows of codes, 64 scales
-template <int FMT>
+// TURNS > 0: every wave runs exactly TURNS ring turns (K a multiple of the turn's 32 k-blocks, or
+// one turn for smaller K), as straight-line code, so the compiler counts the loads in flight
+// exactly and a slot waits only for its own; in a runtime loop it waits for every load at the
+// top of each turn, which drains the ring.  TURNS = 0: the runtime loop (other K).
+template <int FMT, int TURNS>
 __global__ __launch_bounds__(64 * KS_WAVES) void k_gemm_ks(const uint8_t* __restrict__ W, int N, int K,
                                                           const int8_t* __restrict__ xq,
                                                           const float* __restrict__ dxT, GemmOut o) {
@@ -478,7 +482,9 @@ __global__ __launch_bounds__(64 * KS_WAVES) void k_gemm_ks(const uint8_t* __rest
 
   double acc[1][4] = {{0.0, 0.0, 0.0, 0.0}};
   constexpr int STEP = KS_RD * KS_WAVES;
-  const int turns = (KB - kw + STEP - 1) / STEP;
+  const int turns = TURNS > 0 ? TURNS : (KB - kw + STEP - 1) / STEP;
+  constexpr int UNROLL = TURNS > 0 ? TURNS : 1;
+#pragma unroll UNROLL
   for (int t = 0; t < turns; t++) {
 #pragma unroll
     for (int p = 0; p < KS_RD; p++) {
@@ -498,25 +504,46 @@ __global__ __launch_bounds__(64 * KS_WAVES) void k_gemm_ks(const uint8_t* __rest
         acc[0][2] = __builtin_fma((double)sm[2], dw * (double)dx[2], acc[0][2]);
         acc[0][3] = __builtin_fma((double)sm[3], dw * (double)dx[3], acc[0][3]);
       }
-      // refill the slot one ring turn ahead (past the tile: zeros, no traffic)
+      // refill the slot one ring turn ahead (past the tile: zeros, no traffic); the barrier
+      // keeps the refill here, where it has a whole turn to arrive (unrolled, the scheduler
+      // would otherwise sink it next to its use)
       load(kw + (t + 1) * STEP + p * KS_WAVES, s);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   gemm_finish<FMT, 1, 1, KS_WAVES, false>(acc, hres, smem, o, N, 0, ntile, ntile, true, 0, kw);
 }
 
-template <int FMT>
-static hipError_t gemm_ks_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
-                               hipStream_t st) {
+template <int FMT, int TURNS>
+static hipError_t gemm_ks_turns(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
+                                hipStream_t st) {
   size_t lds = (size_t)KS_WAVES * KS_BUF;
   const size_t red = (size_t)KS_WAVES * 4 * 64 * 8;  // every k-wave's partials (after the loop)
   if (red > lds) lds = red;
-  const void* kern = (const void*)k_gemm_ks<FMT>;
+  const void* kern = (const void*)k_gemm_ks<FMT, TURNS>;
   hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemm_ks<FMT>, dim3((unsigned)(N / 16)), dim3(64 * KS_WAVES), lds, st, (const uint8_t*)W, N, K,
-                     xq, dxT, o);
+  hipLaunchKernelGGL((k_gemm_ks<FMT, TURNS>), dim3((unsigned)(N / 16)), dim3(64 * KS_WAVES), lds, st,
+                     (const uint8_t*)W, N, K, xq, dxT, o);
   return hipGetLastError();
+}
+
+// the turn count every wave shares, where it is one of the unrolled instances (K of 4096 and
+// below, 8192, 12288, 16384, 20480), else the runtime loop
+template <int FMT>
+static hipError_t gemm_ks_inst(const void* W, int N, int K, const int8_t* xq, const float* dxT, const GemmOut& o,
+                               hipStream_t st) {
+  constexpr int STEP = KS_RD * KS_WAVES;
+  const int KB = K >> 7;
+  const int turns = KB <= STEP ? 1 : KB % STEP == 0 ? KB / STEP : 0;
+  switch (turns) {
+    case 1: return gemm_ks_turns<FMT, 1>(W, N, K, xq, dxT, o, st);
+    case 2: return gemm_ks_turns<FMT, 2>(W, N, K, xq, dxT, o, st);
+    case 3: return gemm_ks_turns<FMT, 3>(W, N, K, xq, dxT, o, st);
+    case 4: return gemm_ks_turns<FMT, 4>(W, N, K, xq, dxT, o, st);
+    case 5: return gemm_ks_turns<FMT, 5>(W, N, K, xq, dxT, o, st);
+    default: return gemm_ks_turns<FMT, 0>(W, N, K, xq, dxT, o, st);
+  }
 }
 
 // The integer accumulators of the same tiles: sums[m][n][g] for every group (Q4 shifted back).
